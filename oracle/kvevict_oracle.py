@@ -1,0 +1,358 @@
+"""Float64 CPU oracle for the fixed-budget KV-cache evict-and-attend decode step.
+
+TEST INFRASTRUCTURE. Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or call this module. The library and
+its Python binding never do; the oracle shares no code with them (its inputs
+come from the separate ``synthetic`` input module).
+
+What it computes, step by step, in the pages' notation:
+
+* Scorer. KVpop ("KVpop - Key-Value Cache Compression with Predictive Online
+  Pruning"), section 3.3 "Stateless scorers" and Appendix E.1-E.2, Eq. (35)-(36):
+  a per-KV-head two-layer MLP over the concatenation x = [k; v] of a cached
+  token's key and value. Fast KVzip ("Fast KVzip: Efficient and Accurate LLM
+  Inference with Gated KV Eviction"), section 3.1 "Formulation": a per-KV-head
+  gate on the layer's hidden state with output in [0, 1] (here a linear map
+  followed by a sigmoid). Scores are ranked in float32 (KVpop Appendix F,
+  "Training details": top-k ranking and selection in float32).
+* Retention rule. KVpop section 3, Eq. (1) B = s + w + k; section 3.1 Eq. (4)
+  eligible set E(q) = {t | s <= t <= q - w}; Appendix C.1 Eq. (26) retained
+  set = sinks, recent window, and the top-k eligible tokens.
+* Periodic eviction. ForesightKV summary page ("ForesightKV: Optimizing KV
+  Cache Eviction for Reasoning Models by Learning Long-Term Contribution"),
+  "Methodology in plain English": the cache is checked every L new tokens;
+  when it reaches B + L, the recent tokens are protected and the lowest-scored
+  pairs are evicted back to the budget. Fast KVzip Appendix A.5: buffered
+  scoring of the pending tokens and eviction of as many entries.
+* Attention over the retained entries. KVpop Appendix C (decoding attends over
+  the compact cache) and Appendix D.1, Eq. (27)-(29): logits <q, k>/sqrt(d_k),
+  log-sum-exp normaliser, probabilities exp(logit - LSE).
+
+Readings where the pages leave a step open (also listed in the design notes):
+
+* The window holds the W most recent tokens including the newest one
+  (KVpop Appendix C.1, set 2: q - t < w), so eligible tokens satisfy
+  S <= t <= P - W for newest position P.
+* Eviction fires after prefill when n0 > B, and during decode when the cache
+  count n reaches B + L; it evicts n - B entries, so the cache holds B after
+  every eviction and B..B+L-1 between evictions.
+* Ties: among equal float32 scores the older (lower position) token is
+  evicted first; -0.0 is treated as +0.0. Non-finite scores are outside the
+  contract (asserted here).
+* Query head j reads KV head floor(j / G) (contiguous GQA groups).
+
+Parity pins: every function here is pinned by tests in
+``tests/test_oracle_pins.py`` to facts other than its own formula
+(hand-computed fixtures, library routines, brute force, closed forms and
+invariants). No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "Policy", "mlp_score", "gate_score", "score_to_f32", "select_keep",
+    "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
+    "closed_form_retained", "cache_bytes_per_token",
+]
+
+
+@dataclass(frozen=True)
+class Policy:
+    """Budget B, sinks S, window W and eviction length L (KVpop Eq. (1);
+    ForesightKV summary, periodic eviction with length L)."""
+
+    budget: int
+    sinks: int
+    window: int
+    evict_len: int
+
+    @property
+    def k(self) -> int:
+        """Long-range top-k budget k = B - s - w (KVpop Eq. (1))."""
+        return self.budget - self.sinks - self.window
+
+    def check(self) -> None:
+        if self.sinks < 0 or self.window < 0 or self.evict_len < 1:
+            raise ValueError("policy: S, W must be >= 0 and L >= 1")
+        if self.k < 0:
+            raise ValueError("policy: B must be >= S + W")
+
+
+# ---------------------------------------------------------------------------
+# Scorers
+# ---------------------------------------------------------------------------
+
+def _act(a: np.ndarray, act: str) -> np.ndarray:
+    if act == "relu":
+        return np.maximum(a, 0.0)
+    if act == "silu":
+        # SiLU(a) = a * sigmoid(a) (KVpop section 3.3 uses SiLU).
+        return a / (1.0 + np.exp(-a))
+    raise ValueError(act)
+
+
+def mlp_score(k: np.ndarray, v: np.ndarray, w1: np.ndarray, b1: np.ndarray,
+              w2: np.ndarray, b2: float, act: str = "relu") -> np.ndarray:
+    """Stateless head-wise MLP score of each token (KVpop section 3.3 and
+    Appendix E.2, Eq. (36)), input x = [k; v] (Appendix E.1, Eq. (35)).
+
+    k, v: [..., d]; w1: [hidden, 2d] (row j = input weights of hidden unit
+    j); b1: [hidden]; w2: [hidden]; b2: scalar. Returns float64 [...].
+    """
+    x = np.concatenate([np.asarray(k, np.float64), np.asarray(v, np.float64)],
+                       axis=-1)
+    a = x @ np.asarray(w1, np.float64).T + np.asarray(b1, np.float64)
+    h = _act(a, act)
+    return h @ np.asarray(w2, np.float64) + float(b2)
+
+
+def gate_score(hidden: np.ndarray, w: np.ndarray, b: float = 0.0
+               ) -> np.ndarray:
+    """Per-KV-head gate on a token's hidden state (Fast KVzip section 3.1,
+    g_l : R^D -> [0, 1]^H): sigmoid(w . x + b). hidden [..., D], w [D]."""
+    a = np.asarray(hidden, np.float64) @ np.asarray(w, np.float64) + float(b)
+    return 1.0 / (1.0 + np.exp(-a))
+
+
+def score_to_f32(s: np.ndarray) -> np.ndarray:
+    """Scores are ranked in float32 (KVpop Appendix F). -0.0 becomes +0.0."""
+    s32 = np.asarray(s, dtype=np.float64).astype(np.float32)
+    if not np.all(np.isfinite(s32)):
+        raise ValueError("non-finite score: outside the contract")
+    s32 = s32 + np.float32(0.0)  # -0.0 + 0.0 == +0.0 in round-to-nearest
+    return s32
+
+
+# ---------------------------------------------------------------------------
+# Selection and compaction
+# ---------------------------------------------------------------------------
+
+def select_keep(score32: np.ndarray, pos: np.ndarray, length: int,
+                n_keep: int, sinks: int, window: int) -> np.ndarray:
+    """Slots kept when a cache slice of ``length`` entries is cut to
+    ``n_keep`` entries.
+
+    Protected: slots [0, S) (sinks) and [length - W, length) (the recent
+    window). Candidates: slots [S, length - W), i.e. the eligible set E of
+    KVpop Eq. (4) restricted to the cache. The length - n_keep candidates
+    with the smallest (float32 score, position) are evicted; the rest are
+    kept (KVpop Eq. (26): top-k of the eligible tokens).
+
+    Returns the kept slot indices in ascending order (int64).
+    """
+    score32 = np.asarray(score32, dtype=np.float32)
+    pos = np.asarray(pos)
+    if n_keep >= length:
+        return np.arange(length, dtype=np.int64)
+    r = length - n_keep
+    lo, hi = sinks, length - window
+    if hi - lo < r:
+        raise ValueError("not enough eligible entries to evict")
+    cand = np.arange(lo, hi, dtype=np.int64)
+    s = score32[lo:hi] + np.float32(0.0)
+    order = np.lexsort((pos[lo:hi], s))      # ascending score, then position
+    evicted = np.zeros(hi - lo, dtype=bool)
+    evicted[order[:r]] = True
+    keep = np.concatenate([np.arange(0, lo, dtype=np.int64), cand[~evicted],
+                           np.arange(hi, length, dtype=np.int64)])
+    return keep
+
+
+def compact_slice(arrays: Sequence[np.ndarray], keep: np.ndarray
+                  ) -> List[np.ndarray]:
+    """Order-preserving compaction: new row i = old row keep[i] (KVpop
+    Appendix C: the decode cache holds only retained entries)."""
+    return [np.asarray(a)[keep].copy() for a in arrays]
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def attention_probs(q: np.ndarray, K: np.ndarray):
+    """Probabilities of the query heads q [G, d] over the rows K [n, d].
+
+    Logit l = <q, k> / sqrt(d_k) (KVpop Eq. (27)); LSE = log sum exp l
+    (Eq. (28)); p = exp(l - LSE) (Eq. (29)). The maximum logit is subtracted
+    before exponentiation; it cancels exactly in p and is added back to LSE.
+    Returns (p [G, n], lse [G]).
+    """
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    d = q.shape[-1]
+    logits = (q @ K.T) / np.sqrt(d)
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    tot = w.sum(axis=1, keepdims=True)
+    p = w / tot
+    lse = (m + np.log(tot))[:, 0]
+    return p, lse
+
+
+def decode_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray):
+    """Decode attention of G query heads over one KV head's retained rows:
+    out = sum_t p_t v_t. Returns (out [G, d], lse [G])."""
+    p, lse = attention_probs(q, K)
+    return p @ np.asarray(V, np.float64), lse
+
+
+# ---------------------------------------------------------------------------
+# One layer's cache under the policy (incremental form)
+# ---------------------------------------------------------------------------
+
+class OracleLayer:
+    """The decode-time cache of one attention layer, every (batch, KV head)
+    slice holding the same number of entries.
+
+    State per slice: K, V rows (float64 values of the stored dtype), float32
+    score and int64 absolute position, in ascending position order.
+    Scores are computed when a token is appended; the scorer is stateless so
+    this equals scoring the buffered tokens at eviction time.
+    """
+
+    def __init__(self, K0: np.ndarray, V0: np.ndarray, score0_32: np.ndarray,
+                 policy: Policy, group: int):
+        policy.check()
+        self.policy = policy
+        self.group = group
+        self.K = np.array(K0, dtype=np.float64)           # [b][H][n][d]
+        self.V = np.array(V0, dtype=np.float64)
+        self.score = np.array(score0_32, dtype=np.float32)  # [b][H][n]
+        b, H, n, _ = self.K.shape
+        self.pos = np.broadcast_to(np.arange(n, dtype=np.int64),
+                                   (b, H, n)).copy()
+        self.newest = n - 1           # P, absolute position of newest token
+        self.last_evict_newest = None  # P_e
+        self.evictions = 0
+
+    @property
+    def n(self) -> int:
+        return self.K.shape[2]
+
+    def _evict_to(self, n_keep: int) -> np.ndarray:
+        b, H = self.K.shape[:2]
+        keeps = np.empty((b, H, n_keep), dtype=np.int64)
+        for bi in range(b):
+            for h in range(H):
+                keeps[bi, h] = select_keep(self.score[bi, h], self.pos[bi, h],
+                                           self.n, n_keep, self.policy.sinks,
+                                           self.policy.window)
+        idx = keeps[..., None]
+        self.K = np.take_along_axis(self.K, idx, axis=2)
+        self.V = np.take_along_axis(self.V, idx, axis=2)
+        self.score = np.take_along_axis(self.score, keeps, axis=2)
+        self.pos = np.take_along_axis(self.pos, keeps, axis=2)
+        self.last_evict_newest = self.newest
+        self.evictions += 1
+        return keeps
+
+    def prefill_compress(self) -> Optional[np.ndarray]:
+        """One-shot compression after prefill when n0 > B (reading: compress
+        before the first decode step)."""
+        if self.n > self.policy.budget:
+            return self._evict_to(self.policy.budget)
+        return None
+
+    def append(self, k_new: np.ndarray, v_new: np.ndarray,
+               score_new_32: np.ndarray) -> None:
+        """Append the newest token (k, v [b][H][d], score [b][H])."""
+        self.newest += 1
+        self.K = np.concatenate([self.K, np.asarray(k_new, np.float64)[:, :, None]], 2)
+        self.V = np.concatenate([self.V, np.asarray(v_new, np.float64)[:, :, None]], 2)
+        self.score = np.concatenate(
+            [self.score, np.asarray(score_new_32, np.float32)[:, :, None]], 2)
+        b, H = self.K.shape[:2]
+        self.pos = np.concatenate(
+            [self.pos, np.full((b, H, 1), self.newest, dtype=np.int64)], 2)
+
+    def maybe_evict(self) -> Optional[np.ndarray]:
+        """Evict n - B entries once the cache reaches B + L."""
+        p = self.policy
+        if self.n >= p.budget + p.evict_len:
+            return self._evict_to(p.budget)
+        return None
+
+    def attend(self, q: np.ndarray):
+        """q [b][H*G][d] -> out [b][H*G][d], lse [b][H*G]."""
+        b, H = self.K.shape[:2]
+        G = self.group
+        d = q.shape[-1]
+        out = np.empty((b, H * G, d))
+        lse = np.empty((b, H * G))
+        for bi in range(b):
+            for h in range(H):
+                o, l_ = decode_attention(q[bi, h * G:(h + 1) * G],
+                                         self.K[bi, h], self.V[bi, h])
+                out[bi, h * G:(h + 1) * G] = o
+                lse[bi, h * G:(h + 1) * G] = l_
+        return out, lse
+
+    def step(self, k_new, v_new, score_new_32, q):
+        """One decode step: append, evict if due, attend."""
+        self.append(k_new, v_new, score_new_32)
+        keeps = self.maybe_evict()
+        out, lse = self.attend(q)
+        return out, lse, keeps
+
+    def state(self) -> dict:
+        """A copy of the full decode state (checkpoint)."""
+        return {"K": self.K.copy(), "V": self.V.copy(),
+                "score": self.score.copy(), "pos": self.pos.copy(),
+                "newest": self.newest, "last": self.last_evict_newest,
+                "evictions": self.evictions}
+
+    @classmethod
+    def from_state(cls, st: dict, policy: Policy, group: int) -> "OracleLayer":
+        obj = cls.__new__(cls)
+        obj.policy, obj.group = policy, group
+        obj.K, obj.V = st["K"].copy(), st["V"].copy()
+        obj.score, obj.pos = st["score"].copy(), st["pos"].copy()
+        obj.newest, obj.last_evict_newest = st["newest"], st["last"]
+        obj.evictions = st["evictions"]
+        return obj
+
+
+# ---------------------------------------------------------------------------
+# Closed form of the retained set (second, independent oracle)
+# ---------------------------------------------------------------------------
+
+def closed_form_retained(score_by_pos32: np.ndarray, newest: int,
+                         last_evict_newest: Optional[int],
+                         policy: Policy) -> np.ndarray:
+    """Retained positions of one slice after any number of steps, without
+    simulating the loop (KVpop Eq. (26) in cache form).
+
+    With static scores, every evicted token is beaten by k eligible tokens
+    that stay eligible, so at the last eviction (newest position P_e) the
+    kept long-range tokens are exactly TopK_k(E(P_e)); tokens appended since
+    then are all still present. Result: sinks {0..S-1}, the top-k of
+    E(P_e) = {S <= t <= P_e - W} by (score desc, position desc), and every
+    position in (P_e - W, newest]. ``score_by_pos32`` holds the float32
+    score of every position 0..newest. Returns sorted positions.
+    """
+    S, W, k = policy.sinks, policy.window, policy.k
+    if last_evict_newest is None:
+        return np.arange(newest + 1, dtype=np.int64)
+    pe = last_evict_newest
+    elig = np.arange(S, pe - W + 1, dtype=np.int64)
+    s = np.asarray(score_by_pos32, np.float32)[elig] + np.float32(0.0)
+    order = np.lexsort((-elig, -s.astype(np.float64)))  # score desc, pos desc
+    top = elig[order[:k]]
+    recent = np.arange(max(pe - W + 1, S), newest + 1, dtype=np.int64)
+    return np.unique(np.concatenate([np.arange(S, dtype=np.int64), top,
+                                     recent]))
+
+
+# ---------------------------------------------------------------------------
+# Cache size per token
+# ---------------------------------------------------------------------------
+
+def cache_bytes_per_token(layers: int, n_kv: int, head_dim: int,
+                          elem_bytes: int) -> int:
+    """A GQA layer stores 2 * n_kv * d_h scalars per token (KV-Kaizen,
+    section 2.1 "Background and notation"); summed over layers."""
+    return layers * 2 * n_kv * head_dim * elem_bytes

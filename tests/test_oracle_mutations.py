@@ -1,0 +1,128 @@
+"""Planted mistakes in (copies of) the oracle must fail its pins.
+
+Each mutant below is the oracle function with one plausible mistake (a
+dropped term, a swapped operand, a reversed tie-break, an off-by-one). The
+pin checks from ``test_oracle_pins`` are run against it and must fail, which
+shows that the pins constrain every part of the oracle. Runs on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import test_oracle_pins as P
+
+
+def _fails(check, impl):
+    with pytest.raises(AssertionError):
+        check(impl)
+
+
+# --- scorer mutants --------------------------------------------------------
+
+def mlp_vk_order(k, v, w1, b1, w2, b2, act="relu"):
+    return O.mlp_score(v, k, w1, b1, w2, b2, act)
+
+
+def mlp_no_b1(k, v, w1, b1, w2, b2, act="relu"):
+    return O.mlp_score(k, v, w1, np.zeros_like(np.asarray(b1, float)), w2,
+                       b2, act)
+
+
+def mlp_no_activation(k, v, w1, b1, w2, b2, act="relu"):
+    x = np.concatenate([k, v], axis=-1)
+    return (x @ np.asarray(w1).T + b1) @ np.asarray(w2) + b2
+
+
+def gate_linear(hidden, w, b=0.0):
+    return np.asarray(hidden) @ np.asarray(w) + b
+
+
+@pytest.mark.parametrize("mutant", [mlp_vk_order, mlp_no_b1,
+                                    mlp_no_activation])
+def test_mlp_mutants_fail_hand_case(mutant):
+    _fails(P.check_mlp_hand, mutant)
+
+
+def test_mlp_no_activation_fails_one_hot():
+    _fails(P.check_mlp_one_hot, mlp_no_activation)
+
+
+def test_gate_without_sigmoid_fails():
+    _fails(P.check_gate, gate_linear)
+
+
+# --- selection mutants -----------------------------------------------------
+
+def select_newest_first_on_ties(score32, pos, length, n_keep, sinks, window):
+    if n_keep >= length:
+        return np.arange(length)
+    r = length - n_keep
+    lo, hi = sinks, length - window
+    order = np.lexsort((-np.asarray(pos[lo:hi]), score32[lo:hi]))
+    ev = np.zeros(hi - lo, bool)
+    ev[order[:r]] = True
+    return np.concatenate([np.arange(lo), np.arange(lo, hi)[~ev],
+                           np.arange(hi, length)])
+
+
+def select_window_off_by_one(score32, pos, length, n_keep, sinks, window):
+    return O.select_keep(score32, pos, length, n_keep, sinks,
+                         max(window - 1, 0))
+
+
+def select_evicts_highest(score32, pos, length, n_keep, sinks, window):
+    return O.select_keep(-np.asarray(score32), pos, length, n_keep, sinks,
+                         window)
+
+
+@pytest.mark.parametrize("mutant", [select_newest_first_on_ties,
+                                    select_window_off_by_one,
+                                    select_evicts_highest])
+def test_select_mutants_fail(mutant):
+    failed = 0
+    for check in (P.check_select_hand, P.check_select_brute_force):
+        try:
+            check(mutant)
+        except (AssertionError, ValueError):
+            failed += 1
+    assert failed >= 1
+
+
+def closed_form_oldest_kept(score_by_pos32, newest, last, policy):
+    S, W, k = policy.sinks, policy.window, policy.k
+    if last is None:
+        return np.arange(newest + 1)
+    elig = np.arange(S, last - W + 1)
+    s = np.asarray(score_by_pos32, np.float32)[elig]
+    order = np.lexsort((elig, -s.astype(np.float64)))   # pos ascending: wrong
+    top = elig[order[:k]]
+    recent = np.arange(max(last - W + 1, S), newest + 1)
+    return np.unique(np.concatenate([np.arange(S), top, recent]))
+
+
+def test_closed_form_mutant_fails():
+    _fails(P.check_incremental_equals_closed_form, closed_form_oldest_kept)
+
+
+# --- attention mutants -----------------------------------------------------
+
+def attn_no_scale(q, K, V):
+    d = q.shape[-1]
+    return O.decode_attention(np.asarray(q) * np.sqrt(d), K, V)
+
+
+def attn_k_v_swapped(q, K, V):
+    return O.decode_attention(q, V, K)
+
+
+def attn_unnormalised_lse(q, K, V):
+    out, lse = O.decode_attention(q, K, V)
+    logits = np.asarray(q) @ np.asarray(K).T / np.sqrt(q.shape[-1])
+    return out, logits.max(axis=1)
+
+
+@pytest.mark.parametrize("mutant", [attn_no_scale, attn_k_v_swapped,
+                                    attn_unnormalised_lse])
+def test_attention_mutants_fail(mutant):
+    _fails(P.check_attention_hand, mutant)
+    _fails(P.check_attention_vs_torch_sdpa, mutant)

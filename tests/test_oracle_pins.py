@@ -1,0 +1,435 @@
+"""Pins of the float64 oracle to facts other than its own formulas.
+
+Each check below compares the oracle with a hand-derived closed form, a
+library routine (numpy/scipy/torch on the CPU), brute force on tiny inputs,
+or an invariant the pages fix. The checks are written as functions of the
+implementation so that ``test_oracle_mutations.py`` can show that a planted
+mistake in the oracle makes them fail.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle as O
+import synthetic as syn
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Scorer pins
+# ---------------------------------------------------------------------------
+
+def check_mlp_hand(mlp_score):
+    g = golden()["mlp_relu"]
+    s = mlp_score(np.array(g["k"]), np.array(g["v"]), np.array(g["w1"]),
+                  np.array(g["b1"]), np.array(g["w2"]), g["b2"], "relu")
+    assert s == pytest.approx(g["expected"], abs=1e-15)
+
+
+def check_mlp_silu(mlp_score):
+    g = golden()["mlp_relu"]
+    a = np.array([1.0, -1.0, 2.5])          # pre-activations, by hand
+    silu = a * scipy.special.expit(a)       # library sigmoid
+    expected = float(np.dot(np.array(g["w2"]), silu) + g["b2"])
+    s = mlp_score(np.array(g["k"]), np.array(g["v"]), np.array(g["w1"]),
+                  np.array(g["b1"]), np.array(g["w2"]), g["b2"], "silu")
+    assert s == pytest.approx(expected, rel=1e-14)
+
+
+def check_mlp_one_hot(mlp_score):
+    # One-hot first layer + ReLU + unit second layer returns relu(x_i).
+    rng = np.random.default_rng(3)
+    d, hid = 8, 16
+    k = rng.standard_normal((50, d))
+    v = rng.standard_normal((50, d))
+    x = np.concatenate([k, v], axis=1)
+    for i in (0, 3, d, 2 * d - 1):
+        w1 = np.zeros((hid, 2 * d))
+        w1[5, i] = 1.0
+        w2 = np.zeros(hid)
+        w2[5] = 1.0
+        s = mlp_score(k, v, w1, np.zeros(hid), w2, 0.0, "relu")
+        np.testing.assert_array_equal(s, np.maximum(x[:, i], 0.0))
+
+
+def check_gate(gate_score):
+    g = golden()["gate"]
+    assert gate_score(np.array(g["hidden"]), np.array(g["w"]), g["b"]) == \
+        pytest.approx(g["expected"], abs=1e-15)
+    rng = np.random.default_rng(4)
+    h = rng.standard_normal((40, 64))
+    w = rng.standard_normal(64) / 8
+    np.testing.assert_allclose(gate_score(h, w, 0.3),
+                               scipy.special.expit(h @ w + 0.3), rtol=1e-14)
+
+
+def test_mlp_hand_case():
+    check_mlp_hand(O.mlp_score)
+
+
+def test_mlp_silu_vs_library_sigmoid():
+    check_mlp_silu(O.mlp_score)
+
+
+def test_mlp_one_hot_is_relu_of_input():
+    check_mlp_one_hot(O.mlp_score)
+
+
+def test_gate_hand_case_and_expit():
+    check_gate(O.gate_score)
+
+
+def test_score_to_f32_canonical_zero_and_rounding():
+    s = O.score_to_f32(np.array([-0.0, 0.0, 1.0 / 3.0]))
+    assert not np.signbit(s[0])
+    assert s[2] == np.float32(1.0 / 3.0)
+    with pytest.raises(ValueError):
+        O.score_to_f32(np.array([np.nan]))
+
+
+# ---------------------------------------------------------------------------
+# Selection pins
+# ---------------------------------------------------------------------------
+
+def brute_force_keep(scores, length, n_keep, S, W):
+    """Rank every candidate by counting how many candidates precede it in
+    (score, position) order; the r lowest ranks are evicted."""
+    if n_keep >= length:
+        return list(range(length))
+    r = length - n_keep
+    cands = list(range(S, length - W))
+    keep = []
+    for t in range(length):
+        if t < S or t >= length - W:
+            keep.append(t)
+            continue
+        rank = sum(1 for u in cands
+                   if (scores[u] < scores[t]) or
+                   (scores[u] == scores[t] and u < t))
+        if rank >= r:
+            keep.append(t)
+    return keep
+
+
+def check_select_hand(select_keep):
+    g = golden()["selection"]
+    sc = np.array(g["scores"], dtype=np.float32)
+    keep = select_keep(sc, np.arange(len(sc)), g["length"], g["n_keep"],
+                       g["sinks"], g["window"])
+    assert list(keep) == g["expected_keep"]
+
+
+def check_select_brute_force(select_keep):
+    alphabet = np.array([0.5, 1.0, 2.0], dtype=np.float32)
+    for S, W in ((0, 0), (1, 2), (2, 1)):
+        for m in range(0, 6):
+            length = S + W + m
+            for pattern in itertools.product(range(3), repeat=length):
+                sc = alphabet[list(pattern)]
+                pos = np.arange(length) + 100
+                for r in range(0, m + 1):
+                    n_keep = length - r
+                    got = list(select_keep(sc, pos, length, n_keep, S, W))
+                    assert got == brute_force_keep(sc, length, n_keep, S, W)
+
+
+def test_select_hand_case():
+    check_select_hand(O.select_keep)
+
+
+def test_select_matches_brute_force_all_tie_patterns():
+    check_select_brute_force(O.select_keep)
+
+
+def test_select_random_matches_brute_force():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        S, W = rng.integers(0, 4), rng.integers(0, 6)
+        m = rng.integers(0, 25)
+        length = S + W + m
+        sc = rng.integers(0, 5, size=length).astype(np.float32) * 0.25
+        r = rng.integers(0, m + 1)
+        got = list(O.select_keep(sc, np.arange(length), length, length - r,
+                                 S, W))
+        assert got == brute_force_keep(sc, length, length - r, S, W)
+
+
+def test_select_k_zero_keeps_sinks_and_window_only():
+    rng = np.random.default_rng(8)
+    sc = rng.standard_normal(40).astype(np.float32)
+    keep = O.select_keep(sc, np.arange(40), 40, 10, 4, 6)
+    assert list(keep) == [0, 1, 2, 3] + list(range(34, 40))
+
+
+def test_select_budget_above_length_keeps_all():
+    sc = np.ones(30, dtype=np.float32)
+    assert list(O.select_keep(sc, np.arange(30), 30, 64, 4, 8)) == \
+        list(range(30))
+
+
+def test_constant_scores_give_streaming_llm():
+    """Constant scores reduce the policy to sinks + most recent tokens
+    (StreamingLLM, KVpop section 2 'Heuristic eviction methods')."""
+    pol = O.Policy(budget=24, sinks=3, window=5, evict_len=4)
+    rng = np.random.default_rng(9)
+    n0, d = 40, 8
+    K0 = rng.standard_normal((1, 1, n0, d))
+    lay = O.OracleLayer(K0, K0, np.zeros((1, 1, n0), np.float32), pol, 1)
+    lay.prefill_compress()
+    expected = list(range(3)) + list(range(n0 - 21, n0))
+    assert list(lay.pos[0, 0]) == expected
+    for _ in range(13):
+        kn = rng.standard_normal((1, 1, d))
+        lay.append(kn, kn, np.zeros((1, 1), np.float32))
+        if lay.maybe_evict() is not None:
+            P = lay.newest
+            assert list(lay.pos[0, 0]) == list(range(3)) + \
+                list(range(P - 20, P + 1))
+
+
+# ---------------------------------------------------------------------------
+# Incremental loop vs closed form; invariants
+# ---------------------------------------------------------------------------
+
+def run_incremental(policy, n0, steps, scores_by_pos, seed=0, d=4):
+    """Drive OracleLayer with a given score per position (1 slice)."""
+    rng = np.random.default_rng(seed)
+    K0 = rng.standard_normal((1, 1, n0, d))
+    lay = O.OracleLayer(K0, K0, scores_by_pos[None, None, :n0], policy, 1)
+    history = []
+    lay.prefill_compress()
+    history.append((lay.newest, lay.last_evict_newest, lay.pos[0, 0].copy()))
+    for i in range(steps):
+        kn = rng.standard_normal((1, 1, d))
+        lay.append(kn, kn, scores_by_pos[n0 + i].reshape(1, 1))
+        lay.maybe_evict()
+        history.append((lay.newest, lay.last_evict_newest,
+                        lay.pos[0, 0].copy()))
+    return history
+
+
+def check_incremental_equals_closed_form(closed_form):
+    rng = np.random.default_rng(11)
+    for (B, S, W, L, n0) in ((20, 2, 4, 1, 30), (20, 2, 4, 5, 30),
+                             (16, 0, 3, 3, 10), (12, 3, 9, 2, 50),
+                             (32, 4, 8, 8, 31)):
+        pol = O.Policy(B, S, W, L)
+        steps = 60
+        for mode in ("cont", "ties"):
+            if mode == "cont":
+                sc = rng.standard_normal(n0 + steps).astype(np.float32)
+            else:
+                sc = rng.integers(0, 3, n0 + steps).astype(np.float32)
+            for newest, pe, kept in run_incremental(pol, n0, steps, sc):
+                cf = closed_form(sc[:newest + 1], newest, pe, pol)
+                np.testing.assert_array_equal(kept, cf)
+
+
+def test_incremental_loop_equals_closed_form():
+    check_incremental_equals_closed_form(O.closed_form_retained)
+
+
+def test_invariants_over_config1_shape():
+    """Sinks and window are never evicted, count == B after every eviction,
+    positions strictly increasing (KVpop Eq. (1), Eq. (26))."""
+    w = syn.workload(1)
+    pol = O.Policy(w.budget, w.sinks, w.window, w.evict_len)
+    rng = np.random.default_rng(12)
+    n0 = w.n0
+    sc = rng.standard_normal(n0 + w.steps).astype(np.float32)
+    for newest, pe, kept in run_incremental(pol, n0, w.steps, sc):
+        assert np.all(np.diff(kept) > 0)
+        assert set(range(w.sinks)) <= set(kept)
+        assert set(range(newest - w.window + 1, newest + 1)) <= set(kept)
+        assert len(kept) <= w.budget + w.evict_len - 1
+        if pe == newest:
+            assert len(kept) == w.budget
+
+
+def test_checkpoint_resume_is_bitwise_identical():
+    pol = O.Policy(24, 2, 6, 4)
+    rng = np.random.default_rng(13)
+    n0, d, b, H, G = 40, 8, 2, 2, 2
+    K0 = rng.standard_normal((b, H, n0, d))
+    V0 = rng.standard_normal((b, H, n0, d))
+    s0 = rng.standard_normal((b, H, n0)).astype(np.float32)
+    steps = [(rng.standard_normal((b, H, d)), rng.standard_normal((b, H, d)),
+              rng.standard_normal((b, H)).astype(np.float32),
+              rng.standard_normal((b, H * G, d))) for _ in range(20)]
+    a = O.OracleLayer(K0, V0, s0, pol, G)
+    a.prefill_compress()
+    outs_a = [a.step(*s)[:2] for s in steps]
+    c = O.OracleLayer(K0, V0, s0, pol, G)
+    c.prefill_compress()
+    outs_c = [c.step(*s)[:2] for s in steps[:7]]
+    c2 = O.OracleLayer.from_state(c.state(), pol, G)
+    outs_c += [c2.step(*s)[:2] for s in steps[7:]]
+    for (oa, la), (oc, lc) in zip(outs_a, outs_c):
+        np.testing.assert_array_equal(oa, oc)
+        np.testing.assert_array_equal(la, lc)
+
+
+# ---------------------------------------------------------------------------
+# Attention pins
+# ---------------------------------------------------------------------------
+
+def check_attention_hand(decode_attention):
+    g = golden()["attention_two_rows"]
+    out, lse = decode_attention(np.array(g["q"]), np.array(g["K"]),
+                                np.array(g["V"]))
+    e = math.e
+    np.testing.assert_allclose(out[0], [e / (e + 1), 1 / (e + 1), 0, 0],
+                               rtol=1e-15, atol=1e-16)
+    assert lse[0] == pytest.approx(math.log(e + 1), rel=1e-15)
+
+
+def check_attention_vs_torch_sdpa(decode_attention):
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(14)
+    G, n, d = 4, 37, 16
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((n, d)) * 2
+    V = rng.standard_normal((n, d))
+    out, lse = decode_attention(q, K, V)
+    tq = torch.from_numpy(q)[None, :, None, :]           # [1, G, 1, d]
+    tk = torch.from_numpy(K)[None, None].expand(1, G, n, d).contiguous()
+    tv = torch.from_numpy(V)[None, None].expand(1, G, n, d).contiguous()
+    ref = F.scaled_dot_product_attention(tq, tk, tv)[0, :, 0, :].numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    logits = q @ K.T / np.sqrt(d)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(logits, axis=1),
+                               rtol=1e-13)
+
+
+def test_attention_hand_case():
+    check_attention_hand(O.decode_attention)
+
+
+def test_attention_equals_torch_sdpa_float64_and_logsumexp():
+    check_attention_vs_torch_sdpa(O.decode_attention)
+
+
+def test_attention_probabilities_sum_to_one():
+    rng = np.random.default_rng(15)
+    for n in (1, 2, 17, 300):
+        p, _ = O.attention_probs(rng.standard_normal((5, 32)) * 3,
+                                 rng.standard_normal((n, 32)) * 3)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+        assert np.all(p >= 0)
+
+
+def test_attention_single_row_and_identical_keys():
+    rng = np.random.default_rng(16)
+    q = rng.standard_normal((3, 8))
+    k = rng.standard_normal((1, 8))
+    v = rng.standard_normal((1, 8))
+    out, lse = O.decode_attention(q, k, v)
+    np.testing.assert_array_equal(out, np.repeat(v, 3, axis=0))
+    np.testing.assert_allclose(lse, (q @ k.T)[:, 0] / np.sqrt(8), rtol=1e-15)
+    K = np.repeat(k, 10, axis=0)
+    V = rng.standard_normal((10, 8))
+    out, _ = O.decode_attention(q, K, V)
+    np.testing.assert_allclose(out, np.repeat(V.mean(0, keepdims=True), 3, 0),
+                               rtol=1e-13, atol=1e-15)
+
+
+def test_attention_permutation_invariant():
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((4, 16))
+    K = rng.standard_normal((50, 16))
+    V = rng.standard_normal((50, 16))
+    perm = rng.permutation(50)
+    o1, l1 = O.decode_attention(q, K, V)
+    o2, l2 = O.decode_attention(q, K[perm], V[perm])
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13)
+
+
+def test_budget_above_length_equals_dense_attention_every_step():
+    """With B at or above the context length nothing is evicted and each
+    step's output equals dense attention over the whole history."""
+    rng = np.random.default_rng(18)
+    b, H, G, d, n0 = 1, 2, 3, 8, 12
+    pol = O.Policy(budget=64, sinks=2, window=4, evict_len=8)
+    K = rng.standard_normal((b, H, n0, d))
+    V = rng.standard_normal((b, H, n0, d))
+    lay = O.OracleLayer(K, V, rng.standard_normal((b, H, n0)).astype(
+        np.float32), pol, G)
+    assert lay.prefill_compress() is None
+    allK, allV = K.copy(), V.copy()
+    for _ in range(40):
+        kn, vn = rng.standard_normal((b, H, d)), rng.standard_normal((b, H, d))
+        q = rng.standard_normal((b, H * G, d))
+        out, lse, keeps = lay.step(kn, vn, rng.standard_normal((b, H)).astype(
+            np.float32), q)
+        allK = np.concatenate([allK, kn[:, :, None]], 2)
+        allV = np.concatenate([allV, vn[:, :, None]], 2)
+        if lay.n <= pol.budget + pol.evict_len - 1 and keeps is None:
+            for h in range(H):
+                for g in range(G):
+                    logits = allK[0, h] @ q[0, h * G + g] / np.sqrt(d)
+                    p = scipy.special.softmax(logits)
+                    np.testing.assert_allclose(out[0, h * G + g],
+                                               p @ allV[0, h], rtol=1e-12,
+                                               atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting pins (numbers printed on the pages)
+# ---------------------------------------------------------------------------
+
+def test_qwen3_4b_cache_is_4_5_gb_at_32k():
+    """ForesightKV summary, 'Main findings': 4.5 GB bf16 cache for one
+    Qwen3-4B instance at 32K tokens."""
+    per_tok = O.cache_bytes_per_token(36, 8, 128, 2)
+    assert per_tok == 144 * 1024
+    assert per_tok * 32768 == int(4.5 * 2 ** 30)
+
+
+def test_qwen25_14b_cache_is_192_kib_per_token():
+    """KV-Kaizen section 1: 192 KiB per token; 32 sequences of 8k tokens
+    fill 48 GiB."""
+    per_tok = O.cache_bytes_per_token(48, 8, 128, 2)
+    assert per_tok == 192 * 1024
+    assert 32 * 8192 * per_tok == 48 * 2 ** 30
+
+
+# ---------------------------------------------------------------------------
+# Input generator pins
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(19)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.integers(-5, 5, 100000)
+         ).astype(np.float32)
+    x[:4] = [1.00390625, 1.01171875, -1.00390625, 0.0]   # exact ties
+    ours = syn.round_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy(
+        ).view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_generator_is_deterministic_and_keyed():
+    w = syn.workload(2, batch=2, n0=64)
+    a = syn.initial_context(w, 0, 0)
+    b = syn.initial_context(w, 0, 0)
+    c = syn.initial_context(w, 1, 0)
+    np.testing.assert_array_equal(a["k0"].bits, b["k0"].bits)
+    assert not np.array_equal(a["k0"].bits, c["k0"].bits)
+    s0 = syn.step_inputs(w, 0, 0, 0)
+    s1 = syn.step_inputs(w, 0, 0, 1)
+    assert not np.array_equal(s0["q"].bits, s1["q"].bits)
+    assert a["k0"].shape == (2, 8, 64, 128)
