@@ -1,0 +1,231 @@
+/*
+ * libkvevict - fixed-budget KV-cache evict-and-attend decode step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every tensor argument is a plain device pointer into caller-owned
+ * memory (HIP device memory); shape, policy and scorer descriptors are
+ * plain host structs. The library allocates nothing, keeps no state between
+ * calls and never synchronises the device: every call validates its
+ * arguments on the host, enqueues kernels on `stream` and returns. Argument
+ * errors are reported by the returned status before anything is launched.
+ * Device faults (for example a dangling pointer) surface at the caller's next
+ * synchronisation.
+ *
+ * Method (the pages this library follows):
+ *  - KVpop ("KVpop - Key-Value Cache Compression with Predictive Online
+ *    Pruning"): per-KV-head budget B = s + w + k (section 3, Eq. 1); sink
+ *    tokens, a protected window of the w most recent tokens, and the top-k
+ *    eligible tokens E(q) = {t | s <= t <= q - w} (section 3.1, Eq. 4;
+ *    Appendix C.1, Eq. 26); stateless head-wise MLP scorer over [k; v]
+ *    (section 3.3, Appendix E.1-E.2, Eq. 35-36); decode attention directly
+ *    over the compact cache of retained entries (Appendix C), with logits
+ *    <q, k>/sqrt(d_k) and log-sum-exp normaliser (Appendix D.1, Eq. 27-29);
+ *    ranking in float32 (Appendix F).
+ *  - ForesightKV summary page ("ForesightKV: Optimizing KV Cache Eviction for
+ *    Reasoning Models by Learning Long-Term Contribution", "Methodology in
+ *    plain English"): periodic eviction with budget B and eviction length L;
+ *    when the cache reaches B + L the recent tokens are protected and the
+ *    lowest-scored pairs are evicted back to the budget.
+ *  - Fast KVzip ("Fast KVzip: Efficient and Accurate LLM Inference with Gated
+ *    KV Eviction"): per-KV-head gate on the layer's hidden state with output
+ *    in [0, 1] (section 3.1 "Formulation"); buffered scoring of the pending
+ *    tokens in parallel, then eviction of as many entries (section 3.1 and
+ *    Appendix A.5).
+ *
+ * Tensor layouts (row-major, innermost last):
+ *   K, V        [batch][n_kv_heads][capacity][head_dim]   kv_dtype
+ *   score       [batch][n_kv_heads][capacity]             float32
+ *   pos         [batch][n_kv_heads][capacity]             int32
+ *   q           [batch][n_kv_heads*group][head_dim]       kv_dtype
+ *   out         [batch][n_kv_heads*group][head_dim]       float32
+ *   lse         [batch][n_kv_heads*group]                 float32
+ *   k_new,v_new [batch][n_kv_heads][head_dim]             kv_dtype
+ *   keep_slots  [batch][n_kv_heads][n_keep]               int32, ascending
+ * Query head j reads KV head j / group (contiguous GQA groups).
+ * Every (batch, KV head) slice holds the same number of entries `len` in
+ * slots [0, len), in strictly increasing position order; the library keeps
+ * that order (compaction is order-preserving).
+ */
+#ifndef KVEVICT_H
+#define KVEVICT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVE_OK = 0,
+  KVE_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad range */
+  KVE_ERR_POLICY = 2,      /* B < S + W, L < 1, n_keep out of range */
+  KVE_ERR_CAPACITY = 3,    /* len or slot beyond capacity */
+  KVE_ERR_UNSUPPORTED = 4, /* head_dim, dtype, group or scorer shape */
+  KVE_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  KVE_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+} kve_status;
+
+typedef enum { KVE_F32 = 0, KVE_BF16 = 1 } kve_dtype;
+typedef enum { KVE_ACT_RELU = 0, KVE_ACT_SILU = 1 } kve_act;
+typedef enum { KVE_SCORER_MLP_KV = 0, KVE_SCORER_GATE_HIDDEN = 1 } kve_scorer_kind;
+
+/* Shape of one layer's cache. head_dim in {64, 128}; group in [1, 8];
+ * kv_dtype is a kve_dtype. capacity = slots per (batch, KV head) slice. */
+typedef struct {
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t capacity;
+  int32_t kv_dtype;
+} kve_shape;
+
+/* Retention policy: budget B, sinks S, window W, eviction length L.
+ * Requires B >= S + W >= 0 and L >= 1 (KVpop Eq. 1: k = B - S - W >= 0). */
+typedef struct {
+  int32_t budget;
+  int32_t sinks;
+  int32_t window;
+  int32_t evict_len;
+} kve_policy;
+
+/* Device pointers of one layer's cache (layouts above). */
+typedef struct {
+  void* k;
+  void* v;
+  float* score;
+  int32_t* pos;
+} kve_cache;
+
+/* Scorer weights (device pointers).
+ *  MLP over [k; v] (KVpop Eq. 35-36): in_dim = 2 * head_dim;
+ *    score = w2 . act(W1 x + b1) + b2, x = [k; v] (key first).
+ *    w1 [H][hidden][in_dim] in wdtype (row j: input weights of hidden unit j),
+ *    b1 [H][hidden] float32 or NULL, w2 [H][hidden] float32,
+ *    b2 [H] float32 or NULL. hidden in [1, 256]; wdtype == kv_dtype.
+ *  GATE on hidden states (Fast KVzip section 3.1): in_dim = D,
+ *    score = sigmoid(w1[h] . x + b1[h]); w1 [H][D] bf16, b1 [H] float32 or
+ *    NULL; hidden, w2, b2, act unused. D a multiple of 32, H <= 16. */
+typedef struct {
+  int32_t kind;   /* kve_scorer_kind */
+  int32_t act;    /* kve_act (MLP only) */
+  int32_t wdtype; /* kve_dtype of w1 */
+  int32_t in_dim;
+  int32_t hidden;
+  const void* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+} kve_scorer;
+
+/* Host-side decode state of one layer for kve_step (in/out).
+ *  len           entries in every slice, slots [0, len)
+ *  scored_upto   slots [0, scored_upto) hold scores; [scored_upto, len) are
+ *                pending (appended since the last scoring)
+ *  next_position absolute position given to the next appended token
+ *  evicted       set by kve_step: 1 if this step evicted, else 0 */
+typedef struct {
+  int32_t len;
+  int32_t scored_upto;
+  int32_t next_position;
+  int32_t evicted;
+} kve_decode_state;
+
+/* Bytes of workspace that kve_decode_attn / kve_step need for caches of up
+ * to max_len entries (split-K partial results and completion counters).
+ * Returns 0 on invalid arguments. */
+size_t kve_workspace_bytes(const kve_shape* shape, int32_t max_len);
+
+/* Zero-fill a workspace (once, before its first use; the library leaves
+ * the counter region zeroed again after every completed call). Uses a fill
+ * kernel, not a memset, so it may be recorded in a HIP graph. */
+kve_status kve_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* a1 Append (KVpop Appendix C): write one new token per slice into `slot`:
+ * K[b][h][slot] = k_new[b][h], V likewise, pos[b][h][slot] = position.
+ * Requires 0 <= slot < capacity. The score of the slot is left unset
+ * (pending) until kve_score covers it. */
+kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
+                      int32_t position, const void* k_new, const void* v_new,
+                      hipStream_t stream);
+
+/* a2 Score the slots [slot_begin, slot_end) of every slice into
+ * cache->score (float32). MLP reads the cached K, V rows of those slots
+ * (KVpop Eq. 35-36). GATE reads `hidden` [batch][slot_end-slot_begin][D]
+ * bf16, the hidden states of those tokens (Fast KVzip section 3.1);
+ * `hidden` must be NULL for MLP. Runs as a bf16 MFMA GEMM with float32
+ * accumulation (float32 VALU for float32 weights). */
+kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
+                     kve_cache* cache, int32_t slot_begin, int32_t slot_end,
+                     const void* hidden, hipStream_t stream);
+
+/* a3 Select (KVpop Eq. 4 and Eq. 26; ForesightKV periodic eviction): cut
+ * each slice of `len` entries to `n_keep`. Slots [0, S) and [len - W, len)
+ * are protected; among candidate slots [S, len - W) the len - n_keep with
+ * the smallest (float32 score, slot) keys are evicted - equal scores evict
+ * the older entry first, and -0.0 ranks as +0.0. Writes the kept slots in
+ * ascending order to keep_slots [batch][H][n_keep]. Requires
+ * 0 <= n_keep <= len <= capacity, and S + W <= n_keep when n_keep < len;
+ * n_keep == len writes the identity. Scores must be finite. */
+kve_status kve_select_evict(const kve_shape* shape, const kve_policy* policy,
+                            const kve_cache* cache, int32_t len,
+                            int32_t n_keep, int32_t* keep_slots,
+                            hipStream_t stream);
+
+/* a4 Compact in place, order-preserving (KVpop Appendix C): new slot i =
+ * old slot keep_slots[i] for K, V, score and pos, i < n_keep. keep_slots
+ * must be strictly ascending with keep_slots[i] < len <= capacity (as
+ * kve_select_evict writes it). Slots >= n_keep are left as they were. */
+kve_status kve_compact(const kve_shape* shape, kve_cache* cache, int32_t len,
+                       const int32_t* keep_slots, int32_t n_keep,
+                       hipStream_t stream);
+
+/* a5 Decode attention (KVpop Appendix C and D.1, Eq. 27-29) of the
+ * n_kv_heads*group query heads in q over slots [0, len) of their KV head:
+ * out = sum_t softmax_t(<q, k_t> / sqrt(d)) v_t, lse = log sum_t
+ * exp(<q, k_t> / sqrt(d)). Float32 math and output. lse may be NULL.
+ * Requires 1 <= len <= capacity and ws_bytes >= kve_workspace_bytes(shape,
+ * len) of a workspace prepared by kve_workspace_init. */
+kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
+                           int32_t len, const void* q, float* out, float* lse,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* a6 One decode step of one layer, stream-ordered: append the new token at
+ * slot state->len with position state->next_position; score the pending
+ * slots when an eviction is due or L of them have accumulated (buffered
+ * scoring, Fast KVzip section 3.1); when the cache reaches B + L, select
+ * and compact it back to B (keep_slots receives the kept slots); then
+ * attend over the cache. Updates *state on the host.
+ * GATE scorers: hidden_new [batch][D] is the new token's hidden state and
+ * hidden_buf [batch][L][D] (bf16, caller-owned) holds the pending tokens'
+ * hidden states between calls; both must be NULL for MLP.
+ * Requires capacity >= B + L and state->len < capacity. */
+kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
+                    const kve_scorer* scorer, kve_cache* cache,
+                    kve_decode_state* state, const void* k_new,
+                    const void* v_new, const void* hidden_new,
+                    void* hidden_buf, const void* q, float* out, float* lse,
+                    int32_t* keep_slots, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Static string naming a status. */
+const char* kve_status_str(kve_status status);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int32_t kve_version(void);
+
+/* Test hook, not for production use: on != 0 (the default) merges the
+ * split-K partials of kve_decode_attn / kve_step in the last workgroup of
+ * each slice; on == 0 uses a separate combine kernel instead. Results agree
+ * to float32 rounding. Process-wide; not thread-safe against concurrent
+ * calls. */
+void kve_debug_set_fused_combine(int32_t on);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVEVICT_H */

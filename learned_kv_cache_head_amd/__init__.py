@@ -1,0 +1,326 @@
+"""libkvevict: fixed-budget KV-cache evict-and-attend decode step on MI355X.
+
+Thin ctypes binding of the C ABI in ``include/kvevict.h`` (same entry point
+names). It only marshals arguments: torch tensors supply device memory and
+the current HIP stream; every step of the path runs in the library's HIP
+kernels. There is no CPU fallback: if ``_lib/libkvevict.so`` is missing the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+__all__ = [
+    "KveError", "Shape", "Policy", "CacheTensors", "Scorer", "DecodeState",
+    "load_library", "library_path", "kve_version", "kve_status_str",
+    "kve_workspace_bytes", "kve_workspace_init", "kve_append", "kve_score",
+    "kve_select_evict", "kve_compact", "kve_decode_attn", "kve_step",
+    "kve_debug_set_fused_combine", "F32", "BF16", "ACT_RELU", "ACT_SILU",
+    "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "alloc_workspace",
+]
+
+F32, BF16 = 0, 1
+ACT_RELU, ACT_SILU = 0, 1
+SCORER_MLP_KV, SCORER_GATE_HIDDEN = 0, 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "_lib", "libkvevict.so")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+class _Policy(ctypes.Structure):
+    _fields_ = [("budget", ctypes.c_int32), ("sinks", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("evict_len", ctypes.c_int32)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("score", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+
+
+class _Scorer(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("wdtype", ctypes.c_int32), ("in_dim", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("w1", ctypes.c_void_p),
+                ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p)]
+
+
+class _State(ctypes.Structure):
+    _fields_ = [("len", ctypes.c_int32), ("scored_upto", ctypes.c_int32),
+                ("next_position", ctypes.c_int32), ("evicted", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "kve_version": (_I, []),
+    "kve_status_str": (ctypes.c_char_p, [_I]),
+    "kve_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Shape), _I]),
+    "kve_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
+    "kve_append": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Cache), _I,
+                        _I, _P, _P, _P]),
+    "kve_score": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Scorer),
+                       ctypes.POINTER(_Cache), _I, _I, _P, _P]),
+    "kve_select_evict": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
+                              ctypes.POINTER(_Cache), _I, _I, _P, _P]),
+    "kve_compact": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Cache), _I,
+                         _P, _I, _P]),
+    "kve_decode_attn": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Cache),
+                             _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kve_step": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
+                      ctypes.POINTER(_Scorer), ctypes.POINTER(_Cache),
+                      ctypes.POINTER(_State), _P, _P, _P, _P, _P, _P, _P, _P,
+                      _P, ctypes.c_size_t, _P]),
+    "kve_debug_set_fused_combine": (None, [_I]),
+}
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libkvevict.so (built by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"libkvevict is not built ({p} missing); run "
+            "__graft_entry__.build() first")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+class KveError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kve_status_str(status)} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KveError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Host-side descriptors
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Shape:
+    batch: int
+    n_kv_heads: int
+    group: int
+    head_dim: int
+    capacity: int
+    kv_dtype: int  # F32 or BF16
+
+    def c(self) -> _Shape:
+        return _Shape(self.batch, self.n_kv_heads, self.group, self.head_dim,
+                      self.capacity, self.kv_dtype)
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.float32 if self.kv_dtype == F32 else torch.bfloat16
+
+
+@dataclass(frozen=True)
+class Policy:
+    budget: int
+    sinks: int
+    window: int
+    evict_len: int
+
+    def c(self) -> _Policy:
+        return _Policy(self.budget, self.sinks, self.window, self.evict_len)
+
+
+class CacheTensors:
+    """Device tensors of one layer's cache (layouts as in kvevict.h)."""
+
+    def __init__(self, k, v, score, pos):
+        self.k, self.v, self.score, self.pos = k, v, score, pos
+
+    @classmethod
+    def empty(cls, shape: Shape, device="cuda"):
+        import torch
+        b, H, cap, d = (shape.batch, shape.n_kv_heads, shape.capacity,
+                        shape.head_dim)
+        dt = shape.torch_dtype
+        return cls(torch.zeros((b, H, cap, d), dtype=dt, device=device),
+                   torch.zeros((b, H, cap, d), dtype=dt, device=device),
+                   torch.zeros((b, H, cap), dtype=torch.float32, device=device),
+                   torch.zeros((b, H, cap), dtype=torch.int32, device=device))
+
+    def c(self) -> _Cache:
+        return _Cache(_ptr(self.k), _ptr(self.v), _ptr(self.score),
+                      _ptr(self.pos))
+
+
+class Scorer:
+    """Scorer weights on the device plus their descriptor."""
+
+    def __init__(self, kind: int, w1, b1=None, w2=None, b2=None,
+                 act: int = ACT_RELU, hidden: int = 0, in_dim: int = 0,
+                 wdtype: Optional[int] = None):
+        import torch
+        self.kind, self.act = kind, act
+        self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
+        self.hidden, self.in_dim = hidden, in_dim
+        if wdtype is None:
+            wdtype = F32 if w1.dtype == torch.float32 else BF16
+        self.wdtype = wdtype
+
+    @classmethod
+    def mlp(cls, w1, w2, b1=None, b2=None, act: int = ACT_RELU):
+        """w1 [H][hidden][2d], w2 [H][hidden], b1 [H][hidden], b2 [H]."""
+        return cls(SCORER_MLP_KV, w1, b1, w2, b2, act=act,
+                   hidden=w1.shape[1], in_dim=w1.shape[2])
+
+    @classmethod
+    def gate(cls, w, b=None):
+        """w [H][D] bf16, b [H] float32."""
+        return cls(SCORER_GATE_HIDDEN, w, b, in_dim=w.shape[1])
+
+    def c(self) -> _Scorer:
+        return _Scorer(self.kind, self.act, self.wdtype, self.in_dim,
+                       self.hidden, _ptr(self.w1), _ptr(self.b1),
+                       _ptr(self.w2), _ptr(self.b2))
+
+
+@dataclass
+class DecodeState:
+    len: int
+    scored_upto: int
+    next_position: int
+    evicted: int = 0
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def kve_version() -> int:
+    return load_library().kve_version()
+
+
+def kve_status_str(status: int) -> str:
+    return load_library().kve_status_str(status).decode()
+
+
+def kve_workspace_bytes(shape: Shape, max_len: int) -> int:
+    cs = shape.c()
+    return load_library().kve_workspace_bytes(ctypes.byref(cs), max_len)
+
+
+def kve_workspace_init(ws, stream=None) -> None:
+    _check(load_library().kve_workspace_init(
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "kve_workspace_init")
+
+
+def alloc_workspace(shape: Shape, max_len: int, device="cuda", stream=None):
+    """Allocate (torch) and zero-fill (library fill kernel) a workspace."""
+    import torch
+    n = kve_workspace_bytes(shape, max_len)
+    if n == 0:
+        raise ValueError("invalid shape for workspace")
+    ws = torch.empty(n // 4, dtype=torch.int32, device=device)
+    kve_workspace_init(ws, stream)
+    return ws
+
+
+def kve_append(shape: Shape, cache: CacheTensors, slot: int, position: int,
+               k_new, v_new, stream=None) -> None:
+    cs, cc = shape.c(), cache.c()
+    _check(load_library().kve_append(
+        ctypes.byref(cs), ctypes.byref(cc), slot, position, _ptr(k_new),
+        _ptr(v_new), _stream(stream)), "kve_append")
+
+
+def kve_score(shape: Shape, scorer: Scorer, cache: CacheTensors,
+              slot_begin: int, slot_end: int, hidden=None,
+              stream=None) -> None:
+    cs, csc, cc = shape.c(), scorer.c(), cache.c()
+    _check(load_library().kve_score(
+        ctypes.byref(cs), ctypes.byref(csc), ctypes.byref(cc), slot_begin,
+        slot_end, _ptr(hidden), _stream(stream)), "kve_score")
+
+
+def kve_select_evict(shape: Shape, policy: Policy, cache: CacheTensors,
+                     length: int, n_keep: int, keep_slots,
+                     stream=None) -> None:
+    cs, cp, cc = shape.c(), policy.c(), cache.c()
+    _check(load_library().kve_select_evict(
+        ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(cc), length, n_keep,
+        _ptr(keep_slots), _stream(stream)), "kve_select_evict")
+
+
+def kve_compact(shape: Shape, cache: CacheTensors, length: int, keep_slots,
+                n_keep: int, stream=None) -> None:
+    cs, cc = shape.c(), cache.c()
+    _check(load_library().kve_compact(
+        ctypes.byref(cs), ctypes.byref(cc), length, _ptr(keep_slots), n_keep,
+        _stream(stream)), "kve_compact")
+
+
+def kve_decode_attn(shape: Shape, cache: CacheTensors, length: int, q, out,
+                    lse, ws, stream=None) -> None:
+    cs, cc = shape.c(), cache.c()
+    _check(load_library().kve_decode_attn(
+        ctypes.byref(cs), ctypes.byref(cc), length, _ptr(q), _ptr(out),
+        _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "kve_decode_attn")
+
+
+def kve_step(shape: Shape, policy: Policy, scorer: Scorer,
+             cache: CacheTensors, state: DecodeState, k_new, v_new, q, out,
+             lse, keep_slots, ws, hidden_new=None, hidden_buf=None,
+             stream=None) -> DecodeState:
+    """One decode step of one layer; updates and returns ``state``."""
+    cs, cp, csc, cc = shape.c(), policy.c(), scorer.c(), cache.c()
+    st = _State(state.len, state.scored_upto, state.next_position, 0)
+    _check(load_library().kve_step(
+        ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(csc),
+        ctypes.byref(cc), ctypes.byref(st), _ptr(k_new), _ptr(v_new),
+        _ptr(hidden_new), _ptr(hidden_buf), _ptr(q), _ptr(out), _ptr(lse),
+        _ptr(keep_slots), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "kve_step")
+    state.len, state.scored_upto = st.len, st.scored_upto
+    state.next_position, state.evicted = st.next_position, st.evicted
+    return state
+
+
+def kve_debug_set_fused_combine(on: bool) -> None:
+    load_library().kve_debug_set_fused_combine(1 if on else 0)

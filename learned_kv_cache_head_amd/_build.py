@@ -1,0 +1,84 @@
+"""Build libkvevict.so in-tree with hipcc for gfx950.
+
+Each HIP source is compiled to an object in ``_build/`` (in parallel), then
+linked into ``learned_kv_cache_head_amd/_lib/libkvevict.so``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "_lib")
+LIB = os.path.join(LIBDIR, "libkvevict.so")
+BUILD = os.path.join(ROOT, "_build")
+SOURCES = ["kvevict.hip", "attention.hip", "cache_ops.hip", "score.hip"]
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    # Packed FP32 instructions are left to no code path here.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc",
+                 shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature;
+    # that line is expected and dropped.
+    out = "\n".join(l for l in p.stdout.splitlines()
+                    if "is not a recognized feature" not in l)
+    return p.returncode, out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the shared library. Returns its
+    path. Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    cc = hipcc()
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+    def compile_one(src):
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        cmd = [cc, *COMMON_FLAGS, *inc, "-c", os.path.join(CSRC, src),
+               "-o", obj]
+        rc, out = _run(cmd)
+        return src, obj, rc, out, cmd
+
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    for src, obj, rc, out, cmd in results:
+        if verbose or rc != 0:
+            sys.stderr.write(f"[build] {' '.join(cmd)}\n{out}\n")
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src}")
+    tmp = LIB + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+           *[r[1] for r in results]]
+    rc, out = _run(cmd)
+    if verbose or rc != 0:
+        sys.stderr.write(f"[build] {' '.join(cmd)}\n{out}\n")
+    if rc != 0:
+        raise RuntimeError("link failed")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,101 @@
+// Internal launch interface between the C-ABI layer (kvevict.hip) and the
+// kernels. Not installed; the public interface is include/kvevict.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kve {
+
+// ---------------------------------------------------------------------------
+// Device helpers shared by the kernels.
+// ---------------------------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// Orderable 32-bit key of a float32 score: unsigned comparison of keys
+// equals numeric comparison of scores; -0.0 maps to the key of +0.0.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Launch descriptors.
+// ---------------------------------------------------------------------------
+
+struct AttnLaunch {
+  const void* k;        // cache base [batch][H][cap][D]
+  const void* v;
+  const void* q;        // [batch][H*G][D]
+  float* out;           // [batch][H*G][D]
+  float* lse;           // [batch][H*G] or null
+  float* partial;       // [batch][H*G][nsplit][D+2] (m, l, acc[D])
+  uint32_t* counters;   // [batch*H], zero on entry and on exit
+  int batch, H, G, D, cap, len;
+  int nsplit, rows_per_split;
+  int is_bf16;
+  int fused_combine;    // 1: last workgroup of a slice combines the splits
+  // Optional fused append of the newest token into slot new_slot.
+  int new_slot;         // -1: none
+  int new_pos;
+  const void* k_new;    // [batch][H][D]
+  const void* v_new;
+  void* k_store;        // cache base pointers for the append (same as k, v)
+  void* v_store;
+  int32_t* pos;         // [batch][H][cap]
+};
+
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+
+hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
+                         int D, int cap, int elem_bytes, int slot,
+                         int position, const void* k_new, const void* v_new,
+                         const void* hidden_new, void* hidden_buf,
+                         int hidden_dim, int hidden_rows, int hidden_row,
+                         hipStream_t s);
+
+hipError_t launch_select(const float* score, int slices, int cap, int len,
+                         int n_keep, int S, int W, int32_t* keep,
+                         hipStream_t s);
+
+hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
+                          int slices, int cap, int row_bytes,
+                          const int32_t* keep, int n_keep, hipStream_t s);
+
+struct MlpLaunch {
+  const void* k;         // cache base
+  const void* v;
+  float* score;          // [batch][H][cap]
+  const void* w1;        // [H][hidden][in_dim]
+  const float* b1;       // [H][hidden] or null
+  const float* w2;       // [H][hidden]
+  const float* b2;       // [H] or null
+  int batch, H, D, cap, hidden, act, is_bf16;
+  int slot_begin, slot_end;
+};
+hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s);
+
+struct GateLaunch {
+  const void* hidden;    // bf16 [batch][rows_stride][in_dim]
+  long long batch_stride;  // elements between batches of `hidden`
+  float* score;          // [batch][H][cap]
+  const void* w;         // bf16 [H][in_dim]
+  const float* b;        // [H] or null
+  int batch, H, cap, in_dim;
+  int slot_begin, slot_end;
+};
+hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace kve

@@ -1,0 +1,365 @@
+// C-ABI layer of libkvevict: argument validation, launch planning and the
+// fused decode step. Validation happens on the host before any launch; the
+// library never allocates and never synchronises the device.
+#include "../../include/kvevict.h"
+
+#include "kve_internal.h"
+
+namespace {
+
+constexpr int kMaxSplit = 256;
+constexpr int kTargetWorkgroups = 2048;  // 8 per CU on 256 CUs
+constexpr int kMinRowsPerSplit = 128;
+constexpr size_t kAlign = 256;
+
+bool g_fused_combine = true;  // separate combine kernel when false
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dtype) { return dtype == KVE_F32 ? 4 : 2; }
+
+kve_status check_shape(const kve_shape* s) {
+  if (!s) return KVE_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->n_kv_heads < 1 || s->capacity < 1 || s->group < 1)
+    return KVE_ERR_INVALID_ARG;
+  if (s->batch > 65535 || s->n_kv_heads > 65535) return KVE_ERR_UNSUPPORTED;
+  if (s->group > 8) return KVE_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return KVE_ERR_UNSUPPORTED;
+  if (s->kv_dtype != KVE_F32 && s->kv_dtype != KVE_BF16)
+    return KVE_ERR_UNSUPPORTED;
+  return KVE_OK;
+}
+
+kve_status check_policy(const kve_policy* p) {
+  if (!p) return KVE_ERR_INVALID_ARG;
+  if (p->sinks < 0 || p->window < 0 || p->evict_len < 1 || p->budget < 1)
+    return KVE_ERR_POLICY;
+  if ((long long)p->sinks + p->window > p->budget) return KVE_ERR_POLICY;
+  return KVE_OK;
+}
+
+kve_status check_cache(const kve_cache* c) {
+  if (!c || !c->k || !c->v || !c->score || !c->pos) return KVE_ERR_INVALID_ARG;
+  return KVE_OK;
+}
+
+// Split-K plan: enough workgroups to fill the chip, at least
+// kMinRowsPerSplit rows per split. Non-decreasing in len.
+int plan_nsplit(const kve_shape* s, int len) {
+  const long long slices = (long long)s->batch * s->n_kv_heads;
+  long long ns = (kTargetWorkgroups + slices - 1) / slices;
+  const long long by_rows = (len + kMinRowsPerSplit - 1) / kMinRowsPerSplit;
+  if (ns > by_rows) ns = by_rows;
+  if (ns > kMaxSplit) ns = kMaxSplit;
+  if (ns < 1) ns = 1;
+  return (int)ns;
+}
+
+struct WsLayout {
+  size_t counters_off, counters_bytes, partial_off, partial_bytes, total;
+};
+
+WsLayout ws_layout(const kve_shape* s, int nsplit) {
+  WsLayout w;
+  const size_t slices = (size_t)s->batch * s->n_kv_heads;
+  const size_t hq = slices * s->group;
+  w.counters_off = 0;
+  w.counters_bytes = align_up(slices * sizeof(uint32_t));
+  w.partial_off = w.counters_bytes;
+  w.partial_bytes =
+      nsplit > 1 ? align_up(hq * nsplit * (s->head_dim + 2) * sizeof(float)) : 0;
+  w.total = w.partial_off + w.partial_bytes;
+  return w;
+}
+
+kve_status from_hip(hipError_t e) { return e == hipSuccess ? KVE_OK : KVE_ERR_LAUNCH; }
+
+kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
+                     const void* q, float* out, float* lse, void* ws,
+                     size_t ws_bytes, int new_slot, int new_pos,
+                     const void* k_new, const void* v_new, hipStream_t stream) {
+  const int ns_plan = plan_nsplit(shape, len);
+  int rps = (len + ns_plan - 1) / ns_plan;
+  rps = (rps + 31) / 32 * 32;
+  const int nsplit = (len + rps - 1) / rps;
+  const WsLayout w = ws_layout(shape, ns_plan);
+  if (!ws || ws_bytes < w.total) return KVE_ERR_WORKSPACE;
+  kve::AttnLaunch a{};
+  a.k = cache->k;
+  a.v = cache->v;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.partial = (float*)((char*)ws + w.partial_off);
+  a.counters = (uint32_t*)((char*)ws + w.counters_off);
+  a.batch = shape->batch;
+  a.H = shape->n_kv_heads;
+  a.G = shape->group;
+  a.D = shape->head_dim;
+  a.cap = shape->capacity;
+  a.len = len;
+  a.nsplit = nsplit;
+  a.rows_per_split = rps;
+  a.is_bf16 = shape->kv_dtype == KVE_BF16;
+  a.fused_combine = g_fused_combine ? 1 : 0;
+  a.new_slot = new_slot;
+  a.new_pos = new_pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_store = cache->k;
+  a.v_store = cache->v;
+  a.pos = cache->pos;
+  return from_hip(kve::launch_attention(a, stream));
+}
+
+kve_status check_scorer(const kve_shape* shape, const kve_scorer* sc) {
+  if (!sc || !sc->w1) return KVE_ERR_INVALID_ARG;
+  if (sc->kind == KVE_SCORER_MLP_KV) {
+    if (sc->in_dim != 2 * shape->head_dim) return KVE_ERR_UNSUPPORTED;
+    if (sc->hidden < 1 || sc->hidden > 256) return KVE_ERR_UNSUPPORTED;
+    if (sc->wdtype != shape->kv_dtype) return KVE_ERR_UNSUPPORTED;
+    if (sc->act != KVE_ACT_RELU && sc->act != KVE_ACT_SILU)
+      return KVE_ERR_UNSUPPORTED;
+    if (!sc->w2) return KVE_ERR_INVALID_ARG;
+    return KVE_OK;
+  }
+  if (sc->kind == KVE_SCORER_GATE_HIDDEN) {
+    if (sc->wdtype != KVE_BF16) return KVE_ERR_UNSUPPORTED;
+    if (sc->in_dim < 32 || sc->in_dim % 32 != 0) return KVE_ERR_UNSUPPORTED;
+    if (shape->n_kv_heads > 16) return KVE_ERR_UNSUPPORTED;
+    return KVE_OK;
+  }
+  return KVE_ERR_UNSUPPORTED;
+}
+
+kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
+                      kve_cache* cache, int slot_begin, int slot_end,
+                      const void* hidden, long long hidden_batch_stride,
+                      hipStream_t stream) {
+  if (slot_end == slot_begin) return KVE_OK;
+  if (sc->kind == KVE_SCORER_MLP_KV) {
+    kve::MlpLaunch m{};
+    m.k = cache->k;
+    m.v = cache->v;
+    m.score = cache->score;
+    m.w1 = sc->w1;
+    m.b1 = sc->b1;
+    m.w2 = sc->w2;
+    m.b2 = sc->b2;
+    m.batch = shape->batch;
+    m.H = shape->n_kv_heads;
+    m.D = shape->head_dim;
+    m.cap = shape->capacity;
+    m.hidden = sc->hidden;
+    m.act = sc->act;
+    m.is_bf16 = shape->kv_dtype == KVE_BF16;
+    m.slot_begin = slot_begin;
+    m.slot_end = slot_end;
+    return from_hip(kve::launch_score_mlp(m, stream));
+  }
+  kve::GateLaunch g{};
+  g.hidden = hidden;
+  g.batch_stride = hidden_batch_stride;
+  g.score = cache->score;
+  g.w = sc->w1;
+  g.b = sc->b1;
+  g.batch = shape->batch;
+  g.H = shape->n_kv_heads;
+  g.cap = shape->capacity;
+  g.in_dim = sc->in_dim;
+  g.slot_begin = slot_begin;
+  g.slot_end = slot_end;
+  return from_hip(kve::launch_score_gate(g, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kve_version(void) { return 100; }
+
+const char* kve_status_str(kve_status s) {
+  switch (s) {
+    case KVE_OK: return "ok";
+    case KVE_ERR_INVALID_ARG: return "invalid argument";
+    case KVE_ERR_POLICY: return "invalid policy";
+    case KVE_ERR_CAPACITY: return "capacity exceeded";
+    case KVE_ERR_UNSUPPORTED: return "unsupported shape, dtype or scorer";
+    case KVE_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVE_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t kve_workspace_bytes(const kve_shape* shape, int32_t max_len) {
+  if (check_shape(shape) != KVE_OK || max_len < 1) return 0;
+  return ws_layout(shape, plan_nsplit(shape, max_len)).total;
+}
+
+kve_status kve_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || ws_bytes % 4 != 0) return KVE_ERR_INVALID_ARG;
+  return from_hip(kve::launch_fill_zero(ws, ws_bytes, stream));
+}
+
+kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
+                      int32_t position, const void* k_new, const void* v_new,
+                      hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if (!k_new || !v_new) return KVE_ERR_INVALID_ARG;
+  if (slot < 0 || slot >= shape->capacity) return KVE_ERR_CAPACITY;
+  return from_hip(kve::launch_append(
+      cache->k, cache->v, cache->pos, shape->batch, shape->n_kv_heads,
+      shape->head_dim, shape->capacity, elem_bytes(shape->kv_dtype), slot,
+      position, k_new, v_new, nullptr, nullptr, 0, 0, 0, stream));
+}
+
+kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
+                     kve_cache* cache, int32_t slot_begin, int32_t slot_end,
+                     const void* hidden, hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if ((st = check_scorer(shape, scorer)) != KVE_OK) return st;
+  if (slot_begin < 0 || slot_end < slot_begin) return KVE_ERR_INVALID_ARG;
+  if (slot_end > shape->capacity) return KVE_ERR_CAPACITY;
+  const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN;
+  if (gate != (hidden != nullptr)) return KVE_ERR_INVALID_ARG;
+  const long long stride = (long long)(slot_end - slot_begin) * scorer->in_dim;
+  return score_impl(shape, scorer, cache, slot_begin, slot_end, hidden, stride,
+                    stream);
+}
+
+kve_status kve_select_evict(const kve_shape* shape, const kve_policy* policy,
+                            const kve_cache* cache, int32_t len,
+                            int32_t n_keep, int32_t* keep_slots,
+                            hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_policy(policy)) != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if (!keep_slots) return KVE_ERR_INVALID_ARG;
+  if (len < 0 || n_keep < 0) return KVE_ERR_INVALID_ARG;
+  if (len > shape->capacity) return KVE_ERR_CAPACITY;
+  if (n_keep > len) return KVE_ERR_POLICY;
+  if (n_keep < len && (long long)policy->sinks + policy->window > n_keep)
+    return KVE_ERR_POLICY;
+  if (len == 0) return KVE_OK;
+  return from_hip(kve::launch_select(
+      cache->score, shape->batch * shape->n_kv_heads, shape->capacity, len,
+      n_keep, policy->sinks, policy->window, keep_slots, stream));
+}
+
+kve_status kve_compact(const kve_shape* shape, kve_cache* cache, int32_t len,
+                       const int32_t* keep_slots, int32_t n_keep,
+                       hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if (!keep_slots) return KVE_ERR_INVALID_ARG;
+  if (len < 0 || n_keep < 0 || n_keep > len) return KVE_ERR_INVALID_ARG;
+  if (len > shape->capacity) return KVE_ERR_CAPACITY;
+  if (n_keep == 0) return KVE_OK;
+  return from_hip(kve::launch_compact(
+      cache->k, cache->v, cache->score, cache->pos,
+      shape->batch * shape->n_kv_heads, shape->capacity,
+      shape->head_dim * elem_bytes(shape->kv_dtype), keep_slots, n_keep,
+      stream));
+}
+
+kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
+                           int32_t len, const void* q, float* out, float* lse,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if (!q || !out) return KVE_ERR_INVALID_ARG;
+  if (len < 1) return KVE_ERR_INVALID_ARG;
+  if (len > shape->capacity) return KVE_ERR_CAPACITY;
+  return attn_impl(shape, cache, len, q, out, lse, ws, ws_bytes, -1, 0,
+                   nullptr, nullptr, stream);
+}
+
+kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
+                    const kve_scorer* scorer, kve_cache* cache,
+                    kve_decode_state* state, const void* k_new,
+                    const void* v_new, const void* hidden_new,
+                    void* hidden_buf, const void* q, float* out, float* lse,
+                    int32_t* keep_slots, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_policy(policy)) != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if ((st = check_scorer(shape, scorer)) != KVE_OK) return st;
+  if (!state || !k_new || !v_new || !q || !out || !keep_slots)
+    return KVE_ERR_INVALID_ARG;
+  const int B = policy->budget, L = policy->evict_len;
+  if ((long long)B + L > shape->capacity) return KVE_ERR_CAPACITY;
+  const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN;
+  if (gate != (hidden_new != nullptr) || gate != (hidden_buf != nullptr))
+    return KVE_ERR_INVALID_ARG;
+  int len = state->len;
+  int scored = state->scored_upto;
+  if (len < 0 || scored < 0 || scored > len) return KVE_ERR_INVALID_ARG;
+  if (len >= shape->capacity) return KVE_ERR_CAPACITY;
+  if (len - scored >= L) return KVE_ERR_INVALID_ARG;  // pending buffer full
+  // The attention after this step needs the workspace for len + 1 rows at
+  // most (plan is non-decreasing in len).
+  const WsLayout w = ws_layout(shape, plan_nsplit(shape, len + 1));
+  if (!ws || ws_bytes < w.total) return KVE_ERR_WORKSPACE;
+
+  const int slot = len;
+  const int position = state->next_position;
+  const int new_len = len + 1;
+  const bool evict = new_len >= B + L;
+  const bool score_now = evict || (new_len - scored) >= L;
+
+  state->evicted = 0;
+  bool appended = false;
+  if (score_now || gate) {
+    // The new row must be in the cache before scoring or selection.
+    st = from_hip(kve::launch_append(
+        cache->k, cache->v, cache->pos, shape->batch, shape->n_kv_heads,
+        shape->head_dim, shape->capacity, elem_bytes(shape->kv_dtype), slot,
+        position, k_new, v_new, hidden_new, hidden_buf, scorer->in_dim, L,
+        slot - scored, stream));
+    if (st != KVE_OK) return st;
+    appended = true;
+  }
+  len = new_len;
+  if (score_now) {
+    st = score_impl(shape, scorer, cache, scored, len, hidden_buf,
+                    (long long)L * scorer->in_dim, stream);
+    if (st != KVE_OK) return st;
+    scored = len;
+  }
+  if (evict) {
+    st = from_hip(kve::launch_select(
+        cache->score, shape->batch * shape->n_kv_heads, shape->capacity, len, B,
+        policy->sinks, policy->window, keep_slots, stream));
+    if (st != KVE_OK) return st;
+    st = from_hip(kve::launch_compact(
+        cache->k, cache->v, cache->score, cache->pos,
+        shape->batch * shape->n_kv_heads, shape->capacity,
+        shape->head_dim * elem_bytes(shape->kv_dtype), keep_slots, B, stream));
+    if (st != KVE_OK) return st;
+    len = B;
+    scored = B;
+    state->evicted = 1;
+  }
+  st = attn_impl(shape, cache, len, q, out, lse, ws, ws_bytes,
+                 appended ? -1 : slot, position, k_new, v_new, stream);
+  if (st != KVE_OK) return st;
+  state->len = len;
+  state->scored_upto = scored;
+  state->next_position = position + 1;
+  return KVE_OK;
+}
+
+// Test hook: choose between the fused last-workgroup merge of the split-K
+// partials (default) and the separate combine kernel.
+void kve_debug_set_fused_combine(int32_t on) { g_fused_combine = on != 0; }
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Scorers: per-KV-head importance score of each pending cache slot.
+//
+//  * MLP over [k; v] (KVpop section 3.3 "Stateless scorers", Appendix
+//    E.1-E.2, Eq. 35-36): score = w2 . act(W1 [k; v] + b1) + b2, key first.
+//    For bf16 caches the first layer is a dense contraction
+//    (rows x 2d) x (2d x hidden) and runs on MFMA (v_mfma_f32_16x16x32_bf16,
+//    float32 accumulation); the hidden activations stay in float32 for the
+//    second layer. Float32 caches use a float32 VALU kernel.
+//  * Gate on hidden states (Fast KVzip section 3.1, g_l: R^D -> [0,1]^H):
+//    score = sigmoid(w_h . x + b_h), all H heads of a token at once as a
+//    (rows x D) x (D x H) MFMA contraction with H padded to 16.
+//
+// MFMA operand layout used here (16x16x32 bf16): lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each with 8 consecutive
+// contraction indices starting at 8 * (l / 16); the accumulator holds
+// C[4 * (l / 16) + i][l % 16], i = 0..3. A and B always use the same
+// contraction order, so only the row/column mapping matters.
+#include "kve_internal.h"
+
+namespace kve {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
+}
+
+__device__ __forceinline__ float activate(float a, int act) {
+  if (act == 0) return fmaxf(a, 0.f);
+  return a / (1.f + __expf(-a));  // SiLU
+}
+
+// ---------------------------------------------------------------------------
+// MLP scorer on MFMA (bf16 K/V and W1). One wave = 16 rows; 4 waves per
+// workgroup share one (tile, head, batch).
+// ---------------------------------------------------------------------------
+template <int D, int NB>
+__global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
+  constexpr int HID = NB * 16;
+  constexpr int IN = 2 * D;
+  constexpr int KSTEPS = IN / 32;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rows = p.slot_end - p.slot_begin;
+  const int r0 = blockIdx.x * 64 + wave * 16;
+  if (r0 >= rows) return;  // no workgroup barrier below
+  const int rrow = r0 + (lane & 15);
+  const int slot = p.slot_begin + (rrow < rows ? rrow : rows - 1);
+  const size_t slice = (size_t)b * p.H + h;
+  const uint16_t* krow = (const uint16_t*)p.k + (slice * p.cap + slot) * D;
+  const uint16_t* vrow = (const uint16_t*)p.v + (slice * p.cap + slot) * D;
+  const uint16_t* w1 = (const uint16_t*)p.w1 + (size_t)h * HID * IN;
+  const int kq = (lane >> 4) * 8;
+  const int ncol = lane & 15;
+
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int kidx = ks * 32 + kq;
+    const bf16x8_t A = (ks * 32 < D) ? load8(krow + kidx) : load8(vrow + kidx - D);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8_t B = load8(w1 + (size_t)(nb * 16 + ncol) * IN + kidx);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
+    }
+  }
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + ncol;
+    const float bias = p.b1 ? p.b1[(size_t)h * HID + n] : 0.f;
+    const float w2n = p.w2[(size_t)h * HID + n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[i] += activate(acc[nb][i] + bias, p.act) * w2n;
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], off);
+  if (ncol == 0) {
+    const float b2 = p.b2 ? p.b2[h] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * (lane >> 4) + i;
+      if (row < rows) p.score[slice * p.cap + p.slot_begin + row] = part[i] + b2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MLP scorer on the float32 VALU (float32 caches, or shapes the MFMA kernel
+// does not take). One thread per row; the row's [k; v] features in LDS;
+// weights are read with workgroup-uniform addresses.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(64) void mlp_valu_kernel(MlpLaunch p) {
+  extern __shared__ float xs[];  // [64][IN + 1]
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int t = threadIdx.x;
+  const int D = p.D;
+  const int IN = 2 * D;
+  const int rows = p.slot_end - p.slot_begin;
+  const int row = blockIdx.x * 64 + t;
+  const bool ok = row < rows;
+  const int slot = p.slot_begin + (ok ? row : rows - 1);
+  const size_t slice = (size_t)b * p.H + h;
+  float* x = xs + t * (IN + 1);
+  for (int i = 0; i < D; ++i) {
+    const size_t off = (slice * p.cap + slot) * D + i;
+    if constexpr (BF16) {
+      x[i] = __uint_as_float((uint32_t)((const uint16_t*)p.k)[off] << 16);
+      x[D + i] = __uint_as_float((uint32_t)((const uint16_t*)p.v)[off] << 16);
+    } else {
+      x[i] = ((const float*)p.k)[off];
+      x[D + i] = ((const float*)p.v)[off];
+    }
+  }
+  float s = p.b2 ? p.b2[h] : 0.f;
+  for (int j = 0; j < p.hidden; ++j) {
+    const size_t wo = ((size_t)h * p.hidden + j) * IN;
+    float a = p.b1 ? p.b1[(size_t)h * p.hidden + j] : 0.f;
+    for (int i = 0; i < IN; ++i) {
+      float w;
+      if constexpr (BF16) {
+        w = __uint_as_float((uint32_t)((const uint16_t*)p.w1)[wo + i] << 16);
+      } else {
+        w = ((const float*)p.w1)[wo + i];
+      }
+      a = fmaf(w, x[i], a);
+    }
+    s = fmaf(activate(a, p.act), p.w2[(size_t)h * p.hidden + j], s);
+  }
+  if (ok) p.score[slice * p.cap + slot] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Gate scorer on MFMA: one wave = 16 tokens x all H heads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rows = g.slot_end - g.slot_begin;
+  const int r0 = blockIdx.x * 64 + wave * 16;
+  if (r0 >= rows) return;
+  const int rrow = r0 + (lane & 15);
+  const int rc = rrow < rows ? rrow : rows - 1;
+  const uint16_t* x =
+      (const uint16_t*)g.hidden + (size_t)b * g.batch_stride + (size_t)rc * g.in_dim;
+  const int n = lane & 15;
+  const bool has_w = n < g.H;
+  const uint16_t* w = (const uint16_t*)g.w + (size_t)(has_w ? n : 0) * g.in_dim;
+  const int kq = (lane >> 4) * 8;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, u32x4{0u, 0u, 0u, 0u});
+  const int ksteps = g.in_dim / 32;
+#pragma unroll 8
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int kidx = ks * 32 + kq;
+    const bf16x8_t A = load8(x + kidx);
+    const bf16x8_t B = has_w ? load8(w + kidx) : zero;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+  }
+  if (has_w) {
+    const float bias = g.b ? g.b[n] : 0.f;
+    float* out = g.score + ((size_t)b * g.H + n) * g.cap + g.slot_begin;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * (lane >> 4) + i;
+      if (row < rows) out[row] = 1.f / (1.f + __expf(-(acc[i] + bias)));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
+  const int rows = m.slot_end - m.slot_begin;
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + 63) / 64, m.H, m.batch);
+  const bool mfma_ok = m.is_bf16 && (m.hidden % 16 == 0) && m.hidden <= 128 &&
+                       (m.D == 64 || m.D == 128);
+  if (mfma_ok) {
+#define KVE_MLP(DD, NBB)                                                    \
+  if (m.D == DD && m.hidden == NBB * 16) {                                  \
+    hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB>), grid, dim3(256), 0, s, m); \
+    return hipGetLastError();                                               \
+  }
+    KVE_MLP(128, 1) KVE_MLP(128, 2) KVE_MLP(128, 3) KVE_MLP(128, 4)
+    KVE_MLP(128, 5) KVE_MLP(128, 6) KVE_MLP(128, 7) KVE_MLP(128, 8)
+    KVE_MLP(64, 1) KVE_MLP(64, 2) KVE_MLP(64, 3) KVE_MLP(64, 4)
+    KVE_MLP(64, 5) KVE_MLP(64, 6) KVE_MLP(64, 7) KVE_MLP(64, 8)
+#undef KVE_MLP
+  }
+  const size_t lds = (size_t)64 * (2 * m.D + 1) * sizeof(float);
+  if (m.is_bf16) {
+    hipLaunchKernelGGL((mlp_valu_kernel<true>), grid, dim3(64), lds, s, m);
+  } else {
+    hipLaunchKernelGGL((mlp_valu_kernel<false>), grid, dim3(64), lds, s, m);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s) {
+  const int rows = g.slot_end - g.slot_begin;
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + 63) / 64, g.batch);
+  hipLaunchKernelGGL(gate_mfma_kernel, grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace kve

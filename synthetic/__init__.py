@@ -292,3 +292,20 @@ def step_inputs(w: Workload, seed: int, layer: int, step: int) -> dict:
         out["hidden_new"] = Stored(
             g.standard_normal((w.batch, w.hidden)).astype(np.float32), "bf16")
     return out
+
+
+def device_normal(shape, seed: int, key: tuple, dtype=None, device="cuda",
+                  scale: float = 1.0):
+    """N(0, scale^2) draws generated on the device by torch's Philox
+    generator, keyed by (seed, *key); rounded once to ``dtype`` (default
+    bf16). Used for the large workloads whose inputs are too big to draw on
+    the host."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    ss = np.random.SeedSequence([int(seed), *[int(x) for x in key]])
+    g = torch.Generator(device=device)
+    g.manual_seed(int(ss.generate_state(1, np.uint64)[0] & ((1 << 63) - 1)))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x.to(dtype)

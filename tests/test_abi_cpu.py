@@ -1,0 +1,182 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any
+launch (no call here reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import learned_kv_cache_head_amd as kve
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvevict.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kve.library_path()),
+                                reason="libkvevict.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kve_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kve_score", "kve_select_evict", "kve_compact",
+                     "kve_decode_attn", "kve_step", "kve_append",
+                     "kve_workspace_bytes", "kve_workspace_init",
+                     "kve_status_str"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kve.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_binding_covers_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(kve, name), f"binding lacks {name}"
+
+
+def test_version_and_status_strings():
+    assert kve.kve_version() >= 100
+    assert kve.kve_status_str(0) == "ok"
+    assert "policy" in kve.kve_status_str(2)
+    assert kve.kve_status_str(99) == "unknown status"
+
+
+def _lib():
+    return kve.load_library()
+
+
+def _shape(**kw):
+    d = dict(batch=2, n_kv_heads=8, group=4, head_dim=128, capacity=1152,
+             kv_dtype=kve.BF16)
+    d.update(kw)
+    return kve._Shape(**d)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation
+
+
+def _cache():
+    return kve._Cache(FAKE, FAKE, FAKE, FAKE)
+
+
+def test_workspace_bytes_host_math():
+    s = _shape()
+    n = _lib().kve_workspace_bytes(ctypes.byref(s), 1151)
+    # 16 slices -> ceil(2048/16) = 128 splits wanted, capped by rows: 9
+    nsplit = 9
+    counters = 256
+    partial = 2 * 32 * nsplit * 130 * 4
+    partial = (partial + 255) // 256 * 256
+    assert n == counters + partial
+    bad = _shape(head_dim=96)
+    assert _lib().kve_workspace_bytes(ctypes.byref(bad), 100) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 4), (dict(group=9), 4), (dict(kv_dtype=7), 4),
+    (dict(batch=0), 1), (dict(capacity=0), 1)])
+def test_decode_attn_rejects_bad_shapes(kw, status):
+    s, c = _shape(**kw), _cache()
+    st = _lib().kve_decode_attn(ctypes.byref(s), ctypes.byref(c), 10, FAKE,
+                                FAKE, None, FAKE, 1 << 20, None)
+    assert st == status
+
+
+def test_decode_attn_rejects_bad_len_and_workspace():
+    s, c = _shape(), _cache()
+    f = _lib().kve_decode_attn
+    assert f(ctypes.byref(s), ctypes.byref(c), 0, FAKE, FAKE, None, FAKE,
+             1 << 20, None) == 1
+    assert f(ctypes.byref(s), ctypes.byref(c), 2000, FAKE, FAKE, None, FAKE,
+             1 << 20, None) == 3
+    assert f(ctypes.byref(s), ctypes.byref(c), 1000, FAKE, FAKE, None, FAKE,
+             16, None) == 5
+    assert f(ctypes.byref(s), ctypes.byref(c), 1000, FAKE, FAKE, None, None,
+             1 << 20, None) == 5
+    assert f(ctypes.byref(s), ctypes.byref(c), 1000, None, FAKE, None, FAKE,
+             1 << 20, None) == 1
+
+
+@pytest.mark.parametrize("pol,length,n_keep,status", [
+    ((100, 60, 50, 8), 500, 100, 2),     # S + W > B
+    ((100, 4, 8, 0), 500, 100, 2),       # L < 1
+    ((100, 4, 8, 8), 500, 8, 2),         # n_keep < S + W while evicting
+    ((100, 4, 8, 8), 500, 600, 2),       # n_keep > len
+    ((100, 4, 8, 8), 2000, 100, 3),      # len > capacity
+    ((100, -1, 8, 8), 500, 100, 2),
+])
+def test_select_rejects_bad_policy(pol, length, n_keep, status):
+    s, c, p = _shape(), _cache(), kve._Policy(*pol)
+    st = _lib().kve_select_evict(ctypes.byref(s), ctypes.byref(p),
+                                 ctypes.byref(c), length, n_keep, FAKE, None)
+    assert st == status
+
+
+def test_compact_and_append_reject_bad_args():
+    s, c = _shape(), _cache()
+    lib = _lib()
+    assert lib.kve_compact(ctypes.byref(s), ctypes.byref(c), 100, None, 50,
+                           None) == 1
+    assert lib.kve_compact(ctypes.byref(s), ctypes.byref(c), 100, FAKE, 200,
+                           None) == 1
+    assert lib.kve_compact(ctypes.byref(s), ctypes.byref(c), 5000, FAKE, 200,
+                           None) == 3
+    assert lib.kve_append(ctypes.byref(s), ctypes.byref(c), 1152, 0, FAKE,
+                          FAKE, None) == 3
+    assert lib.kve_append(ctypes.byref(s), ctypes.byref(c), 5, 0, None,
+                          FAKE, None) == 1
+    nullc = kve._Cache(FAKE, None, FAKE, FAKE)
+    assert lib.kve_append(ctypes.byref(s), ctypes.byref(nullc), 5, 0, FAKE,
+                          FAKE, None) == 1
+
+
+def test_score_rejects_bad_scorers():
+    s, c = _shape(), _cache()
+    lib = _lib()
+    mlp_bad_in = kve._Scorer(0, 0, kve.BF16, 128, 64, FAKE, None, FAKE, None)
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(mlp_bad_in),
+                         ctypes.byref(c), 0, 10, None, None) == 4
+    mlp_dtype = kve._Scorer(0, 0, kve.F32, 256, 64, FAKE, None, FAKE, None)
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(mlp_dtype),
+                         ctypes.byref(c), 0, 10, None, None) == 4
+    mlp = kve._Scorer(0, 0, kve.BF16, 256, 64, FAKE, None, FAKE, None)
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(mlp), ctypes.byref(c),
+                         0, 10, FAKE, None) == 1   # hidden given to MLP
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(mlp), ctypes.byref(c),
+                         5, 2, None, None) == 1
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(mlp), ctypes.byref(c),
+                         0, 2000, None, None) == 3
+    gate = kve._Scorer(1, 0, kve.BF16, 5120, 0, FAKE, None, None, None)
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(gate), ctypes.byref(c),
+                         0, 10, None, None) == 1   # gate needs hidden
+    gate_bad = kve._Scorer(1, 0, kve.BF16, 5000, 0, FAKE, None, None, None)
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(gate_bad),
+                         ctypes.byref(c), 0, 10, FAKE, None) == 4
+
+
+def test_step_rejects_bad_state():
+    s, c = _shape(), _cache()
+    lib = _lib()
+    p = kve._Policy(1024, 4, 128, 128)
+    mlp = kve._Scorer(0, 0, kve.BF16, 256, 64, FAKE, None, FAKE, None)
+
+    def call(state, shape=s, pol=p, ws_bytes=1 << 24):
+        return lib.kve_step(ctypes.byref(shape), ctypes.byref(pol),
+                            ctypes.byref(mlp), ctypes.byref(c),
+                            ctypes.byref(state), FAKE, FAKE, None, None, FAKE,
+                            FAKE, None, FAKE, FAKE, ws_bytes, None)
+
+    assert call(kve._State(1152, 1024, 9000, 0)) == 3       # cache full
+    assert call(kve._State(1100, 1200, 9000, 0)) == 1       # scored > len
+    assert call(kve._State(1100, 900, 9000, 0)) == 1        # pending >= L
+    small = _shape(capacity=1100)
+    assert call(kve._State(1000, 1000, 9000, 0), shape=small) == 3  # cap < B+L
+    assert call(kve._State(1030, 1024, 9000, 0), ws_bytes=64) == 5

@@ -1,0 +1,114 @@
+"""a5 decode attention: HIP kernel vs the float64 oracle, element by element.
+
+Sizes span several workgroup passes (32 rows), several splits and ragged
+tails; slots beyond len hold NaN so any read past the retained rows would
+show. Tolerance: 2e-3 * max|out| (float32 accumulation over bf16 inputs).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as syn
+from kvharness import attn_close, kve, LSE_ATOL
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, head_dim, group, n_kv, batch, len, capacity, key scale
+    ("f32", 64, 2, 2, 1, 192, 256, 1.0),        # tiny workload shape
+    ("bf16", 128, 4, 8, 2, 1087, 1152, 1.0),    # Qwen3-4B layer, mid-cycle
+    ("bf16", 128, 4, 8, 2, 1024, 1152, 1.0),    # right after an eviction
+    ("bf16", 128, 4, 2, 1, 1, 64, 1.0),         # single retained row
+    ("bf16", 128, 4, 2, 1, 33, 64, 1.0),        # ragged tail
+    ("bf16", 128, 5, 8, 1, 5000, 5000, 1.0),    # group 5, many splits
+    ("bf16", 64, 1, 3, 2, 300, 320, 1.0),
+    ("f32", 128, 8, 2, 1, 700, 700, 1.0),
+    ("bf16", 128, 3, 4, 3, 4097, 4100, 1.0),
+    ("bf16", 128, 4, 2, 2, 2000, 2048, 6.0),    # peaked softmax
+    ("f32", 64, 2, 2, 1, 2303, 2304, 4.0),
+]
+
+
+def _rows(rng, shape, dtype, scale):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return syn.Stored(x, dtype)
+
+
+def _poison(t, length):
+    import torch
+    t[:, :, length:] = float("nan")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2]}-n{c[5]}"
+                                             for c in CASES])
+def test_decode_attention_matches_oracle(case, fused):
+    import torch
+    k = kve()
+    dt, D, G, H, B, n, cap, kscale = case
+    print(f"[attn] {case} fused={fused}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    Ks = _rows(rng, (B, H, cap, D), dt, kscale)
+    Vs = _rows(rng, (B, H, cap, D), dt, 1.0)
+    Qs = _rows(rng, (B, H * G, D), dt, 1.0)
+    shape = k.Shape(B, H, G, D, cap, k.F32 if dt == "f32" else k.BF16)
+    dev = torch.device("cuda")
+    cache = k.CacheTensors.empty(shape, dev)
+    cache.k.copy_(Ks.torch(dev))
+    cache.v.copy_(Vs.torch(dev))
+    _poison(cache.k, n)
+    _poison(cache.v, n)
+    q = Qs.torch(dev)
+    out = torch.full((B, H * G, D), float("nan"), device=dev)
+    lse = torch.full((B, H * G), float("nan"), device=dev)
+    ws = k.alloc_workspace(shape, n, dev)
+    k.kve_debug_set_fused_combine(fused)
+    try:
+        k.kve_decode_attn(shape, cache, n, q, out, lse, ws)
+        torch.cuda.synchronize()
+    finally:
+        k.kve_debug_set_fused_combine(True)
+    got = out.cpu().double().numpy()
+    got_lse = lse.cpu().double().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref, ref_lse = O.decode_attention(Qs.f64[b, h * G:(h + 1) * G],
+                                              Ks.f64[b, h, :n],
+                                              Vs.f64[b, h, :n])
+            attn_close(got[b, h * G:(h + 1) * G], ref, f"b{b} h{h}")
+            np.testing.assert_allclose(got_lse[b, h * G:(h + 1) * G], ref_lse,
+                                       atol=LSE_ATOL, rtol=1e-5)
+    # the split-K completion counters must be back to zero
+    nslices = B * H
+    assert int(ws[:nslices].abs().sum().item()) == 0
+
+
+def test_decode_attention_deterministic_and_len_sweep():
+    """Bitwise-identical reruns; every len from 1 to 130 on one shape."""
+    import torch
+    k = kve()
+    rng = np.random.default_rng(5)
+    B, H, G, D, cap = 1, 2, 4, 128, 160
+    Ks = _rows(rng, (B, H, cap, D), "bf16", 1.0)
+    Vs = _rows(rng, (B, H, cap, D), "bf16", 1.0)
+    Qs = _rows(rng, (B, H * G, D), "bf16", 1.0)
+    shape = k.Shape(B, H, G, D, cap, k.BF16)
+    dev = torch.device("cuda")
+    cache = k.CacheTensors.empty(shape, dev)
+    cache.k.copy_(Ks.torch(dev))
+    cache.v.copy_(Vs.torch(dev))
+    q = Qs.torch(dev)
+    ws = k.alloc_workspace(shape, cap, dev)
+    out = torch.empty((B, H * G, D), device=dev)
+    for n in list(range(1, 131)) + [cap]:
+        k.kve_decode_attn(shape, cache, n, q, out, None, ws)
+        first = out.clone()
+        k.kve_decode_attn(shape, cache, n, q, out, None, ws)
+        assert torch.equal(first, out), f"nondeterministic at len {n}"
+        got = out.cpu().double().numpy()
+        for h in range(H):
+            ref, _ = O.decode_attention(Qs.f64[0, h * G:(h + 1) * G],
+                                        Ks.f64[0, h, :n], Vs.f64[0, h, :n])
+            attn_close(got[0, h * G:(h + 1) * G], ref, f"len {n} h{h}")

@@ -1,0 +1,254 @@
+"""a6 fused decode step end to end (kve_step through the C ABI) against the
+float64 oracle's incremental policy loop, on inputs drawn on the host from
+the synthetic module.
+
+Every step checks: retained positions of every slice equal the oracle's
+(except tokens whose oracle score lies within 1e-3 of the cut), GPU scores
+within 1e-3 of the oracle's, and attention outputs within 2e-3 * max|out|
+(computed by the oracle over the GPU's retained set when a tie made the sets
+differ; the oracle is then resynchronised to that set).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as syn
+from kvharness import (attn_close, kve, oracle_gate_scores, oracle_mlp_scores,
+                       shape_of, SCORE_ATOL)
+
+pytestmark = pytest.mark.gpu
+
+
+class Tracker:
+    """All tokens' K/V/score by position for every slice, plus the oracle
+    layer; used to compare retained sets and recompute attention."""
+
+    def __init__(self, w, k0, v0, s0, policy):
+        self.w = w
+        self.policy = policy
+        npos = w.n0 + w.steps
+        b, H, d = w.batch, w.n_kv, w.head_dim
+        self.K = np.zeros((b, H, npos, d))
+        self.V = np.zeros((b, H, npos, d))
+        self.S = np.zeros((b, H, npos), np.float32)
+        self.K[:, :, :w.n0], self.V[:, :, :w.n0] = k0, v0
+        self.S[:, :, :w.n0] = s0
+        self.lay = O.OracleLayer(k0, v0, s0, policy, w.group)
+        self.cut = np.full((b, H), np.nan)
+
+    def _record_cut(self):
+        p = self.policy
+        lo, hi = p.sinks, p.budget - p.window
+        if hi > lo:
+            self.cut = self.lay.score[:, :, lo:hi].min(axis=2).astype(np.float64)
+
+    def prefill(self):
+        if self.lay.prefill_compress() is not None:
+            self._record_cut()
+
+    def step(self, pos, k, v, s):
+        self.K[:, :, pos], self.V[:, :, pos], self.S[:, :, pos] = k, v, s
+        self.lay.append(k, v, s)
+        if self.lay.maybe_evict() is not None:
+            self._record_cut()
+
+    def check_and_sync(self, gpu_pos):
+        """Compare the GPU's retained positions [b][H][n] with the oracle's;
+        resynchronise the oracle to the GPU set on tolerated tie flips."""
+        b, H, n = gpu_pos.shape
+        assert n == self.lay.n, f"cache count {n} != oracle {self.lay.n}"
+        for bi in range(b):
+            for h in range(H):
+                g = gpu_pos[bi, h]
+                o = self.lay.pos[bi, h]
+                if np.array_equal(g, o):
+                    continue
+                diff = set(g.tolist()) ^ set(o.tolist())
+                for t in diff:
+                    assert abs(float(self.S[bi, h, t]) - self.cut[bi, h]) <= \
+                        SCORE_ATOL, f"slice {bi},{h}: token {t} differs"
+                self.lay.K[bi, h] = self.K[bi, h, g]
+                self.lay.V[bi, h] = self.V[bi, h, g]
+                self.lay.score[bi, h] = self.S[bi, h, g]
+                self.lay.pos[bi, h] = g
+
+
+def run_e2e(w, seed=0, fused=True, check_stride=1, layer=0):
+    import torch
+    k = kve()
+    dev = torch.device("cuda")
+    mlp = w.scorer == "mlp"
+    ctx = syn.initial_context(w, seed, layer)
+    if mlp:
+        wts = syn.draw_mlp_weights(w, seed, layer, biases=True)
+        s0 = oracle_mlp_scores(ctx["k0"].f64, ctx["v0"].f64, wts, w.act)
+        sc = k.Scorer.mlp(wts["w1"].torch(dev), wts["w2"].torch(dev),
+                          wts["b1"].torch(dev), wts["b2"].torch(dev),
+                          act=k.ACT_RELU if w.act == "relu" else k.ACT_SILU)
+    else:
+        gw = syn.draw_gate_weights(w, seed, layer, bias=True)
+        s0 = oracle_gate_scores(ctx["hidden0"].f64, gw)
+        sc = k.Scorer.gate(gw["w"].torch(dev), gw["b"].torch(dev))
+    pol_o = O.Policy(w.budget, w.sinks, w.window, w.evict_len)
+    tr = Tracker(w, ctx["k0"].f64, ctx["v0"].f64, s0, pol_o)
+
+    shape = shape_of(w)
+    pol = k.Policy(w.budget, w.sinks, w.window, w.evict_len)
+    cache = k.CacheTensors.empty(shape, dev)
+    cache.k[:, :, :w.n0] = ctx["k0"].torch(dev)
+    cache.v[:, :, :w.n0] = ctx["v0"].torch(dev)
+    cache.pos[:, :, :w.n0] = torch.arange(w.n0, dtype=torch.int32, device=dev)
+    keep = torch.zeros((w.batch, w.n_kv, w.capacity), dtype=torch.int32,
+                       device=dev)
+    ws = k.alloc_workspace(shape, w.capacity, dev)
+    hbuf = None
+    if mlp:
+        k.kve_score(shape, sc, cache, 0, w.n0)
+    else:
+        k.kve_score(shape, sc, cache, 0, w.n0, hidden=ctx["hidden0"].torch(dev))
+        hbuf = torch.zeros((w.batch, w.evict_len, w.hidden),
+                           dtype=torch.bfloat16, device=dev)
+    got_s = cache.score[:, :, :w.n0].cpu().numpy()
+    np.testing.assert_allclose(got_s, s0, rtol=0, atol=SCORE_ATOL)
+    tr.prefill()
+    n = w.n0
+    if w.n0 > w.budget:
+        k.kve_select_evict(shape, pol, cache, w.n0, w.budget, keep)
+        k.kve_compact(shape, cache, w.n0, keep, w.budget)
+        n = w.budget
+    tr.check_and_sync(cache.pos[:, :, :n].cpu().numpy().astype(np.int64))
+    state = k.DecodeState(n, n, w.n0)
+    out = torch.zeros((w.batch, w.n_q, w.head_dim), device=dev)
+    lse = torch.zeros((w.batch, w.n_q), device=dev)
+    k.kve_debug_set_fused_combine(fused)
+    G = w.group
+    evictions = 0
+    try:
+        for i in range(w.steps):
+            st = syn.step_inputs(w, seed, layer, i)
+            if mlp:
+                sn = oracle_mlp_scores(st["k_new"].f64[:, :, None],
+                                       st["v_new"].f64[:, :, None], wts,
+                                       w.act)[:, :, 0]
+                k.kve_step(shape, pol, sc, cache, state, st["k_new"].torch(dev),
+                           st["v_new"].torch(dev), st["q"].torch(dev), out, lse,
+                           keep, ws)
+            else:
+                sn = oracle_gate_scores(st["hidden_new"].f64[:, None], gw)[:, :, 0]
+                k.kve_step(shape, pol, sc, cache, state, st["k_new"].torch(dev),
+                           st["v_new"].torch(dev), st["q"].torch(dev), out, lse,
+                           keep, ws, hidden_new=st["hidden_new"].torch(dev),
+                           hidden_buf=hbuf)
+            tr.step(w.n0 + i, st["k_new"].f64, st["v_new"].f64, sn)
+            evictions += state.evicted
+            if i % check_stride and not state.evicted and i != w.steps - 1:
+                continue
+            torch.cuda.synchronize()
+            gpu_pos = cache.pos[:, :, :state.len].cpu().numpy().astype(np.int64)
+            assert state.len == tr.lay.n
+            tr.check_and_sync(gpu_pos)
+            if state.evicted:
+                # scores of the retained entries match the oracle's by position
+                gs = cache.score[:, :, :state.len].cpu().numpy()
+                ref = np.take_along_axis(tr.S, gpu_pos, axis=2)
+                np.testing.assert_allclose(gs, ref, rtol=0, atol=SCORE_ATOL)
+            ref_out, _ = tr.lay.attend(st["q"].f64)
+            attn_close(out.cpu().double().numpy(), ref_out, f"step {i}")
+    finally:
+        k.kve_debug_set_fused_combine(True)
+    return evictions, tr
+
+
+def test_tiny_workload_full_run():
+    """Config 1: fp32, d=64, G=2, n0=512 -> B=192, L=1, 64 steps."""
+    w = syn.workload(1)
+    print(f"[step] {w.name}", flush=True)
+    ev, _ = run_e2e(w)
+    assert ev == w.steps  # L = 1 evicts at every step once saturated
+
+
+def test_tiny_workload_separate_combine():
+    w = syn.workload(1, steps=16)
+    run_e2e(w, fused=False, seed=1)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_qwen3_layer_structured(seed):
+    """Config 2 shapes (structured rows, heavy hitters), batch cut to 2:
+    n0=8192 -> B=1024, L=128, 256 steps (two periodic evictions)."""
+    w = syn.workload(2, batch=2)
+    print(f"[step] {w.name} batch=2 seed={seed}", flush=True)
+    ev, _ = run_e2e(w, seed=seed, check_stride=8)
+    assert ev == 2
+
+
+def test_qwen3_layer_silu_and_odd_policy():
+    w = syn.workload(2, batch=1, n0=700, budget=300, sinks=3, window=37,
+                     evict_len=45, steps=100, act="silu", structured=False)
+    ev, _ = run_e2e(w, seed=3)
+    assert ev == 2
+
+
+def test_no_eviction_equals_dense_attention():
+    """B above the context: nothing is evicted, the step is dense decode."""
+    w = syn.workload(2, batch=1, n0=200, budget=600, window=64, evict_len=64,
+                     steps=40, structured=False)
+    ev, tr = run_e2e(w, seed=4)
+    assert ev == 0
+    assert tr.lay.n == 240
+
+
+def test_gate_scorer_workload():
+    """Config 5 structure (gate on 5120-dim hidden states, G=5, W=512,
+    L=64) at a reduced prompt: n0=4096 -> 30% budget, 130 steps."""
+    w = syn.workload(5, n0=4096, budget=int(0.3 * 4096), steps=130)
+    print(f"[step] gate n0=4096 B={w.budget}", flush=True)
+    ev, _ = run_e2e(w, seed=0, check_stride=4)
+    assert ev == 2
+
+
+def test_checkpoint_resume_bitwise():
+    """Save the device state mid-run, continue, restore, replay: identical
+    outputs and caches (the decode state is K, V, score, pos and len)."""
+    import torch
+    k = kve()
+    dev = torch.device("cuda")
+    w = syn.workload(2, batch=1, n0=1500, steps=300, structured=False)
+    ctx = syn.initial_context(w, 0, 0)
+    wts = syn.draw_mlp_weights(w, 0, 0)
+    shape = shape_of(w)
+    pol = k.Policy(w.budget, w.sinks, w.window, w.evict_len)
+    sc = k.Scorer.mlp(wts["w1"].torch(dev), wts["w2"].torch(dev))
+    cache = k.CacheTensors.empty(shape, dev)
+    cache.k[:, :, :w.n0] = ctx["k0"].torch(dev)
+    cache.v[:, :, :w.n0] = ctx["v0"].torch(dev)
+    cache.pos[:, :, :w.n0] = torch.arange(w.n0, dtype=torch.int32, device=dev)
+    keep = torch.zeros((1, w.n_kv, w.capacity), dtype=torch.int32, device=dev)
+    ws = k.alloc_workspace(shape, w.capacity, dev)
+    k.kve_score(shape, sc, cache, 0, w.n0)
+    k.kve_select_evict(shape, pol, cache, w.n0, w.budget, keep)
+    k.kve_compact(shape, cache, w.n0, keep, w.budget)
+    state = k.DecodeState(w.budget, w.budget, w.n0)
+    out = torch.zeros((1, w.n_q, w.head_dim), device=dev)
+    inputs = [syn.step_inputs(w, 0, 0, i) for i in range(w.steps)]
+
+    def run(i0, i1, st):
+        outs = []
+        for i in range(i0, i1):
+            x = inputs[i]
+            k.kve_step(shape, pol, sc, cache, st, x["k_new"].torch(dev),
+                       x["v_new"].torch(dev), x["q"].torch(dev), out, None,
+                       keep, ws)
+            outs.append(out.clone())
+        return outs
+
+    first = run(0, 100, state)
+    snap = (cache.k.clone(), cache.v.clone(), cache.score.clone(),
+            cache.pos.clone(), k.DecodeState(**vars(state)))
+    a = run(100, w.steps, state)
+    cache.k.copy_(snap[0]); cache.v.copy_(snap[1])
+    cache.score.copy_(snap[2]); cache.pos.copy_(snap[3])
+    b = run(100, w.steps, snap[4])
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert first  # the first leg ran
