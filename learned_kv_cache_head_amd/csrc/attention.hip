@@ -191,9 +191,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if constexpr (BF16) {
+              // Copy the vector element to a scalar before the bit cast:
+              // a bit cast applied directly to an ext_vector element lvalue
+              // reads element 0 with this compiler.
+              const uint32_t kw = kc[u][c][i];
+              const uint32_t qv = qw[g][c * 4 + i];
               t = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2_t, qw[g][c * 4 + i]),
-                  __builtin_bit_cast(bf16x2_t, kc[u][c][i]), t, false);
+                  __builtin_bit_cast(bf16x2_t, qv),
+                  __builtin_bit_cast(bf16x2_t, kw), t, false);
             } else {
               t = fmaf(qf[g][c * 4 + i], __uint_as_float(kc[u][c][i]), t);
             }
