@@ -1,0 +1,422 @@
+"""Decode-step benchmark of libkvevict on one MI355X.
+
+One step = one decode token through every attention layer of the stack for
+the whole batch: per layer, ``kve_step`` appends the new K/V row, and on
+every L-th step scores the pending rows (MLP over [k; v]), selects the
+evicted rows and compacts the cache back to the budget B; then it runs GQA
+decode attention over the retained rows. Inputs are synthetic and already
+resident in HBM when the timed region starts.
+
+Default workload: Qwen3-4B-shaped attention stack (36 layers, 8 KV heads, 32
+query heads, head_dim 128, bf16 K/V/Q, float32 accumulation), batch 96,
+every sequence holding a compressed cache of B = 1024 entries (S = 4 sinks,
+W = 128 window, eviction length L = 128) after an 8192-token prompt that the
+library itself scores, selects and compacts during set-up.
+
+Prints one JSON line with tokens/s, the achieved bandwidth of the dominant
+kernel (decode attention) against the HBM roofline, and the float64 CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
+WORKLOAD_BY_NAME = {
+    "qwen3-4b-36layer-b96-B1024": 4,
+    "qwen3-4b-36layer-b8-B2048": 3,
+    "qwen3-4b-1layer-b16": 2,
+}
+DEFAULT_WORKLOAD = "qwen3-4b-36layer-b96-B1024"
+ATTN_SOURCE = os.path.join(ROOT, "learned_kv_cache_head_amd", "csrc",
+                           "attention.hip")
+METRIC = ("evict+decode tokens/s at budget B and achieved HBM GB/s vs "
+          "MI355X peak")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes (what the method has to move; no dense-cache bytes)
+# ---------------------------------------------------------------------------
+
+def attn_launch_bytes(w, n: int, fused_append: bool) -> int:
+    """Bytes one decode-attention launch must move over all (batch, KV head)
+    slices at n retained rows (n counts the new row when the append is
+    fused): the n K and V rows, the q rows of the group, the float32 output
+    rows; with the fused append also the new row's store and position."""
+    d, e, G = w.head_dim, w.elem_bytes, w.group
+    per = n * 2 * d * e + G * d * e + G * d * 4
+    if fused_append:
+        per += 2 * d * e + 4  # new K/V row written into the cache + position
+    return w.batch * w.n_kv * per
+
+
+def evict_extra_bytes(w, n_before: int, moved: int) -> int:
+    """Bytes of an evicting step besides its attention launch, one layer:
+    append (new row read + stored + position), scorer (L pending rows read,
+    L scores written, per-head weights once), select (candidate scores read,
+    kept slots written), compaction (each moved row's K, V, score, position
+    read and written). ``moved`` counts moved rows over all slices."""
+    d, e, L, hid = w.head_dim, w.elem_bytes, w.evict_len, w.hidden
+    slices = w.batch * w.n_kv
+    append = slices * (2 * d * e * 2 + 4)
+    score = slices * (L * 2 * d * e + L * 4) + w.n_kv * (hid * 2 * d * e + hid * 4)
+    cand = n_before - w.sinks - w.window
+    select = slices * (cand * 4 + w.budget * 4)
+    compact = moved * 2 * (2 * d * e + 8)
+    return append + score + select + compact
+
+
+# ---------------------------------------------------------------------------
+# Device set-up
+# ---------------------------------------------------------------------------
+
+class Stack:
+    """Per-layer caches, scorer weights, step runners and input pools."""
+
+    def __init__(self, w, seed: int, pool_steps: int, dev):
+        import torch
+        import learned_kv_cache_head_amd as kve
+        import synthetic as syn
+        self.w, self.dev = w, dev
+        T = syn.TENSOR_IDS
+        b, H, d, G = w.batch, w.n_kv, w.head_dim, w.group
+        self.shape = kve.Shape(b, H, G, d, w.budget + w.evict_len, kve.BF16)
+        self.policy = kve.Policy(w.budget, w.sinks, w.window, w.evict_len)
+        pre_shape = kve.Shape(b, H, G, d, w.n0, kve.BF16)
+        scratch = kve.CacheTensors.empty(pre_shape, dev)
+        scratch_pos = torch.arange(w.n0, dtype=torch.int32, device=dev)
+        keep_pre = torch.empty((b, H, w.budget), dtype=torch.int32, device=dev)
+        self.ws = kve.alloc_workspace(self.shape, self.shape.capacity, dev)
+        self.caches, self.scorers, self.runners = [], [], []
+        self.k_pool, self.v_pool, self.q_pool = [], [], []
+        cfg = w.cfg_id
+        for l in range(w.layers):
+            dn = syn.device_normal
+            w1 = dn((H, w.hidden, 2 * d), seed, (cfg, l, 0, T["w1"]),
+                    torch.bfloat16, dev, scale=(2 * d) ** -0.5)
+            w2 = dn((H, w.hidden), seed, (cfg, l, 0, T["w2"]), torch.float32,
+                    dev, scale=w.hidden ** -0.5)
+            sc = kve.Scorer.mlp(w1, w2)
+            # Prompt of n0 tokens, scored and compressed to B by the library.
+            scratch.k.copy_(dn((b, H, w.n0, d), seed, (cfg, l, 0, T["k0"]),
+                               torch.bfloat16, dev))
+            scratch.v.copy_(dn((b, H, w.n0, d), seed, (cfg, l, 0, T["v0"]),
+                               torch.bfloat16, dev))
+            scratch.pos.copy_(scratch_pos.expand(b, H, w.n0))
+            kve.kve_score(pre_shape, sc, scratch, 0, w.n0)
+            kve.kve_select_evict(pre_shape, self.policy, scratch, w.n0,
+                                 w.budget, keep_pre)
+            kve.kve_compact(pre_shape, scratch, w.n0, keep_pre, w.budget)
+            c = kve.CacheTensors.empty(self.shape, dev)
+            B = w.budget
+            c.k[:, :, :B].copy_(scratch.k[:, :, :B])
+            c.v[:, :, :B].copy_(scratch.v[:, :, :B])
+            c.score[:, :, :B].copy_(scratch.score[:, :, :B])
+            c.pos[:, :, :B].copy_(scratch.pos[:, :, :B])
+            st = kve.DecodeState(B, B, w.n0)
+            self.caches.append(c)
+            self.scorers.append(sc)
+            self.runners.append(kve.LayerStep(self.shape, self.policy, sc, c,
+                                              st, self.ws))
+            self.k_pool.append(dn((pool_steps, b, H, d), seed,
+                                  (cfg, l, 1, T["k_new"]), torch.bfloat16, dev))
+            self.v_pool.append(dn((pool_steps, b, H, d), seed,
+                                  (cfg, l, 1, T["v_new"]), torch.bfloat16, dev))
+            self.q_pool.append(dn((pool_steps, b, H * G, d), seed,
+                                  (cfg, l, 1, T["q"]), torch.bfloat16, dev))
+        del scratch
+        self.pool_steps = pool_steps
+        self.out = torch.empty((b, H * G, d), dtype=torch.float32, device=dev)
+        self.keep_scratch = [torch.empty((b, H, self.shape.capacity),
+                                         dtype=torch.int32, device=dev)
+                             for _ in range(w.layers)]
+        torch.cuda.synchronize()
+
+    def run_step(self, i: int, keep_for=None, events=None, ev_base=0):
+        """Decode step i over all layers. keep_for(l) may supply the buffer
+        that receives the kept slots of an evicting call; events[ev_base+l+1]
+        is recorded after layer l."""
+        j = i % self.pool_steps
+        for l, r in enumerate(self.runners):
+            keep = self.keep_scratch[l]
+            if keep_for is not None and r.evicts_next():
+                keep = keep_for(l)
+            r(self.k_pool[l][j], self.v_pool[l][j], self.q_pool[l][j],
+              self.out, None, keep)
+            if events is not None:
+                events[ev_base + l + 1].record()
+
+
+# ---------------------------------------------------------------------------
+# Oracle CPU baseline (bounded sample)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, seed: int, sample_batch: int, sample_steps: int) -> dict:
+    """Time the float64 oracle on one layer of the same workload for
+    ``sample_batch`` sequences over ``sample_steps`` decode steps (whole
+    eviction cycles), starting from its own compressed prompt; scale to the
+    full stack's tokens/s (tokens / (time x layers))."""
+    import numpy as np
+    import oracle as O
+    import synthetic as syn
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    ws = syn.workload(w.cfg_id, batch=sample_batch)
+    ctx = syn.initial_context(ws, seed, 0)
+    wts = syn.draw_mlp_weights(ws, seed, 0)
+
+    def scores(k64, v64):
+        out = np.empty(k64.shape[:3], dtype=np.float32)
+        for bi in range(k64.shape[0]):
+            for h in range(k64.shape[1]):
+                out[bi, h] = O.score_to_f32(O.mlp_score(
+                    k64[bi, h], v64[bi, h], wts["w1"].f64[h], wts["b1"].f64[h],
+                    wts["w2"].f64[h], wts["b2"].f64[h], ws.act))
+        return out
+
+    lay = O.OracleLayer(ctx["k0"].f64, ctx["v0"].f64,
+                        scores(ctx["k0"].f64, ctx["v0"].f64),
+                        O.Policy(ws.budget, ws.sinks, ws.window, ws.evict_len),
+                        ws.group)
+    lay.prefill_compress()
+    del ctx
+    inputs = [syn.step_inputs(ws, seed, 0, i) for i in range(sample_steps)]
+    t0 = time.perf_counter()
+    for x in inputs:
+        sn = scores(x["k_new"].f64[:, :, None], x["v_new"].f64[:, :, None])
+        lay.step(x["k_new"].f64, x["v_new"].f64, sn[:, :, 0], x["q"].f64)
+    dt = time.perf_counter() - t0
+    tokens = sample_batch * sample_steps
+    return {
+        "value": tokens / (dt * w.layers),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 oracle, 1 of {w.layers} layers, {sample_batch} "
+                   f"of {w.batch} sequences, {sample_steps} decode steps "
+                   f"({sample_steps // w.evict_len} eviction cycles) from a "
+                   f"compressed {w.n0}-token prompt; {dt:.1f} s wall; scaled "
+                   f"to the {w.layers}-layer step as tokens/(time x layers)"),
+    }
+
+
+# ---------------------------------------------------------------------------
+# Recorded rocprofv3 traffic of the attention kernel
+# ---------------------------------------------------------------------------
+
+def traffic_ratio(workload: str):
+    """Measured HBM bytes over algorithmic bytes of one attention launch, from
+    the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE passes,
+    each scaled by what the counter reads for a plain copy of known size), or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if rec.get("attention_source_sha256") != src:
+        return None
+    try:
+        return float(rec["traffic_over_algorithmic"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default 2 eviction cycles)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 1 eviction cycle)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(WORKLOAD_BY_NAME))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time only the whole region (no per-launch events)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-batch", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=None)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed region, run a plain 1 GiB "
+                         "elementwise copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "libkvevict runs on one GPU; --gpus "
+                          f"{args.gpus} is not supported (the step shards "
+                          "by batch or KV head with no exchange, but only "
+                          "the one-GPU path is built)"}))
+        return 2
+
+    import torch
+    import synthetic as syn
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = syn.workload(WORKLOAD_BY_NAME[args.workload])
+    L = w.evict_len
+    steps = args.steps if args.steps is not None else 2 * L
+    warmup = args.warmup if args.warmup is not None else L
+    pool = min(warmup + steps, 3 * L)
+    log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
+        f"B={w.budget} L={L} steps={steps} warmup={warmup}")
+    t0 = time.perf_counter()
+    stack = Stack(w, args.seed, pool, dev)
+    log(f"set-up {time.perf_counter() - t0:.1f} s")
+
+    for i in range(warmup):
+        stack.run_step(i)
+    torch.cuda.synchronize()
+    log("warm-up done")
+
+    # Expected retained count per step, and keep buffers of the evictions
+    # inside the timed region (to count the rows that compaction moves).
+    n_layers = w.layers
+    lens = []
+    keep_bufs = {}
+    n = stack.runners[0].state.len
+    for i in range(steps):
+        n += 1
+        ev = n >= w.budget + L
+        lens.append((n, ev))
+        if ev:
+            n = w.budget
+
+    taken = {}
+
+    def keep_for(l):
+        c = taken.get(l, 0)
+        taken[l] = c + 1
+        buf = torch.empty((w.batch, w.n_kv, w.budget), dtype=torch.int32,
+                          device=dev)
+        keep_bufs[(l, c)] = buf
+        return buf
+
+    use_events = not args.no_kernel_events
+    events = None
+    if use_events:
+        events = [torch.cuda.Event(enable_timing=True)
+                  for _ in range(steps * n_layers + 1)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    if use_events:
+        events[0].record()
+    for s in range(steps):
+        stack.run_step(warmup + s, keep_for, events, s * n_layers)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"timed {steps} steps in {wall * 1e3:.1f} ms")
+
+    if args.calib_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # Algorithmic bytes over the timed region.
+    moved = {}
+    for (l, c), buf in keep_bufs.items():
+        idx = torch.arange(w.budget, dtype=torch.int32, device=dev)
+        moved[(l, c)] = int((buf != idx).sum().item())
+    total_bytes = 0
+    attn_bytes, attn_ms = [], []
+    ev_count = {}
+    for s, (n, ev) in enumerate(lens):
+        for l in range(n_layers):
+            if ev:
+                c = ev_count.get(l, 0)
+                ev_count[l] = c + 1
+                total_bytes += evict_extra_bytes(w, n, moved[(l, c)])
+                total_bytes += attn_launch_bytes(w, w.budget, False)
+            else:
+                b_ = attn_launch_bytes(w, n, True)
+                total_bytes += b_
+                if use_events:
+                    j = s * n_layers + l
+                    attn_bytes.append(b_)
+                    attn_ms.append(events[j].elapsed_time(events[j + 1]))
+
+    tokens_s = w.batch * steps / wall
+    step_gbps = total_bytes / wall / 1e9
+    roof = None
+    if use_events and attn_ms:
+        mean_ms = sum(attn_ms) / len(attn_ms)
+        mean_bytes = sum(attn_bytes) / len(attn_bytes)
+        achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
+        ratio = traffic_ratio(args.workload)
+        traffic = None if ratio is None else int(ratio * mean_bytes)
+        roof = {"bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic,
+                "kernel": "attn_kernel (decode attention, fused append)",
+                "launches": len(attn_ms),
+                "mean_launch_us": round(mean_ms * 1e3, 2),
+                "algorithmic_bytes_per_launch": int(mean_bytes)}
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layers": w.layers,
+                   "batch": w.batch, "n_kv_heads": w.n_kv,
+                   "n_q_heads": w.n_q, "head_dim": w.head_dim,
+                   "budget": w.budget, "sinks": w.sinks, "window": w.window,
+                   "evict_len": w.evict_len, "prompt_len": w.n0,
+                   "scorer": f"mlp {2 * w.head_dim}-{w.hidden}-1 relu",
+                   "parallelism": "none"},
+        "step_gbps": round(step_gbps, 1),
+        "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del stack
+        torch.cuda.empty_cache()
+        cs = args.cpu_steps if args.cpu_steps is not None else L
+        log(f"cpu baseline: oracle on {args.cpu_batch} sequences x {cs} steps")
+        cb = cpu_baseline(w, args.seed, args.cpu_batch, cs)
+        cb["value"] = round(cb["value"], 3)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -135,14 +135,13 @@ typedef struct {
 } kve_decode_state;
 
 /* Bytes of workspace that kve_decode_attn / kve_step need for caches of up
- * to max_len entries (split-K partial results and completion counters).
- * Returns 0 on invalid arguments. */
+ * to max_len entries: the split-K partial results (per query head and split:
+ * head_dim accumulator sums, running maximum and normaliser, float32). The
+ * size depends on the shape and max_len only. The workspace needs no
+ * initialisation; its contents are scratch and undefined between calls, and
+ * calls that share one workspace must be ordered (same stream). Returns 0
+ * on invalid arguments. */
 size_t kve_workspace_bytes(const kve_shape* shape, int32_t max_len);
-
-/* Zero-fill a workspace (once, before its first use; the library leaves
- * the counter region zeroed again after every completed call). Uses a fill
- * kernel, not a memset, so it may be recorded in a HIP graph. */
-kve_status kve_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* a1 Append (KVpop Appendix C): write one new token per slice into `slot`:
  * K[b][h][slot] = k_new[b][h], V likewise, pos[b][h][slot] = position.
@@ -188,7 +187,7 @@ kve_status kve_compact(const kve_shape* shape, kve_cache* cache, int32_t len,
  * out = sum_t softmax_t(<q, k_t> / sqrt(d)) v_t, lse = log sum_t
  * exp(<q, k_t> / sqrt(d)). Float32 math and output. lse may be NULL.
  * Requires 1 <= len <= capacity and ws_bytes >= kve_workspace_bytes(shape,
- * len) of a workspace prepared by kve_workspace_init. */
+ * len). */
 kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
                            int32_t len, const void* q, float* out, float* lse,
                            void* ws, size_t ws_bytes, hipStream_t stream);
@@ -216,13 +215,6 @@ const char* kve_status_str(kve_status status);
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int32_t kve_version(void);
-
-/* Test hook, not for production use: on != 0 (the default) merges the
- * split-K partials of kve_decode_attn / kve_step in the last workgroup of
- * each slice; on == 0 uses a separate combine kernel instead. Results agree
- * to float32 rounding. Process-wide; not thread-safe against concurrent
- * calls. */
-void kve_debug_set_fused_combine(int32_t on);
 
 #ifdef __cplusplus
 }

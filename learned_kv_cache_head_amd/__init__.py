@@ -16,10 +16,10 @@ from typing import Optional
 __all__ = [
     "KveError", "Shape", "Policy", "CacheTensors", "Scorer", "DecodeState",
     "load_library", "library_path", "kve_version", "kve_status_str",
-    "kve_workspace_bytes", "kve_workspace_init", "kve_append", "kve_score",
+    "kve_workspace_bytes", "kve_append", "kve_score",
     "kve_select_evict", "kve_compact", "kve_decode_attn", "kve_step",
-    "kve_debug_set_fused_combine", "F32", "BF16", "ACT_RELU", "ACT_SILU",
-    "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "alloc_workspace",
+    "F32", "BF16", "ACT_RELU", "ACT_SILU",
+    "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "alloc_workspace", "LayerStep",
 ]
 
 F32, BF16 = 0, 1
@@ -68,7 +68,6 @@ _SIGS = {
     "kve_version": (_I, []),
     "kve_status_str": (ctypes.c_char_p, [_I]),
     "kve_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Shape), _I]),
-    "kve_workspace_init": (_I, [_P, ctypes.c_size_t, _P]),
     "kve_append": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Cache), _I,
                         _I, _P, _P, _P]),
     "kve_score": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Scorer),
@@ -83,7 +82,6 @@ _SIGS = {
                       ctypes.POINTER(_Scorer), ctypes.POINTER(_Cache),
                       ctypes.POINTER(_State), _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, ctypes.c_size_t, _P]),
-    "kve_debug_set_fused_combine": (None, [_I]),
 }
 
 _lib = None
@@ -244,21 +242,13 @@ def kve_workspace_bytes(shape: Shape, max_len: int) -> int:
     return load_library().kve_workspace_bytes(ctypes.byref(cs), max_len)
 
 
-def kve_workspace_init(ws, stream=None) -> None:
-    _check(load_library().kve_workspace_init(
-        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-        "kve_workspace_init")
-
-
-def alloc_workspace(shape: Shape, max_len: int, device="cuda", stream=None):
-    """Allocate (torch) and zero-fill (library fill kernel) a workspace."""
+def alloc_workspace(shape: Shape, max_len: int, device="cuda"):
+    """Allocate (torch) a workspace for caches of up to max_len entries."""
     import torch
     n = kve_workspace_bytes(shape, max_len)
     if n == 0:
         raise ValueError("invalid shape for workspace")
-    ws = torch.empty(n // 4, dtype=torch.int32, device=device)
-    kve_workspace_init(ws, stream)
-    return ws
+    return torch.empty((n + 3) // 4, dtype=torch.int32, device=device)
 
 
 def kve_append(shape: Shape, cache: CacheTensors, slot: int, position: int,
@@ -322,5 +312,47 @@ def kve_step(shape: Shape, policy: Policy, scorer: Scorer,
     return state
 
 
-def kve_debug_set_fused_combine(on: bool) -> None:
-    load_library().kve_debug_set_fused_combine(1 if on else 0)
+class LayerStep:
+    """Repeated ``kve_step`` calls on one layer with the descriptors built
+    once: per call only the tensor pointers of the new token and the outputs
+    are marshalled, so a Python decode loop keeps the GPU queue fed.
+
+    ``state`` (a DecodeState) is updated after every call, as by kve_step.
+    """
+
+    def __init__(self, shape: Shape, policy: Policy, scorer: Scorer,
+                 cache: CacheTensors, state: DecodeState, ws, stream=None):
+        self._lib = load_library()
+        self._fn = self._lib.kve_step
+        self._shape, self._policy = shape.c(), policy.c()
+        self._scorer, self._cache = scorer.c(), cache.c()
+        self._st = _State(state.len, state.scored_upto, state.next_position, 0)
+        self._refs = (ctypes.byref(self._shape), ctypes.byref(self._policy),
+                      ctypes.byref(self._scorer), ctypes.byref(self._cache),
+                      ctypes.byref(self._st))
+        self._ws_ptr = _ptr(ws)
+        self._ws_bytes = ws.numel() * ws.element_size()
+        self._stream = _stream(stream)
+        self._keepalive = (scorer, cache, ws)
+        self.state = state
+        self.budget, self.evict_len = policy.budget, policy.evict_len
+
+    def evicts_next(self) -> bool:
+        """True if the next call reaches B + L and evicts."""
+        return self._st.len + 1 >= self.budget + self.evict_len
+
+    def __call__(self, k_new, v_new, q, out, lse, keep_slots,
+                 hidden_new=None, hidden_buf=None) -> int:
+        """One decode step; returns 1 if it evicted, else 0."""
+        r = self._refs
+        status = self._fn(r[0], r[1], r[2], r[3], r[4], k_new.data_ptr(),
+                          v_new.data_ptr(), _ptr(hidden_new), _ptr(hidden_buf),
+                          q.data_ptr(), out.data_ptr(), _ptr(lse),
+                          keep_slots.data_ptr(), self._ws_ptr, self._ws_bytes,
+                          self._stream)
+        if status != 0:
+            raise KveError(status, "kve_step")
+        st, s = self._st, self.state
+        s.len, s.scored_upto = st.len, st.scored_upto
+        s.next_position, s.evicted = st.next_position, st.evicted
+        return st.evicted

@@ -1,31 +1,34 @@
 // Split-K flash-decode GQA attention over the compact retained cache.
 //
-// Computes, for every batch b, KV head h and query head j = h*G + g
-// (contiguous GQA groups, KVpop section 3.1), the decode attention over the
-// len retained rows of the slice (KVpop Appendix C: decoding attends
-// directly over the compact cache; Appendix D.1, Eq. 27-29: logits
-// <q, k>/sqrt(d_k), log-sum-exp normaliser):
-//     out_j = sum_t softmax_t(<q_j, k_t>/sqrt(d)) v_t,   lse_j = log sum_t exp(.)
+// For every batch b, KV head h and query head j = h*G + g (contiguous GQA
+// groups: the G query heads of a group share one KV head, KVpop section
+// 3.1), decode attention over the len retained rows of the slice (KVpop
+// Appendix C: decoding attends directly over the compact cache; Appendix
+// D.1, Eq. 27-29: logits <q, k>/sqrt(d_k), log-sum-exp normaliser):
+//     out_j = sum_t softmax_t(<q_j, k_t>/sqrt(d)) v_t,  lse_j = log sum_t exp(.)
 //
 // Decode attention streams every retained K/V row once per step and is
-// bound by HBM bandwidth (KV-Kaizen section 1: every decoded token reads
-// the whole cache). Design for gfx950:
-//  * one workgroup = 4 waves = one (split, KV head, batch) triple; the slice's
-//    rows are split over enough workgroups (split-K) to put several
-//    workgroups on each of the 256 CUs;
-//  * 8 lanes own one 256-byte row (lane i reads 16-byte chunks i and i+8, so
-//    every load instruction covers whole 128-byte lines), a wave covers 8
-//    rows per load, and every loaded K/V row is used by all G query heads of
-//    the group before it is dropped;
-//  * q.k partial dot products use v_dot2_f32_bf16 on the raw bf16 pairs
-//    (float32 FMAs for float32 caches) and are summed over the 8 lanes with
-//    three DPP steps (quad_perm and row_half_mirror);
-//  * online softmax in base 2 with a wave-uniform skip of the accumulator
-//    rescale when no running maximum moved; P.V in float32;
-//  * the per-workgroup partials (m, l, acc) of a slice are merged by the
-//    last workgroup to finish (device-scope atomic ticket, self-resetting),
-//    so a decode step of one layer is a single launch; a separate combine
-//    kernel is kept for comparison.
+// bound by HBM bandwidth (KV-Kaizen section 1: each decoded token reads the
+// whole cache, so decoding is limited by memory bandwidth). At 4 flop/byte
+// (G = 4) the q.k and p.v products fit the float32 VALU with room to spare,
+// so the design is about keeping enough bytes in flight:
+//  * one workgroup = 4 waves = one (split, KV head, batch) triple; each lane
+//    owns one 16-byte chunk of a row (16 lanes per bf16 d = 128 row), so one
+//    load instruction reads 4 whole 256-byte rows per wave, and every loaded
+//    K/V element is used by all G query heads of the group from registers;
+//  * software pipelining: each wave holds two stages of 16 rows in
+//    registers and issues the loads of the next stage before it computes on
+//    the current one;
+//  * q.k partial products with v_dot2_f32_bf16 on the raw bf16 pairs
+//    (float32 FMAs for float32 caches), summed over the lanes of a row with
+//    DPP (quad_perm, row_half_mirror, row_mirror);
+//  * online softmax in base 2, accumulator rescale skipped (wave-uniform)
+//    when no running maximum moved; p.v in float32;
+//  * no split (direct output) whenever the slices alone fill the chip; else
+//    per-workgroup partials (m, l, acc) merged by a separate combine kernel.
+//    The split workgroups never synchronise with each other: a device-scope
+//    fence on this chip writes back and invalidates the L2 of the issuing
+//    XCD, which costs far more than the second launch.
 #include <float.h>
 
 #include "kve_internal.h"
@@ -35,18 +38,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLPR = 8;                                 // lanes per row
-constexpr int kRowsPerPass = kWaves * (64 / kLPR);      // 32 rows
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-template <bool BF16>
-struct Elem {
-  static constexpr int kBytes = BF16 ? 2 : 4;
-  static constexpr int kPerChunk = 16 / kBytes;  // elements per 16-byte chunk
-};
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -55,11 +50,15 @@ __device__ __forceinline__ float dpp_mov(float x) {
                                          0xF, 0xF, false));
 }
 
-// Sum over the 8 lanes of an aligned lane octet (lane bits 0..2).
-__device__ __forceinline__ float sum_octet(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
-  x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <-> 7 - i in the octet
+// Sum over the LPR consecutive lanes that hold one row (LPR a power of 2).
+template <int LPR>
+__device__ __forceinline__ float sum_row_lanes(float x) {
+  if constexpr (LPR >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (LPR >= 16) x += dpp_mov<0x140>(x); // row_mirror
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+  if constexpr (LPR >= 64) x += __shfl_xor(x, 32);
   return x;
 }
 
@@ -67,27 +66,35 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
-__device__ __forceinline__ uint32_t wave_any(bool p) {
+__device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0ull;
 }
 
-// Element e of a lane's register slice sits at head-dim index
-// (sub + 8*c) * kPerChunk + j, with c = e / kPerChunk, j = e % kPerChunk.
-template <int PER_CHUNK>
-__device__ __forceinline__ int dim_of(int sub, int e) {
-  return (sub + kLPR * (e / PER_CHUNK)) * PER_CHUNK + (e % PER_CHUNK);
-}
+// Geometry of one kernel instantiation.
+template <bool BF16, int D>
+struct Geo {
+  static constexpr int kEB = BF16 ? 2 : 4;        // bytes per element
+  static constexpr int kRowB = D * kEB;           // bytes per row
+  static constexpr int kLPR = kRowB / 16;         // lanes per row
+  static constexpr int kEPL = 16 / kEB;           // elements per lane
+  static constexpr int kRPL = 64 / kLPR;          // rows per wave load
+  static constexpr int kU = (BF16 ? 16 : 8) / kRPL;  // loads per lane per stage
+  static constexpr int kWaveRows = kRPL * kU;     // rows per wave per stage
+  static constexpr int kStageRows = kWaves * kWaveRows;
+  static_assert(kLPR >= 1 && kLPR <= 64 && kU >= 1, "unsupported row size");
+};
+
+template <int U>
+struct Stage {
+  u32x4 k[U];
+  u32x4 v[U];
+};
 
 template <bool BF16, int D, int G>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
-  using E = Elem<BF16>;
-  constexpr int CE = E::kPerChunk;
-  constexpr int NCH = D / CE;        // 16-byte chunks per row
-  constexpr int CPL = NCH / kLPR;    // chunks per lane
-  constexpr int EPL = CPL * CE;      // elements per lane
-  constexpr int ROWB = D * E::kBytes;
-  constexpr int U = 2;               // rows per lane octet per iteration
-  static_assert(CPL >= 1, "row must span at least one chunk per lane");
+  using Gm = Geo<BF16, D>;
+  constexpr int LPR = Gm::kLPR, EPL = Gm::kEPL, RPL = Gm::kRPL, U = Gm::kU;
+  constexpr int ROWB = Gm::kRowB;
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -95,25 +102,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int grp = lane >> 3;
-  const int sub = lane & 7;
-  const int H = a.H;
-  const int Hq = H * G;
-  const size_t slice = (size_t)b * H + h;
+  const int rslot = lane / LPR;  // which of the RPL rows of a load
+  const int sub = lane % LPR;    // which 16-byte chunk of the row
+  const int Hq = a.H * G;
+  const size_t slice = (size_t)b * a.H + h;
   const int r_begin = split * a.rows_per_split;
   const int r_end = min(a.len, r_begin + a.rows_per_split);
 
   const char* kbase = (const char*)a.k + slice * (size_t)a.cap * ROWB;
   const char* vbase = (const char*)a.v + slice * (size_t)a.cap * ROWB;
+  const int new_slot = a.new_slot;
   const char* knew = nullptr;
   const char* vnew = nullptr;
-  const int new_slot = a.new_slot;
   if (new_slot >= 0) {
     knew = (const char*)a.k_new + slice * ROWB;
     vnew = (const char*)a.v_new + slice * ROWB;
     // Fused append: the workgroup whose rows contain the new slot stores the
-    // new row into the cache (no thread of this launch reads it back from
-    // there: the row is read straight from k_new / v_new below).
+    // new row into the cache. No thread of this launch reads that slot from
+    // the cache: the row is read straight from k_new / v_new below.
     if (new_slot >= r_begin && new_slot < r_end) {
       constexpr int NV = ROWB / 16;
       char* ks = (char*)a.k_store + (slice * (size_t)a.cap + new_slot) * ROWB;
@@ -128,25 +134,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
     }
   }
 
-  // Query registers, same element order as the K chunks a lane loads.
+  // This lane's chunk of every query head of the group (same element order
+  // as the K chunk it loads). Logits are taken in base 2.
   const float qscale = kLog2e * rsqrtf((float)D);
-  uint32_t qw[G][BF16 ? EPL / 2 : 1];
-  float qf[G][BF16 ? 1 : EPL];
+  u32x4 qv[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const char* qrow =
         (const char*)a.q + ((size_t)b * Hq + (size_t)h * G + g) * ROWB;
+    qv[g] = *(const u32x4*)(qrow + sub * 16);
+    if constexpr (!BF16) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const u32x4 w = *(const u32x4*)(qrow + (sub + kLPR * c) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (BF16) {
-          qw[g][c * 4 + i] = w[i];
-        } else {
-          qf[g][c * 4 + i] = __uint_as_float(w[i]) * qscale;
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        qv[g][i] = __float_as_uint(__uint_as_float(qv[g][i]) * qscale);
     }
   }
 
@@ -160,71 +160,63 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
   }
 
   const int nrows = r_end - r_begin;
-  const int n_iter = (nrows + kRowsPerPass * U - 1) / (kRowsPerPass * U);
-  const int my0 = r_begin + wave * (64 / kLPR) + grp;
+  const int n_stages = (nrows + Gm::kStageRows - 1) / Gm::kStageRows;
+  const int row0 = r_begin + wave * Gm::kWaveRows + rslot;
 
-  for (int it = 0; it < n_iter; ++it) {
-    u32x4 kc[U][CPL], vc[U][CPL];
-    bool ok[U];
+  auto load = [&](Stage<U>& st, int s) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = my0 + (it * U + u) * kRowsPerPass;
-      ok[u] = row < r_end;
-      const int rc = ok[u] ? row : r_end - 1;  // clamp: always in bounds
+      const int row = row0 + s * Gm::kStageRows + u * RPL;
+      const int rc = row < r_end ? row : r_end - 1;  // clamp: in bounds
       const char* kr = (rc == new_slot) ? knew : kbase + (size_t)rc * ROWB;
       const char* vr = (rc == new_slot) ? vnew : vbase + (size_t)rc * ROWB;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        kc[u][c] = *(const u32x4*)(kr + (sub + kLPR * c) * 16);
-        vc[u][c] = *(const u32x4*)(vr + (sub + kLPR * c) * 16);
-      }
+      st.k[u] = *(const u32x4*)(kr + sub * 16);
+      st.v[u] = *(const u32x4*)(vr + sub * 16);
     }
+  };
 
-    float s[U][G];
+  auto compute = [&](const Stage<U>& st, int s) {
+    float sc[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const bool ok = row0 + s * Gm::kStageRows + u * RPL < r_end;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float t = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (BF16) {
-              // Copy the vector element to a scalar before the bit cast:
-              // a bit cast applied directly to an ext_vector element lvalue
-              // reads element 0 with this compiler.
-              const uint32_t kw = kc[u][c][i];
-              const uint32_t qv = qw[g][c * 4 + i];
-              t = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2_t, qv),
-                  __builtin_bit_cast(bf16x2_t, kw), t, false);
-            } else {
-              t = fmaf(qf[g][c * 4 + i], __uint_as_float(kc[u][c][i]), t);
-            }
+        for (int i = 0; i < 4; ++i) {
+          // Copy the vector elements to scalars before the bit casts: a bit
+          // cast applied directly to an ext_vector element lvalue reads
+          // element 0 with this compiler.
+          const uint32_t kw = st.k[u][i];
+          const uint32_t qw = qv[g][i];
+          if constexpr (BF16) {
+            t = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2_t, qw),
+                __builtin_bit_cast(bf16x2_t, kw), t, false);
+          } else {
+            t = fmaf(__uint_as_float(qw), __uint_as_float(kw), t);
           }
         }
-        t = sum_octet(t);
+        t = sum_row_lanes<LPR>(t);
         if constexpr (BF16) t *= qscale;
-        s[u][g] = ok[u] ? t : -INFINITY;
+        sc[u][g] = ok ? t : -INFINITY;
       }
     }
-
-    float p[U][G];
+    float p[U][G], alpha[G];
     bool moved = false;
-    float alpha[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float mx = m[g];
 #pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][g]);
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
       alpha[g] = fast_exp2(m[g] - mx);
       moved |= (mx != m[g]);
       m[g] = mx;
       float lsum = l[g] * alpha[g];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        p[u][g] = fast_exp2(s[u][g] - mx);
+        p[u][g] = fast_exp2(sc[u][g] - mx);
         lsum += p[u][g];
       }
       l[g] = lsum;
@@ -235,20 +227,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha[g];
     }
-
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float vf[EPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (BF16) {
-            vf[c * 8 + 2 * i] = bf16lo(vc[u][c][i]);
-            vf[c * 8 + 2 * i + 1] = bf16hi(vc[u][c][i]);
-          } else {
-            vf[c * 4 + i] = __uint_as_float(vc[u][c][i]);
-          }
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = st.v[u][i];
+        if constexpr (BF16) {
+          vf[2 * i] = __uint_as_float(w << 16);
+          vf[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+        } else {
+          vf[i] = __uint_as_float(w);
         }
       }
 #pragma unroll
@@ -256,12 +245,32 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
     }
+  };
+
+  // Two register stages. The loads inside the loop are unconditional, so
+  // every path into the loop header has the same loads outstanding and the
+  // compiler waits only for the stage about to be used.
+  Stage<U> sa, sb;
+  load(sa, 0);
+  int s = 0;
+  for (; s + 2 < n_stages; s += 2) {
+    load(sb, s + 1);
+    compute(sa, s);
+    load(sa, s + 2);
+    compute(sb, s + 1);
+  }
+  if (s + 1 < n_stages) {
+    load(sb, s + 1);
+    compute(sa, s);
+    compute(sb, s + 1);
+  } else {
+    compute(sa, s);
   }
 
-  // Merge the 8 lane octets of the wave (they hold the same head-dim slice
-  // for different rows): butterfly over lane bits 3..5.
+  // Merge the RPL row slots of the wave (lanes that hold the same chunk for
+  // different rows): butterfly over the lane bits above the row's lanes.
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float mo = __shfl_xor(m[g], off);
@@ -279,11 +288,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
 
   // Merge the waves through LDS; the result is this workgroup's partial.
   __shared__ float red[kWaves][G][D + 2];
-  if (grp == 0) {
+  if (rslot == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) red[wave][g][dim_of<CE>(sub, e)] = acc[g][e];
+      for (int e = 0; e < EPL; ++e) red[wave][g][sub * EPL + e] = acc[g][e];
       if (sub == 0) {
         red[wave][g][D] = m[g];
         red[wave][g][D + 1] = l[g];
@@ -319,122 +328,98 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
       }
     }
   }
-  if (nsplit == 1 || !a.fused_combine) return;
-
-  // Last-arriving workgroup of the slice merges the nsplit partials.
-  __shared__ int last;
-  __threadfence();  // make this workgroup's partial visible device-wide
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned ticket = atomicAdd(&a.counters[slice], 1u);
-    last = (ticket == (unsigned)(nsplit - 1));
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();  // acquire the other workgroups' partials
-
-  __shared__ float wts[G][256];
-  __shared__ float Ms[G], Ls[G];
-  for (int g = 0; g < G; ++g) {
-    const size_t hq = (size_t)b * Hq + (size_t)h * G + g;
-    const float* part = a.partial + hq * nsplit * (D + 2);
-    if (tid < 64) {
-      float mx = -FLT_MAX;
-      for (int s = tid; s < nsplit; s += 64) mx = fmaxf(mx, part[s * (D + 2) + D]);
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      float lsum = 0.f;
-      for (int s = tid; s < nsplit; s += 64) {
-        const float wt = fast_exp2(part[s * (D + 2) + D] - mx);
-        wts[g][s] = wt;
-        lsum += part[s * (D + 2) + D + 1] * wt;
-      }
-      for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-      if (tid == 0) {
-        Ms[g] = mx;
-        Ls[g] = lsum;
-      }
-    }
-  }
-  __syncthreads();
-  for (int item = tid; item < G * D; item += kThreads) {
-    const int g = item / D;
-    const int d = item % D;
-    const size_t hq = (size_t)b * Hq + (size_t)h * G + g;
-    const float* part = a.partial + hq * nsplit * (D + 2);
-    float O = 0.f;
-    for (int s = 0; s < nsplit; ++s) O += part[s * (D + 2) + d] * wts[g][s];
-    a.out[hq * D + d] = O / Ls[g];
-    if (d == 0 && a.lse) a.lse[hq] = (Ms[g] + log2f(Ls[g])) * kLn2;
-  }
-  if (tid == 0) atomicExch(&a.counters[slice], 0u);
 }
 
-// Separate merge of the split partials (one workgroup per query head).
+// Merge of the split partials: one workgroup per query head, one thread per
+// head-dim element; each thread folds the splits in order with the online
+// softmax rule (the loads of a batch of splits are independent, so they are
+// all in flight at once).
 template <int D>
-__global__ __launch_bounds__(128) void combine_kernel(AttnLaunch a) {
-  const int hq_local = blockIdx.x;  // 0 .. H*G-1
-  const int b = blockIdx.y;
-  const int Hq = a.H * a.G;
-  const size_t hq = (size_t)b * Hq + hq_local;
+__global__ __launch_bounds__(D) void combine_kernel(AttnLaunch a) {
+  const size_t hq = (size_t)blockIdx.y * a.H * a.G + blockIdx.x;
   const int nsplit = a.nsplit;
   const float* part = a.partial + hq * nsplit * (D + 2);
-  __shared__ float wts[256];
-  __shared__ float ML[2];
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    float mx = -FLT_MAX;
-    for (int s = tid; s < nsplit; s += 64) mx = fmaxf(mx, part[s * (D + 2) + D]);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    float lsum = 0.f;
-    for (int s = tid; s < nsplit; s += 64) {
-      const float wt = fast_exp2(part[s * (D + 2) + D] - mx);
-      wts[s] = wt;
-      lsum += part[s * (D + 2) + D + 1] * wt;
-    }
-    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-    if (tid == 0) {
-      ML[0] = mx;
-      ML[1] = lsum;
-    }
+  const int d = threadIdx.x;
+  float M = -FLT_MAX, L = 0.f, O = 0.f;
+#pragma unroll 16
+  for (int s = 0; s < nsplit; ++s) {
+    const float* p = part + (size_t)s * (D + 2);
+    const float ms = p[D], ls = p[D + 1], os = p[d];
+    const float mx = fmaxf(M, ms);
+    const float c0 = fast_exp2(M - mx);
+    const float c1 = fast_exp2(ms - mx);
+    L = L * c0 + ls * c1;
+    O = O * c0 + os * c1;
+    M = mx;
   }
-  __syncthreads();
-  for (int d = tid; d < D; d += 128) {
-    float O = 0.f;
-    for (int s = 0; s < nsplit; ++s) O += part[s * (D + 2) + d] * wts[s];
-    a.out[hq * D + d] = O / ML[1];
-    if (d == 0 && a.lse) a.lse[hq] = (ML[0] + log2f(ML[1])) * kLn2;
-  }
+  a.out[hq * D + d] = O / L;
+  if (d == 0 && a.lse) a.lse[hq] = (M + log2f(L)) * kLn2;
+}
+
+template <bool BF16, int D, int G>
+hipError_t launch_one(const AttnLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<BF16, D, G>), dim3(a.nsplit, a.H, a.batch),
+                     dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.H * G, a.batch), dim3(D), 0,
+                     s, a);
+  return hipGetLastError();
 }
 
 template <bool BF16, int D>
 hipError_t launch_g(const AttnLaunch& a, hipStream_t s) {
-  dim3 grid(a.nsplit, a.H, a.batch);
   switch (a.G) {
-#define KVE_CASE(GG)                                                      \
-  case GG:                                                                \
-    hipLaunchKernelGGL((attn_kernel<BF16, D, GG>), grid, dim3(kThreads), 0, \
-                       s, a);                                             \
-    break;
-    KVE_CASE(1) KVE_CASE(2) KVE_CASE(3) KVE_CASE(4)
-    KVE_CASE(5) KVE_CASE(6) KVE_CASE(7) KVE_CASE(8)
-#undef KVE_CASE
-    default:
-      return hipErrorInvalidValue;
+    case 1: return launch_one<BF16, D, 1>(a, s);
+    case 2: return launch_one<BF16, D, 2>(a, s);
+    case 3: return launch_one<BF16, D, 3>(a, s);
+    case 4: return launch_one<BF16, D, 4>(a, s);
+    case 5: return launch_one<BF16, D, 5>(a, s);
+    case 6: return launch_one<BF16, D, 6>(a, s);
+    case 7: return launch_one<BF16, D, 7>(a, s);
+    case 8: return launch_one<BF16, D, 8>(a, s);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.nsplit > 1 && !a.fused_combine) {
-    hipLaunchKernelGGL((combine_kernel<D>), dim3(a.H * a.G, a.batch),
-                       dim3(128), 0, s, a);
-    e = hipGetLastError();
+  return hipErrorInvalidValue;
+}
+
+template <bool BF16, int D, int G>
+int resident_one() {
+  static int n = 0;  // per process; the same code object on every device
+  if (n == 0) {
+    int r = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &r, reinterpret_cast<const void*>(&attn_kernel<BF16, D, G>),
+            kThreads, 0) != hipSuccess || r < 1)
+      r = 1;
+    n = r;
   }
-  return e;
+  return n;
+}
+
+template <bool BF16, int D>
+int resident_g(int G) {
+  switch (G) {
+    case 1: return resident_one<BF16, D, 1>();
+    case 2: return resident_one<BF16, D, 2>();
+    case 3: return resident_one<BF16, D, 3>();
+    case 4: return resident_one<BF16, D, 4>();
+    case 5: return resident_one<BF16, D, 5>();
+    case 6: return resident_one<BF16, D, 6>();
+    case 7: return resident_one<BF16, D, 7>();
+    case 8: return resident_one<BF16, D, 8>();
+  }
+  return 1;
 }
 
 }  // namespace
 
+int attention_resident_workgroups(int is_bf16, int D, int G) {
+  if (is_bf16) return D == 128 ? resident_g<true, 128>(G) : resident_g<true, 64>(G);
+  return D == 128 ? resident_g<false, 128>(G) : resident_g<false, 64>(G);
+}
+
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s) {
-  if (a.nsplit < 1 || a.nsplit > 256) return hipErrorInvalidValue;
+  if (a.nsplit < 1 || a.nsplit > kMaxSplit) return hipErrorInvalidValue;
   if (a.is_bf16) {
     if (a.D == 128) return launch_g<true, 128>(a, s);
     if (a.D == 64) return launch_g<true, 64>(a, s);

@@ -1,5 +1,5 @@
 // Cache maintenance kernels: append, select (radix select of the eviction
-// cut), in-place order-preserving compaction, and a workspace fill.
+// cut) and in-place order-preserving compaction.
 //
 // Retention rule (KVpop section 3, Eq. 1 and 4; Appendix C.1, Eq. 26):
 // slots [0, S) are sink tokens and [len - W, len) the protected recent
@@ -239,12 +239,6 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(
   }
 }
 
-__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
 }  // namespace
 
 hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
@@ -279,16 +273,6 @@ hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
   hipLaunchKernelGGL(compact_kernel, dim3(slices, parts), dim3(kCompThreads),
                      0, s, (char*)k, (char*)v, score, pos, cap, row_bytes,
                      keep, n_keep);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
-  const size_t n = bytes / 4;
-  if (n == 0) return hipSuccess;
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s,
-                     (uint32_t*)p, n);
   return hipGetLastError();
 }
 

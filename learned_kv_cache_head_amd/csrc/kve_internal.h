@@ -33,18 +33,18 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // Launch descriptors.
 // ---------------------------------------------------------------------------
 
+constexpr int kMaxSplit = 256;  // split-K pieces per slice, at most
+
 struct AttnLaunch {
   const void* k;        // cache base [batch][H][cap][D]
   const void* v;
   const void* q;        // [batch][H*G][D]
   float* out;           // [batch][H*G][D]
   float* lse;           // [batch][H*G] or null
-  float* partial;       // [batch][H*G][nsplit][D+2] (m, l, acc[D])
-  uint32_t* counters;   // [batch*H], zero on entry and on exit
+  float* partial;       // [batch][H*G][nsplit][D+2] (acc[D], m, l); nsplit > 1
   int batch, H, G, D, cap, len;
   int nsplit, rows_per_split;
   int is_bf16;
-  int fused_combine;    // 1: last workgroup of a slice combines the splits
   // Optional fused append of the newest token into slot new_slot.
   int new_slot;         // -1: none
   int new_pos;
@@ -54,6 +54,9 @@ struct AttnLaunch {
   void* v_store;
   int32_t* pos;         // [batch][H][cap]
 };
+
+// Workgroups of the attention kernel for (dtype, D, G) that fit on one CU.
+int attention_resident_workgroups(int is_bf16, int D, int G);
 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 
@@ -95,7 +98,5 @@ struct GateLaunch {
   int slot_begin, slot_end;
 };
 hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s);
-
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace kve

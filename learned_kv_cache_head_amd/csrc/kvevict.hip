@@ -1,18 +1,19 @@
 // C-ABI layer of libkvevict: argument validation, launch planning and the
 // fused decode step. Validation happens on the host before any launch; the
 // library never allocates and never synchronises the device.
-#include "../../include/kvevict.h"
+#include "kvevict.h"
 
 #include "kve_internal.h"
 
 namespace {
 
-constexpr int kMaxSplit = 256;
-constexpr int kTargetWorkgroups = 2048;  // 8 per CU on 256 CUs
-constexpr int kMinRowsPerSplit = 128;
+// Split-K planning constants (rows are cache rows of one slice).
+constexpr int kSplitRowQuantum = 16;   // rows per split: a multiple of this
+constexpr int kMinRowsPerSplit = 64;   // no split shorter than this
+constexpr int kSplitTargetWGs = 4096;  // bound on slices * splits
+constexpr int kWgOverheadRows = 32;    // fixed cost of a workgroup, in rows
+constexpr int kCombineRows = 64;       // cost of the combine launch, in rows
 constexpr size_t kAlign = 256;
-
-bool g_fused_combine = true;  // separate combine kernel when false
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -43,33 +44,72 @@ kve_status check_cache(const kve_cache* c) {
   return KVE_OK;
 }
 
-// Split-K plan: enough workgroups to fill the chip, at least
-// kMinRowsPerSplit rows per split. Non-decreasing in len.
-int plan_nsplit(const kve_shape* s, int len) {
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Largest split count the planner may choose for a slice of len rows; it
+// depends on the shape only (not on the device) and never decreases with
+// len, so a workspace sized for max_len serves every len <= max_len.
+int split_cap(const kve_shape* s, int len) {
   const long long slices = (long long)s->batch * s->n_kv_heads;
-  long long ns = (kTargetWorkgroups + slices - 1) / slices;
-  const long long by_rows = (len + kMinRowsPerSplit - 1) / kMinRowsPerSplit;
+  long long ns = ceil_div(kSplitTargetWGs, slices);
+  const long long by_rows = ceil_div(len, kMinRowsPerSplit);
   if (ns > by_rows) ns = by_rows;
-  if (ns > kMaxSplit) ns = kMaxSplit;
+  if (ns > kve::kMaxSplit) ns = kve::kMaxSplit;
   if (ns < 1) ns = 1;
   return (int)ns;
 }
 
-struct WsLayout {
-  size_t counters_off, counters_bytes, partial_off, partial_bytes, total;
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n < 1)
+    n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+struct SplitPlan {
+  int nsplit, rows_per_split;
 };
 
-WsLayout ws_layout(const kve_shape* s, int nsplit) {
-  WsLayout w;
-  const size_t slices = (size_t)s->batch * s->n_kv_heads;
-  const size_t hq = slices * s->group;
-  w.counters_off = 0;
-  w.counters_bytes = align_up(slices * sizeof(uint32_t));
-  w.partial_off = w.counters_bytes;
-  w.partial_bytes =
-      nsplit > 1 ? align_up(hq * nsplit * (s->head_dim + 2) * sizeof(float)) : 0;
-  w.total = w.partial_off + w.partial_bytes;
-  return w;
+// Split-K plan of one decode-attention launch: the split count that
+// minimises (rounds of resident workgroups) x (rows per workgroup + fixed
+// cost) plus the combine launch when split. Ties go to fewer splits.
+SplitPlan plan_split(const kve_shape* s, int len) {
+  const long long slices = (long long)s->batch * s->n_kv_heads;
+  const long long slots =
+      (long long)device_cus() *
+      kve::attention_resident_workgroups(s->kv_dtype == KVE_BF16,
+                                         s->head_dim, s->group);
+  const int cap = split_cap(s, len);
+  SplitPlan best{1, len};
+  long long best_cost = -1;
+  for (int ns = 1; ns <= cap; ++ns) {
+    int rps = (int)ceil_div(len, ns);
+    rps = (int)ceil_div(rps, kSplitRowQuantum) * kSplitRowQuantum;
+    const int eff = (int)ceil_div(len, rps);
+    if (eff != ns) continue;  // same as a smaller split count
+    const long long rounds = ceil_div(slices * eff, slots);
+    const long long cost = rounds * (rps + kWgOverheadRows) +
+                           (eff > 1 ? kCombineRows : 0);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = SplitPlan{eff, eff == 1 ? len : rps};
+    }
+  }
+  return best;
+}
+
+// Workspace: split-K partial results (acc[D], m, l) per query head and split.
+size_t ws_bytes_for(const kve_shape* s, int nsplit) {
+  const size_t hq = (size_t)s->batch * s->n_kv_heads * s->group;
+  return nsplit > 1 ? align_up(hq * nsplit * (s->head_dim + 2) * sizeof(float))
+                    : 0;
 }
 
 kve_status from_hip(hipError_t e) { return e == hipSuccess ? KVE_OK : KVE_ERR_LAUNCH; }
@@ -78,30 +118,26 @@ kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
                      const void* q, float* out, float* lse, void* ws,
                      size_t ws_bytes, int new_slot, int new_pos,
                      const void* k_new, const void* v_new, hipStream_t stream) {
-  const int ns_plan = plan_nsplit(shape, len);
-  int rps = (len + ns_plan - 1) / ns_plan;
-  rps = (rps + 31) / 32 * 32;
-  const int nsplit = (len + rps - 1) / rps;
-  const WsLayout w = ws_layout(shape, ns_plan);
-  if (!ws || ws_bytes < w.total) return KVE_ERR_WORKSPACE;
+  const SplitPlan plan = plan_split(shape, len);
+  if (ws_bytes < ws_bytes_for(shape, plan.nsplit) ||
+      (plan.nsplit > 1 && !ws))
+    return KVE_ERR_WORKSPACE;
   kve::AttnLaunch a{};
   a.k = cache->k;
   a.v = cache->v;
   a.q = q;
   a.out = out;
   a.lse = lse;
-  a.partial = (float*)((char*)ws + w.partial_off);
-  a.counters = (uint32_t*)((char*)ws + w.counters_off);
+  a.partial = (float*)ws;
   a.batch = shape->batch;
   a.H = shape->n_kv_heads;
   a.G = shape->group;
   a.D = shape->head_dim;
   a.cap = shape->capacity;
   a.len = len;
-  a.nsplit = nsplit;
-  a.rows_per_split = rps;
+  a.nsplit = plan.nsplit;
+  a.rows_per_split = plan.rows_per_split;
   a.is_bf16 = shape->kv_dtype == KVE_BF16;
-  a.fused_combine = g_fused_combine ? 1 : 0;
   a.new_slot = new_slot;
   a.new_pos = new_pos;
   a.k_new = k_new;
@@ -193,12 +229,9 @@ const char* kve_status_str(kve_status s) {
 
 size_t kve_workspace_bytes(const kve_shape* shape, int32_t max_len) {
   if (check_shape(shape) != KVE_OK || max_len < 1) return 0;
-  return ws_layout(shape, plan_nsplit(shape, max_len)).total;
-}
-
-kve_status kve_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!ws || ws_bytes % 4 != 0) return KVE_ERR_INVALID_ARG;
-  return from_hip(kve::launch_fill_zero(ws, ws_bytes, stream));
+  // At least one aligned block, so a valid workspace pointer always exists.
+  const size_t n = ws_bytes_for(shape, split_cap(shape, max_len));
+  return n > 0 ? n : kAlign;
 }
 
 kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
@@ -305,10 +338,10 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   if (len < 0 || scored < 0 || scored > len) return KVE_ERR_INVALID_ARG;
   if (len >= shape->capacity) return KVE_ERR_CAPACITY;
   if (len - scored >= L) return KVE_ERR_INVALID_ARG;  // pending buffer full
-  // The attention after this step needs the workspace for len + 1 rows at
-  // most (plan is non-decreasing in len).
-  const WsLayout w = ws_layout(shape, plan_nsplit(shape, len + 1));
-  if (!ws || ws_bytes < w.total) return KVE_ERR_WORKSPACE;
+  // The attention after this step covers len + 1 rows at most, and the
+  // split cap never decreases with len.
+  if (!ws || ws_bytes < ws_bytes_for(shape, split_cap(shape, len + 1)))
+    return KVE_ERR_WORKSPACE;
 
   const int slot = len;
   const int position = state->next_position;
@@ -357,9 +390,5 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   state->next_position = position + 1;
   return KVE_OK;
 }
-
-// Test hook: choose between the fused last-workgroup merge of the split-K
-// partials (default) and the separate combine kernel.
-void kve_debug_set_fused_combine(int32_t on) { g_fused_combine = on != 0; }
 
 }  // extern "C"

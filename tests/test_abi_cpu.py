@@ -26,8 +26,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("kve_score", "kve_select_evict", "kve_compact",
                      "kve_decode_attn", "kve_step", "kve_append",
-                     "kve_workspace_bytes", "kve_workspace_init",
-                     "kve_status_str"):
+                     "kve_workspace_bytes", "kve_status_str"):
         assert required in names
 
 
@@ -70,14 +69,21 @@ def _cache():
 def test_workspace_bytes_host_math():
     s = _shape()
     n = _lib().kve_workspace_bytes(ctypes.byref(s), 1151)
-    # 16 slices -> ceil(2048/16) = 128 splits wanted, capped by rows: 9
-    nsplit = 9
-    counters = 256
+    # 16 slices: split cap = min(ceil(4096 / 16), ceil(1151 / 64), 256) = 18
+    # splits; per query head and split: 128 sums + max + normaliser, float32
+    nsplit = 18
     partial = 2 * 32 * nsplit * 130 * 4
-    partial = (partial + 255) // 256 * 256
-    assert n == counters + partial
+    assert n == (partial + 255) // 256 * 256
+    # enough slices for one split per slice: one aligned block
+    wide = _shape(batch=1024)
+    assert _lib().kve_workspace_bytes(ctypes.byref(wide), 64) == 256
+    # never decreases with max_len
+    sizes = [_lib().kve_workspace_bytes(ctypes.byref(s), m)
+             for m in range(1, 3000, 7)]
+    assert sizes == sorted(sizes)
     bad = _shape(head_dim=96)
     assert _lib().kve_workspace_bytes(ctypes.byref(bad), 100) == 0
+    assert _lib().kve_workspace_bytes(ctypes.byref(s), 0) == 0
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -18,6 +18,12 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # dtype, head_dim, group, n_kv, batch, len, capacity, key scale
     ("f32", 64, 2, 2, 1, 192, 256, 1.0),        # tiny workload shape
+    ("bf16", 128, 4, 8, 96, 1088, 1152, 1.0),   # batch-96 stack layer: no split
+    ("bf16", 128, 4, 8, 96, 1025, 1152, 1.0),   # ragged tail, no split
+    ("bf16", 128, 4, 8, 16, 1087, 1152, 1.0),   # batch-16 layer: split
+    ("bf16", 128, 4, 8, 8, 2175, 2304, 1.0),    # batch-8, B=2048 layer
+    ("bf16", 64, 2, 8, 64, 333, 400, 1.0),      # d = 64, many slices
+    ("f32", 128, 4, 8, 48, 257, 260, 1.0),      # float32, many slices
     ("bf16", 128, 4, 8, 2, 1087, 1152, 1.0),    # Qwen3-4B layer, mid-cycle
     ("bf16", 128, 4, 8, 2, 1024, 1152, 1.0),    # right after an eviction
     ("bf16", 128, 4, 2, 1, 1, 64, 1.0),         # single retained row
@@ -41,14 +47,13 @@ def _poison(t, length):
     t[:, :, length:] = float("nan")
 
 
-@pytest.mark.parametrize("fused", [True, False])
-@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2]}-n{c[5]}"
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2]}-b{c[4]}-n{c[5]}"
                                              for c in CASES])
-def test_decode_attention_matches_oracle(case, fused):
+def test_decode_attention_matches_oracle(case):
     import torch
     k = kve()
     dt, D, G, H, B, n, cap, kscale = case
-    print(f"[attn] {case} fused={fused}", flush=True)
+    print(f"[attn] {case}", flush=True)
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
     Ks = _rows(rng, (B, H, cap, D), dt, kscale)
     Vs = _rows(rng, (B, H, cap, D), dt, 1.0)
@@ -64,12 +69,8 @@ def test_decode_attention_matches_oracle(case, fused):
     out = torch.full((B, H * G, D), float("nan"), device=dev)
     lse = torch.full((B, H * G), float("nan"), device=dev)
     ws = k.alloc_workspace(shape, n, dev)
-    k.kve_debug_set_fused_combine(fused)
-    try:
-        k.kve_decode_attn(shape, cache, n, q, out, lse, ws)
-        torch.cuda.synchronize()
-    finally:
-        k.kve_debug_set_fused_combine(True)
+    k.kve_decode_attn(shape, cache, n, q, out, lse, ws)
+    torch.cuda.synchronize()
     got = out.cpu().double().numpy()
     got_lse = lse.cpu().double().numpy()
     for b in range(B):
@@ -80,9 +81,6 @@ def test_decode_attention_matches_oracle(case, fused):
             attn_close(got[b, h * G:(h + 1) * G], ref, f"b{b} h{h}")
             np.testing.assert_allclose(got_lse[b, h * G:(h + 1) * G], ref_lse,
                                        atol=LSE_ATOL, rtol=1e-5)
-    # the split-K completion counters must be back to zero
-    nslices = B * H
-    assert int(ws[:nslices].abs().sum().item()) == 0
 
 
 def test_decode_attention_deterministic_and_len_sweep():

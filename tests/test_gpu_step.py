@@ -73,7 +73,7 @@ class Tracker:
                 self.lay.pos[bi, h] = g
 
 
-def run_e2e(w, seed=0, fused=True, check_stride=1, layer=0):
+def run_e2e(w, seed=0, check_stride=1, layer=0):
     import torch
     k = kve()
     dev = torch.device("cuda")
@@ -120,42 +120,38 @@ def run_e2e(w, seed=0, fused=True, check_stride=1, layer=0):
     state = k.DecodeState(n, n, w.n0)
     out = torch.zeros((w.batch, w.n_q, w.head_dim), device=dev)
     lse = torch.zeros((w.batch, w.n_q), device=dev)
-    k.kve_debug_set_fused_combine(fused)
     G = w.group
     evictions = 0
-    try:
-        for i in range(w.steps):
-            st = syn.step_inputs(w, seed, layer, i)
-            if mlp:
-                sn = oracle_mlp_scores(st["k_new"].f64[:, :, None],
-                                       st["v_new"].f64[:, :, None], wts,
-                                       w.act)[:, :, 0]
-                k.kve_step(shape, pol, sc, cache, state, st["k_new"].torch(dev),
-                           st["v_new"].torch(dev), st["q"].torch(dev), out, lse,
-                           keep, ws)
-            else:
-                sn = oracle_gate_scores(st["hidden_new"].f64[:, None], gw)[:, :, 0]
-                k.kve_step(shape, pol, sc, cache, state, st["k_new"].torch(dev),
-                           st["v_new"].torch(dev), st["q"].torch(dev), out, lse,
-                           keep, ws, hidden_new=st["hidden_new"].torch(dev),
-                           hidden_buf=hbuf)
-            tr.step(w.n0 + i, st["k_new"].f64, st["v_new"].f64, sn)
-            evictions += state.evicted
-            if i % check_stride and not state.evicted and i != w.steps - 1:
-                continue
-            torch.cuda.synchronize()
-            gpu_pos = cache.pos[:, :, :state.len].cpu().numpy().astype(np.int64)
-            assert state.len == tr.lay.n
-            tr.check_and_sync(gpu_pos)
-            if state.evicted:
-                # scores of the retained entries match the oracle's by position
-                gs = cache.score[:, :, :state.len].cpu().numpy()
-                ref = np.take_along_axis(tr.S, gpu_pos, axis=2)
-                np.testing.assert_allclose(gs, ref, rtol=0, atol=SCORE_ATOL)
-            ref_out, _ = tr.lay.attend(st["q"].f64)
-            attn_close(out.cpu().double().numpy(), ref_out, f"step {i}")
-    finally:
-        k.kve_debug_set_fused_combine(True)
+    for i in range(w.steps):
+        st = syn.step_inputs(w, seed, layer, i)
+        if mlp:
+            sn = oracle_mlp_scores(st["k_new"].f64[:, :, None],
+                                   st["v_new"].f64[:, :, None], wts,
+                                   w.act)[:, :, 0]
+            k.kve_step(shape, pol, sc, cache, state, st["k_new"].torch(dev),
+                       st["v_new"].torch(dev), st["q"].torch(dev), out, lse,
+                       keep, ws)
+        else:
+            sn = oracle_gate_scores(st["hidden_new"].f64[:, None], gw)[:, :, 0]
+            k.kve_step(shape, pol, sc, cache, state, st["k_new"].torch(dev),
+                       st["v_new"].torch(dev), st["q"].torch(dev), out, lse,
+                       keep, ws, hidden_new=st["hidden_new"].torch(dev),
+                       hidden_buf=hbuf)
+        tr.step(w.n0 + i, st["k_new"].f64, st["v_new"].f64, sn)
+        evictions += state.evicted
+        if i % check_stride and not state.evicted and i != w.steps - 1:
+            continue
+        torch.cuda.synchronize()
+        gpu_pos = cache.pos[:, :, :state.len].cpu().numpy().astype(np.int64)
+        assert state.len == tr.lay.n
+        tr.check_and_sync(gpu_pos)
+        if state.evicted:
+            # scores of the retained entries match the oracle's by position
+            gs = cache.score[:, :, :state.len].cpu().numpy()
+            ref = np.take_along_axis(tr.S, gpu_pos, axis=2)
+            np.testing.assert_allclose(gs, ref, rtol=0, atol=SCORE_ATOL)
+        ref_out, _ = tr.lay.attend(st["q"].f64)
+        attn_close(out.cpu().double().numpy(), ref_out, f"step {i}")
     return evictions, tr
 
 
@@ -167,9 +163,9 @@ def test_tiny_workload_full_run():
     assert ev == w.steps  # L = 1 evicts at every step once saturated
 
 
-def test_tiny_workload_separate_combine():
+def test_tiny_workload_other_seed():
     w = syn.workload(1, steps=16)
-    run_e2e(w, fused=False, seed=1)
+    run_e2e(w, seed=1)
 
 
 @pytest.mark.parametrize("seed", [0, 1])
