@@ -31,6 +31,8 @@
 //    XCD, which costs far more than the second launch.
 #include <float.h>
 
+#include <type_traits>
+
 #include "kve_internal.h"
 
 namespace kve {
@@ -61,6 +63,34 @@ __device__ __forceinline__ float sum_row_lanes(float x) {
   if constexpr (LPR >= 64) x += __shfl_xor(x, 32);
   return x;
 }
+
+// Value of lane J of this lane's quad.
+template <int J>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return dpp_mov<J * 0x55>(x);
+}
+
+// Sums of four per-lane values (one per head of a quad of query heads) over
+// the 16 lanes of a row, reduce-scattered: quad lane j = lane & 3 of every
+// quad ends up with the full sum of one head (see quad_lane_of_head).
+// Two exchange steps inside the quad halve the values each time; two rotations
+// by 4 and 8 lanes inside the row add the four quads.
+__device__ __forceinline__ float reduce_scatter4(float t0, float t1, float t2,
+                                                 float t3, bool odd, bool hi) {
+  float a0 = odd ? t2 : t0, b0 = odd ? t0 : t2;
+  float a1 = odd ? t3 : t1, b1 = odd ? t1 : t3;
+  a0 += dpp_mov<0xB1>(b0);  // partner lane ^ 1
+  a1 += dpp_mov<0xB1>(b1);
+  float c = hi ? a1 : a0;
+  const float d = hi ? a0 : a1;
+  c += dpp_mov<0x4E>(d);    // partner lane ^ 2
+  c += dpp_mov<0x124>(c);   // row_ror:4
+  c += dpp_mov<0x128>(c);   // row_ror:8
+  return c;
+}
+// Quad lane j owns head ((j & 1) << 1) | (j >> 1) after reduce_scatter4; the
+// map is its own inverse, so head h sits in quad lane ((h & 1) << 1) | (h >> 1).
+constexpr int quad_lane_of_head(int h) { return ((h & 1) << 1) | (h >> 1); }
 
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
@@ -150,153 +180,302 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
     }
   }
 
-  float m[G], l[G], acc[G][EPL];
+  // Reduce-scatter path: 16 lanes per row and whole quads of query heads.
+  // Each lane then owns one head of every quad for the softmax bookkeeping.
+  constexpr bool RS = (LPR == 16) && (G % 4 == 0);
+  constexpr int NQ = RS ? G / 4 : 1;   // quads of query heads
+  constexpr int NS = RS ? NQ : G;      // softmax states per lane
+  const bool odd = (lane & 1) != 0;
+  const bool hi = (lane & 2) != 0;
+
+  // Running maximum (raw q.k in the reduce-scatter path, base-2 scaled logit
+  // otherwise), normaliser and accumulators.
+  float m[NS], l[NS], acc[G][EPL];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -FLT_MAX;
-    l[g] = 0.f;
+  for (int c = 0; c < NS; ++c) {
+    m[c] = -FLT_MAX;
+    l[c] = 0.f;
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  }
 
   const int nrows = r_end - r_begin;
   const int n_stages = (nrows + Gm::kStageRows - 1) / Gm::kStageRows;
   const int row0 = r_begin + wave * Gm::kWaveRows + rslot;
 
-  auto load = [&](Stage<U>& st, int s) {
+  using Full = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+
+  // Loads of one stage. The appended row (if any) is the last row of the
+  // slice, so it can only fall in the last stage of the last split: only
+  // that stage (MASK) clamps rows to r_end and reads the new row from k_new /
+  // v_new; full stages address the slice with 32-bit offsets.
+  const uint32_t lane_off =
+      (uint32_t)(wave * Gm::kWaveRows + rslot) * ROWB + (uint32_t)sub * 16;
+  auto load = [&](Stage<U>& st, int s, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = row0 + s * Gm::kStageRows + u * RPL;
-      const int rc = row < r_end ? row : r_end - 1;  // clamp: in bounds
-      const char* kr = (rc == new_slot) ? knew : kbase + (size_t)rc * ROWB;
-      const char* vr = (rc == new_slot) ? vnew : vbase + (size_t)rc * ROWB;
-      st.k[u] = *(const u32x4*)(kr + sub * 16);
-      st.v[u] = *(const u32x4*)(vr + sub * 16);
+      if constexpr (MASK) {
+        const int row = row0 + s * Gm::kStageRows + u * RPL;
+        const int rc = row < r_end ? row : r_end - 1;  // clamp: in bounds
+        const char* kr = (rc == new_slot) ? knew : kbase + (size_t)rc * ROWB;
+        const char* vr = (rc == new_slot) ? vnew : vbase + (size_t)rc * ROWB;
+        st.k[u] = *(const u32x4*)(kr + sub * 16);
+        st.v[u] = *(const u32x4*)(vr + sub * 16);
+      } else {
+        const uint32_t off = (uint32_t)(r_begin + s * Gm::kStageRows + u * RPL) *
+                                 ROWB + lane_off;
+        st.k[u] = *(const u32x4*)(kbase + off);
+        st.v[u] = *(const u32x4*)(vbase + off);
+      }
     }
   };
 
-  auto compute = [&](const Stage<U>& st, int s) {
-    float sc[U][G];
+  // This lane's partial q.k of row u for head g (its 16-byte chunk).
+  auto partial_dot = [&](const Stage<U>& st, int u, int g) {
+    float t = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = row0 + s * Gm::kStageRows + u * RPL < r_end;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float t = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // Copy the vector elements to scalars before the bit casts: a bit
-          // cast applied directly to an ext_vector element lvalue reads
-          // element 0 with this compiler.
-          const uint32_t kw = st.k[u][i];
-          const uint32_t qw = qv[g][i];
-          if constexpr (BF16) {
-            t = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_bit_cast(bf16x2_t, qw),
-                __builtin_bit_cast(bf16x2_t, kw), t, false);
-          } else {
-            t = fmaf(__uint_as_float(qw), __uint_as_float(kw), t);
-          }
-        }
-        t = sum_row_lanes<LPR>(t);
-        if constexpr (BF16) t *= qscale;
-        sc[u][g] = ok ? t : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      // Copy the vector elements to scalars before the bit casts: a bit
+      // cast applied directly to an ext_vector element lvalue reads
+      // element 0 with this compiler.
+      const uint32_t kw = st.k[u][i];
+      const uint32_t qw = qv[g][i];
+      if constexpr (BF16) {
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw),
+                                            __builtin_bit_cast(bf16x2_t, kw),
+                                            t, false);
+      } else {
+        t = fmaf(__uint_as_float(qw), __uint_as_float(kw), t);
       }
     }
-    float p[U][G], alpha[G];
-    bool moved = false;
+    return t;
+  };
+
+  auto v_floats = [&](const Stage<U>& st, int u, float (&vf)[EPL]) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = m[g];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = st.v[u][i];
+      if constexpr (BF16) {
+        vf[2 * i] = __uint_as_float(w << 16);
+        vf[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+      } else {
+        vf[i] = __uint_as_float(w);
+      }
+    }
+  };
+
+  // One stage of rows. MASK: some rows of the stage may lie past r_end (only
+  // the last stage of a workgroup).
+  auto compute = [&](const Stage<U>& st, int s, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    bool ok[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
-      alpha[g] = fast_exp2(m[g] - mx);
-      moved |= (mx != m[g]);
-      m[g] = mx;
-      float lsum = l[g] * alpha[g];
+    for (int u = 0; u < U; ++u)
+      ok[u] = !MASK || (row0 + s * Gm::kStageRows + u * RPL < r_end);
+    if constexpr (RS) {
+      // Scores of the owned heads, raw q.k (the 1/sqrt(d) and log2(e) factor
+      // qscale > 0 is applied inside the exponentials).
+      float sc[U][NQ];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+          const float t = reduce_scatter4(
+              partial_dot(st, u, 4 * c), partial_dot(st, u, 4 * c + 1),
+              partial_dot(st, u, 4 * c + 2), partial_dot(st, u, 4 * c + 3),
+              odd, hi);
+          sc[u][c] = ok[u] ? t : -INFINITY;
+        }
+      float p[U][NQ], alpha[NQ];
+      bool moved = false;
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        float mx = m[c];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][c]);
+        moved |= (mx != m[c]);
+        alpha[c] = fast_exp2((m[c] - mx) * qscale);
+        const float nmx = -mx * qscale;
+        float lsum = l[c] * alpha[c];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          p[u][c] = fast_exp2(fmaf(sc[u][c], qscale, nmx));
+          lsum += p[u][c];
+        }
+        l[c] = lsum;
+        m[c] = mx;
+      }
+      if (wave_any(moved)) {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+          const float al[4] = {quad_bcast<quad_lane_of_head(0)>(alpha[c]),
+                               quad_bcast<quad_lane_of_head(1)>(alpha[c]),
+                               quad_bcast<quad_lane_of_head(2)>(alpha[c]),
+                               quad_bcast<quad_lane_of_head(3)>(alpha[c])};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[4 * c + j][e] *= al[j];
+        }
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        p[u][g] = fast_exp2(sc[u][g] - mx);
-        lsum += p[u][g];
-      }
-      l[g] = lsum;
-    }
-    if (wave_any(moved)) {
+        float vf[EPL];
+        v_floats(st, u, vf);
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+        for (int c = 0; c < NQ; ++c) {
+          const float pb[4] = {quad_bcast<quad_lane_of_head(0)>(p[u][c]),
+                               quad_bcast<quad_lane_of_head(1)>(p[u][c]),
+                               quad_bcast<quad_lane_of_head(2)>(p[u][c]),
+                               quad_bcast<quad_lane_of_head(3)>(p[u][c])};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha[g];
-    }
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[EPL];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = st.v[u][i];
-        if constexpr (BF16) {
-          vf[2 * i] = __uint_as_float(w << 16);
-          vf[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
-        } else {
-          vf[i] = __uint_as_float(w);
+            for (int e = 0; e < EPL; ++e)
+              acc[4 * c + j][e] = fmaf(pb[j], vf[e], acc[4 * c + j][e]);
         }
       }
+    } else {
+      // Every lane keeps all G heads: full row sums by DPP.
+      float sc[U][G];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
+        for (int g = 0; g < G; ++g) {
+          float t = sum_row_lanes<LPR>(partial_dot(st, u, g));
+          if constexpr (BF16) t *= qscale;
+          sc[u][g] = ok[u] ? t : -INFINITY;
+        }
+      float p[U][G], alpha[G];
+      bool moved = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = m[g];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
+        alpha[g] = fast_exp2(m[g] - mx);
+        moved |= (mx != m[g]);
+        m[g] = mx;
+        float lsum = l[g] * alpha[g];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          p[u][g] = fast_exp2(sc[u][g] - mx);
+          lsum += p[u][g];
+        }
+        l[g] = lsum;
+      }
+      if (wave_any(moved)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha[g];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float vf[EPL];
+        v_floats(st, u, vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
+      }
     }
   };
 
   // Two register stages. The loads inside the loop are unconditional, so
   // every path into the loop header has the same loads outstanding and the
-  // compiler waits only for the stage about to be used.
+  // compiler waits only for the stage about to be used. Only the last stage
+  // can hold rows past r_end.
   Stage<U> sa, sb;
-  load(sa, 0);
-  int s = 0;
-  for (; s + 2 < n_stages; s += 2) {
-    load(sb, s + 1);
-    compute(sa, s);
-    load(sa, s + 2);
-    compute(sb, s + 1);
-  }
-  if (s + 1 < n_stages) {
-    load(sb, s + 1);
-    compute(sa, s);
-    compute(sb, s + 1);
+  if (n_stages == 1) {
+    load(sa, 0, Masked{});
+    compute(sa, 0, Masked{});
   } else {
-    compute(sa, s);
-  }
-
-  // Merge the RPL row slots of the wave (lanes that hold the same chunk for
-  // different rows): butterfly over the lane bits above the row's lanes.
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      const float mx = fmaxf(m[g], mo);
-      const float a0 = fast_exp2(m[g] - mx);
-      const float a1 = fast_exp2(mo - mx);
-      l[g] = l[g] * a0 + lo * a1;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        acc[g][e] = acc[g][e] * a0 + __shfl_xor(acc[g][e], off) * a1;
-      m[g] = mx;
+    load(sa, 0, Full{});
+    int s = 0;
+    for (; s + 2 < n_stages; s += 2) {
+      load(sb, s + 1, Full{});
+      compute(sa, s, Full{});
+      if (s + 2 == n_stages - 1) {
+        load(sa, s + 2, Masked{});
+      } else {
+        load(sa, s + 2, Full{});
+      }
+      compute(sb, s + 1, Full{});
+    }
+    if (s + 1 < n_stages) {
+      load(sb, s + 1, Masked{});
+      compute(sa, s, Full{});
+      compute(sb, s + 1, Masked{});
+    } else {
+      compute(sa, s, Masked{});
     }
   }
 
-  // Merge the waves through LDS; the result is this workgroup's partial.
-  __shared__ float red[kWaves][G][D + 2];
-  if (rslot == 0) {
+  // Per-head (scaled maximum, normaliser) in every lane.
+  float mh[G], lh[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) red[wave][g][sub * EPL + e] = acc[g][e];
-      if (sub == 0) {
-        red[wave][g][D] = m[g];
-        red[wave][g][D + 1] = l[g];
+  for (int g = 0; g < G; ++g) {
+    if constexpr (RS) {
+      float mv, lv;
+      switch (g & 3) {
+        case 0: mv = quad_bcast<quad_lane_of_head(0)>(m[g >> 2]);
+                lv = quad_bcast<quad_lane_of_head(0)>(l[g >> 2]); break;
+        case 1: mv = quad_bcast<quad_lane_of_head(1)>(m[g >> 2]);
+                lv = quad_bcast<quad_lane_of_head(1)>(l[g >> 2]); break;
+        case 2: mv = quad_bcast<quad_lane_of_head(2)>(m[g >> 2]);
+                lv = quad_bcast<quad_lane_of_head(2)>(l[g >> 2]); break;
+        default: mv = quad_bcast<quad_lane_of_head(3)>(m[g >> 2]);
+                 lv = quad_bcast<quad_lane_of_head(3)>(l[g >> 2]); break;
       }
+      mh[g] = mv * qscale;
+      lh[g] = lv;
+    } else {
+      mh[g] = m[g];
+      lh[g] = l[g];
+    }
+  }
+
+  // Merge the 4 * RPL partial states of the workgroup (one per wave and row
+  // slot; each holds every head and, across its LPR lanes, every dim)
+  // through LDS: per head, the weight of each partial first, then one
+  // weighted sum per output element.
+  constexpr int NP = kWaves * RPL;
+  __shared__ float red[NP][G][D];
+  __shared__ float ml[NP][G][2];
+  __shared__ float wts[G][NP];
+  __shared__ float tot[G][2];
+  const int pidx = wave * RPL + rslot;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) red[pidx][g][sub * EPL + e] = acc[g][e];
+    if (sub == 0) {
+      ml[pidx][g][0] = mh[g];
+      ml[pidx][g][1] = lh[g];
+    }
+  }
+  __syncthreads();
+  for (int g = wave; g < G; g += kWaves) {
+    // One wave per head: lane i < NP takes partial i.
+    const int i = lane;
+    const float mi = i < NP ? ml[i][g][0] : -FLT_MAX;
+    float M = mi;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = i < NP ? fast_exp2(mi - M) : 0.f;
+    float L = i < NP ? ml[i][g][1] * w : 0.f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (i < NP) wts[g][i] = w;
+    if (i == 0) {
+      tot[g][0] = M;
+      tot[g][1] = L;
     }
   }
   __syncthreads();
@@ -305,16 +484,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
   for (int item = tid; item < G * D; item += kThreads) {
     const int g = item / D;
     const int d = item % D;
-    float M = red[0][g][D];
+    float O = 0.f;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w][g][D]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(red[w][g][D] - M);
-      L += red[w][g][D + 1] * wt;
-      O += red[w][g][d] * wt;
-    }
+    for (int q = 0; q < NP; ++q) O = fmaf(red[q][g][d], wts[g][q], O);
+    const float M = tot[g][0], L = tot[g][1];
     const size_t hq = (size_t)b * Hq + (size_t)h * G + g;
     if (nsplit == 1) {
       a.out[hq * D + d] = O / L;

@@ -118,6 +118,9 @@ kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
                      const void* q, float* out, float* lse, void* ws,
                      size_t ws_bytes, int new_slot, int new_pos,
                      const void* k_new, const void* v_new, hipStream_t stream) {
+  // The attention kernel reads the appended row from k_new / v_new only in
+  // the last stage of the last split, so it must be the slice's last row.
+  if (new_slot >= 0 && new_slot != len - 1) return KVE_ERR_INVALID_ARG;
   const SplitPlan plan = plan_split(shape, len);
   if (ws_bytes < ws_bytes_for(shape, plan.nsplit) ||
       (plan.nsplit > 1 && !ws))
