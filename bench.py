@@ -145,10 +145,9 @@ class Stack:
                              for _ in range(w.layers)]
         torch.cuda.synchronize()
 
-    def run_step(self, i: int, keep_for=None, events=None, ev_base=0):
+    def run_step(self, i: int, keep_for=None):
         """Decode step i over all layers. keep_for(l) may supply the buffer
-        that receives the kept slots of an evicting call; events[ev_base+l+1]
-        is recorded after layer l."""
+        that receives the kept slots of an evicting call."""
         j = i % self.pool_steps
         for l, r in enumerate(self.runners):
             keep = self.keep_scratch[l]
@@ -156,8 +155,6 @@ class Stack:
                 keep = keep_for(l)
             r(self.k_pool[l][j], self.v_pool[l][j], self.q_pool[l][j],
               self.out, None, keep)
-            if events is not None:
-                events[ev_base + l + 1].record()
 
 
 # ---------------------------------------------------------------------------
@@ -318,17 +315,23 @@ def main() -> int:
         keep_bufs[(l, c)] = buf
         return buf
 
+    # One event after every step (plus one before the first): a step without
+    # an eviction is exactly one attention launch per layer, so its duration
+    # over the layer count is the mean launch duration of the kernel,
+    # measured on the stream the launches go to.
     use_events = not args.no_kernel_events
     events = None
     if use_events:
         events = [torch.cuda.Event(enable_timing=True)
-                  for _ in range(steps * n_layers + 1)]
+                  for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     if use_events:
         events[0].record()
     for s in range(steps):
-        stack.run_step(warmup + s, keep_for, events, s * n_layers)
+        stack.run_step(warmup + s, keep_for)
+        if use_events:
+            events[s + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {steps} steps in {wall * 1e3:.1f} ms")
@@ -357,12 +360,11 @@ def main() -> int:
                 total_bytes += evict_extra_bytes(w, n, moved[(l, c)])
                 total_bytes += attn_launch_bytes(w, w.budget, False)
             else:
-                b_ = attn_launch_bytes(w, n, True)
-                total_bytes += b_
-                if use_events:
-                    j = s * n_layers + l
-                    attn_bytes.append(b_)
-                    attn_ms.append(events[j].elapsed_time(events[j + 1]))
+                total_bytes += attn_launch_bytes(w, n, True)
+        if use_events and not ev:
+            step_ms = events[s].elapsed_time(events[s + 1])
+            attn_bytes += [attn_launch_bytes(w, n, True)] * n_layers
+            attn_ms += [step_ms / n_layers] * n_layers
 
     tokens_s = w.batch * steps / wall
     step_gbps = total_bytes / wall / 1e9
