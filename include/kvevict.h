@@ -43,8 +43,9 @@
  *   keep_slots  [batch][n_kv_heads][n_keep]               int32, ascending
  * Query head j reads KV head j / group (contiguous GQA groups).
  * Every (batch, KV head) slice holds the same number of entries `len` in
- * slots [0, len), in strictly increasing position order; the library keeps
- * that order (compaction is order-preserving).
+ * slots [0, len), with distinct positions in any slot order: new tokens are
+ * appended at slot len, and compaction moves entries from the end into the
+ * slots it frees.
  */
 #ifndef KVEVICT_H
 #define KVEVICT_H
@@ -162,22 +163,29 @@ kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
                      const void* hidden, hipStream_t stream);
 
 /* a3 Select (KVpop Eq. 4 and Eq. 26; ForesightKV periodic eviction): cut
- * each slice of `len` entries to `n_keep`. Slots [0, S) and [len - W, len)
- * are protected; among candidate slots [S, len - W) the len - n_keep with
- * the smallest (float32 score, slot) keys are evicted - equal scores evict
- * the older entry first, and -0.0 ranks as +0.0. Writes the kept slots in
- * ascending order to keep_slots [batch][H][n_keep]. Requires
- * 0 <= n_keep <= len <= capacity, and S + W <= n_keep when n_keep < len;
- * n_keep == len writes the identity. Scores must be finite. */
+ * each slice of `len` entries to `n_keep`. With P the newest position in the
+ * slice, entries with position < S (sinks) or > P - W (recent window) are
+ * protected; among the eligible entries (S <= position <= P - W) the
+ * len - n_keep with the smallest (float32 score, position) keys are evicted:
+ * equal scores evict the older entry first, and -0.0 ranks as +0.0. Writes
+ * the kept slots in ascending order to keep_slots [batch][H][n_keep].
+ * Requires 0 <= n_keep <= len <= capacity, and S + W <= n_keep when
+ * n_keep < len; n_keep == len writes the identity. Scores must be finite;
+ * positions distinct, with the S oldest and W newest present (as the
+ * library's own appends and compaction keep them). */
 kve_status kve_select_evict(const kve_shape* shape, const kve_policy* policy,
                             const kve_cache* cache, int32_t len,
                             int32_t n_keep, int32_t* keep_slots,
                             hipStream_t stream);
 
-/* a4 Compact in place, order-preserving (KVpop Appendix C): new slot i =
- * old slot keep_slots[i] for K, V, score and pos, i < n_keep. keep_slots
- * must be strictly ascending with keep_slots[i] < len <= capacity (as
- * kve_select_evict writes it). Slots >= n_keep are left as they were. */
+/* a4 Compact in place (KVpop Appendix C: the cache keeps only retained
+ * entries) after kve_select_evict: keep_slots lists the n_keep kept slots
+ * of each slice in ascending order (each < len <= capacity). Kept entries
+ * in slots below n_keep stay in place; the slots below n_keep that were not
+ * kept, in ascending order, receive the kept entries from slots at or above
+ * n_keep, in ascending order (K, V, score and pos move together). At most
+ * min(n_keep, len - n_keep) rows per slice move. Slots >= n_keep are left
+ * as they were. */
 kve_status kve_compact(const kve_shape* shape, kve_cache* cache, int32_t len,
                        const int32_t* keep_slots, int32_t n_keep,
                        hipStream_t stream);

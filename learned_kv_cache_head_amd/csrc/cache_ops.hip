@@ -1,13 +1,14 @@
 // Cache maintenance kernels: append, select (radix select of the eviction
-// cut) and in-place order-preserving compaction.
+// cut) and in-place compaction by hole filling.
 //
 // Retention rule (KVpop section 3, Eq. 1 and 4; Appendix C.1, Eq. 26):
-// slots [0, S) are sink tokens and [len - W, len) the protected recent
-// window; the other slots are the eligible long-range candidates, of which
-// the top ones by score are kept. Periodic eviction (ForesightKV summary,
+// positions below S are sink tokens and the W most recent positions the
+// protected window; the other entries are the eligible long-range
+// candidates, of which the top ones by score are kept. Periodic eviction (ForesightKV summary,
 // "Methodology in plain English"; Fast KVzip Appendix A.5) cuts a slice of
 // len entries back to n_keep = B entries. Ranking uses float32 scores
-// (KVpop Appendix F) with the older entry evicted first among equal scores.
+// (KVpop Appendix F) with the older entry (lower position) evicted first
+// among equal scores.
 #include "kve_internal.h"
 
 namespace kve {
@@ -44,12 +45,19 @@ __global__ __launch_bounds__(64) void append_kernel(
 // ---------------------------------------------------------------------------
 // Select: one workgroup per slice.
 //
-// Among the m = len - S - W candidates, evict the r = len - n_keep with the
-// smallest (score, slot) keys. A four-pass 8-bit MSB radix select finds the
-// r-th smallest 32-bit score key thr and the number need of entries equal
-// to thr that fall below the cut; a final ordered pass evicts every key
-// < thr and the first `need` keys == thr in slot order (older first), and
-// writes the survivors' slots in ascending order with a block-wide scan.
+// Candidates are the entries of the eligible set E(P) = {S <= pos <= P - W}
+// with P the newest position present (KVpop Eq. 4); all other entries (sink
+// tokens, recent window) are kept. Among the candidates, the r = len -
+// n_keep with the smallest (score, position) keys are evicted.
+//  1. block max of the positions -> P;
+//  2. four 8-bit MSB radix passes over the orderable 32-bit score keys of
+//     the candidates -> the r-th smallest key thr, the number `need` of
+//     entries with key thr to evict and the number of candidates with it;
+//  3. if some but not all candidates with key thr are evicted, four radix
+//     passes over their positions -> the need-th smallest such position;
+//  4. an ordered pass writes the kept slots ascending (block-wide scan).
+// Every output write is bounded by n_keep, so positions that break the
+// contract (duplicates, missing sinks or window) cannot write out of bounds.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -82,34 +90,29 @@ __device__ __forceinline__ uint32_t block_excl_count(bool flag, uint32_t* sh,
   return before + in_wave;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const float* score, int cap, int len, int n_keep, int S, int W,
-    int32_t* keep) {
-  const size_t slice = blockIdx.x;
-  const float* sc = score + slice * (size_t)cap;
-  int32_t* out = keep + slice * (size_t)n_keep;
+// Radix select over 32-bit keys: the value of the `rank`-th smallest key
+// (1-based) among the entries i < len with take(i), and how many of those
+// keys equal it must still be taken (`rank` minus the number of smaller
+// keys). `count_eq` receives how many such entries have exactly that key.
+template <typename KeyFn, typename TakeFn>
+__device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
+                             TakeFn take, uint32_t* hist, uint32_t* wsum,
+                             uint32_t* sh, uint32_t* key_out,
+                             uint32_t* need_out, uint32_t* count_eq_out) {
   const int tid = threadIdx.x;
-
-  if (n_keep >= len) {  // nothing to evict: identity
-    for (int i = tid; i < len; i += kSelThreads) out[i] = i;
-    return;
-  }
-  const int m = len - S - W;      // candidates, slots [S, len - W)
-  const int r = len - n_keep;     // entries to evict, 1 <= r <= m
-  for (int i = tid; i < S; i += kSelThreads) out[i] = i;
-  for (int j = tid; j < W; j += kSelThreads) out[n_keep - W + j] = len - W + j;
-
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[kSelWaves];
-  __shared__ uint32_t sh_digit, sh_below;
-  uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)r;
+  uint32_t prefix = 0, mask = 0, remaining = rank, count_eq = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    if (tid == 0) {
+      sh[0] = 255u;   // defaults: last bin, nothing below (never read if
+      sh[1] = 0u;     // rank <= number of entries, which the caller ensures)
+      sh[2] = 0u;
+    }
     __syncthreads();
-    for (int c = tid; c < m; c += kSelThreads) {
-      const uint32_t key = score_key(sc[S + c]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int c = tid; c < len; c += kSelThreads) {
+      if (!take(c)) continue;
+      const uint32_t k = key_of(c);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
     // Inclusive scan of the 256 bins by threads 0..255 (4 waves).
@@ -129,113 +132,170 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (tid < 256) {
       for (int w = 0; w < (tid >> 6); ++w) incl += wsum[w];
       if (incl >= remaining && incl - v < remaining) {
-        sh_digit = (uint32_t)tid;
-        sh_below = incl - v;
+        sh[0] = (uint32_t)tid;
+        sh[1] = incl - v;
+        sh[2] = v;
       }
     }
     __syncthreads();
-    prefix |= sh_digit << shift;
+    const uint32_t digit = sh[0];
+    prefix |= digit << shift;
     mask |= 255u << shift;
-    remaining -= sh_below;
+    remaining -= sh[1];
+    count_eq = sh[2];
     __syncthreads();
   }
-  const uint32_t thr = prefix;     // key of the r-th smallest candidate
-  const uint32_t need = remaining; // keys == thr to evict (oldest first)
+  *key_out = prefix;
+  *need_out = remaining;
+  *count_eq_out = count_eq;
+}
 
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* score, const int32_t* pos, int cap, int len, int n_keep,
+    int S, int W, int32_t* keep) {
+  const size_t slice = blockIdx.x;
+  const float* sc = score + slice * (size_t)cap;
+  const int32_t* ps = pos + slice * (size_t)cap;
+  int32_t* out = keep + slice * (size_t)n_keep;
+  const int tid = threadIdx.x;
+
+  if (n_keep >= len) {  // nothing to evict: identity
+    for (int i = tid; i < len; i += kSelThreads) out[i] = i;
+    return;
+  }
+  const uint32_t r = (uint32_t)(len - n_keep);  // entries to evict
+
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t sh[4];
+  __shared__ int32_t sh_max[kSelWaves];
+
+  // 1. Newest position present.
+  int32_t mx = INT32_MIN;
+  for (int c = tid; c < len; c += kSelThreads) mx = max(mx, ps[c]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) sh_max[tid >> 6] = mx;
+  __syncthreads();
+  int32_t newest = sh_max[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) newest = max(newest, sh_max[w]);
+  const long long last_eligible = (long long)newest - W;
+  auto is_cand = [&](int c) {
+    const int32_t p = ps[c];
+    return p >= S && (long long)p <= last_eligible;
+  };
+  auto skey = [&](int c) { return score_key(sc[c]); };
+
+  // 2. Cut score key.
+  uint32_t thr, need, count_eq;
+  radix_select(len, r, skey, is_cand, hist, wsum, sh, &thr, &need, &count_eq);
+
+  // 3. Among candidates with key thr, evict the `need` (>= 1) oldest: all of
+  // them unless the cut falls inside the tie.
+  uint32_t pthr = 0xffffffffu;
+  if (need < count_eq) {
+    auto tied = [&](int c) { return is_cand(c) && skey(c) == thr; };
+    auto pkey = [&](int c) { return (uint32_t)ps[c]; };
+    uint32_t pneed, pcount;
+    radix_select(len, need, pkey, tied, hist, wsum, sh, &pthr, &pneed,
+                 &pcount);
+  }
+
+  // 4. Kept slots, ascending.
   __shared__ uint32_t scan_sh[kSelWaves];
-  uint32_t carry_eq = 0, carry_keep = 0;
-  for (int base = 0; base < m; base += kSelThreads) {
+  uint32_t carry = 0;
+  for (int base = 0; base < len; base += kSelThreads) {
     const int c = base + tid;
-    const bool valid = c < m;
-    const uint32_t key = valid ? score_key(sc[S + c]) : 0u;
-    const bool is_eq = valid && key == thr;
-    const bool is_lt = valid && key < thr;
-    uint32_t tot_eq, tot_keep;
-    const uint32_t eq_rank = carry_eq + block_excl_count(is_eq, scan_sh, &tot_eq);
-    const bool kept = valid && !is_lt && !(is_eq && eq_rank < need);
-    const uint32_t kidx =
-        carry_keep + block_excl_count(kept, scan_sh, &tot_keep);
-    if (kept) out[S + kidx] = S + c;
-    carry_eq += tot_eq;
-    carry_keep += tot_keep;
+    bool kept = false;
+    if (c < len) {
+      kept = true;
+      if (is_cand(c)) {
+        const uint32_t k = skey(c);
+        if (k < thr) kept = false;
+        else if (k == thr && (uint32_t)ps[c] <= pthr)
+          kept = false;
+      }
+    }
+    uint32_t tot;
+    const uint32_t idx = carry + block_excl_count(kept, scan_sh, &tot);
+    if (kept && idx < (uint32_t)n_keep) out[idx] = c;
+    carry += tot;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Compact in place, order-preserving: new slot i = old slot keep[i].
+// Compact in place by filling holes (KVpop Appendix C: the decode cache
+// holds only retained entries): keep[0..n_keep) lists the kept slots
+// ascending. Kept entries below n_keep stay where they are; the j-th slot
+// below n_keep that was not kept (a hole, ascending) receives the j-th kept
+// entry at or above n_keep (ascending). Sources lie at or above n_keep and
+// destinations below it, so no copy can overwrite an unread source, and all
+// copies run in parallel.
 //
-// Grid: (slice, part); each part owns one 128-byte column block of the K or
-// V rows (part 0 also moves score and pos). keep is strictly ascending, so
-// keep[i] >= i and the destination of output i never lies after its source.
-// Outputs are processed in ascending chunks; every chunk reads all of its
-// sources before any of its writes (barrier in between), and later chunks'
-// sources lie beyond this chunk's destinations, so no unread source is ever
-// overwritten. Slots before the first hole (keep[i] == i) are skipped.
+// With i0 kept slots below n_keep, the number of holes before keep[i]
+// (i < i0) is c(i) = keep[i] - i, non-decreasing, and c(i0) = n_keep - i0 =
+// the number of holes. Hole j lies in the gap before the first i with
+// c(i) > j, at slot j + i.
+//
+// Grid: (slice, group of kCompRows moved rows); 8 threads per row copy its
+// K and V bytes with 16-byte accesses.
 // ---------------------------------------------------------------------------
 constexpr int kCompThreads = 256;
-constexpr int kCompRowsPerLoad = kCompThreads / 8;  // 8 lanes x 16 B per row
-constexpr int kCompLoads = 4;
-constexpr int kCompChunk = kCompRowsPerLoad * kCompLoads;  // 128 rows
+constexpr int kCompRows = kCompThreads / 8;  // rows per workgroup
 
 __global__ __launch_bounds__(kCompThreads) void compact_kernel(
     char* k, char* v, float* score, int32_t* pos, int cap, int row_bytes,
     const int32_t* keep, int n_keep) {
   const size_t slice = blockIdx.x;
-  const int parts_per_tensor = row_bytes / 128;
-  const int part = blockIdx.y;
-  const int tensor = part / parts_per_tensor;
-  const int col = part % parts_per_tensor;
-  char* base = (tensor == 0 ? k : v) + slice * (size_t)cap * row_bytes + col * 128;
-  const bool meta = (part == 0);
-  float* sc = score + slice * (size_t)cap;
-  int32_t* ps = pos + slice * (size_t)cap;
   const int32_t* kp = keep + slice * (size_t)n_keep;
   const int tid = threadIdx.x;
-
-  // First index that moves: keep[i] == i holds exactly for i < first.
-  __shared__ int sh_first;
+  __shared__ int sh_i0;
+  __shared__ int dst_sh[kCompRows], src_sh[kCompRows];
   if (tid == 0) {
-    int lo = 0, hi = n_keep;  // invariant: keep[i] == i for i < lo
+    int lo = 0, hi = n_keep;  // first i with keep[i] >= n_keep
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (kp[mid] == mid) lo = mid + 1; else hi = mid;
+      if (kp[mid] < n_keep) lo = mid + 1; else hi = mid;
     }
-    sh_first = lo;
+    sh_i0 = lo;
   }
   __syncthreads();
-  const int first = sh_first;
-
-  const int r_in = tid >> 3;        // row within a load
-  const int c16 = (tid & 7) * 16;   // byte offset within the 128-byte block
-  for (int c0 = first; c0 < n_keep; c0 += kCompChunk) {
-    u32x4 val[kCompLoads];
-    float sv = 0.f;
-    int32_t pv = 0;
-#pragma unroll
-    for (int j = 0; j < kCompLoads; ++j) {
-      const int i = c0 + j * kCompRowsPerLoad + r_in;
-      if (i < n_keep) {
-        const int src = kp[i];
-        val[j] = *(const u32x4*)(base + (size_t)src * row_bytes + c16);
+  const int i0 = sh_i0;
+  const int holes = n_keep - i0;
+  const int j0 = blockIdx.y * kCompRows;
+  if (j0 >= holes) return;  // uniform: no barrier below for this group
+  if (tid < kCompRows) {
+    const int j = j0 + tid;
+    int d = -1, src = -1;
+    if (j < holes) {
+      int lo = 0, hi = i0;  // first i in [0, i0] with c(i) > j
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (kp[mid] - mid > j) hi = mid; else lo = mid + 1;
       }
+      d = j + lo;
+      src = kp[i0 + j];
     }
-    const int im = c0 + tid;
-    if (meta && tid < kCompChunk && im < n_keep) {
-      const int src = kp[im];
-      sv = sc[src];
-      pv = ps[src];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kCompLoads; ++j) {
-      const int i = c0 + j * kCompRowsPerLoad + r_in;
-      if (i < n_keep) *(u32x4*)(base + (size_t)i * row_bytes + c16) = val[j];
-    }
-    if (meta && tid < kCompChunk && im < n_keep) {
-      sc[im] = sv;
-      ps[im] = pv;
-    }
-    __syncthreads();
+    dst_sh[tid] = d;
+    src_sh[tid] = src;
+  }
+  __syncthreads();
+  const int row = tid >> 3;
+  const int sub = tid & 7;
+  const int d = dst_sh[row];
+  const int src = src_sh[row];
+  if (d < 0) return;
+  const size_t base = slice * (size_t)cap;
+  const size_t drow = (base + d) * (size_t)row_bytes;
+  const size_t srow = (base + src) * (size_t)row_bytes;
+  for (int c = sub * 16; c < row_bytes; c += 128) {
+    *(u32x4*)(k + drow + c) = *(const u32x4*)(k + srow + c);
+    *(u32x4*)(v + drow + c) = *(const u32x4*)(v + srow + c);
+  }
+  if (sub == 0) {
+    score[base + d] = score[base + src];
+    pos[base + d] = pos[base + src];
   }
 }
 
@@ -257,20 +317,25 @@ hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* score, int slices, int cap, int len,
-                         int n_keep, int S, int W, int32_t* keep,
-                         hipStream_t s) {
+hipError_t launch_select(const float* score, const int32_t* pos, int slices,
+                         int cap, int len, int n_keep, int S, int W,
+                         int32_t* keep, hipStream_t s) {
   hipLaunchKernelGGL(select_kernel, dim3(slices), dim3(kSelThreads), 0, s,
-                     score, cap, len, n_keep, S, W, keep);
+                     score, pos, cap, len, n_keep, S, W, keep);
   return hipGetLastError();
 }
 
 hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
-                          int slices, int cap, int row_bytes,
+                          int slices, int cap, int row_bytes, int len,
                           const int32_t* keep, int n_keep, hipStream_t s) {
   if (row_bytes % 128 != 0) return hipErrorInvalidValue;
-  const int parts = 2 * (row_bytes / 128);
-  hipLaunchKernelGGL(compact_kernel, dim3(slices, parts), dim3(kCompThreads),
+  // Moved rows per slice: at most the slots at or above n_keep, and at most
+  // the holes below it.
+  const int max_moves = n_keep < len - n_keep ? n_keep : len - n_keep;
+  if (max_moves <= 0) return hipSuccess;
+  const int groups = (max_moves + kCompRows - 1) / kCompRows;
+  if (groups > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(compact_kernel, dim3(slices, groups), dim3(kCompThreads),
                      0, s, (char*)k, (char*)v, score, pos, cap, row_bytes,
                      keep, n_keep);
   return hipGetLastError();

@@ -32,7 +32,10 @@ Readings where the pages leave a step open (also listed in the design notes):
 
 * The window holds the W most recent tokens including the newest one
   (KVpop Appendix C.1, set 2: q - t < w), so eligible tokens satisfy
-  S <= t <= P - W for newest position P.
+  S <= t <= P - W for newest position P. Sinks, window and candidates are
+  identified by position, not by slot.
+* Compaction keeps kept entries below the new count in place and moves the
+  kept entries above it into the freed slots, both in ascending slot order.
 * Eviction fires after prefill when n0 > B, and during decode when the cache
   count n reaches B + L; it evicts n - B entries, so the cache holds B after
   every eviction and B..B+L-1 between evictions.
@@ -54,8 +57,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "Policy", "mlp_score", "gate_score", "score_to_f32", "select_keep",
-    "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
+    "Policy", "mlp_score", "gate_score", "score_to_f32", "eligible_mask",
+    "select_keep", "compaction_sources", "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
     "closed_form_retained", "cache_bytes_per_token",
 ]
 
@@ -131,42 +134,71 @@ def score_to_f32(s: np.ndarray) -> np.ndarray:
 # Selection and compaction
 # ---------------------------------------------------------------------------
 
+def eligible_mask(pos: np.ndarray, sinks: int, window: int) -> np.ndarray:
+    """Entries that may be evicted: position t with S <= t <= P - W, where P
+    is the newest position present (KVpop Eq. (4), the eligible set E(P));
+    the others are the sink tokens and the recent window."""
+    pos = np.asarray(pos)
+    if pos.size == 0:
+        return np.zeros(0, dtype=bool)
+    newest = pos.max()
+    return (pos >= sinks) & (pos <= newest - window)
+
+
 def select_keep(score32: np.ndarray, pos: np.ndarray, length: int,
                 n_keep: int, sinks: int, window: int) -> np.ndarray:
     """Slots kept when a cache slice of ``length`` entries is cut to
     ``n_keep`` entries.
 
-    Protected: slots [0, S) (sinks) and [length - W, length) (the recent
-    window). Candidates: slots [S, length - W), i.e. the eligible set E of
-    KVpop Eq. (4) restricted to the cache. The length - n_keep candidates
-    with the smallest (float32 score, position) are evicted; the rest are
-    kept (KVpop Eq. (26): top-k of the eligible tokens).
+    Candidates are the entries of the eligible set E(P) (``eligible_mask``).
+    The length - n_keep candidates with the smallest (float32 score,
+    position) are evicted; every other entry is kept (KVpop Eq. (26): sinks,
+    recent window and the top-k eligible tokens).
 
     Returns the kept slot indices in ascending order (int64).
     """
-    score32 = np.asarray(score32, dtype=np.float32)
-    pos = np.asarray(pos)
+    score32 = np.asarray(score32, dtype=np.float32)[:length]
+    pos = np.asarray(pos)[:length]
     if n_keep >= length:
         return np.arange(length, dtype=np.int64)
     r = length - n_keep
-    lo, hi = sinks, length - window
-    if hi - lo < r:
+    cand = np.nonzero(eligible_mask(pos, sinks, window))[0]
+    if cand.size < r:
         raise ValueError("not enough eligible entries to evict")
-    cand = np.arange(lo, hi, dtype=np.int64)
-    s = score32[lo:hi] + np.float32(0.0)
-    order = np.lexsort((pos[lo:hi], s))      # ascending score, then position
-    evicted = np.zeros(hi - lo, dtype=bool)
-    evicted[order[:r]] = True
-    keep = np.concatenate([np.arange(0, lo, dtype=np.int64), cand[~evicted],
-                           np.arange(hi, length, dtype=np.int64)])
-    return keep
+    s = score32[cand] + np.float32(0.0)
+    order = np.lexsort((pos[cand], s))      # ascending score, then position
+    evicted = np.zeros(length, dtype=bool)
+    evicted[cand[order[:r]]] = True
+    return np.nonzero(~evicted)[0].astype(np.int64)
+
+
+def compaction_sources(keep: np.ndarray) -> np.ndarray:
+    """Where each slot of the compacted slice comes from (KVpop Appendix C:
+    the decode cache holds only retained entries).
+
+    ``keep`` lists the n_keep kept slots in ascending order. Kept entries in
+    slots below n_keep stay where they are; the slots below n_keep that were
+    not kept (holes), in ascending order, receive the kept entries from slots
+    at or above n_keep, in ascending order. Returns src with
+    new[i] = old[src[i]] for i < n_keep.
+    """
+    keep = np.asarray(keep, dtype=np.int64)
+    n_keep = keep.size
+    below = keep[keep < n_keep]
+    movers = keep[keep >= n_keep]
+    holes = np.setdiff1d(np.arange(n_keep, dtype=np.int64), below)
+    assert holes.size == movers.size
+    src = np.arange(n_keep, dtype=np.int64)
+    src[holes] = movers
+    return src
 
 
 def compact_slice(arrays: Sequence[np.ndarray], keep: np.ndarray
                   ) -> List[np.ndarray]:
-    """Order-preserving compaction: new row i = old row keep[i] (KVpop
-    Appendix C: the decode cache holds only retained entries)."""
-    return [np.asarray(a)[keep].copy() for a in arrays]
+    """The compacted rows of each array: new row i = old row src[i]
+    (``compaction_sources``)."""
+    src = compaction_sources(keep)
+    return [np.asarray(a)[src].copy() for a in arrays]
 
 
 # ---------------------------------------------------------------------------
@@ -209,7 +241,9 @@ class OracleLayer:
     slice holding the same number of entries.
 
     State per slice: K, V rows (float64 values of the stored dtype), float32
-    score and int64 absolute position, in ascending position order.
+    score and int64 absolute position. New tokens go to the end; evictions
+    fill holes from the end (``compaction_sources``), so slot order is not
+    position order.
     Scores are computed when a token is appended; the scorer is stateless so
     this equals scoring the buffered tokens at eviction time.
     """
@@ -236,16 +270,18 @@ class OracleLayer:
     def _evict_to(self, n_keep: int) -> np.ndarray:
         b, H = self.K.shape[:2]
         keeps = np.empty((b, H, n_keep), dtype=np.int64)
+        srcs = np.empty((b, H, n_keep), dtype=np.int64)
         for bi in range(b):
             for h in range(H):
                 keeps[bi, h] = select_keep(self.score[bi, h], self.pos[bi, h],
                                            self.n, n_keep, self.policy.sinks,
                                            self.policy.window)
-        idx = keeps[..., None]
+                srcs[bi, h] = compaction_sources(keeps[bi, h])
+        idx = srcs[..., None]
         self.K = np.take_along_axis(self.K, idx, axis=2)
         self.V = np.take_along_axis(self.V, idx, axis=2)
-        self.score = np.take_along_axis(self.score, keeps, axis=2)
-        self.pos = np.take_along_axis(self.pos, keeps, axis=2)
+        self.score = np.take_along_axis(self.score, srcs, axis=2)
+        self.pos = np.take_along_axis(self.pos, srcs, axis=2)
         self.last_evict_newest = self.newest
         self.evictions += 1
         return keeps

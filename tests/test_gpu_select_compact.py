@@ -1,5 +1,6 @@
 """a3 select and a4 compact: bit-exact against the oracle when both sides
-are given the same float32 scores, including every kind of tie."""
+are given the same float32 scores and positions, including every kind of
+tie and caches whose slot order is not position order."""
 import numpy as np
 import pytest
 
@@ -42,37 +43,50 @@ SELECT_CASES = [
 ]
 
 
-def _cache_for_scores(k, shape, scores_np, dev):
+def _cache_for_scores(k, shape, scores_np, pos_np, dev):
     import torch
     tiny = torch.zeros(1, device=dev)
     c = k.CacheTensors(tiny, tiny, torch.from_numpy(scores_np).to(dev),
-                       torch.zeros(1, dtype=torch.int32, device=dev))
+                       torch.from_numpy(pos_np.astype(np.int32)).to(dev))
     return c
 
 
+def _positions(rng, B, H, cap, n, order):
+    """Positions 0..n-1 per slice (slots past n: -1), in slot order or
+    shuffled (a cache whose evictions filled holes from the end)."""
+    pos = np.full((B, H, cap), -1, np.int64)
+    for b in range(B):
+        for h in range(H):
+            pos[b, h, :n] = (np.arange(n) if order == "sorted"
+                             else rng.permutation(n))
+    return pos
+
+
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
 @pytest.mark.parametrize("pattern", ["normal", "ties3", "const", "zeros",
                                      "sigmoid", "wide"])
 @pytest.mark.parametrize("case", SELECT_CASES,
                          ids=[f"S{c[0]}W{c[1]}n{c[2]}k{c[3]}"
                               for c in SELECT_CASES])
-def test_select_bit_exact(case, pattern):
+def test_select_bit_exact(case, pattern, order):
     import torch
     k = kve()
     S, W, n, nk, B, H = case
-    print(f"[select] {case} {pattern}", flush=True)
+    print(f"[select] {case} {pattern} {order}", flush=True)
     cap = n + 7
     rng = np.random.default_rng(n * 31 + nk)
     sc = _scores(rng, pattern, (B, H, cap))
+    pos = _positions(rng, B, H, cap, n, order)
     shape = k.Shape(B, H, 1, 128, cap, k.BF16)
     pol = k.Policy(max(nk, S + W), S, W, 1)
     dev = torch.device("cuda")
-    cache = _cache_for_scores(k, shape, sc, dev)
+    cache = _cache_for_scores(k, shape, sc, pos, dev)
     keep = torch.full((B, H, nk), -1, dtype=torch.int32, device=dev)
     k.kve_select_evict(shape, pol, cache, n, nk, keep)
     got = keep.cpu().numpy()
     for b in range(B):
         for h in range(H):
-            ref = O.select_keep(sc[b, h, :n], np.arange(n), n, nk, S, W)
+            ref = O.select_keep(sc[b, h, :n], pos[b, h, :n], n, nk, S, W)
             np.testing.assert_array_equal(got[b, h], ref,
                                           err_msg=f"slice {b},{h}")
 
@@ -84,15 +98,16 @@ def test_select_one_shot_compression_131k():
     S, W, n, nk, B, H = 4, 512, 131072, 39321, 1, 8
     rng = np.random.default_rng(99)
     sc = _scores(rng, "sigmoid", (B, H, n))
+    pos = _positions(rng, B, H, n, n, "sorted")
     shape = k.Shape(B, H, 5, 128, n, k.BF16)
     pol = k.Policy(nk, S, W, 64)
     dev = torch.device("cuda")
-    cache = _cache_for_scores(k, shape, sc, dev)
+    cache = _cache_for_scores(k, shape, sc, pos, dev)
     keep = torch.full((B, H, nk), -1, dtype=torch.int32, device=dev)
     k.kve_select_evict(shape, pol, cache, n, nk, keep)
     got = keep.cpu().numpy()
     for h in range(H):
-        ref = O.select_keep(sc[0, h], np.arange(n), n, nk, S, W)
+        ref = O.select_keep(sc[0, h], pos[0, h], n, nk, S, W)
         np.testing.assert_array_equal(got[0, h], ref)
 
 
@@ -153,7 +168,10 @@ def test_compact_bit_exact(case):
     keep_t = torch.from_numpy(keeps).to(dev)
     k.kve_compact(shape, cache, n, keep_t, nk)
     torch.cuda.synchronize()
-    idx = torch.from_numpy(keeps.astype(np.int64)).to(dev)
+    # expected placement: the oracle's hole filling
+    srcs = np.stack([[O.compaction_sources(keeps[b, h]) for h in range(H)]
+                     for b in range(B)])
+    idx = torch.from_numpy(srcs.astype(np.int64)).to(dev)
     expK = torch.gather(K0, 2, idx[..., None].expand(B, H, nk, D))
     expV = torch.gather(V0, 2, idx[..., None].expand(B, H, nk, D))
     iv = torch.int16 if dt == "bf16" else torch.int32

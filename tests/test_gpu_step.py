@@ -37,10 +37,15 @@ class Tracker:
         self.cut = np.full((b, H), np.nan)
 
     def _record_cut(self):
+        """Lowest kept score among the eligible entries right after an
+        eviction (positions S..P-W): the cut of the next comparison."""
         p = self.policy
-        lo, hi = p.sinks, p.budget - p.window
-        if hi > lo:
-            self.cut = self.lay.score[:, :, lo:hi].min(axis=2).astype(np.float64)
+        b, H = self.lay.pos.shape[:2]
+        for bi in range(b):
+            for h in range(H):
+                m = O.eligible_mask(self.lay.pos[bi, h], p.sinks, p.window)
+                if m.any():
+                    self.cut[bi, h] = float(self.lay.score[bi, h][m].min())
 
     def prefill(self):
         if self.lay.prefill_compress() is not None:

@@ -57,12 +57,24 @@ def select_newest_first_on_ties(score32, pos, length, n_keep, sinks, window):
     if n_keep >= length:
         return np.arange(length)
     r = length - n_keep
-    lo, hi = sinks, length - window
-    order = np.lexsort((-np.asarray(pos[lo:hi]), score32[lo:hi]))
-    ev = np.zeros(hi - lo, bool)
-    ev[order[:r]] = True
-    return np.concatenate([np.arange(lo), np.arange(lo, hi)[~ev],
-                           np.arange(hi, length)])
+    pos = np.asarray(pos)[:length]
+    cand = np.nonzero(O.eligible_mask(pos, sinks, window))[0]
+    order = np.lexsort((-pos[cand], np.asarray(score32)[cand]))
+    ev = np.zeros(length, bool)
+    ev[cand[order[:r]]] = True
+    return np.nonzero(~ev)[0]
+
+
+def select_by_slot_ranges(score32, pos, length, n_keep, sinks, window):
+    """Protects slots [0, S) and [len - W, len) instead of positions."""
+    if n_keep >= length:
+        return np.arange(length)
+    r = length - n_keep
+    cand = np.arange(sinks, length - window)
+    order = np.lexsort((np.asarray(pos)[cand], np.asarray(score32)[cand]))
+    ev = np.zeros(length, bool)
+    ev[cand[order[:r]]] = True
+    return np.nonzero(~ev)[0]
 
 
 def select_window_off_by_one(score32, pos, length, n_keep, sinks, window):
@@ -76,6 +88,7 @@ def select_evicts_highest(score32, pos, length, n_keep, sinks, window):
 
 
 @pytest.mark.parametrize("mutant", [select_newest_first_on_ties,
+                                    select_by_slot_ranges,
                                     select_window_off_by_one,
                                     select_evicts_highest])
 def test_select_mutants_fail(mutant):
@@ -98,6 +111,25 @@ def closed_form_oldest_kept(score_by_pos32, newest, last, policy):
     top = elig[order[:k]]
     recent = np.arange(max(last - W + 1, S), newest + 1)
     return np.unique(np.concatenate([np.arange(S), top, recent]))
+
+
+def sources_order_preserving(keep):
+    return np.asarray(keep)
+
+
+def sources_movers_reversed(keep):
+    keep = np.asarray(keep)
+    n = keep.size
+    src = np.arange(n)
+    holes = np.setdiff1d(np.arange(n), keep[keep < n])
+    src[holes] = keep[keep >= n][::-1]
+    return src
+
+
+@pytest.mark.parametrize("mutant", [sources_order_preserving,
+                                    sources_movers_reversed])
+def test_compaction_mutants_fail(mutant):
+    _fails(P.check_compaction, mutant)
 
 
 def test_closed_form_mutant_fails():

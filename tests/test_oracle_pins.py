@@ -102,21 +102,24 @@ def test_score_to_f32_canonical_zero_and_rounding():
 # Selection pins
 # ---------------------------------------------------------------------------
 
-def brute_force_keep(scores, length, n_keep, S, W):
+def brute_force_keep(scores, pos, length, n_keep, S, W):
     """Rank every candidate by counting how many candidates precede it in
-    (score, position) order; the r lowest ranks are evicted."""
+    (score, position) order; the r lowest ranks are evicted. Candidates are
+    the entries whose position t satisfies S <= t <= P - W (P the newest
+    position present)."""
     if n_keep >= length:
         return list(range(length))
     r = length - n_keep
-    cands = list(range(S, length - W))
+    P = max(pos[:length])
+    cands = [u for u in range(length) if S <= pos[u] <= P - W]
     keep = []
     for t in range(length):
-        if t < S or t >= length - W:
+        if t not in cands:
             keep.append(t)
             continue
         rank = sum(1 for u in cands
                    if (scores[u] < scores[t]) or
-                   (scores[u] == scores[t] and u < t))
+                   (scores[u] == scores[t] and pos[u] < pos[t]))
         if rank >= r:
             keep.append(t)
     return keep
@@ -132,16 +135,20 @@ def check_select_hand(select_keep):
 
 def check_select_brute_force(select_keep):
     alphabet = np.array([0.5, 1.0, 2.0], dtype=np.float32)
+    rng = np.random.default_rng(6)
     for S, W in ((0, 0), (1, 2), (2, 1)):
         for m in range(0, 6):
             length = S + W + m
             for pattern in itertools.product(range(3), repeat=length):
                 sc = alphabet[list(pattern)]
-                pos = np.arange(length) + 100
-                for r in range(0, m + 1):
-                    n_keep = length - r
-                    got = list(select_keep(sc, pos, length, n_keep, S, W))
-                    assert got == brute_force_keep(sc, length, n_keep, S, W)
+                # positions 0..length-1 in slot order, and shuffled (a cache
+                # whose evictions filled holes from the end)
+                for pos in (np.arange(length), rng.permutation(length)):
+                    for r in range(0, m + 1):
+                        n_keep = length - r
+                        got = list(select_keep(sc, pos, length, n_keep, S, W))
+                        assert got == brute_force_keep(sc, pos, length,
+                                                       n_keep, S, W)
 
 
 def test_select_hand_case():
@@ -160,9 +167,9 @@ def test_select_random_matches_brute_force():
         length = S + W + m
         sc = rng.integers(0, 5, size=length).astype(np.float32) * 0.25
         r = rng.integers(0, m + 1)
-        got = list(O.select_keep(sc, np.arange(length), length, length - r,
-                                 S, W))
-        assert got == brute_force_keep(sc, length, length - r, S, W)
+        pos = rng.permutation(length) + 0
+        got = list(O.select_keep(sc, pos, length, length - r, S, W))
+        assert got == brute_force_keep(sc, pos, length, length - r, S, W)
 
 
 def test_select_k_zero_keeps_sinks_and_window_only():
@@ -188,14 +195,67 @@ def test_constant_scores_give_streaming_llm():
     lay = O.OracleLayer(K0, K0, np.zeros((1, 1, n0), np.float32), pol, 1)
     lay.prefill_compress()
     expected = list(range(3)) + list(range(n0 - 21, n0))
-    assert list(lay.pos[0, 0]) == expected
+    assert sorted(lay.pos[0, 0]) == expected
     for _ in range(13):
         kn = rng.standard_normal((1, 1, d))
         lay.append(kn, kn, np.zeros((1, 1), np.float32))
         if lay.maybe_evict() is not None:
             P = lay.newest
-            assert list(lay.pos[0, 0]) == list(range(3)) + \
+            assert sorted(lay.pos[0, 0]) == list(range(3)) + \
                 list(range(P - 20, P + 1))
+
+
+def brute_force_sources(keep, n_keep):
+    """Hole filling written out slot by slot: walk the slots below n_keep in
+    order; a kept slot stays, a hole takes the next kept slot at or above
+    n_keep (in order)."""
+    kept = set(int(x) for x in keep)
+    movers = [int(x) for x in keep if x >= n_keep]
+    src, nxt = [], 0
+    for i in range(n_keep):
+        if i in kept:
+            src.append(i)
+        else:
+            src.append(movers[nxt])
+            nxt += 1
+    assert nxt == len(movers)
+    return src
+
+
+def check_compaction(compaction_sources):
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        length = int(rng.integers(1, 40))
+        n_keep = int(rng.integers(0, length + 1))
+        keep = np.sort(rng.choice(length, n_keep, replace=False))
+        src = list(compaction_sources(keep))
+        assert src == brute_force_sources(keep, n_keep)
+        # the compacted slice holds exactly the kept entries ...
+        assert sorted(src) == list(keep)
+        # ... kept entries below n_keep never move, and only the kept
+        # entries at or above n_keep are moved
+        for i, j in enumerate(src):
+            if j != i:
+                assert j >= n_keep and i not in set(keep.tolist())
+    # hand case: slots 0..7 cut to 5, keep {0, 2, 5, 6, 7}: holes 1, 3, 4
+    # take 5, 6, 7 in order
+    assert list(compaction_sources(np.array([0, 2, 5, 6, 7]))) == \
+        [0, 5, 2, 6, 7]
+
+
+def test_compaction_hole_filling():
+    check_compaction(O.compaction_sources)
+
+
+def test_compact_slice_moves_rows_bitwise():
+    rng = np.random.default_rng(22)
+    K = rng.standard_normal((12, 3))
+    pos = np.arange(12) * 7
+    keep = np.array([0, 1, 4, 8, 9, 11])
+    K2, pos2 = O.compact_slice([K, pos], keep)
+    src = [0, 1, 8, 9, 4, 11]   # holes 2, 3, 5 take 8, 9, 11
+    np.testing.assert_array_equal(K2, K[src])
+    np.testing.assert_array_equal(pos2, pos[src])
 
 
 # ---------------------------------------------------------------------------
@@ -209,13 +269,14 @@ def run_incremental(policy, n0, steps, scores_by_pos, seed=0, d=4):
     lay = O.OracleLayer(K0, K0, scores_by_pos[None, None, :n0], policy, 1)
     history = []
     lay.prefill_compress()
-    history.append((lay.newest, lay.last_evict_newest, lay.pos[0, 0].copy()))
+    history.append((lay.newest, lay.last_evict_newest,
+                    np.sort(lay.pos[0, 0])))
     for i in range(steps):
         kn = rng.standard_normal((1, 1, d))
         lay.append(kn, kn, scores_by_pos[n0 + i].reshape(1, 1))
         lay.maybe_evict()
         history.append((lay.newest, lay.last_evict_newest,
-                        lay.pos[0, 0].copy()))
+                        np.sort(lay.pos[0, 0])))
     return history
 
 
@@ -242,14 +303,14 @@ def test_incremental_loop_equals_closed_form():
 
 def test_invariants_over_config1_shape():
     """Sinks and window are never evicted, count == B after every eviction,
-    positions strictly increasing (KVpop Eq. (1), Eq. (26))."""
+    positions distinct (KVpop Eq. (1), Eq. (26))."""
     w = syn.workload(1)
     pol = O.Policy(w.budget, w.sinks, w.window, w.evict_len)
     rng = np.random.default_rng(12)
     n0 = w.n0
     sc = rng.standard_normal(n0 + w.steps).astype(np.float32)
     for newest, pe, kept in run_incremental(pol, n0, w.steps, sc):
-        assert np.all(np.diff(kept) > 0)
+        assert np.all(np.diff(kept) > 0)           # sorted, hence distinct
         assert set(range(w.sinks)) <= set(kept)
         assert set(range(newest - w.window + 1, newest + 1)) <= set(kept)
         assert len(kept) <= w.budget + w.evict_len - 1
