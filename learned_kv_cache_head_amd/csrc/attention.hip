@@ -558,41 +558,7 @@ hipError_t launch_g(const AttnLaunch& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <bool BF16, int D, int G>
-int resident_one() {
-  static int n = 0;  // per process; the same code object on every device
-  if (n == 0) {
-    int r = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &r, reinterpret_cast<const void*>(&attn_kernel<BF16, D, G>),
-            kThreads, 0) != hipSuccess || r < 1)
-      r = 1;
-    n = r;
-  }
-  return n;
-}
-
-template <bool BF16, int D>
-int resident_g(int G) {
-  switch (G) {
-    case 1: return resident_one<BF16, D, 1>();
-    case 2: return resident_one<BF16, D, 2>();
-    case 3: return resident_one<BF16, D, 3>();
-    case 4: return resident_one<BF16, D, 4>();
-    case 5: return resident_one<BF16, D, 5>();
-    case 6: return resident_one<BF16, D, 6>();
-    case 7: return resident_one<BF16, D, 7>();
-    case 8: return resident_one<BF16, D, 8>();
-  }
-  return 1;
-}
-
 }  // namespace
-
-int attention_resident_workgroups(int is_bf16, int D, int G) {
-  if (is_bf16) return D == 128 ? resident_g<true, 128>(G) : resident_g<true, 64>(G);
-  return D == 128 ? resident_g<false, 128>(G) : resident_g<false, 64>(G);
-}
 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s) {
   if (a.nsplit < 1 || a.nsplit > kMaxSplit) return hipErrorInvalidValue;

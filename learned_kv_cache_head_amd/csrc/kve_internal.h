@@ -55,9 +55,6 @@ struct AttnLaunch {
   int32_t* pos;         // [batch][H][cap]
 };
 
-// Workgroups of the attention kernel for (dtype, D, G) that fit on one CU.
-int attention_resident_workgroups(int is_bf16, int D, int G);
-
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 
 hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,

@@ -77,15 +77,15 @@ struct SplitPlan {
   int nsplit, rows_per_split;
 };
 
-// Split-K plan of one decode-attention launch: the split count that
-// minimises (rounds of resident workgroups) x (rows per workgroup + fixed
-// cost) plus the combine launch when split. Ties go to fewer splits.
+// Split-K plan of one decode-attention launch. One workgroup with its
+// non-temporal loads in flight streams at about a CU's share of HBM
+// bandwidth, so the model is per CU: the rows its workgroups stream, plus a
+// fixed cost per workgroup it runs, plus the combine launch when split. The
+// plan minimises that; ties go to fewer splits. (Measured: when slices are
+// fewer than CUs the best plan is one workgroup per CU.)
 SplitPlan plan_split(const kve_shape* s, int len) {
   const long long slices = (long long)s->batch * s->n_kv_heads;
-  const long long slots =
-      (long long)device_cus() *
-      kve::attention_resident_workgroups(s->kv_dtype == KVE_BF16,
-                                         s->head_dim, s->group);
+  const long long cus = device_cus();
   const int cap = split_cap(s, len);
   SplitPlan best{1, len};
   long long best_cost = -1;
@@ -94,8 +94,8 @@ SplitPlan plan_split(const kve_shape* s, int len) {
     rps = (int)ceil_div(rps, kSplitRowQuantum) * kSplitRowQuantum;
     const int eff = (int)ceil_div(len, rps);
     if (eff != ns) continue;  // same as a smaller split count
-    const long long rounds = ceil_div(slices * eff, slots);
-    const long long cost = rounds * (rps + kWgOverheadRows) +
+    const long long per_cu = ceil_div(slices * eff, cus);
+    const long long cost = per_cu * (rps + kWgOverheadRows) +
                            (eff > 1 ? kCombineRows : 0);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
