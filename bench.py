@@ -255,7 +255,7 @@ def main() -> int:
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-batch", type=int, default=8)
+    ap.add_argument("--cpu-batch", type=int, default=16)
     ap.add_argument("--cpu-steps", type=int, default=None)
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, run a plain 1 GiB "
@@ -411,7 +411,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         del stack
         torch.cuda.empty_cache()
-        cs = args.cpu_steps if args.cpu_steps is not None else L
+        cs = args.cpu_steps if args.cpu_steps is not None else 2 * L
         log(f"cpu baseline: oracle on {args.cpu_batch} sequences x {cs} steps")
         cb = cpu_baseline(w, args.seed, args.cpu_batch, cs)
         cb["value"] = round(cb["value"], 3)

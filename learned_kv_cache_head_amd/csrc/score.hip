@@ -4,8 +4,9 @@
 //    E.1-E.2, Eq. 35-36): score = w2 . act(W1 [k; v] + b1) + b2, key first.
 //    For bf16 caches the first layer is a dense contraction
 //    (rows x 2d) x (2d x hidden) and runs on MFMA (v_mfma_f32_16x16x32_bf16,
-//    float32 accumulation); the hidden activations stay in float32 for the
-//    second layer. Float32 caches use a float32 VALU kernel.
+//    float32 accumulation) with W1 staged in LDS; the hidden activations
+//    stay in float32 for the second layer. Float32 caches use a float32 VALU
+//    kernel.
 //  * Gate on hidden states (Fast KVzip section 3.1, g_l: R^D -> [0,1]^H):
 //    score = sigmoid(w_h . x + b_h), all H heads of a token at once as a
 //    (rows x D) x (D x H) MFMA contraction with H padded to 16.
@@ -33,63 +34,118 @@ __device__ __forceinline__ float activate(float a, int act) {
 }
 
 // ---------------------------------------------------------------------------
-// MLP scorer on MFMA (bf16 K/V and W1). One wave = 16 rows; 4 waves per
-// workgroup share one (tile, head, batch).
+// MLP scorer on MFMA (bf16 K/V and W1). A workgroup scores kMlpRowsPerWG
+// rows of one KV head, flattened over (batch, slot); the head's W1 is staged
+// once in LDS (rows padded by 16 bytes against bank conflicts) and every
+// wave loops over kMlpTiles tiles of 16 rows, loading the next tile's [k; v]
+// operands before the MFMAs of the current one.
 // ---------------------------------------------------------------------------
+constexpr int kMlpWaves = 4;
+constexpr int kMlpTiles = 4;                       // tiles per wave
+constexpr int kMlpRowsPerWG = kMlpWaves * kMlpTiles * 16;
+
 template <int D, int NB>
 __global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
   constexpr int HID = NB * 16;
   constexpr int IN = 2 * D;
-  constexpr int KSTEPS = IN / 32;
+  constexpr int KSTEPS = IN / 32;   // 32-wide contraction steps
+  constexpr int KHALF = D / 32;     // steps taken from the key
+  constexpr int LSTR = IN + 8;      // bf16 per staged W1 row
+  __shared__ uint16_t w1s[HID * LSTR];
   const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int rows = p.slot_end - p.slot_begin;
-  const int r0 = blockIdx.x * 64 + wave * 16;
-  if (r0 >= rows) return;  // no workgroup barrier below
-  const int rrow = r0 + (lane & 15);
-  const int slot = p.slot_begin + (rrow < rows ? rrow : rows - 1);
-  const size_t slice = (size_t)b * p.H + h;
-  const uint16_t* krow = (const uint16_t*)p.k + (slice * p.cap + slot) * D;
-  const uint16_t* vrow = (const uint16_t*)p.v + (slice * p.cap + slot) * D;
-  const uint16_t* w1 = (const uint16_t*)p.w1 + (size_t)h * HID * IN;
-  const int kq = (lane >> 4) * 8;
-  const int ncol = lane & 15;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rows = p.slot_end - p.slot_begin;  // rows per slice
+  const long long total = (long long)p.batch * rows;
+  const long long wg_row0 = (long long)blockIdx.x * kMlpRowsPerWG;
 
-  f32x4_t acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    const int kidx = ks * 32 + kq;
-    const bf16x8_t A = (ks * 32 < D) ? load8(krow + kidx) : load8(vrow + kidx - D);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8_t B = load8(w1 + (size_t)(nb * 16 + ncol) * IN + kidx);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
-    }
+  const uint16_t* w1 = (const uint16_t*)p.w1 + (size_t)h * HID * IN;
+  for (int c = tid; c < HID * IN / 8; c += 256) {
+    const int n = c / (IN / 8);
+    const int k8 = c % (IN / 8);
+    *(u32x4*)(w1s + n * LSTR + k8 * 8) =
+        *(const u32x4*)(w1 + (size_t)n * IN + k8 * 8);
   }
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  const int ncol = lane & 15;       // MFMA column = hidden unit within block
+  const int kq = (lane >> 4) * 8;   // this lane's 8 contraction indices
+  float bias[NB], w2v[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = nb * 16 + ncol;
-    const float bias = p.b1 ? p.b1[(size_t)h * HID + n] : 0.f;
-    const float w2n = p.w2[(size_t)h * HID + n];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[i] += activate(acc[nb][i] + bias, p.act) * w2n;
+    bias[nb] = p.b1 ? p.b1[(size_t)h * HID + n] : 0.f;
+    w2v[nb] = p.w2[(size_t)h * HID + n];
   }
+  const float b2 = p.b2 ? p.b2[h] : 0.f;
+  __syncthreads();
+
+  // Tile t of this wave covers rows wg_row0 + (t * kMlpWaves + wave) * 16 ..
+  // +15. Rows past the end are clamped (computed, never written), so every
+  // load below is unconditional and in bounds.
+  auto tile_row0 = [&](int t) {
+    return wg_row0 + (long long)(t * kMlpWaves + wave) * 16;
+  };
+  auto load_tile = [&](bf16x8_t (&a)[KSTEPS], int t) {
+    long long rid = tile_row0(t) + (lane & 15);
+    if (rid >= total) rid = total - 1;
+    const int b = (int)(rid / rows);
+    const int slot = p.slot_begin + (int)(rid - (long long)b * rows);
+    const size_t slice = (size_t)b * p.H + h;
+    const uint16_t* krow = (const uint16_t*)p.k + (slice * p.cap + slot) * D;
+    const uint16_t* vrow = (const uint16_t*)p.v + (slice * p.cap + slot) * D;
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1)
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      a[ks] = ks < KHALF ? load8(krow + ks * 32 + kq)
+                         : load8(vrow + (ks - KHALF) * 32 + kq);
+  };
+  auto compute_tile = [&](const bf16x8_t (&a)[KSTEPS], int t) {
+    f32x4_t acc[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], off);
-  if (ncol == 0) {
-    const float b2 = p.b2 ? p.b2[h] : 0.f;
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * (lane >> 4) + i;
-      if (row < rows) p.score[slice * p.cap + p.slot_begin + row] = part[i] + b2;
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8_t B = __builtin_bit_cast(
+            bf16x8_t, *(const u32x4*)(w1s + (nb * 16 + ncol) * LSTR +
+                                       ks * 32 + kq));
+        acc[nb] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], B, acc[nb], 0, 0, 0);
+      }
     }
+    // Row 4 * (lane >> 4) + i of the tile: second layer over the 16 hidden
+    // units of this lane's columns, then summed over the 16 columns.
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part[i] += activate(acc[nb][i] + bias[nb], p.act) * w2v[nb];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], off);
+    if (ncol == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long rid = tile_row0(t) + 4 * (lane >> 4) + i;
+        if (rid < total) {
+          const int b = (int)(rid / rows);
+          const int slot = p.slot_begin + (int)(rid - (long long)b * rows);
+          p.score[((size_t)b * p.H + h) * p.cap + slot] = part[i] + b2;
+        }
+      }
+    }
+  };
+
+  bf16x8_t a0[KSTEPS], a1[KSTEPS];
+  load_tile(a0, 0);
+#pragma unroll
+  for (int t = 0; t < kMlpTiles; t += 2) {
+    load_tile(a1, t + 1);
+    compute_tile(a0, t);
+    if (t + 2 < kMlpTiles) load_tile(a0, t + 2);
+    compute_tile(a1, t + 1);
   }
 }
 
@@ -188,10 +244,14 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
   const bool mfma_ok = m.is_bf16 && (m.hidden % 16 == 0) && m.hidden <= 128 &&
                        (m.D == 64 || m.D == 128);
   if (mfma_ok) {
-#define KVE_MLP(DD, NBB)                                                    \
-  if (m.D == DD && m.hidden == NBB * 16) {                                  \
-    hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB>), grid, dim3(256), 0, s, m); \
-    return hipGetLastError();                                               \
+    const long long total = (long long)m.batch * rows;
+    const long long wgs = (total + kMlpRowsPerWG - 1) / kMlpRowsPerWG;
+    if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 mgrid((unsigned)wgs, m.H);
+#define KVE_MLP(DD, NBB)                                                     \
+  if (m.D == DD && m.hidden == NBB * 16) {                                   \
+    hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB>), mgrid, dim3(256), 0, s, m); \
+    return hipGetLastError();                                                \
   }
     KVE_MLP(128, 1) KVE_MLP(128, 2) KVE_MLP(128, 3) KVE_MLP(128, 4)
     KVE_MLP(128, 5) KVE_MLP(128, 6) KVE_MLP(128, 7) KVE_MLP(128, 8)
