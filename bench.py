@@ -86,7 +86,7 @@ def evict_extra_bytes(w, n_before: int, moved: int) -> int:
 class Stack:
     """Per-layer caches, scorer weights, step runners and input pools."""
 
-    def __init__(self, w, seed: int, pool_steps: int, dev):
+    def __init__(self, w, seed: int, pool_steps: int, dev, decay=False):
         import torch
         import learned_kv_cache_head_amd as kve
         import synthetic as syn
@@ -94,7 +94,14 @@ class Stack:
         T = syn.TENSOR_IDS
         b, H, d, G = w.batch, w.n_kv, w.head_dim, w.group
         self.shape = kve.Shape(b, H, G, d, w.budget + w.evict_len, kve.BF16)
-        self.policy = kve.Policy(w.budget, w.sinks, w.window, w.evict_len)
+        log_gamma = None
+        if decay:
+            # per-KV-head decay factors spread over KVpop's range (Table 3:
+            # gamma from 0.999 to 0.999999), decay step 1
+            g = torch.linspace(0.999, 0.999999, H, dtype=torch.float64)
+            log_gamma = torch.log(g).to(torch.float32).to(dev)
+        self.policy = kve.Policy(w.budget, w.sinks, w.window, w.evict_len,
+                                 log_gamma=log_gamma)
         pre_shape = kve.Shape(b, H, G, d, w.n0, kve.BF16)
         scratch = kve.CacheTensors.empty(pre_shape, dev)
         scratch_pos = torch.arange(w.n0, dtype=torch.int32, device=dev)
@@ -255,6 +262,8 @@ def main() -> int:
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only the whole region (no per-launch events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decay", action="store_true",
+                    help="rank with KVpop temporal decay (static priority)")
     ap.add_argument("--cpu-batch", type=int, default=16)
     ap.add_argument("--cpu-steps", type=int, default=None)
     ap.add_argument("--calib-copy", action="store_true",
@@ -284,7 +293,7 @@ def main() -> int:
     log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")
     t0 = time.perf_counter()
-    stack = Stack(w, args.seed, pool, dev)
+    stack = Stack(w, args.seed, pool, dev, decay=args.decay)
     log(f"set-up {time.perf_counter() - t0:.1f} s")
 
     for i in range(warmup):
@@ -402,6 +411,7 @@ def main() -> int:
                    "budget": w.budget, "sinks": w.sinks, "window": w.window,
                    "evict_len": w.evict_len, "prompt_len": w.n0,
                    "scorer": f"mlp {2 * w.head_dim}-{w.hidden}-1 relu",
+                   "decay": bool(args.decay),
                    "parallelism": "none"},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),

@@ -85,12 +85,17 @@ typedef struct {
 } kve_shape;
 
 /* Retention policy: budget B, sinks S, window W, eviction length L.
- * Requires B >= S + W >= 0 and L >= 1 (KVpop Eq. 1: k = B - S - W >= 0). */
+ * Requires B >= S + W >= 0 and L >= 1 (KVpop Eq. 1: k = B - S - W >= 0).
+ * log_gamma: NULL, or a device array [n_kv_heads] of float32 log decay
+ * factors (KVpop Eq. 5 with decay step 1, gamma in (0, 1)): eligible entries
+ * are then ranked by the static priority score - position * log_gamma[h]
+ * (KVpop Appendix B.3, Eq. 20), both operations rounded to float32. */
 typedef struct {
   int32_t budget;
   int32_t sinks;
   int32_t window;
   int32_t evict_len;
+  const float* log_gamma;
 } kve_policy;
 
 /* Device pointers of one layer's cache (layouts above). */
@@ -166,8 +171,9 @@ kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
  * each slice of `len` entries to `n_keep`. With P the newest position in the
  * slice, entries with position < S (sinks) or > P - W (recent window) are
  * protected; among the eligible entries (S <= position <= P - W) the
- * len - n_keep with the smallest (float32 score, position) keys are evicted:
- * equal scores evict the older entry first, and -0.0 ranks as +0.0. Writes
+ * len - n_keep with the smallest (float32 key, position) are evicted, the
+ * key being the score or, with policy->log_gamma, the static priority:
+ * equal keys evict the older entry first, and -0.0 ranks as +0.0. Writes
  * the kept slots in ascending order to keep_slots [batch][H][n_keep].
  * Requires 0 <= n_keep <= len <= capacity, and S + W <= n_keep when
  * n_keep < len; n_keep == len writes the identity. Scores must be finite;

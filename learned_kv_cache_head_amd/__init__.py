@@ -41,7 +41,8 @@ class _Shape(ctypes.Structure):
 
 class _Policy(ctypes.Structure):
     _fields_ = [("budget", ctypes.c_int32), ("sinks", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("evict_len", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("evict_len", ctypes.c_int32),
+                ("log_gamma", ctypes.c_void_p)]
 
 
 class _Cache(ctypes.Structure):
@@ -155,13 +156,17 @@ class Shape:
 
 @dataclass(frozen=True)
 class Policy:
+    """Budget B, sinks S, window W, eviction length L; optional per-KV-head
+    float32 log decay factors (a device tensor [n_kv_heads])."""
     budget: int
     sinks: int
     window: int
     evict_len: int
+    log_gamma: object = None
 
     def c(self) -> _Policy:
-        return _Policy(self.budget, self.sinks, self.window, self.evict_len)
+        return _Policy(self.budget, self.sinks, self.window, self.evict_len,
+                       _ptr(self.log_gamma))
 
 
 class CacheTensors:
@@ -333,7 +338,7 @@ class LayerStep:
         self._ws_ptr = _ptr(ws)
         self._ws_bytes = ws.numel() * ws.element_size()
         self._stream = _stream(stream)
-        self._keepalive = (scorer, cache, ws)
+        self._keepalive = (scorer, cache, ws, policy)
         self.state = state
         self.budget, self.evict_len = policy.budget, policy.evict_len
 

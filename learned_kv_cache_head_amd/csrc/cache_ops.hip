@@ -48,7 +48,8 @@ __global__ __launch_bounds__(64) void append_kernel(
 // Candidates are the entries of the eligible set E(P) = {S <= pos <= P - W}
 // with P the newest position present (KVpop Eq. 4); all other entries (sink
 // tokens, recent window) are kept. Among the candidates, the r = len -
-// n_keep with the smallest (score, position) keys are evicted.
+// n_keep with the smallest (key, position) are evicted; the key is the score
+// or, with temporal decay, the static priority (KVpop Appendix B.3).
 //  1. block max of the positions -> P;
 //  2. four 8-bit MSB radix passes over the orderable 32-bit score keys of
 //     the candidates -> the r-th smallest key thr, the number `need` of
@@ -151,8 +152,8 @@ __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const float* score, const int32_t* pos, int cap, int len, int n_keep,
-    int S, int W, int32_t* keep) {
+    const float* score, const int32_t* pos, const float* log_gamma, int H,
+    int cap, int len, int n_keep, int S, int W, int32_t* keep) {
   const size_t slice = blockIdx.x;
   const float* sc = score + slice * (size_t)cap;
   const int32_t* ps = pos + slice * (size_t)cap;
@@ -185,7 +186,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int32_t p = ps[c];
     return p >= S && (long long)p <= last_eligible;
   };
-  auto skey = [&](int c) { return score_key(sc[c]); };
+  // Ranking key: the score, or under temporal decay the static priority
+  // score - position * log(gamma) (KVpop Eq. 20), each operation rounded to
+  // float32 separately (no fused multiply-add).
+  const float lg = log_gamma ? log_gamma[slice % H] : 0.f;
+  const bool decay = log_gamma != nullptr;
+  auto skey = [&](int c) {
+    float r = sc[c];
+    if (decay) r = __fsub_rn(r, __fmul_rn((float)ps[c], lg));
+    return score_key(r);
+  };
 
   // 2. Cut score key.
   uint32_t thr, need, count_eq;
@@ -317,11 +327,12 @@ hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* score, const int32_t* pos, int slices,
-                         int cap, int len, int n_keep, int S, int W,
-                         int32_t* keep, hipStream_t s) {
+hipError_t launch_select(const float* score, const int32_t* pos,
+                         const float* log_gamma, int H, int slices, int cap,
+                         int len, int n_keep, int S, int W, int32_t* keep,
+                         hipStream_t s) {
   hipLaunchKernelGGL(select_kernel, dim3(slices), dim3(kSelThreads), 0, s,
-                     score, pos, cap, len, n_keep, S, W, keep);
+                     score, pos, log_gamma, H, cap, len, n_keep, S, W, keep);
   return hipGetLastError();
 }
 

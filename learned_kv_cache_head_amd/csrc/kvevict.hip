@@ -283,9 +283,9 @@ kve_status kve_select_evict(const kve_shape* shape, const kve_policy* policy,
     return KVE_ERR_POLICY;
   if (len == 0) return KVE_OK;
   return from_hip(kve::launch_select(
-      cache->score, cache->pos, shape->batch * shape->n_kv_heads,
-      shape->capacity, len, n_keep, policy->sinks, policy->window, keep_slots,
-      stream));
+      cache->score, cache->pos, policy->log_gamma, shape->n_kv_heads,
+      shape->batch * shape->n_kv_heads, shape->capacity, len, n_keep,
+      policy->sinks, policy->window, keep_slots, stream));
 }
 
 kve_status kve_compact(const kve_shape* shape, kve_cache* cache, int32_t len,
@@ -374,9 +374,9 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   }
   if (evict) {
     st = from_hip(kve::launch_select(
-        cache->score, cache->pos, shape->batch * shape->n_kv_heads,
-        shape->capacity, len, B, policy->sinks, policy->window, keep_slots,
-        stream));
+        cache->score, cache->pos, policy->log_gamma, shape->n_kv_heads,
+        shape->batch * shape->n_kv_heads, shape->capacity, len, B,
+        policy->sinks, policy->window, keep_slots, stream));
     if (st != KVE_OK) return st;
     st = from_hip(kve::launch_compact(
         cache->k, cache->v, cache->score, cache->pos,

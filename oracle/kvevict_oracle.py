@@ -42,6 +42,8 @@ Readings where the pages leave a step open (also listed in the design notes):
 * Ties: among equal float32 scores the older (lower position) token is
   evicted first; -0.0 is treated as +0.0. Non-finite scores are outside the
   contract (asserted here).
+* Temporal decay (optional, per KV head): decay step n = 1 only (KVpop Table
+  3 uses n = 1), ranking by the static priority of Eq. (20) in float32.
 * Query head j reads KV head floor(j / G) (contiguous GQA groups).
 
 Parity pins: every function here is pinned by tests in
@@ -57,7 +59,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "Policy", "mlp_score", "gate_score", "score_to_f32", "eligible_mask",
+    "Policy", "mlp_score", "gate_score", "score_to_f32", "static_priority",
+    "eligible_mask",
     "select_keep", "compaction_sources", "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
     "closed_form_retained", "cache_bytes_per_token",
 ]
@@ -66,12 +69,15 @@ __all__ = [
 @dataclass(frozen=True)
 class Policy:
     """Budget B, sinks S, window W and eviction length L (KVpop Eq. (1);
-    ForesightKV summary, periodic eviction with length L)."""
+    ForesightKV summary, periodic eviction with length L). ``log_gamma``
+    optionally holds one log decay factor per KV head (KVpop Eq. (5) with
+    decay step n = 1; ranking by the static priority of Eq. (20))."""
 
     budget: int
     sinks: int
     window: int
     evict_len: int
+    log_gamma: Optional[tuple] = None
 
     @property
     def k(self) -> int:
@@ -134,6 +140,21 @@ def score_to_f32(s: np.ndarray) -> np.ndarray:
 # Selection and compaction
 # ---------------------------------------------------------------------------
 
+def static_priority(score32: np.ndarray, pos: np.ndarray,
+                    log_gamma: Optional[float]) -> np.ndarray:
+    """Ranking key with temporal decay, KVpop Appendix B.3: for decay step
+    n = 1 the effective score r + (q - t) log(gamma) (Eq. (18)-(19)) ranks
+    eligible tokens like the static priority r - t log(gamma) (Eq. (20)),
+    since q log(gamma) is common to all of them. Ranking is in float32
+    (Appendix F): the product t * log(gamma) is rounded to float32, then the
+    difference. Without decay the key is the score itself."""
+    s = np.asarray(score32, dtype=np.float32)
+    if log_gamma is None:
+        return s
+    prod = np.asarray(pos).astype(np.float32) * np.float32(log_gamma)
+    return (s - prod).astype(np.float32)
+
+
 def eligible_mask(pos: np.ndarray, sinks: int, window: int) -> np.ndarray:
     """Entries that may be evicted: position t with S <= t <= P - W, where P
     is the newest position present (KVpop Eq. (4), the eligible set E(P));
@@ -146,19 +167,22 @@ def eligible_mask(pos: np.ndarray, sinks: int, window: int) -> np.ndarray:
 
 
 def select_keep(score32: np.ndarray, pos: np.ndarray, length: int,
-                n_keep: int, sinks: int, window: int) -> np.ndarray:
+                n_keep: int, sinks: int, window: int,
+                log_gamma: Optional[float] = None) -> np.ndarray:
     """Slots kept when a cache slice of ``length`` entries is cut to
     ``n_keep`` entries.
 
     Candidates are the entries of the eligible set E(P) (``eligible_mask``).
-    The length - n_keep candidates with the smallest (float32 score,
+    The length - n_keep candidates with the smallest (float32 ranking key,
     position) are evicted; every other entry is kept (KVpop Eq. (26): sinks,
-    recent window and the top-k eligible tokens).
+    recent window and the top-k eligible tokens). The key is the score, or
+    the static priority under temporal decay (``static_priority``).
 
     Returns the kept slot indices in ascending order (int64).
     """
-    score32 = np.asarray(score32, dtype=np.float32)[:length]
     pos = np.asarray(pos)[:length]
+    score32 = static_priority(np.asarray(score32, dtype=np.float32)[:length],
+                              pos, log_gamma)
     if n_keep >= length:
         return np.arange(length, dtype=np.int64)
     r = length - n_keep
@@ -271,11 +295,13 @@ class OracleLayer:
         b, H = self.K.shape[:2]
         keeps = np.empty((b, H, n_keep), dtype=np.int64)
         srcs = np.empty((b, H, n_keep), dtype=np.int64)
+        lg = self.policy.log_gamma
         for bi in range(b):
             for h in range(H):
                 keeps[bi, h] = select_keep(self.score[bi, h], self.pos[bi, h],
                                            self.n, n_keep, self.policy.sinks,
-                                           self.policy.window)
+                                           self.policy.window,
+                                           None if lg is None else lg[h])
                 srcs[bi, h] = compaction_sources(keeps[bi, h])
         idx = srcs[..., None]
         self.K = np.take_along_axis(self.K, idx, axis=2)
@@ -358,15 +384,17 @@ class OracleLayer:
 
 def closed_form_retained(score_by_pos32: np.ndarray, newest: int,
                          last_evict_newest: Optional[int],
-                         policy: Policy) -> np.ndarray:
+                         policy: Policy,
+                         log_gamma: Optional[float] = None) -> np.ndarray:
     """Retained positions of one slice after any number of steps, without
     simulating the loop (KVpop Eq. (26) in cache form).
 
-    With static scores, every evicted token is beaten by k eligible tokens
-    that stay eligible, so at the last eviction (newest position P_e) the
-    kept long-range tokens are exactly TopK_k(E(P_e)); tokens appended since
-    then are all still present. Result: sinks {0..S-1}, the top-k of
-    E(P_e) = {S <= t <= P_e - W} by (score desc, position desc), and every
+    With a static ranking key (the score, or the static priority of Eq. (20)
+    under decay), every evicted token is beaten by k eligible tokens that
+    stay eligible, so at the last eviction (newest position P_e) the kept
+    long-range tokens are exactly TopK_k(E(P_e)); tokens appended since then
+    are all still present. Result: sinks {0..S-1}, the top-k of
+    E(P_e) = {S <= t <= P_e - W} by (key desc, position desc), and every
     position in (P_e - W, newest]. ``score_by_pos32`` holds the float32
     score of every position 0..newest. Returns sorted positions.
     """
@@ -375,8 +403,9 @@ def closed_form_retained(score_by_pos32: np.ndarray, newest: int,
         return np.arange(newest + 1, dtype=np.int64)
     pe = last_evict_newest
     elig = np.arange(S, pe - W + 1, dtype=np.int64)
-    s = np.asarray(score_by_pos32, np.float32)[elig] + np.float32(0.0)
-    order = np.lexsort((-elig, -s.astype(np.float64)))  # score desc, pos desc
+    s = static_priority(np.asarray(score_by_pos32, np.float32)[elig], elig,
+                        log_gamma) + np.float32(0.0)
+    order = np.lexsort((-elig, -s.astype(np.float64)))  # key desc, pos desc
     top = elig[order[:k]]
     recent = np.arange(max(pe - W + 1, S), newest + 1, dtype=np.int64)
     return np.unique(np.concatenate([np.arange(S, dtype=np.int64), top,

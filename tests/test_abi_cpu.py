@@ -186,3 +186,11 @@ def test_step_rejects_bad_state():
     small = _shape(capacity=1100)
     assert call(kve._State(1000, 1000, 9000, 0), shape=small) == 3  # cap < B+L
     assert call(kve._State(1030, 1024, 9000, 0), ws_bytes=64) == 5
+
+
+def test_policy_struct_layout_matches_header():
+    """kve_policy: four int32 fields, then the log_gamma pointer."""
+    assert ctypes.sizeof(kve._Policy) == 24
+    assert kve._Policy.log_gamma.offset == 16
+    p = kve.Policy(1024, 4, 128, 128).c()
+    assert p.log_gamma is None

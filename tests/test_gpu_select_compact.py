@@ -91,6 +91,48 @@ def test_select_bit_exact(case, pattern, order):
                                           err_msg=f"slice {b},{h}")
 
 
+DECAY_CASES = [
+    # S, W, len, n_keep, batch, H
+    (4, 64, 193, 192, 1, 2),
+    (4, 128, 1152, 1024, 2, 8),
+    (4, 512, 39385, 39321, 1, 8),
+    (2, 3, 40, 20, 1, 3),
+]
+
+
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+@pytest.mark.parametrize("pattern", ["normal", "ties3", "const"])
+@pytest.mark.parametrize("case", DECAY_CASES,
+                         ids=[f"S{c[0]}W{c[1]}n{c[2]}k{c[3]}"
+                              for c in DECAY_CASES])
+def test_select_with_decay_bit_exact(case, pattern, order):
+    """Temporal decay (KVpop Eq. 20): ranking by score - pos * log(gamma_h),
+    per KV head, in float32 on both sides."""
+    import torch
+    k = kve()
+    S, W, n, nk, B, H = case
+    print(f"[select-decay] {case} {pattern} {order}", flush=True)
+    cap = n + 5
+    rng = np.random.default_rng(n * 7 + nk)
+    sc = _scores(rng, pattern, (B, H, cap))
+    pos = _positions(rng, B, H, cap, n, order)
+    lg = np.log(np.linspace(0.9, 0.999999, H)).astype(np.float32)
+    shape = k.Shape(B, H, 1, 128, cap, k.BF16)
+    dev = torch.device("cuda")
+    pol = k.Policy(max(nk, S + W), S, W, 1,
+                   log_gamma=torch.from_numpy(lg).to(dev))
+    cache = _cache_for_scores(k, shape, sc, pos, dev)
+    keep = torch.full((B, H, nk), -1, dtype=torch.int32, device=dev)
+    k.kve_select_evict(shape, pol, cache, n, nk, keep)
+    got = keep.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref = O.select_keep(sc[b, h, :n], pos[b, h, :n], n, nk, S, W,
+                                float(lg[h]))
+            np.testing.assert_array_equal(got[b, h], ref,
+                                          err_msg=f"slice {b},{h}")
+
+
 def test_select_one_shot_compression_131k():
     """Qwen2.5-14B prompt of 131072 tokens cut to a 30% budget in one go."""
     import torch

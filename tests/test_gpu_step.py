@@ -26,6 +26,7 @@ class Tracker:
     def __init__(self, w, k0, v0, s0, policy):
         self.w = w
         self.policy = policy
+        self.lg = policy.log_gamma
         npos = w.n0 + w.steps
         b, H, d = w.batch, w.n_kv, w.head_dim
         self.K = np.zeros((b, H, npos, d))
@@ -45,7 +46,13 @@ class Tracker:
             for h in range(H):
                 m = O.eligible_mask(self.lay.pos[bi, h], p.sinks, p.window)
                 if m.any():
-                    self.cut[bi, h] = float(self.lay.score[bi, h][m].min())
+                    key = self._key(self.lay.score[bi, h], self.lay.pos[bi, h], h)
+                    self.cut[bi, h] = float(key[m].min())
+
+    def _key(self, score32, pos, h):
+        """The ranking key: score, or static priority under decay."""
+        return O.static_priority(score32, pos,
+                                 None if self.lg is None else self.lg[h])
 
     def prefill(self):
         if self.lay.prefill_compress() is not None:
@@ -70,15 +77,17 @@ class Tracker:
                     continue
                 diff = set(g.tolist()) ^ set(o.tolist())
                 for t in diff:
-                    assert abs(float(self.S[bi, h, t]) - self.cut[bi, h]) <= \
-                        SCORE_ATOL, f"slice {bi},{h}: token {t} differs"
+                    key = float(self._key(self.S[bi, h, t:t + 1],
+                                          np.array([t]), h)[0])
+                    assert abs(key - self.cut[bi, h]) <= SCORE_ATOL, \
+                        f"slice {bi},{h}: token {t} differs"
                 self.lay.K[bi, h] = self.K[bi, h, g]
                 self.lay.V[bi, h] = self.V[bi, h, g]
                 self.lay.score[bi, h] = self.S[bi, h, g]
                 self.lay.pos[bi, h] = g
 
 
-def run_e2e(w, seed=0, check_stride=1, layer=0):
+def run_e2e(w, seed=0, check_stride=1, layer=0, gammas=None):
     import torch
     k = kve()
     dev = torch.device("cuda")
@@ -94,11 +103,16 @@ def run_e2e(w, seed=0, check_stride=1, layer=0):
         gw = syn.draw_gate_weights(w, seed, layer, bias=True)
         s0 = oracle_gate_scores(ctx["hidden0"].f64, gw)
         sc = k.Scorer.gate(gw["w"].torch(dev), gw["b"].torch(dev))
-    pol_o = O.Policy(w.budget, w.sinks, w.window, w.evict_len)
+    lg = None
+    if gammas is not None:
+        lg = np.log(np.asarray(gammas, np.float64)).astype(np.float32)
+    pol_o = O.Policy(w.budget, w.sinks, w.window, w.evict_len,
+                     log_gamma=None if lg is None else tuple(float(x) for x in lg))
     tr = Tracker(w, ctx["k0"].f64, ctx["v0"].f64, s0, pol_o)
 
     shape = shape_of(w)
-    pol = k.Policy(w.budget, w.sinks, w.window, w.evict_len)
+    pol = k.Policy(w.budget, w.sinks, w.window, w.evict_len,
+                   log_gamma=None if lg is None else torch.from_numpy(lg).to(dev))
     cache = k.CacheTensors.empty(shape, dev)
     cache.k[:, :, :w.n0] = ctx["k0"].torch(dev)
     cache.v[:, :, :w.n0] = ctx["v0"].torch(dev)
@@ -187,6 +201,18 @@ def test_qwen3_layer_silu_and_odd_policy():
     w = syn.workload(2, batch=1, n0=700, budget=300, sinks=3, window=37,
                      evict_len=45, steps=100, act="silu", structured=False)
     ev, _ = run_e2e(w, seed=3)
+    assert ev == 2
+
+
+def test_temporal_decay_end_to_end():
+    """KVpop temporal decay (decay step 1, per-head gamma in the Table 3
+    range and below it) through kve_step, tiny and Qwen3-4B-layer shapes."""
+    w = syn.workload(1, steps=48)
+    ev, _ = run_e2e(w, seed=5, gammas=[0.99, 0.999999])
+    assert ev == w.steps
+    w = syn.workload(2, batch=1, steps=256)
+    ev, _ = run_e2e(w, seed=6, check_stride=8,
+                    gammas=np.linspace(0.999, 0.999999, 8))
     assert ev == 2
 
 

@@ -158,3 +158,21 @@ def attn_unnormalised_lse(q, K, V):
 def test_attention_mutants_fail(mutant):
     _fails(P.check_attention_hand, mutant)
     _fails(P.check_attention_vs_torch_sdpa, mutant)
+
+
+def select_decay_wrong_sign(score32, pos, length, n_keep, sinks, window,
+                            log_gamma=None):
+    """Adds t log(gamma) instead of subtracting it (favours old tokens)."""
+    lg = None if log_gamma is None else -log_gamma
+    return O.select_keep(score32, pos, length, n_keep, sinks, window, lg)
+
+
+def select_decay_ignored(score32, pos, length, n_keep, sinks, window,
+                         log_gamma=None):
+    return O.select_keep(score32, pos, length, n_keep, sinks, window)
+
+
+@pytest.mark.parametrize("mutant", [select_decay_wrong_sign,
+                                    select_decay_ignored])
+def test_decay_mutants_fail(mutant):
+    _fails(P.check_decay_ranking, mutant)

@@ -494,3 +494,88 @@ def test_generator_is_deterministic_and_keyed():
     s1 = syn.step_inputs(w, 0, 0, 1)
     assert not np.array_equal(s0["q"].bits, s1["q"].bits)
     assert a["k0"].shape == (2, 8, 64, 128)
+
+
+# ---------------------------------------------------------------------------
+# Temporal decay (KVpop Eq. (5), Appendix B.3 Eq. (18)-(20), n = 1)
+# ---------------------------------------------------------------------------
+
+def brute_force_keep_effective(scores, pos, length, n_keep, S, W, log_gamma):
+    """Evict the r eligible tokens with the lowest effective score at the
+    newest position q = P, r + (q - t) log(gamma), computed in float64 (ties
+    by older position first)."""
+    if n_keep >= length:
+        return list(range(length))
+    r = length - n_keep
+    q = max(pos[:length])
+    cands = [u for u in range(length) if S <= pos[u] <= q - W]
+    eff = {u: float(scores[u]) + (q - pos[u]) * log_gamma for u in cands}
+    order = sorted(cands, key=lambda u: (eff[u], pos[u]))
+    evicted = set(order[:r])
+    return [t for t in range(length) if t not in evicted]
+
+
+def check_decay_ranking(select_keep):
+    """Eq. (19)-(20): at a fixed query position the effective-score ranking
+    equals the static-priority ranking (checked where the float64 effective
+    scores are far apart compared with float32 rounding)."""
+    rng = np.random.default_rng(31)
+    checked = 0
+    for _ in range(400):
+        S, W = int(rng.integers(0, 4)), int(rng.integers(0, 6))
+        m = int(rng.integers(1, 30))
+        length = S + W + m
+        pos = rng.permutation(length) + 0
+        sc = rng.standard_normal(length).astype(np.float32)
+        lg = float(np.log(rng.uniform(0.5, 0.99)))
+        q = pos.max()
+        eff = np.sort(sc.astype(np.float64) + (q - pos) * lg)
+        if np.min(np.diff(eff)) < 1e-4:
+            continue
+        r = int(rng.integers(0, m + 1))
+        got = list(select_keep(sc, pos, length, length - r, S, W, lg))
+        assert got == brute_force_keep_effective(sc, pos, length, length - r,
+                                                 S, W, lg)
+        checked += 1
+    assert checked > 200
+
+
+def test_decay_ranking_equals_effective_score_ranking():
+    check_decay_ranking(O.select_keep)
+
+
+def test_decay_hand_case():
+    # positions 0..5, S = 1, W = 1: candidates are positions 1..4 with
+    # scores 0.6, 0.9, 0.9, 0.45. With log(gamma) = -0.1 the static
+    # priorities r - t log(gamma) are 0.7, 1.1, 1.2, 0.85, so evicting one
+    # drops the old t = 1; without decay the lowest score, t = 4, goes.
+    sc = np.array([9.0, 0.6, 0.9, 0.9, 0.45, 9.0], np.float32)
+    keep = O.select_keep(sc, np.arange(6), 6, 5, 1, 1, -0.1)
+    assert list(keep) == [0, 2, 3, 4, 5]
+    assert list(O.select_keep(sc, np.arange(6), 6, 5, 1, 1)) == \
+        [0, 1, 2, 3, 5]
+
+
+def test_decay_zero_is_no_decay_and_prefers_recent():
+    rng = np.random.default_rng(32)
+    sc = rng.standard_normal(50).astype(np.float32)
+    pos = rng.permutation(50)
+    assert list(O.select_keep(sc, pos, 50, 30, 2, 5, 0.0)) == \
+        list(O.select_keep(sc, pos, 50, 30, 2, 5))
+    # equal scores: decay evicts the oldest eligible positions first
+    flat = np.ones(50, np.float32)
+    keep = O.select_keep(flat, np.arange(50), 50, 30, 2, 5, -1e-3)
+    assert list(keep) == [0, 1] + list(range(22, 50))
+
+
+def test_decay_incremental_loop_equals_closed_form():
+    rng = np.random.default_rng(33)
+    for (B, S, W, L, n0) in ((20, 2, 4, 1, 30), (20, 2, 4, 5, 30),
+                             (32, 4, 8, 8, 31)):
+        lg = float(np.log(0.9))
+        pol = O.Policy(B, S, W, L, log_gamma=(lg,))
+        steps = 60
+        sc = rng.standard_normal(n0 + steps).astype(np.float32)
+        for newest, pe, kept in run_incremental(pol, n0, steps, sc):
+            cf = O.closed_form_retained(sc[:newest + 1], newest, pe, pol, lg)
+            np.testing.assert_array_equal(kept, cf)
