@@ -60,6 +60,8 @@ import numpy as np
 
 __all__ = [
     "Policy", "mlp_score", "gate_score", "score_to_f32", "static_priority",
+    "hedgehog", "MlstmWeights", "mlstm_features", "mlstm_readout",
+    "MlstmScorer", "mlstm_scores_parallel",
     "eligible_mask",
     "select_keep", "compaction_sources", "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
     "closed_form_retained", "cache_bytes_per_token",
@@ -125,6 +127,110 @@ def gate_score(hidden: np.ndarray, w: np.ndarray, b: float = 0.0
     g_l : R^D -> [0, 1]^H): sigmoid(w . x + b). hidden [..., D], w [D]."""
     a = np.asarray(hidden, np.float64) @ np.asarray(w, np.float64) + float(b)
     return 1.0 / (1.0 + np.exp(-a))
+
+
+def hedgehog(y: np.ndarray) -> np.ndarray:
+    """Hedgehog feature map in softmax form (KVpop Appendix A): [softmax(y);
+    softmax(-y)] over the last (feature) axis."""
+    y = np.asarray(y, np.float64)
+
+    def softmax(u):
+        e = np.exp(u - u.max(axis=-1, keepdims=True))
+        return e / e.sum(axis=-1, keepdims=True)
+    return np.concatenate([softmax(y), softmax(-y)], axis=-1)
+
+
+@dataclass
+class MlstmWeights:
+    """One KV head's stateful scorer (KVpop section 3.3 "Stateful scorers",
+    Appendix A and E.3-E.4): projections W_q, W_k, W_v [P][2d] of
+    x = [k; v], input/forget gate weights w_i, w_f [2d] and biases, readout
+    a [P] and bias b."""
+
+    wq: np.ndarray
+    wk: np.ndarray
+    wv: np.ndarray
+    wi: np.ndarray
+    wf: np.ndarray
+    bi: float
+    bf: float
+    a: np.ndarray
+    b: float
+
+
+def mlstm_features(x: np.ndarray, w: MlstmWeights):
+    """Per-token read/write features (KVpop Eq. (37), (40)): q~ = phi(W_q x),
+    k~ = phi(W_k x), v~ = W_v x, input gate i = exp(w_i . x + b_i), forget
+    gate f = sigmoid(w_f . x + b_f). x [..., 2d]."""
+    x = np.asarray(x, np.float64)
+    qf = hedgehog(x @ np.asarray(w.wq, np.float64).T)
+    kf = hedgehog(x @ np.asarray(w.wk, np.float64).T)
+    vf = x @ np.asarray(w.wv, np.float64).T
+    ig = np.exp(x @ np.asarray(w.wi, np.float64) + w.bi)
+    fg = 1.0 / (1.0 + np.exp(-(x @ np.asarray(w.wf, np.float64) + w.bf)))
+    return qf, kf, vf, ig, fg
+
+
+def mlstm_readout(qf_u: np.ndarray, C: np.ndarray, z: np.ndarray,
+                  w: MlstmWeights) -> float:
+    """Delayed readout h = (q~_u^T C_q) / (q~_u^T z_q) (KVpop Eq. (41)) and
+    raw score a^T SiLU(h) + b (Eq. (42), without the optional norm)."""
+    h = (qf_u @ C) / (qf_u @ z)
+    return float(np.dot(np.asarray(w.a, np.float64), h / (1.0 + np.exp(-h))) + w.b)
+
+
+class MlstmScorer:
+    """The recurrent scorer state of one KV head: matrix memory C [2P][P]
+    and normaliser z [2P] (KVpop Eq. (38)-(39)), updated token by token in
+    plain (unstabilised) float64. At query position q the token u = q - W
+    leaves the window and is scored from the state that has absorbed token
+    q (Appendix E.4)."""
+
+    def __init__(self, w: MlstmWeights, window: int):
+        self.w, self.window = w, window
+        P = np.asarray(w.wv).shape[0]
+        self.C = np.zeros((2 * P, P))
+        self.z = np.zeros(2 * P)
+        self.qf = {}       # q~ of tokens still waiting for their readout
+        self.q = -1
+
+    def push(self, x: np.ndarray):
+        """Absorb token q = previous + 1 with input x [2d]; return
+        (u, score) for the token leaving the window, or None."""
+        self.q += 1
+        qf, kf, vf, ig, fg = mlstm_features(x, self.w)
+        self.C = fg * self.C + ig * np.outer(kf, vf)
+        self.z = fg * self.z + ig * kf
+        self.qf[self.q] = qf
+        u = self.q - self.window
+        if u < 0:
+            return None
+        return u, mlstm_readout(self.qf.pop(u), self.C, self.z, self.w)
+
+
+def mlstm_scores_parallel(x: np.ndarray, w: MlstmWeights, window: int
+                          ) -> np.ndarray:
+    """The same scores in parallel form (KVpop Appendix A: the recurrent and
+    parallel views are equivalent): with D[q, t] = i_t prod_{t<j<=q} f_j
+    for t <= q, token u read at q = u + W gets
+    h = sum_t D[q, t] (q~_u . k~_t) v~_t / sum_t D[q, t] (q~_u . k~_t).
+    x [n][2d]; returns float64 scores of tokens 0..n-1-W."""
+    qf, kf, vf, ig, fg = mlstm_features(x, w)
+    n = x.shape[0]
+    logf = np.log(fg)
+    cum = np.concatenate([[0.0], np.cumsum(logf)])   # cum[j] = sum_{<j}
+    out = np.empty(max(n - window, 0))
+    for u in range(n - window):
+        q = u + window
+        t = np.arange(q + 1)
+        decay = ig[t] * np.exp(cum[q + 1] - cum[t + 1])
+        sim = kf[t] @ qf[u]
+        num = (decay * sim) @ vf[t]
+        den = (decay * sim).sum()
+        h = num / den
+        out[u] = float(np.dot(np.asarray(w.a, np.float64),
+                              h / (1.0 + np.exp(-h))) + w.b)
+    return out
 
 
 def score_to_f32(s: np.ndarray) -> np.ndarray:

@@ -176,3 +176,66 @@ def select_decay_ignored(score32, pos, length, n_keep, sinks, window,
                                     select_decay_ignored])
 def test_decay_mutants_fail(mutant):
     _fails(P.check_decay_ranking, mutant)
+
+
+# --- mLSTM scorer mutants --------------------------------------------------
+
+class MlstmNoForget(O.MlstmScorer):
+    """Ignores the forget gate (f = 1)."""
+
+    def push(self, x):
+        self.q += 1
+        qf, kf, vf, ig, fg = O.mlstm_features(x, self.w)
+        self.C = self.C + ig * np.outer(kf, vf)
+        self.z = self.z + ig * kf
+        self.qf[self.q] = qf
+        u = self.q - self.window
+        if u < 0:
+            return None
+        return u, O.mlstm_readout(self.qf.pop(u), self.C, self.z, self.w)
+
+
+class MlstmReadBeforeWrite(O.MlstmScorer):
+    """Reads token u out of the state before absorbing token q."""
+
+    def push(self, x):
+        self.q += 1
+        qf, kf, vf, ig, fg = O.mlstm_features(x, self.w)
+        self.qf[self.q] = qf
+        u = self.q - self.window
+        res = None
+        if u >= 0 and self.q > 0:
+            res = (u, O.mlstm_readout(self.qf.pop(u), self.C, self.z, self.w))
+        self.C = fg * self.C + ig * np.outer(kf, vf)
+        self.z = fg * self.z + ig * kf
+        if u >= 0 and res is None:
+            res = (u, O.mlstm_readout(self.qf.pop(u), self.C, self.z, self.w))
+        return res
+
+
+class MlstmNoNormaliser(O.MlstmScorer):
+    """Reads h = q~ . C without dividing by the normaliser q~ . z."""
+
+    def push(self, x):
+        self.q += 1
+        qf, kf, vf, ig, fg = O.mlstm_features(x, self.w)
+        self.C = fg * self.C + ig * np.outer(kf, vf)
+        self.z = fg * self.z + ig * kf
+        self.qf[self.q] = qf
+        u = self.q - self.window
+        if u < 0:
+            return None
+        h = self.qf.pop(u) @ self.C
+        return u, float(self.w.a @ (h / (1.0 + np.exp(-h))) + self.w.b)
+
+
+@pytest.mark.parametrize("mutant", [MlstmNoForget, MlstmReadBeforeWrite,
+                                    MlstmNoNormaliser])
+def test_mlstm_mutants_fail(mutant):
+    failed = 0
+    for check in (P.check_mlstm_hand, P.check_mlstm_recurrent_equals_parallel):
+        try:
+            check(mutant)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1

@@ -579,3 +579,98 @@ def test_decay_incremental_loop_equals_closed_form():
         for newest, pe, kept in run_incremental(pol, n0, steps, sc):
             cf = O.closed_form_retained(sc[:newest + 1], newest, pe, pol, lg)
             np.testing.assert_array_equal(kept, cf)
+
+
+# ---------------------------------------------------------------------------
+# Stateful mLSTM scorer (KVpop section 3.3, Appendix A, E.3-E.4)
+# ---------------------------------------------------------------------------
+
+def _mlstm_weights(rng, d, P, bias_f=0.5, scale=1.0):
+    r = lambda *s: rng.standard_normal(s) / np.sqrt(2 * d) * scale
+    return O.MlstmWeights(r(P, 2 * d), r(P, 2 * d), r(P, 2 * d), r(2 * d),
+                          r(2 * d), 0.1, bias_f, rng.standard_normal(P), 0.2)
+
+
+def _recurrent_scores(weights, x, window):
+    sc = O.MlstmScorer(weights, window)
+    out = {}
+    for t in range(x.shape[0]):
+        r = sc.push(x[t])
+        if r is not None:
+            out[r[0]] = r[1]
+    return out
+
+
+def check_mlstm_hand(scorer_cls):
+    g = golden()["mlstm_scalar"]
+    z2 = np.zeros((1, 2))
+    w = O.MlstmWeights(z2, z2, np.array([[1.0, 0.0]]), np.zeros(2),
+                       np.zeros(2), 0.0, 0.0, np.array([1.0]), 0.0)
+    sc = scorer_cls(w, g["window"])
+    got = None
+    for v in g["v"]:
+        r = sc.push(np.array([v, 0.0]))
+        if r is not None and r[0] == 0:
+            got = r[1]
+    assert got == pytest.approx(g["expected_u0"], rel=1e-12)
+
+
+def check_mlstm_recurrent_equals_parallel(scorer_cls):
+    rng = np.random.default_rng(41)
+    for d, P, W, n in ((8, 4, 3, 30), (16, 8, 5, 40), (4, 2, 0, 12)):
+        w = _mlstm_weights(rng, d, P)
+        x = rng.standard_normal((n, 2 * d))
+        sc = scorer_cls(w, W)
+        rec = {}
+        for t in range(n):
+            r = sc.push(x[t])
+            if r is not None:
+                rec[r[0]] = r[1]
+        par = O.mlstm_scores_parallel(x, w, W)
+        assert sorted(rec) == list(range(n - W))
+        np.testing.assert_allclose([rec[u] for u in range(n - W)], par,
+                                   rtol=1e-11, atol=1e-12)
+
+
+def test_mlstm_hand_case():
+    check_mlstm_hand(O.MlstmScorer)
+
+
+def test_mlstm_recurrent_equals_parallel_form():
+    check_mlstm_recurrent_equals_parallel(O.MlstmScorer)
+
+
+def test_mlstm_unit_gates_reduce_to_linear_attention():
+    """i = f = 1 (zero gate weights, forget bias -> large) turns the state
+    into linear attention with Hedgehog features (KVpop Appendix A): the
+    readout is the similarity-weighted mean of the values."""
+    rng = np.random.default_rng(42)
+    d, P, W, n = 8, 4, 4, 25
+    w = _mlstm_weights(rng, d, P)
+    w.wi[:] = 0.0
+    w.wf[:] = 0.0
+    w.bi = 0.0
+    w.bf = 60.0   # sigmoid(60) == 1 in float64
+    x = rng.standard_normal((n, 2 * d))
+    rec = _recurrent_scores(w, x, W)
+    qf = O.hedgehog(x @ w.wq.T)
+    kf = O.hedgehog(x @ w.wk.T)
+    vf = x @ w.wv.T
+    for u in range(n - W):
+        q = u + W
+        sim = kf[:q + 1] @ qf[u]
+        h = (sim @ vf[:q + 1]) / sim.sum()
+        ref = float(w.a @ (h * scipy.special.expit(h)) + w.b)
+        assert rec[u] == pytest.approx(ref, rel=1e-12)
+
+
+def test_hedgehog_feature_map():
+    rng = np.random.default_rng(43)
+    y = rng.standard_normal((5, 6))
+    f = O.hedgehog(y)
+    np.testing.assert_allclose(f[:, :6].sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(f[:, 6:].sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(f[:, :6], scipy.special.softmax(y, axis=1),
+                               rtol=1e-14)
+    np.testing.assert_allclose(O.hedgehog(-y), np.concatenate(
+        [f[:, 6:], f[:, :6]], axis=1), rtol=1e-14)
