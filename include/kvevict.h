@@ -71,7 +71,11 @@ typedef enum {
 
 typedef enum { KVE_F32 = 0, KVE_BF16 = 1 } kve_dtype;
 typedef enum { KVE_ACT_RELU = 0, KVE_ACT_SILU = 1 } kve_act;
-typedef enum { KVE_SCORER_MLP_KV = 0, KVE_SCORER_GATE_HIDDEN = 1 } kve_scorer_kind;
+typedef enum {
+  KVE_SCORER_MLP_KV = 0,
+  KVE_SCORER_GATE_HIDDEN = 1,
+  KVE_SCORER_MLSTM = 2
+} kve_scorer_kind;
 
 /* Shape of one layer's cache. head_dim in {64, 128}; group in [1, 8];
  * kv_dtype is a kve_dtype. capacity = slots per (batch, KV head) slice. */
@@ -98,12 +102,17 @@ typedef struct {
   const float* log_gamma;
 } kve_policy;
 
-/* Device pointers of one layer's cache (layouts above). */
+/* Device pointers of one layer's cache (layouts above). scorer_state is
+ * the recurrent state of a stateful (MLSTM) scorer,
+ * kve_scorer_state_bytes() bytes, caller-owned: all-zero bytes are the
+ * empty state (no token absorbed), its layout is otherwise private to the
+ * library. NULL for stateless scorers. */
 typedef struct {
   void* k;
   void* v;
   float* score;
   int32_t* pos;
+  float* scorer_state;
 } kve_cache;
 
 /* Scorer weights (device pointers).
@@ -114,7 +123,17 @@ typedef struct {
  *    b2 [H] float32 or NULL. hidden in [1, 256]; wdtype == kv_dtype.
  *  GATE on hidden states (Fast KVzip section 3.1): in_dim = D,
  *    score = sigmoid(w1[h] . x + b1[h]); w1 [H][D] bf16, b1 [H] float32 or
- *    NULL; hidden, w2, b2, act unused. D a multiple of 32, H <= 16. */
+ *    NULL; hidden, w2, b2, act unused. D a multiple of 32, H <= 16.
+ *  MLSTM, stateful with delayed read-out (KVpop section 3.3, Appendix E.3-
+ *    E.4, Eq. 37-42, Hedgehog features of Appendix A): x = [k; v],
+ *    in_dim = 2 * head_dim, hidden = P = head_dim / 2 (projection width; the
+ *    features q~, k~ have 2P entries). w1 [H][3P + 2][in_dim] bf16 holds the
+ *    rows of W_q (P rows), W_k (P), W_v (P), then w_i and w_f; b1 [H][2]
+ *    float32 (b_i, b_f) or NULL; w2 [H][P] float32 is the read-out a, b2 [H]
+ *    float32 or NULL its bias. delay = W: after absorbing the token at
+ *    position q the scorer scores position q - W (no score while fewer than
+ *    W tokens precede q in the state). kv_dtype and wdtype bf16; act unused.
+ *  delay is read for MLSTM only. */
 typedef struct {
   int32_t kind;   /* kve_scorer_kind */
   int32_t act;    /* kve_act (MLP only) */
@@ -125,6 +144,7 @@ typedef struct {
   const float* b1;
   const float* w2;
   const float* b2;
+  int32_t delay;
 } kve_scorer;
 
 /* Host-side decode state of one layer for kve_step (in/out).
@@ -149,6 +169,12 @@ typedef struct {
  * on invalid arguments. */
 size_t kve_workspace_bytes(const kve_shape* shape, int32_t max_len);
 
+/* Bytes of scorer_state that a stateful scorer needs for this shape:
+ * batch * n_kv_heads slices of float32 state (matrix memory C [2P][P],
+ * normaliser z [2P], log scale and token count). 0 for stateless scorers
+ * and on invalid arguments. */
+size_t kve_scorer_state_bytes(const kve_shape* shape, const kve_scorer* scorer);
+
 /* a1 Append (KVpop Appendix C): write one new token per slice into `slot`:
  * K[b][h][slot] = k_new[b][h], V likewise, pos[b][h][slot] = position.
  * Requires 0 <= slot < capacity. The score of the slot is left unset
@@ -161,8 +187,15 @@ kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
  * cache->score (float32). MLP reads the cached K, V rows of those slots
  * (KVpop Eq. 35-36). GATE reads `hidden` [batch][slot_end-slot_begin][D]
  * bf16, the hidden states of those tokens (Fast KVzip section 3.1);
- * `hidden` must be NULL for MLP. Runs as a bf16 MFMA GEMM with float32
- * accumulation (float32 VALU for float32 weights). */
+ * `hidden` must be NULL for MLP and MLSTM. Runs as a bf16 MFMA GEMM with
+ * float32 accumulation (float32 VALU for float32 weights).
+ * MLSTM absorbs the cached tokens of those slots into cache->scorer_state in
+ * slot order and writes the score of every token it reads out, into that
+ * token's slot (KVpop Eq. 41-42). The slots must hold consecutive positions
+ * that continue the state's history, every token read out must be cached in
+ * a slot below slot_end, and the tokens of slots [0, slot_begin) must be
+ * older than those absorbed. Projections on MFMA (bf16, float32
+ * accumulation), the recurrence in float32. */
 kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
                      kve_cache* cache, int32_t slot_begin, int32_t slot_end,
                      const void* hidden, hipStream_t stream);
@@ -214,7 +247,10 @@ kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
  * attend over the cache. Updates *state on the host.
  * GATE scorers: hidden_new [batch][D] is the new token's hidden state and
  * hidden_buf [batch][L][D] (bf16, caller-owned) holds the pending tokens'
- * hidden states between calls; both must be NULL for MLP.
+ * hidden states between calls; both must be NULL for MLP and MLSTM.
+ * MLSTM scorers absorb the pending tokens at that point (the same scores as
+ * absorbing every token as it arrives) and need scorer->delay equal to the
+ * policy window.
  * Requires capacity >= B + L and state->len < capacity. */
 kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
                     const kve_scorer* scorer, kve_cache* cache,

@@ -19,12 +19,13 @@ __all__ = [
     "kve_workspace_bytes", "kve_append", "kve_score",
     "kve_select_evict", "kve_compact", "kve_decode_attn", "kve_step",
     "F32", "BF16", "ACT_RELU", "ACT_SILU",
-    "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "alloc_workspace", "LayerStep",
+    "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "SCORER_MLSTM",
+    "kve_scorer_state_bytes", "alloc_workspace", "LayerStep",
 ]
 
 F32, BF16 = 0, 1
 ACT_RELU, ACT_SILU = 0, 1
-SCORER_MLP_KV, SCORER_GATE_HIDDEN = 0, 1
+SCORER_MLP_KV, SCORER_GATE_HIDDEN, SCORER_MLSTM = 0, 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 
@@ -47,7 +48,8 @@ class _Policy(ctypes.Structure):
 
 class _Cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("score", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+                ("score", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("scorer_state", ctypes.c_void_p)]
 
 
 class _Scorer(ctypes.Structure):
@@ -55,7 +57,7 @@ class _Scorer(ctypes.Structure):
                 ("wdtype", ctypes.c_int32), ("in_dim", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("w1", ctypes.c_void_p),
                 ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("b2", ctypes.c_void_p)]
+                ("b2", ctypes.c_void_p), ("delay", ctypes.c_int32)]
 
 
 class _State(ctypes.Structure):
@@ -69,6 +71,8 @@ _SIGS = {
     "kve_version": (_I, []),
     "kve_status_str": (ctypes.c_char_p, [_I]),
     "kve_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Shape), _I]),
+    "kve_scorer_state_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Shape),
+                                                 ctypes.POINTER(_Scorer)]),
     "kve_append": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Cache), _I,
                         _I, _P, _P, _P]),
     "kve_score": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Scorer),
@@ -170,10 +174,12 @@ class Policy:
 
 
 class CacheTensors:
-    """Device tensors of one layer's cache (layouts as in kvevict.h)."""
+    """Device tensors of one layer's cache (layouts as in kvevict.h);
+    ``scorer_state`` is the stateful scorer's recurrent state or None."""
 
-    def __init__(self, k, v, score, pos):
+    def __init__(self, k, v, score, pos, scorer_state=None):
         self.k, self.v, self.score, self.pos = k, v, score, pos
+        self.scorer_state = scorer_state
 
     @classmethod
     def empty(cls, shape: Shape, device="cuda"):
@@ -186,9 +192,20 @@ class CacheTensors:
                    torch.zeros((b, H, cap), dtype=torch.float32, device=device),
                    torch.zeros((b, H, cap), dtype=torch.int32, device=device))
 
+    def attach_scorer_state(self, shape: "Shape", scorer: "Scorer"):
+        """Allocate an empty (zeroed) recurrent state for a stateful scorer;
+        returns it."""
+        import torch
+        n = kve_scorer_state_bytes(shape, scorer)
+        if n == 0:
+            raise ValueError("scorer has no recurrent state for this shape")
+        self.scorer_state = torch.zeros(n // 4, dtype=torch.float32,
+                                        device=self.k.device)
+        return self.scorer_state
+
     def c(self) -> _Cache:
         return _Cache(_ptr(self.k), _ptr(self.v), _ptr(self.score),
-                      _ptr(self.pos))
+                      _ptr(self.pos), _ptr(self.scorer_state))
 
 
 class Scorer:
@@ -196,9 +213,9 @@ class Scorer:
 
     def __init__(self, kind: int, w1, b1=None, w2=None, b2=None,
                  act: int = ACT_RELU, hidden: int = 0, in_dim: int = 0,
-                 wdtype: Optional[int] = None):
+                 wdtype: Optional[int] = None, delay: int = 0):
         import torch
-        self.kind, self.act = kind, act
+        self.kind, self.act, self.delay = kind, act, delay
         self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
         self.hidden, self.in_dim = hidden, in_dim
         if wdtype is None:
@@ -216,10 +233,18 @@ class Scorer:
         """w [H][D] bf16, b [H] float32."""
         return cls(SCORER_GATE_HIDDEN, w, b, in_dim=w.shape[1])
 
+    @classmethod
+    def mlstm(cls, w, a, gate_b=None, b=None, delay: int = 0):
+        """Stateful mLSTM scorer: w [H][3P+2][2d] bf16 (rows of W_q, W_k,
+        W_v, then w_i, w_f), a [H][P] float32 read-out, gate_b [H][2]
+        float32 (b_i, b_f), b [H] float32; delay = the window W."""
+        return cls(SCORER_MLSTM, w, gate_b, a, b, hidden=a.shape[1],
+                   in_dim=w.shape[2], delay=delay)
+
     def c(self) -> _Scorer:
         return _Scorer(self.kind, self.act, self.wdtype, self.in_dim,
                        self.hidden, _ptr(self.w1), _ptr(self.b1),
-                       _ptr(self.w2), _ptr(self.b2))
+                       _ptr(self.w2), _ptr(self.b2), self.delay)
 
 
 @dataclass
@@ -245,6 +270,12 @@ def kve_status_str(status: int) -> str:
 def kve_workspace_bytes(shape: Shape, max_len: int) -> int:
     cs = shape.c()
     return load_library().kve_workspace_bytes(ctypes.byref(cs), max_len)
+
+
+def kve_scorer_state_bytes(shape: Shape, scorer: Scorer) -> int:
+    cs, csc = shape.c(), scorer.c()
+    return load_library().kve_scorer_state_bytes(ctypes.byref(cs),
+                                                 ctypes.byref(csc))
 
 
 def alloc_workspace(shape: Shape, max_len: int, device="cuda"):

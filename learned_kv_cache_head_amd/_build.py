@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libkvevict.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["kvevict.hip", "attention.hip", "cache_ops.hip", "score.hip"]
+SOURCES = ["kvevict.hip", "attention.hip", "cache_ops.hip", "score.hip",
+           "mlstm.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

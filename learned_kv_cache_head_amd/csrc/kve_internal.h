@@ -97,4 +97,21 @@ struct GateLaunch {
 };
 hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s);
 
+struct MlstmLaunch {
+  const void* k;         // cache base (bf16)
+  const void* v;
+  const int32_t* pos;    // [batch][H][cap]
+  float* score;          // [batch][H][cap]
+  float* state;          // [batch][H][mlstm_state_floats(D)]
+  const void* w;         // bf16 [H][3P+2][2D]: W_q, W_k, W_v rows, w_i, w_f
+  const float* b;        // [H][2] (b_i, b_f) or null
+  const float* a;        // [H][P] read-out weights
+  const float* b2;       // [H] or null
+  int batch, H, D, cap;
+  int slot_begin, slot_end;
+  int delay;             // read-out delay W
+};
+hipError_t launch_score_mlstm(const MlstmLaunch& m, hipStream_t s);
+size_t mlstm_state_floats(int D);  // 0 for an unsupported head_dim
+
 }  // namespace kve

@@ -168,6 +168,16 @@ kve_status check_scorer(const kve_shape* shape, const kve_scorer* sc) {
     if (shape->n_kv_heads > 16) return KVE_ERR_UNSUPPORTED;
     return KVE_OK;
   }
+  if (sc->kind == KVE_SCORER_MLSTM) {
+    if (shape->kv_dtype != KVE_BF16 || sc->wdtype != KVE_BF16)
+      return KVE_ERR_UNSUPPORTED;
+    if (sc->in_dim != 2 * shape->head_dim) return KVE_ERR_UNSUPPORTED;
+    if (sc->hidden != shape->head_dim / 2) return KVE_ERR_UNSUPPORTED;
+    if (kve::mlstm_state_floats(shape->head_dim) == 0) return KVE_ERR_UNSUPPORTED;
+    if (!sc->w2) return KVE_ERR_INVALID_ARG;
+    if (sc->delay < 0) return KVE_ERR_INVALID_ARG;
+    return KVE_OK;
+  }
   return KVE_ERR_UNSUPPORTED;
 }
 
@@ -176,6 +186,27 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
                       const void* hidden, long long hidden_batch_stride,
                       hipStream_t stream) {
   if (slot_end == slot_begin) return KVE_OK;
+  if (sc->kind == KVE_SCORER_MLSTM) {
+    if (!cache->scorer_state) return KVE_ERR_INVALID_ARG;
+    kve::MlstmLaunch m{};
+    m.k = cache->k;
+    m.v = cache->v;
+    m.pos = cache->pos;
+    m.score = cache->score;
+    m.state = cache->scorer_state;
+    m.w = sc->w1;
+    m.b = sc->b1;
+    m.a = sc->w2;
+    m.b2 = sc->b2;
+    m.batch = shape->batch;
+    m.H = shape->n_kv_heads;
+    m.D = shape->head_dim;
+    m.cap = shape->capacity;
+    m.slot_begin = slot_begin;
+    m.slot_end = slot_end;
+    m.delay = sc->delay;
+    return from_hip(kve::launch_score_mlstm(m, stream));
+  }
   if (sc->kind == KVE_SCORER_MLP_KV) {
     kve::MlpLaunch m{};
     m.k = cache->k;
@@ -237,6 +268,15 @@ size_t kve_workspace_bytes(const kve_shape* shape, int32_t max_len) {
   return n > 0 ? n : kAlign;
 }
 
+size_t kve_scorer_state_bytes(const kve_shape* shape,
+                              const kve_scorer* scorer) {
+  if (check_shape(shape) != KVE_OK || check_scorer(shape, scorer) != KVE_OK)
+    return 0;
+  if (scorer->kind != KVE_SCORER_MLSTM) return 0;
+  return (size_t)shape->batch * shape->n_kv_heads *
+         kve::mlstm_state_floats(shape->head_dim) * sizeof(float);
+}
+
 kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
                       int32_t position, const void* k_new, const void* v_new,
                       hipStream_t stream) {
@@ -262,6 +302,8 @@ kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
   if (slot_end > shape->capacity) return KVE_ERR_CAPACITY;
   const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN;
   if (gate != (hidden != nullptr)) return KVE_ERR_INVALID_ARG;
+  if (scorer->kind == KVE_SCORER_MLSTM && !cache->scorer_state)
+    return KVE_ERR_INVALID_ARG;
   const long long stride = (long long)(slot_end - slot_begin) * scorer->in_dim;
   return score_impl(shape, scorer, cache, slot_begin, slot_end, hidden, stride,
                     stream);
@@ -337,6 +379,10 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN;
   if (gate != (hidden_new != nullptr) || gate != (hidden_buf != nullptr))
     return KVE_ERR_INVALID_ARG;
+  if (scorer->kind == KVE_SCORER_MLSTM) {
+    if (!cache->scorer_state) return KVE_ERR_INVALID_ARG;
+    if (scorer->delay != policy->window) return KVE_ERR_POLICY;
+  }
   int len = state->len;
   int scored = state->scored_upto;
   if (len < 0 || scored < 0 || scored > len) return KVE_ERR_INVALID_ARG;

@@ -437,6 +437,15 @@ class OracleLayer:
         self.pos = np.concatenate(
             [self.pos, np.full((b, H, 1), self.newest, dtype=np.int64)], 2)
 
+    def set_scores(self, position: int, score_32: np.ndarray) -> None:
+        """Give the token at ``position`` its score (score [b][H]): a
+        stateful scorer scores a token only when it leaves the window (KVpop
+        section 3.3, Eq. 10-11), after the token was appended."""
+        hit = self.pos == position
+        assert np.all(hit.sum(axis=2) == 1), "token not cached in every slice"
+        sc = np.asarray(score_32, np.float32)
+        self.score[hit] = np.broadcast_to(sc[:, :, None], hit.shape)[hit]
+
     def maybe_evict(self) -> Optional[np.ndarray]:
         """Evict n - B entries once the cache reaches B + L."""
         p = self.policy

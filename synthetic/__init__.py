@@ -24,6 +24,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "rng_for", "round_to_bf16_bits",
     "bf16_bits_to_f32", "draw_rows", "draw_mlp_weights", "draw_gate_weights",
+    "draw_mlstm_weights",
     "initial_context", "step_inputs", "TENSOR_IDS",
 ]
 
@@ -46,8 +47,10 @@ class Workload:
     evict_len: int     # L
     steps: int         # decode steps
     layers: int
-    scorer: str        # "mlp" ([k;v] MLP) or "gate" (hidden-state gate)
-    hidden: int        # MLP hidden width, or gate input dim D
+    scorer: str        # "mlp" ([k;v] MLP), "gate" (hidden-state gate) or
+                       # "mlstm" (stateful scorer over [k;v])
+    hidden: int        # MLP hidden width, gate input dim D, or the mLSTM
+                       # projection width P = d / 2
     act: str           # "relu" or "silu" (MLP only)
     structured: bool   # low-rank shared direction + heavy-hitter tokens
     heavy_frac: float = 0.01
@@ -59,7 +62,7 @@ class Workload:
 
     @property
     def in_dim(self) -> int:
-        return 2 * self.head_dim if self.scorer == "mlp" else self.hidden
+        return self.hidden if self.scorer == "gate" else 2 * self.head_dim
 
     @property
     def capacity(self) -> int:
@@ -110,6 +113,7 @@ TENSOR_IDS = {
     "k0": 1, "v0": 2, "k_new": 3, "v_new": 4, "q": 5, "heavy": 6,
     "dir_k": 7, "dir_v": 8, "w1": 9, "w2": 10, "b1": 11, "b2": 12,
     "gate_w": 13, "hidden0": 14, "hidden_new": 15, "misc": 16,
+    "mlstm_w": 17, "mlstm_gb": 18, "mlstm_a": 19,
 }
 
 
@@ -250,6 +254,30 @@ def draw_gate_weights(w: Workload, seed: int, layer: int,
     else:
         b = np.zeros((w.n_kv,))
     return {"w": Stored(gw.astype(np.float32), "bf16"),
+            "b": Stored(b.astype(np.float32), "f32")}
+
+
+def draw_mlstm_weights(w: Workload, seed: int, layer: int) -> dict:
+    """Per-KV-head stateful-scorer weights, P = d / 2:
+    w [H][3P+2][2d] bf16 (rows W_q, W_k, W_v, then w_i, w_f), N(0, 1/(2d)),
+    with the W_q and W_k rows scaled by 2 so that the Hedgehog features are
+    not flat; gate_b [H][2] float32: input bias N(0, 0.5^2), forget bias
+    3 + N(0, 1) (a forget gate near 0.95, long memory); a [H][P] float32,
+    N(0, 1/P); b [H] float32, N(0, 0.1^2)."""
+    P = w.head_dim // 2
+    in_dim = 2 * w.head_dim
+    g = rng_for(seed, w.cfg_id, layer, -1, "mlstm_w")
+    wt = g.standard_normal((w.n_kv, 3 * P + 2, in_dim)) / np.sqrt(in_dim)
+    wt[:, :2 * P] *= 2.0
+    gg = rng_for(seed, w.cfg_id, layer, -1, "mlstm_gb")
+    gb = np.stack([0.5 * gg.standard_normal(w.n_kv),
+                   3.0 + gg.standard_normal(w.n_kv)], axis=1)
+    ga = rng_for(seed, w.cfg_id, layer, -1, "mlstm_a")
+    a = ga.standard_normal((w.n_kv, P)) / np.sqrt(P)
+    b = 0.1 * ga.standard_normal(w.n_kv)
+    return {"w": Stored(wt.astype(np.float32), "bf16"),
+            "gate_b": Stored(gb.astype(np.float32), "f32"),
+            "a": Stored(a.astype(np.float32), "f32"),
             "b": Stored(b.astype(np.float32), "f32")}
 
 

@@ -194,3 +194,64 @@ def test_policy_struct_layout_matches_header():
     assert kve._Policy.log_gamma.offset == 16
     p = kve.Policy(1024, 4, 128, 128).c()
     assert p.log_gamma is None
+
+
+def test_cache_and_scorer_struct_layout_matches_header():
+    """kve_cache: four pointers then scorer_state; kve_scorer: five int32,
+    four pointers, then the int32 delay."""
+    assert ctypes.sizeof(kve._Cache) == 40
+    assert kve._Cache.scorer_state.offset == 32
+    assert kve._Scorer.w1.offset == 24
+    assert kve._Scorer.delay.offset == 56
+    assert ctypes.sizeof(kve._Scorer) == 64
+
+
+def _mlstm(delay=128, hidden=64, in_dim=256, wdtype=kve.BF16, w2=FAKE):
+    return kve._Scorer(2, 0, wdtype, in_dim, hidden, FAKE, None, w2, None,
+                       delay)
+
+
+def test_mlstm_state_bytes():
+    lib = _lib()
+    s = _shape()            # batch 2, 8 KV heads, head_dim 128
+    n = lib.kve_scorer_state_bytes(ctypes.byref(s), ctypes.byref(_mlstm()))
+    # C [128][64] + z [128] + one 64-float block (log scale, count)
+    assert n == 2 * 8 * (128 * 64 + 128 + 64) * 4
+    s64 = _shape(head_dim=64)
+    n64 = lib.kve_scorer_state_bytes(ctypes.byref(s64), ctypes.byref(
+        _mlstm(hidden=32, in_dim=128)))
+    assert n64 == 2 * 8 * (64 * 32 + 64 + 64) * 4
+    mlp = kve._Scorer(0, 0, kve.BF16, 256, 64, FAKE, None, FAKE, None)
+    assert lib.kve_scorer_state_bytes(ctypes.byref(s), ctypes.byref(mlp)) == 0
+    assert lib.kve_scorer_state_bytes(ctypes.byref(s), ctypes.byref(
+        _mlstm(hidden=32))) == 0   # P must be head_dim / 2
+
+
+def test_mlstm_rejects_bad_arguments():
+    lib = _lib()
+    s = _shape()
+    with_state = kve._Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    no_state = _cache()
+
+    def score(sc, cache=with_state, shape=s, hidden=None):
+        return lib.kve_score(ctypes.byref(shape), ctypes.byref(sc),
+                             ctypes.byref(cache), 0, 10, hidden, None)
+
+    assert score(_mlstm(), cache=no_state) == 1
+    assert score(_mlstm(), hidden=FAKE) == 1
+    assert score(_mlstm(hidden=32)) == 4
+    assert score(_mlstm(in_dim=128)) == 4
+    assert score(_mlstm(delay=-1)) == 1
+    assert score(_mlstm(w2=None)) == 1
+    assert score(_mlstm(), shape=_shape(kv_dtype=kve.F32)) == 4
+    p = kve._Policy(1024, 4, 128, 128)
+
+    def step(sc, cache=with_state):
+        st = kve._State(1030, 1024, 9000, 0)
+        return lib.kve_step(ctypes.byref(s), ctypes.byref(p), ctypes.byref(sc),
+                            ctypes.byref(cache), ctypes.byref(st), FAKE, FAKE,
+                            None, None, FAKE, FAKE, None, FAKE, FAKE, 1 << 24,
+                            None)
+
+    assert step(_mlstm(delay=64)) == 2          # delay != window
+    assert step(_mlstm(), cache=no_state) == 1
