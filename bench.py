@@ -63,16 +63,41 @@ def attn_launch_bytes(w, n: int, fused_append: bool) -> int:
     return w.batch * w.n_kv * per
 
 
-def evict_extra_bytes(w, n_before: int, moved: int) -> int:
-    """Bytes of an evicting step besides its attention launch, one layer:
-    append (new row read + stored + position), scorer (L pending rows read,
-    L scores written, per-head weights once), select (candidate scores read,
-    kept slots written), compaction (each moved row's K, V, score, position
-    read and written). ``moved`` counts moved rows over all slices."""
+def mlstm_state_bytes(w) -> int:
+    """Recurrent state of one slice: C [d][d/2] and z [d] float32 plus one
+    64-float block (log scale, token count)."""
+    d = w.head_dim
+    return (d * (d // 2) + d + 64) * 4
+
+
+def score_bytes(w, scorer: str) -> int:
+    """Bytes of one layer's buffered scoring of L pending rows.
+    MLP: the L rows read, L scores written, per-head weights once.
+    mLSTM: the L absorbed rows and the L read-out rows read, L scores
+    written, the state read and written once, the slot lookup of the first
+    W read-outs (ceil(W/32) scans of the B older positions), per-head
+    weights once."""
     d, e, L, hid = w.head_dim, w.elem_bytes, w.evict_len, w.hidden
     slices = w.batch * w.n_kv
+    if scorer == "mlstm":
+        P = d // 2
+        scans = -(-min(w.window, L) // 32) if w.window else 0
+        per = (2 * L * 2 * d * e + L * 4 + 2 * mlstm_state_bytes(w)
+               + scans * w.budget * 4)
+        return slices * per + w.n_kv * ((3 * P + 2) * 2 * d * e + 4 * P + 12)
+    return slices * (L * 2 * d * e + L * 4) + w.n_kv * (hid * 2 * d * e + hid * 4)
+
+
+def evict_extra_bytes(w, n_before: int, moved: int, scorer: str = "mlp") -> int:
+    """Bytes of an evicting step besides its attention launch, one layer:
+    append (new row read + stored + position), scorer (``score_bytes``),
+    select (candidate scores read, kept slots written), compaction (each
+    moved row's K, V, score, position read and written). ``moved`` counts
+    moved rows over all slices."""
+    d, e = w.head_dim, w.elem_bytes
+    slices = w.batch * w.n_kv
     append = slices * (2 * d * e * 2 + 4)
-    score = slices * (L * 2 * d * e + L * 4) + w.n_kv * (hid * 2 * d * e + hid * 4)
+    score = score_bytes(w, scorer)
     cand = n_before - w.sinks - w.window
     select = slices * (cand * 4 + w.budget * 4)
     compact = moved * 2 * (2 * d * e + 8)
@@ -86,7 +111,8 @@ def evict_extra_bytes(w, n_before: int, moved: int) -> int:
 class Stack:
     """Per-layer caches, scorer weights, step runners and input pools."""
 
-    def __init__(self, w, seed: int, pool_steps: int, dev, decay=False):
+    def __init__(self, w, seed: int, pool_steps: int, dev, decay=False,
+                 scorer="mlp"):
         import torch
         import learned_kv_cache_head_amd as kve
         import synthetic as syn
@@ -112,11 +138,26 @@ class Stack:
         cfg = w.cfg_id
         for l in range(w.layers):
             dn = syn.device_normal
-            w1 = dn((H, w.hidden, 2 * d), seed, (cfg, l, 0, T["w1"]),
-                    torch.bfloat16, dev, scale=(2 * d) ** -0.5)
-            w2 = dn((H, w.hidden), seed, (cfg, l, 0, T["w2"]), torch.float32,
-                    dev, scale=w.hidden ** -0.5)
-            sc = kve.Scorer.mlp(w1, w2)
+            if scorer == "mlstm":
+                # KVpop Appendix E.3 shapes, P = d / 2; forget bias 3 (a
+                # forget gate near 0.95), input bias 0.
+                P = d // 2
+                wq = dn((H, 3 * P + 2, 2 * d), seed, (cfg, l, 0, T["mlstm_w"]),
+                        torch.float32, dev, scale=(2 * d) ** -0.5)
+                wq[:, :2 * P] *= 2.0
+                gb = torch.zeros((H, 2), dtype=torch.float32, device=dev)
+                gb[:, 1] = 3.0
+                a = dn((H, P), seed, (cfg, l, 0, T["mlstm_a"]), torch.float32,
+                       dev, scale=P ** -0.5)
+                sc = kve.Scorer.mlstm(wq.to(torch.bfloat16), a, gate_b=gb,
+                                      delay=w.window)
+                scratch.attach_scorer_state(pre_shape, sc)
+            else:
+                w1 = dn((H, w.hidden, 2 * d), seed, (cfg, l, 0, T["w1"]),
+                        torch.bfloat16, dev, scale=(2 * d) ** -0.5)
+                w2 = dn((H, w.hidden), seed, (cfg, l, 0, T["w2"]),
+                        torch.float32, dev, scale=w.hidden ** -0.5)
+                sc = kve.Scorer.mlp(w1, w2)
             # Prompt of n0 tokens, scored and compressed to B by the library.
             scratch.k.copy_(dn((b, H, w.n0, d), seed, (cfg, l, 0, T["k0"]),
                                torch.bfloat16, dev))
@@ -133,6 +174,9 @@ class Stack:
             c.v[:, :, :B].copy_(scratch.v[:, :, :B])
             c.score[:, :, :B].copy_(scratch.score[:, :, :B])
             c.pos[:, :, :B].copy_(scratch.pos[:, :, :B])
+            # The recurrent state does not depend on the capacity.
+            c.scorer_state = scratch.scorer_state
+            scratch.scorer_state = None
             st = kve.DecodeState(B, B, w.n0)
             self.caches.append(c)
             self.scorers.append(sc)
@@ -168,7 +212,8 @@ class Stack:
 # Oracle CPU baseline (bounded sample)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, seed: int, sample_batch: int, sample_steps: int) -> dict:
+def cpu_baseline(w, seed: int, sample_batch: int, sample_steps: int,
+                 scorer: str = "mlp") -> dict:
     """Time the float64 oracle on one layer of the same workload for
     ``sample_batch`` sequences over ``sample_steps`` decode steps (whole
     eviction cycles), starting from its own compressed prompt; scale to the
@@ -182,6 +227,8 @@ def cpu_baseline(w, seed: int, sample_batch: int, sample_steps: int) -> dict:
         threads = max([i.get("num_threads", 1) for i in info] or [1])
     except Exception:
         threads = 1
+    if scorer == "mlstm":
+        return cpu_baseline_mlstm(w, seed, sample_batch, sample_steps, threads)
     ws = syn.workload(w.cfg_id, batch=sample_batch)
     ctx = syn.initial_context(ws, seed, 0)
     wts = syn.draw_mlp_weights(ws, seed, 0)
@@ -218,6 +265,69 @@ def cpu_baseline(w, seed: int, sample_batch: int, sample_steps: int) -> dict:
                    f"({sample_steps // w.evict_len} eviction cycles) from a "
                    f"compressed {w.n0}-token prompt; {dt:.1f} s wall; scaled "
                    f"to the {w.layers}-layer step as tokens/(time x layers)"),
+    }
+
+
+def cpu_baseline_mlstm(w, seed, sample_batch, sample_steps, threads) -> dict:
+    """The oracle's decode loop with the stateful scorer: every new token
+    is absorbed by the slice's float64 recurrence and the token leaving the
+    window is scored (the prompt is absorbed untimed)."""
+    import numpy as np
+    import oracle as O
+    import synthetic as syn
+    ws = syn.workload(w.cfg_id, batch=sample_batch, scorer="mlstm",
+                      hidden=w.head_dim // 2)
+    ctx = syn.initial_context(ws, seed, 0)
+    wts = syn.draw_mlstm_weights(ws, seed, 0)
+    P = w.head_dim // 2
+
+    def head(h):
+        x, gb = wts["w"].f64[h], wts["gate_b"].f64[h]
+        return O.MlstmWeights(x[:P], x[P:2 * P], x[2 * P:3 * P], x[3 * P],
+                              x[3 * P + 1], gb[0], gb[1], wts["a"].f64[h],
+                              float(wts["b"].f64[h]))
+    W = ws.window
+    scs = [[O.MlstmScorer(head(h), W) for h in range(ws.n_kv)]
+           for _ in range(sample_batch)]
+    s0 = np.zeros((sample_batch, ws.n_kv, ws.n0), np.float32)
+    for bi in range(sample_batch):
+        for h in range(ws.n_kv):
+            for t in range(ws.n0):
+                r = scs[bi][h].push(np.concatenate(
+                    [ctx["k0"].f64[bi, h, t], ctx["v0"].f64[bi, h, t]]))
+                if r is not None:
+                    s0[bi, h, r[0]] = r[1]
+    lay = O.OracleLayer(ctx["k0"].f64, ctx["v0"].f64, s0,
+                        O.Policy(ws.budget, ws.sinks, ws.window, ws.evict_len),
+                        ws.group)
+    lay.prefill_compress()
+    del ctx
+    inputs = [syn.step_inputs(ws, seed, 0, i) for i in range(sample_steps)]
+    t0 = time.perf_counter()
+    for i, x in enumerate(inputs):
+        su = np.empty((sample_batch, ws.n_kv), np.float32)
+        for bi in range(sample_batch):
+            for h in range(ws.n_kv):
+                _, su[bi, h] = scs[bi][h].push(np.concatenate(
+                    [x["k_new"].f64[bi, h], x["v_new"].f64[bi, h]]))
+        lay.append(x["k_new"].f64, x["v_new"].f64,
+                   np.zeros((sample_batch, ws.n_kv), np.float32))
+        lay.set_scores(ws.n0 + i - W, su)
+        lay.maybe_evict()
+        lay.attend(x["q"].f64)
+    dt = time.perf_counter() - t0
+    tokens = sample_batch * sample_steps
+    return {
+        "value": tokens / (dt * w.layers),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 oracle with the mLSTM scorer, 1 of {w.layers} "
+                   f"layers, {sample_batch} of {w.batch} sequences, "
+                   f"{sample_steps} decode steps from a compressed "
+                   f"{w.n0}-token prompt (absorbed untimed); {dt:.1f} s wall; "
+                   f"scaled to the {w.layers}-layer step as "
+                   f"tokens/(time x layers)"),
     }
 
 
@@ -264,7 +374,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decay", action="store_true",
                     help="rank with KVpop temporal decay (static priority)")
-    ap.add_argument("--cpu-batch", type=int, default=16)
+    ap.add_argument("--scorer", default="mlp", choices=["mlp", "mlstm"],
+                    help="stateless MLP over [k; v], or the stateful mLSTM "
+                         "scorer with delayed read-out")
+    ap.add_argument("--cpu-batch", type=int, default=None,
+                    help="oracle sample sequences (default 16; 2 for mLSTM)")
     ap.add_argument("--cpu-steps", type=int, default=None)
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, run a plain 1 GiB "
@@ -293,7 +407,8 @@ def main() -> int:
     log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")
     t0 = time.perf_counter()
-    stack = Stack(w, args.seed, pool, dev, decay=args.decay)
+    stack = Stack(w, args.seed, pool, dev, decay=args.decay,
+                  scorer=args.scorer)
     log(f"set-up {time.perf_counter() - t0:.1f} s")
 
     for i in range(warmup):
@@ -366,7 +481,8 @@ def main() -> int:
             if ev:
                 c = ev_count.get(l, 0)
                 ev_count[l] = c + 1
-                total_bytes += evict_extra_bytes(w, n, moved[(l, c)])
+                total_bytes += evict_extra_bytes(w, n, moved[(l, c)],
+                                                 args.scorer)
                 total_bytes += attn_launch_bytes(w, w.budget, False)
             else:
                 total_bytes += attn_launch_bytes(w, n, True)
@@ -410,7 +526,10 @@ def main() -> int:
                    "n_q_heads": w.n_q, "head_dim": w.head_dim,
                    "budget": w.budget, "sinks": w.sinks, "window": w.window,
                    "evict_len": w.evict_len, "prompt_len": w.n0,
-                   "scorer": f"mlp {2 * w.head_dim}-{w.hidden}-1 relu",
+                   "scorer": (f"mlp {2 * w.head_dim}-{w.hidden}-1 relu"
+                              if args.scorer == "mlp" else
+                              f"mlstm P={w.head_dim // 2} hedgehog, delayed "
+                              f"read-out W={w.window}"),
                    "decay": bool(args.decay),
                    "parallelism": "none"},
         "step_gbps": round(step_gbps, 1),
@@ -422,8 +541,11 @@ def main() -> int:
         del stack
         torch.cuda.empty_cache()
         cs = args.cpu_steps if args.cpu_steps is not None else 2 * L
-        log(f"cpu baseline: oracle on {args.cpu_batch} sequences x {cs} steps")
-        cb = cpu_baseline(w, args.seed, args.cpu_batch, cs)
+        cbatch = args.cpu_batch
+        if cbatch is None:
+            cbatch = 2 if args.scorer == "mlstm" else 16
+        log(f"cpu baseline: oracle on {cbatch} sequences x {cs} steps")
+        cb = cpu_baseline(w, args.seed, cbatch, cs, args.scorer)
         cb["value"] = round(cb["value"], 3)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)

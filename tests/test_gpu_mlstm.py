@@ -127,6 +127,14 @@ def test_mlstm_renormalises_under_steep_gates():
              wscale=8.0)
 
 
+def test_mlstm_renormalises_between_chunks():
+    """Forget gate near 1/2: the log scale falls by about 0.7 per token, so
+    the chunk reference moves past the renormalisation threshold every few
+    chunks while each chunk's spread stays small."""
+    print("[mlstm] chunk renormalisation", flush=True)
+    run_case(2, 2, 128, 1000, 64, (1000,), seed=7, gate_b=(0.0, 0.0))
+
+
 def test_mlstm_long_memory():
     """Forget gate at 1 - 2e-9 (float32 rounds it to 1): a long sum without
     decay, 4096 tokens."""
