@@ -15,6 +15,11 @@ What it computes, step by step, in the pages' notation:
   gate on the layer's hidden state with output in [0, 1] (here a linear map
   followed by a sigmoid). Scores are ranked in float32 (KVpop Appendix F,
   "Training details": top-k ranking and selection in float32).
+* Stateful scorer. KVpop section 3.3 "Stateful scorers", Appendix A and
+  E.3-E.4, Eq. (10)-(11) and (37)-(42): per KV head, Hedgehog features of
+  small projections of x = [k; v], a gated matrix memory C and normaliser z
+  updated by every token, and a delayed read-out: after absorbing position q
+  the token at q - W is scored from the state that has seen q.
 * Retention rule. KVpop section 3, Eq. (1) B = s + w + k; section 3.1 Eq. (4)
   eligible set E(q) = {t | s <= t <= q - w}; Appendix C.1 Eq. (26) retained
   set = sinks, recent window, and the top-k eligible tokens.
@@ -45,6 +50,10 @@ Readings where the pages leave a step open (also listed in the design notes):
 * Temporal decay (optional, per KV head): decay step n = 1 only (KVpop Table
   3 uses n = 1), ranking by the static priority of Eq. (20) in float32.
 * Query head j reads KV head floor(j / G) (contiguous GQA groups).
+* Stateful scorer: the Hedgehog variant with projection width P = d/2
+  (features of 2P entries), scalar affine gate preactivations with biases, no
+  output gate, soft-cap, norm or skip connection; the read-out delay equals
+  the window W; the plain (unstabilised) recurrence in float64.
 
 Parity pins: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` to facts other than its own formula
