@@ -15,6 +15,11 @@ What it computes, step by step, in the pages' notation:
   gate on the layer's hidden state with output in [0, 1] (here a linear map
   followed by a sigmoid). Scores are ranked in float32 (KVpop Appendix F,
   "Training details": top-k ranking and selection in float32).
+* Prefill selection and masked prefill attention. KVpop section 3.2
+  "Running top-k sparse attention" and Appendix C.1-C.2, Eq. (26): each
+  query position q keeps the sinks, its recent window and the eligible
+  tokens whose static-priority rank is within the rank tau_q of the k-th
+  best eligible token; attention over the prompt uses that mask.
 * Stateful scorer. KVpop section 3.3 "Stateful scorers", Appendix A and
   E.3-E.4, Eq. (10)-(11) and (37)-(42): per KV head, Hedgehog features of
   small projections of x = [k; v], a gated matrix memory C and normaliser z
@@ -71,6 +76,7 @@ __all__ = [
     "Policy", "mlp_score", "gate_score", "score_to_f32", "static_priority",
     "hedgehog", "MlstmWeights", "mlstm_features", "mlstm_readout",
     "MlstmScorer", "mlstm_scores_parallel",
+    "prefill_ranks", "prefill_cutoffs", "prefill_mask", "prefill_attention",
     "eligible_mask",
     "select_keep", "compaction_sources", "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
     "closed_form_retained", "cache_bytes_per_token",
@@ -539,6 +545,86 @@ def closed_form_retained(score_by_pos32: np.ndarray, newest: int,
 # ---------------------------------------------------------------------------
 # Cache size per token
 # ---------------------------------------------------------------------------
+
+def prefill_ranks(score32: np.ndarray, log_gamma: Optional[float] = None
+                  ) -> np.ndarray:
+    """rank(t) of every prompt token t = 0..n-1 under the static priority
+    (KVpop Appendix C.1; Eq. (20) with decay): rank 0 is the highest
+    priority. Order by the float32 key descending, and among equal keys by
+    position descending, the reverse of the eviction order of
+    ``select_keep`` (equal keys evict the older token first). score32 is
+    indexed by position."""
+    s = np.asarray(score32, dtype=np.float32)
+    n = s.shape[0]
+    pos = np.arange(n)
+    key = static_priority(s, pos, log_gamma).astype(np.float64) + 0.0
+    order = np.lexsort((-pos, -key))  # last key is primary
+    rank = np.empty(n, dtype=np.int64)
+    rank[order] = np.arange(n)
+    return rank
+
+
+def prefill_cutoffs(rank: np.ndarray, sinks: int, window: int, k: int
+                    ) -> np.ndarray:
+    """Cutoff rank tau_q for every query position q = 0..n-1 (KVpop
+    Appendix C.1-C.2): the rank of the k-th best token of the eligible set
+    E(q) = {t : S <= t <= q - W}. Encoded as n when E(q) holds fewer than k
+    tokens (every eligible token is kept) and -1 when k = 0 (none is)."""
+    rank = np.asarray(rank, dtype=np.int64)
+    n = rank.shape[0]
+    tau = np.empty(n, dtype=np.int64)
+    for q in range(n):
+        elig = rank[sinks:max(q - window + 1, sinks)]
+        if k == 0:
+            tau[q] = -1
+        elif elig.shape[0] < k:
+            tau[q] = n
+        else:
+            tau[q] = np.sort(elig)[k - 1]
+    return tau
+
+
+def prefill_mask(rank: np.ndarray, tau: np.ndarray, sinks: int, window: int
+                 ) -> np.ndarray:
+    """The fixed-budget sparse mask of KVpop Appendix C.1, Eq. (26), over
+    causal pairs: M[q, t] = t <= q and (t < S, or q - t < W, or t in E(q)
+    with rank(t) <= tau_q). Returns bool [n][n]."""
+    n = np.asarray(rank).shape[0]
+    q = np.arange(n)[:, None]
+    t = np.arange(n)[None, :]
+    sink = t < sinks
+    recent = (q - t) < window
+    elig = (t >= sinks) & (t <= q - window)
+    top = elig & (np.asarray(rank)[None, :] <= np.asarray(tau)[:, None])
+    return (t <= q) & (sink | recent | top)
+
+
+def prefill_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                      masks: np.ndarray, group: int):
+    """Masked attention over the prompt (KVpop Appendix C, Eq. (26) applied
+    inside the attention of Appendix D.1, Eq. (27)-(29)) for one sequence:
+    Q [H*G][n][d], K and V [H][n][d], masks [H][n][n] (per KV head; query
+    head j reads KV head floor(j / G)). Returns out [H*G][n][d] and the
+    natural-log normaliser lse [H*G][n]; a query with no kept key gets
+    out = 0 and lse = -inf."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    hq, n, d = Q.shape
+    out = np.zeros((hq, n, d))
+    lse = np.full((hq, n), -np.inf)
+    for j in range(hq):
+        h = j // group
+        z = (Q[j] @ K[h].T) / np.sqrt(d)
+        z = np.where(masks[h], z, -np.inf)
+        m = z.max(axis=1)
+        ok = np.isfinite(m)
+        e = np.exp(z[ok] - m[ok, None])
+        ssum = e.sum(axis=1)
+        out[j, ok] = (e / ssum[:, None]) @ V[h]
+        lse[j, ok] = m[ok] + np.log(ssum)
+    return out, lse
+
 
 def cache_bytes_per_token(layers: int, n_kv: int, head_dim: int,
                           elem_bytes: int) -> int:

@@ -239,3 +239,48 @@ def test_mlstm_mutants_fail(mutant):
         except AssertionError:
             failed += 1
     assert failed >= 1
+
+
+# --- prefill selection mutants ----------------------------------------------
+
+def ranks_ties_older_first(s32, log_gamma=None):
+    """Equal keys ranked older-first (the wrong tie order)."""
+    n = s32.shape[0]
+    key = O.static_priority(s32, np.arange(n), log_gamma).astype(np.float64) + 0.0
+    order = np.lexsort((np.arange(n), -key))
+    r = np.empty(n, dtype=np.int64)
+    r[order] = np.arange(n)
+    return r
+
+
+def cutoffs_off_by_one(rank, sinks, window, k):
+    """The (k+1)-th best instead of the k-th."""
+    return O.prefill_cutoffs(rank, sinks, window, k + 1)
+
+
+def mask_window_inclusive(rank, tau, sinks, window):
+    """Window read as q - t <= W."""
+    return O.prefill_mask(rank, tau, sinks, window + 1)
+
+
+def mask_without_sinks(rank, tau, sinks, window):
+    n = np.asarray(rank).shape[0]
+    M = O.prefill_mask(rank, tau, sinks, window)
+    elig = np.arange(n)[None, :] >= sinks
+    return M & (elig | (np.arange(n)[:, None] - np.arange(n)[None, :] < window))
+
+
+@pytest.mark.parametrize("fns", [
+    (ranks_ties_older_first, O.prefill_cutoffs, O.prefill_mask),
+    (O.prefill_ranks, cutoffs_off_by_one, O.prefill_mask),
+    (O.prefill_ranks, O.prefill_cutoffs, mask_window_inclusive),
+    (O.prefill_ranks, O.prefill_cutoffs, mask_without_sinks),
+], ids=["rank-ties", "cutoff-k+1", "window-inclusive", "no-sinks"])
+def test_prefill_mutants_fail(fns):
+    failed = 0
+    for check in (P.check_prefill_hand, P.check_prefill_mask_equals_decode_loop):
+        try:
+            check(*fns)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1

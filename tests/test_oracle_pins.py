@@ -674,3 +674,149 @@ def test_hedgehog_feature_map():
                                rtol=1e-14)
     np.testing.assert_allclose(O.hedgehog(-y), np.concatenate(
         [f[:, 6:], f[:, :6]], axis=1), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Prefill selection: ranks, running top-k cutoff, Eq. (26) mask, attention
+# ---------------------------------------------------------------------------
+
+def check_prefill_hand(ranks_fn, cutoffs_fn, mask_fn):
+    g = golden()["prefill_cutoff"]
+    s = np.asarray(g["scores"], np.float32)
+    r = ranks_fn(s)
+    assert r.tolist() == g["expected_rank"]
+    tau = cutoffs_fn(r, g["sinks"], g["window"], g["k"])
+    assert tau.tolist() == g["expected_tau"]
+    M = mask_fn(r, tau, g["sinks"], g["window"])
+    assert np.flatnonzero(M[7]).tolist() == g["expected_row7"]
+    assert np.flatnonzero(M[4]).tolist() == g["expected_row4"]
+
+
+def brute_force_ranks(s32, log_gamma=None):
+    n = s32.shape[0]
+    key = O.static_priority(s32, np.arange(n), log_gamma).astype(np.float64)
+    r = np.zeros(n, dtype=np.int64)
+    for t in range(n):
+        for u in range(n):
+            if key[u] > key[t] or (key[u] == key[t] and u > t):
+                r[t] += 1
+    return r
+
+
+def decode_loop_rows(s32, sinks, window, k, log_gamma=None):
+    """Retained positions after each append of the L = 1 decode loop
+    (OracleLayer), starting from the first token."""
+    n = s32.shape[0]
+    B = sinks + window + k
+    lay = O.OracleLayer(np.zeros((1, 1, 1, 1)), np.zeros((1, 1, 1, 1)),
+                        s32[None, None, :1],
+                        O.Policy(B, sinks, window, 1,
+                                 log_gamma=None if log_gamma is None
+                                 else (log_gamma,)), 1)
+    rows = [sorted(lay.pos[0, 0].tolist())]
+    for q in range(1, n):
+        lay.append(np.zeros((1, 1, 1)), np.zeros((1, 1, 1)),
+                   s32[None, None, q])
+        lay.maybe_evict()
+        rows.append(sorted(lay.pos[0, 0].tolist()))
+    return rows
+
+
+def check_prefill_mask_equals_decode_loop(ranks_fn, cutoffs_fn, mask_fn):
+    rng = np.random.default_rng(51)
+    for (n, S, W, k, lg, alphabet) in ((40, 2, 5, 6, None, 4),
+                                       (60, 0, 3, 10, None, 0),
+                                       (50, 4, 0, 7, -0.01, 3),
+                                       (30, 3, 4, 0, None, 0),
+                                       (45, 1, 1, 1, -0.2, 5)):
+        s = (rng.integers(0, alphabet, n) if alphabet
+             else rng.standard_normal(n)).astype(np.float32)
+        r = ranks_fn(s, lg)
+        tau = cutoffs_fn(r, S, W, k)
+        M = mask_fn(r, tau, S, W)
+        rows = decode_loop_rows(s, S, W, k, lg)
+        for q in range(n):
+            assert np.flatnonzero(M[q]).tolist() == rows[q], (n, S, W, k, q)
+
+
+def test_prefill_hand_case():
+    check_prefill_hand(O.prefill_ranks, O.prefill_cutoffs, O.prefill_mask)
+
+
+def test_prefill_ranks_brute_force():
+    rng = np.random.default_rng(52)
+    for lg in (None, -0.05):
+        for alphabet in (2, 3, 0):
+            n = 30
+            s = (rng.integers(0, alphabet, n) if alphabet
+                 else rng.standard_normal(n)).astype(np.float32)
+            s[::7] = -0.0 if alphabet else s[::7]
+            assert O.prefill_ranks(s, lg).tolist() == \
+                brute_force_ranks(s, lg).tolist()
+
+
+def test_prefill_mask_equals_l1_decode_loop():
+    """Eq. (26) rows are the retained sets of the L = 1 decode loop: with
+    static priorities the running top-k of E(q) is what per-token eviction
+    keeps (KVpop section 3.2)."""
+    check_prefill_mask_equals_decode_loop(O.prefill_ranks, O.prefill_cutoffs,
+                                          O.prefill_mask)
+
+
+def test_prefill_cutoff_monotone_and_budget():
+    rng = np.random.default_rng(53)
+    n, S, W, k = 200, 4, 16, 24
+    r = O.prefill_ranks(rng.standard_normal(n).astype(np.float32))
+    tau = O.prefill_cutoffs(r, S, W, k)
+    defined = tau < n
+    first = int(np.argmax(defined))
+    assert defined[first:].all()
+    assert np.all(np.diff(tau[first:]) <= 0)  # more eligible tokens: cutoff only tightens
+    M = O.prefill_mask(r, tau, S, W)
+    assert np.all(M.sum(axis=1) == np.minimum(np.arange(n) + 1, S + W + k))
+
+
+def test_prefill_attention_dense_limit():
+    """k >= n keeps every causal pair: the masked attention is causal
+    attention (float64 scaled_dot_product_attention)."""
+    import torch
+    rng = np.random.default_rng(54)
+    H, G, n, d = 2, 3, 33, 16
+    Q = rng.standard_normal((H * G, n, d))
+    K = rng.standard_normal((H, n, d))
+    V = rng.standard_normal((H, n, d))
+    r = O.prefill_ranks(rng.standard_normal(n).astype(np.float32))
+    tau = O.prefill_cutoffs(r, 2, 3, n)
+    M = np.stack([O.prefill_mask(r, tau, 2, 3)] * H)
+    assert M[0].sum() == n * (n + 1) // 2
+    out, lse = O.prefill_attention(Q, K, V, M, G)
+    Kx = torch.from_numpy(np.repeat(K, G, axis=0))
+    Vx = torch.from_numpy(np.repeat(V, G, axis=0))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), Kx, Vx, is_causal=True).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    z = np.einsum("jqd,jtd->jqt", Q, Kx.numpy()) / np.sqrt(d)
+    z = np.where(np.tril(np.ones((n, n), bool)), z, -np.inf)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(z, axis=2),
+                               rtol=1e-12)
+
+
+def test_prefill_attention_rows_are_decode_attention():
+    """Row q of the masked attention equals decode attention over the
+    tokens the mask keeps at q."""
+    rng = np.random.default_rng(55)
+    H, G, n, d, S, W, k = 2, 2, 48, 8, 2, 5, 7
+    Q = rng.standard_normal((H * G, n, d))
+    K = rng.standard_normal((H, n, d))
+    V = rng.standard_normal((H, n, d))
+    r = O.prefill_ranks(rng.standard_normal(n).astype(np.float32))
+    tau = O.prefill_cutoffs(r, S, W, k)
+    M1 = O.prefill_mask(r, tau, S, W)
+    out, lse = O.prefill_attention(Q, K, V, np.stack([M1] * H), G)
+    for q in (0, 9, 20, 47):
+        keep = np.flatnonzero(M1[q])
+        for j in range(H * G):
+            o, l = O.decode_attention(Q[j, q][None], K[j // G, keep],
+                                      V[j // G, keep])
+            np.testing.assert_allclose(out[j, q], o[0], rtol=1e-12, atol=1e-14)
+            assert lse[j, q] == pytest.approx(float(l[0]), rel=1e-12)
