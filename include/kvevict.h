@@ -260,6 +260,38 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
                     int32_t* keep_slots, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* Prefill selection (KVpop section 3.2 "Running top-k sparse attention",
+ * Appendix C.1-C.2) for a prompt of len tokens held in slots [0, len) with
+ * slot s holding position s, scored in cache->score (by kve_score):
+ *  rank [batch][H][len] int32: rank(t) under the static priority, the score
+ *    or, with policy->log_gamma, score - t * log_gamma[h] (both rounded to
+ *    float32, as in kve_select_evict); rank 0 is the best, equal keys rank
+ *    the newer token first;
+ *  tau [batch][H][len] int32: for each query position q, the rank of the
+ *    k-th best token of E(q) = {S <= t <= q - W}, k = B - S - W; len when
+ *    E(q) holds fewer than k tokens, -1 when k = 0.
+ * ws: kve_prefill_workspace_bytes(shape, len) bytes of scratch (sorted
+ * keys). Requires 1 <= len <= min(capacity, 262144); scores finite. */
+size_t kve_prefill_workspace_bytes(const kve_shape* shape, int32_t len);
+kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
+                              const kve_cache* cache, int32_t len,
+                              int32_t* rank, int32_t* tau, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* Masked prefill attention (KVpop Appendix C.1, Eq. 26, in the attention of
+ * Appendix D.1 Eq. 27-29): for every query position q < len and query head
+ * j (KV head j / G), attention over the keys t <= q that are sinks (t < S),
+ * in the recent window (q - t < W) or eligible with rank(t) <= tau_q, with
+ * rank and tau from kve_prefill_select. q [batch][H*G][len][d] bf16; out
+ * [batch][H*G][len][d] float32; lse [batch][H*G][len] float32 natural-log
+ * normaliser or NULL. bf16 caches only; MFMA (bf16 inputs, float32
+ * accumulation and softmax). */
+kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
+                            const kve_cache* cache, int32_t len,
+                            const int32_t* rank, const int32_t* tau,
+                            const void* q, float* out, float* lse,
+                            hipStream_t stream);
+
 /* Static string naming a status. */
 const char* kve_status_str(kve_status status);
 

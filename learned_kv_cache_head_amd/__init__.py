@@ -21,6 +21,7 @@ __all__ = [
     "F32", "BF16", "ACT_RELU", "ACT_SILU",
     "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "SCORER_MLSTM",
     "kve_scorer_state_bytes", "alloc_workspace", "LayerStep",
+    "kve_prefill_workspace_bytes", "kve_prefill_select", "kve_prefill_attn",
 ]
 
 F32, BF16 = 0, 1
@@ -83,6 +84,14 @@ _SIGS = {
                          _P, _I, _P]),
     "kve_decode_attn": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Cache),
                              _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kve_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Shape),
+                                                      _I]),
+    "kve_prefill_select": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
+                                ctypes.POINTER(_Cache), _I, _P, _P, _P,
+                                ctypes.c_size_t, _P]),
+    "kve_prefill_attn": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
+                              ctypes.POINTER(_Cache), _I, _P, _P, _P, _P, _P,
+                              _P]),
     "kve_step": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
                       ctypes.POINTER(_Scorer), ctypes.POINTER(_Cache),
                       ctypes.POINTER(_State), _P, _P, _P, _P, _P, _P, _P, _P,
@@ -346,6 +355,38 @@ def kve_step(shape: Shape, policy: Policy, scorer: Scorer,
     state.len, state.scored_upto = st.len, st.scored_upto
     state.next_position, state.evicted = st.next_position, st.evicted
     return state
+
+
+def kve_prefill_workspace_bytes(shape: Shape, length: int) -> int:
+    cs = shape.c()
+    return load_library().kve_prefill_workspace_bytes(ctypes.byref(cs), length)
+
+
+def kve_prefill_select(shape: Shape, policy: Policy, cache: CacheTensors,
+                       length: int, rank, tau, ws=None, stream=None) -> None:
+    """Ranks and running top-k cutoffs of a prompt (slot s = position s).
+    Allocates the scratch workspace with torch when none is given."""
+    import torch
+    if ws is None:
+        n = kve_prefill_workspace_bytes(shape, length)
+        if n == 0:
+            raise ValueError("invalid shape or length for prefill selection")
+        ws = torch.empty(n // 8, dtype=torch.int64, device=rank.device)
+    cs, cp, cc = shape.c(), policy.c(), cache.c()
+    _check(load_library().kve_prefill_select(
+        ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(cc), length,
+        _ptr(rank), _ptr(tau), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "kve_prefill_select")
+
+
+def kve_prefill_attn(shape: Shape, policy: Policy, cache: CacheTensors,
+                     length: int, rank, tau, q, out, lse=None,
+                     stream=None) -> None:
+    cs, cp, cc = shape.c(), policy.c(), cache.c()
+    _check(load_library().kve_prefill_attn(
+        ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(cc), length,
+        _ptr(rank), _ptr(tau), _ptr(q), _ptr(out), _ptr(lse),
+        _stream(stream)), "kve_prefill_attn")
 
 
 class LayerStep:

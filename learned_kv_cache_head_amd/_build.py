@@ -18,7 +18,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libkvevict.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["kvevict.hip", "attention.hip", "cache_ops.hip", "score.hip",
-           "mlstm.hip"]
+           "mlstm.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

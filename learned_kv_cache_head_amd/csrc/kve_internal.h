@@ -112,6 +112,26 @@ struct MlstmLaunch {
   int delay;             // read-out delay W
 };
 hipError_t launch_score_mlstm(const MlstmLaunch& m, hipStream_t s);
+
+// Prefill selection and masked prefill attention.
+constexpr int kMaxPrefillLen = 262144;  // the cutoff bitmap lives in LDS
+size_t prefill_ws_bytes(long long slices, int n);
+hipError_t launch_prefill_select(const float* score, const float* lg, int H,
+                                 int slices, int cap, int n, int S, int W,
+                                 int k, void* ws, int32_t* rank, int32_t* tau,
+                                 hipStream_t s);
+struct PrefillAttnLaunch {
+  const void* k;         // cache base (bf16), slot = position
+  const void* v;
+  const int32_t* rank;   // [batch][H][n]
+  const int32_t* tau;    // [batch][H][n]
+  const void* q;         // bf16 [batch][H*G][n][D]
+  float* out;            // [batch][H*G][n][D]
+  float* lse;            // [batch][H*G][n] or null
+  int batch, H, G, D, cap, n, S, W;
+  int gsub, nsub;        // query heads per workgroup, head subsets per KV head
+};
+hipError_t launch_prefill_attn(const PrefillAttnLaunch& a, hipStream_t s);
 size_t mlstm_state_floats(int D);  // 0 for an unsupported head_dim
 
 }  // namespace kve

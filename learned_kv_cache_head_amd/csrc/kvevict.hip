@@ -248,6 +248,72 @@ extern "C" {
 
 int32_t kve_version(void) { return 100; }
 
+size_t kve_prefill_workspace_bytes(const kve_shape* shape, int32_t len) {
+  if (check_shape(shape) != KVE_OK || len < 1 || len > kve::kMaxPrefillLen)
+    return 0;
+  return kve::prefill_ws_bytes((long long)shape->batch * shape->n_kv_heads, len);
+}
+
+kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
+                              const kve_cache* cache, int32_t len,
+                              int32_t* rank, int32_t* tau, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_policy(policy)) != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if (!rank || !tau) return KVE_ERR_INVALID_ARG;
+  if (len < 1) return KVE_ERR_INVALID_ARG;
+  if (len > shape->capacity) return KVE_ERR_CAPACITY;
+  if (len > kve::kMaxPrefillLen) return KVE_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < kve_prefill_workspace_bytes(shape, len))
+    return KVE_ERR_WORKSPACE;
+  if ((long long)shape->batch * shape->n_kv_heads > 65535)
+    return KVE_ERR_UNSUPPORTED;  // one grid row per slice
+  const int k = policy->budget - policy->sinks - policy->window;
+  return from_hip(kve::launch_prefill_select(
+      cache->score, policy->log_gamma, shape->n_kv_heads,
+      shape->batch * shape->n_kv_heads, shape->capacity, len, policy->sinks,
+      policy->window, k, ws, rank, tau, stream));
+}
+
+kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
+                            const kve_cache* cache, int32_t len,
+                            const int32_t* rank, const int32_t* tau,
+                            const void* q, float* out, float* lse,
+                            hipStream_t stream) {
+  kve_status st = check_shape(shape);
+  if (st != KVE_OK) return st;
+  if ((st = check_policy(policy)) != KVE_OK) return st;
+  if ((st = check_cache(cache)) != KVE_OK) return st;
+  if (!rank || !tau || !q || !out) return KVE_ERR_INVALID_ARG;
+  if (len < 1) return KVE_ERR_INVALID_ARG;
+  if (len > shape->capacity) return KVE_ERR_CAPACITY;
+  if (len > kve::kMaxPrefillLen) return KVE_ERR_UNSUPPORTED;
+  if (shape->kv_dtype != KVE_BF16) return KVE_ERR_UNSUPPORTED;
+  kve::PrefillAttnLaunch a{};
+  a.k = cache->k;
+  a.v = cache->v;
+  a.rank = rank;
+  a.tau = tau;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.batch = shape->batch;
+  a.H = shape->n_kv_heads;
+  a.G = shape->group;
+  a.D = shape->head_dim;
+  a.cap = shape->capacity;
+  a.n = len;
+  a.S = policy->sinks;
+  a.W = policy->window;
+  // Query heads of a KV head in subsets of at most 4 per workgroup.
+  a.nsub = (shape->group + 3) / 4;
+  a.gsub = (shape->group + a.nsub - 1) / a.nsub;
+  if ((long long)a.H * a.nsub > 65535) return KVE_ERR_UNSUPPORTED;
+  return from_hip(kve::launch_prefill_attn(a, stream));
+}
+
 const char* kve_status_str(kve_status s) {
   switch (s) {
     case KVE_OK: return "ok";

@@ -1,0 +1,443 @@
+// Prefill side of the fixed-budget policy (KVpop section 3.2 "Running top-k
+// sparse attention", Appendix C.1-C.2, Eq. 26):
+//
+//  * ranks: rank(t) of every prompt token under its static priority (the
+//    score, or score - t log(gamma) with decay, float32), rank 0 best; equal
+//    keys rank the newer token first (the reverse of the eviction order);
+//  * cutoffs: tau_q, the rank of the k-th best token of the eligible set
+//    E(q) = {S <= t <= q - W}, for every query position q;
+//  * masked prefill attention: each query q attends to the sinks, its
+//    recent window and the eligible tokens with rank(t) <= tau_q.
+//
+// Ranks: each workgroup sorts a chunk of 4096 (key, position) pairs in LDS
+// (bitonic sort, descending); a token's rank is then the number of larger
+// pairs, summed over the chunks by binary search.
+//
+// Cutoffs: as q grows by one, one token enters E(q), and tau_q can only move
+// to a better (smaller) rank. One wave per slice keeps the inserted ranks as
+// a bitmap in LDS: when the k-th token enters, tau is the largest inserted
+// rank; afterwards a new token better than tau pushes tau to the next
+// smaller inserted rank (the predecessor in the bitmap, found 64 words at a
+// time with a ballot). Total work is O(n + n / 32) per slice. (The pages use
+// a Fenwick tree with binary lifting; the monotone cutoff makes a bitmap
+// predecessor search enough.)
+//
+// Attention: a flash-attention forward on MFMA (v_mfma_f32_16x16x32_bf16,
+// float32 accumulation) with the Eq. 26 predicate applied to each logit. A
+// workgroup owns 64 query positions of one KV head and up to 4 of its query
+// heads; the 4 waves take 16 positions each. Each 32-key block of K and V
+// is staged in LDS (V transposed) and shared by all of them. The kernel
+// computes S^T = K Q^T, so a lane's accumulators hold 8 keys of one query
+// column: those are exactly the operand of P^T that O^T = V^T P^T needs,
+// and the online-softmax state is one value per lane and head.
+#include "kve_internal.h"
+
+namespace kve {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kSortChunk = 4096;   // pairs sorted per workgroup
+constexpr int kSortThreads = 512;
+
+// Orderable 32-bit key of a token's static priority (KVpop Eq. 20),
+// rounded like the select kernel: the product, then the difference.
+__device__ __forceinline__ uint32_t priority_key(float s, int pos,
+                                                 const float* lg, int h) {
+  if (lg) s = __fsub_rn(s, __fmul_rn((float)pos, lg[h]));
+  return score_key(s);
+}
+
+// ---------------------------------------------------------------------------
+// Chunk sort: pairs v = key << 32 | position, descending, padded with 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSortThreads) void rank_sort_kernel(
+    const float* score, const float* lg, int H, int cap, int n, int npad,
+    uint64_t* sorted) {
+  __shared__ uint64_t v[kSortChunk];
+  const int slice = blockIdx.y;
+  const int c0 = blockIdx.x * kSortChunk;
+  const float* sc = score + (size_t)slice * cap;
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) {
+    const int t = c0 + i;
+    v[i] = t < n ? ((uint64_t)priority_key(sc[t], t, lg, slice % H) << 32) |
+                       (uint32_t)t
+                 : 0ull;
+  }
+  __syncthreads();
+  for (int size = 2; size <= kSortChunk; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < kSortChunk / 2; i += kSortThreads) {
+        // pair (a, a + stride) inside blocks of 2 * stride
+        const int a = (i / stride) * 2 * stride + (i % stride);
+        const int b = a + stride;
+        // descending overall: blocks whose bit `size` is clear sort down
+        const bool desc = (a & size) == 0;
+        const uint64_t x = v[a], y = v[b];
+        if ((x < y) == desc) {
+          v[a] = y;
+          v[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  uint64_t* out = sorted + (size_t)slice * npad + c0;
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) out[i] = v[i];
+}
+
+// rank(t) = number of pairs larger than token t's, over all chunks.
+__global__ __launch_bounds__(256) void rank_count_kernel(
+    const float* score, const float* lg, int H, int cap, int n, int npad,
+    const uint64_t* sorted, int32_t* rank) {
+  const int slice = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const uint64_t v =
+      ((uint64_t)priority_key(score[(size_t)slice * cap + t], t, lg, slice % H)
+       << 32) | (uint32_t)t;
+  const uint64_t* base = sorted + (size_t)slice * npad;
+  int r = 0;
+  for (int c0 = 0; c0 < npad; c0 += kSortChunk) {
+    // first index in the descending chunk whose pair is <= v
+    int lo = 0, hi = kSortChunk;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (base[c0 + mid] > v) lo = mid + 1;
+      else hi = mid;
+    }
+    r += lo;
+  }
+  rank[(size_t)slice * n + t] = r;
+}
+
+// ---------------------------------------------------------------------------
+// Running cutoffs, one wave per slice.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void cutoff_kernel(const int32_t* rank, int n,
+                                                    int S, int W, int k,
+                                                    int32_t* tau) {
+  __shared__ uint32_t bm[kMaxPrefillLen / 32];
+  const int slice = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t* rk = rank + (size_t)slice * n;
+  int32_t* out = tau + (size_t)slice * n;
+  const int words = (n + 31) >> 5;
+  for (int w = lane; w < words; w += 64) bm[w] = 0u;
+  __syncthreads();
+  int count = 0;   // tokens in E(q)
+  int cut = n;     // tau while count >= k
+  int maxr = -1;   // largest inserted rank (tau when count reaches k)
+  for (int q0 = 0; q0 < n; q0 += 64) {
+    const int ql = q0 + lane;
+    const int tl = ql - W;
+    const int rl = (ql < n && tl >= S) ? rk[tl] : -1;  // rank entering at ql
+    int mine = 0;
+    const int m = min(64, n - q0);
+    for (int i = 0; i < m; ++i) {
+      const int r = __builtin_amdgcn_readlane(rl, i);
+      if (r >= 0 && k > 0) {
+        if (lane == 0) bm[r >> 5] |= 1u << (r & 31);
+        ++count;
+        maxr = max(maxr, r);
+        if (count == k) {
+          cut = maxr;
+        } else if (count > k && r < cut) {
+          // next smaller inserted rank below cut
+          int w0 = (cut - 1) >> 5;
+          const uint32_t below = (cut & 31) ? ((1u << (cut & 31)) - 1u) : ~0u;
+          int found = -1;
+          while (found < 0) {
+            const int w = w0 - lane;
+            uint32_t word = 0u;
+            if (w >= 0) {
+              word = bm[w];
+              if (w == (cut >> 5)) word &= below;
+            }
+            const uint64_t nz = __ballot(word != 0u);
+            if (nz) {
+              const int l = __ffsll((unsigned long long)nz) - 1;  // highest word
+              const uint32_t wv = __shfl(word, l);
+              found = (w0 - l) * 32 + 31 - __clz(wv);
+            } else {
+              w0 -= 64;
+            }
+          }
+          cut = found;
+        }
+      }
+      const int t = k == 0 ? -1 : (count >= k ? cut : n);
+      mine = lane == i ? t : mine;
+    }
+    if (lane < m) out[q0 + lane] = mine;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Masked prefill attention.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+constexpr int kQB = 64;   // query positions per workgroup
+constexpr int kKB = 32;   // keys per block
+
+template <int D, int GS>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) {
+  constexpr int KS = D / 32;      // contraction steps of S^T
+  constexpr int DT = D / 16;      // 16-row tiles of O^T
+  constexpr int KSTR = D + 8;     // bf16 per staged K row
+  constexpr int VSTR = kKB + 4;   // bf16 per staged V^T row
+  __shared__ __align__(16) uint16_t ks[2][kKB * KSTR];
+  __shared__ __align__(16) uint16_t vt[2][D * VSTR];
+  __shared__ int rks[2][kKB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nqb = (p.n + kQB - 1) / kQB;
+  const int qb = nqb - 1 - blockIdx.x;  // heavy (late) query blocks first
+  const int h = blockIdx.y / p.nsub;
+  const int sub = blockIdx.y % p.nsub;
+  const int b = blockIdx.z;
+  const int q0 = qb * kQB;
+  const size_t slice = (size_t)b * p.H + h;
+  const uint16_t* kc = (const uint16_t*)p.k + slice * p.cap * D;
+  const uint16_t* vc = (const uint16_t*)p.v + slice * p.cap * D;
+  const int32_t* rk = p.rank + slice * p.n;
+  const int hq = p.H * p.G;
+
+  // This lane's query column: position qpos, heads sub*GS + gi.
+  const int qpos = q0 + wave * 16 + (lane & 15);
+  const int qc = min(qpos, p.n - 1);
+  const int tau = p.tau[slice * p.n + qc];
+  const int g8 = (lane >> 4) * 8;
+  bf16x8_t qf[GS][KS];
+#pragma unroll
+  for (int gi = 0; gi < GS; ++gi) {
+    const int g = min(sub * GS + gi, p.G - 1);
+    const uint16_t* qr =
+        (const uint16_t*)p.q + (((size_t)b * hq + h * p.G + g) * p.n + qc) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[gi][s] = load8(qr + s * 32 + g8);
+  }
+
+  f32x4_t o[DT][GS];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int gi = 0; gi < GS; ++gi) o[dt][gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun[GS], lrun[GS];
+#pragma unroll
+  for (int gi = 0; gi < GS; ++gi) {
+    mrun[gi] = -__builtin_inff();
+    lrun[gi] = 0.f;
+  }
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
+
+  // Staging: each of the 256 threads moves 16 B of K and 16 B of V per
+  // 32-key block (32 rows of D bf16 = D/8 chunks per row).
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  u32x4 kreg[kKB * CPR / 256], vreg[kKB * CPR / 256];
+  int rreg = 0;
+  const int last_q = min(q0 + kQB, p.n) - 1;
+  const int nkb = last_q / kKB + 1;
+  auto fetch = [&](int kb) {
+    const int t0 = kb * kKB;
+#pragma unroll
+    for (int c = 0; c < kKB * CPR / 256; ++c) {
+      const int idx = threadIdx.x + c * 256;
+      const int row = idx / CPR;
+      const int ch = idx % CPR;
+      const int t = min(t0 + row, p.n - 1);
+      kreg[c] = *(const u32x4*)(kc + (size_t)t * D + ch * 8);
+      vreg[c] = *(const u32x4*)(vc + (size_t)t * D + ch * 8);
+    }
+    if (threadIdx.x < kKB) {
+      const int t = t0 + threadIdx.x;
+      rreg = t < p.n ? rk[t] : 0x7fffffff;
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < kKB * CPR / 256; ++c) {
+      const int idx = threadIdx.x + c * 256;
+      const int row = idx / CPR;
+      const int ch = idx % CPR;
+      *(u32x4*)(&ks[buf][row * KSTR + ch * 8]) = kreg[c];
+      const uint32_t w[4] = {vreg[c].x, vreg[c].y, vreg[c].z, vreg[c].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vt[buf][(ch * 8 + e) * VSTR + row] =
+            (uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+    }
+    if (threadIdx.x < kKB) rks[buf][threadIdx.x] = rreg;
+  };
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    const int t0 = kb * kKB;
+    if (kb + 1 < nkb) fetch(kb + 1);
+
+    // A block whose keys are all eligible for every query of this wave and
+    // all ranked below the wave's loosest cutoff (tau at its first
+    // position: tau only tightens as q grows) contributes nothing.
+    bool skip = false;
+    const int qmin = q0 + wave * 16;
+    if (t0 >= p.S && t0 + kKB - 1 <= qmin - p.W) {
+      int mn = rks[buf][lane & 31];
+      for (int off = 16; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off));
+      skip = mn > __shfl(tau, 0);
+    }
+    if (!skip) {
+      // S^T = K Q^T: two 16-key tiles x GS query tiles.
+      f32x4_t s[2][GS];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int gi = 0; gi < GS; ++gi) s[kt][gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const bf16x8_t A = __builtin_bit_cast(
+              bf16x8_t, *(const u32x4*)(&ks[buf][(kt * 16 + (lane & 15)) * KSTR +
+                                                  st * 32 + g8]));
+#pragma unroll
+          for (int gi = 0; gi < GS; ++gi)
+            s[kt][gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qf[gi][st],
+                                                                s[kt][gi], 0, 0, 0);
+        }
+      }
+      // Eq. 26 predicate for this lane's 8 keys and its query position.
+      bool keep[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kr = kt * 16 + 4 * (lane >> 4) + i;
+          const int t = t0 + kr;
+          keep[kt][i] = t <= qpos &&
+                        (t < p.S || t > qpos - p.W || rks[buf][kr] <= tau);
+        }
+      // Online softmax per query column, then O^T += V^T P^T.
+      uint32_t pk[GS][4];
+#pragma unroll
+      for (int gi = 0; gi < GS; ++gi) {
+        float x[8];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = keep[kt][i] ? s[kt][gi][i] * qscale : -__builtin_inff();
+            x[kt * 4 + i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun[gi], mx);
+        const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+        const float alpha = exp2f(mrun[gi] - mref);
+        // p goes to the MFMA in bf16 (relative error <= 2^-9 per weight);
+        // the normaliser, and so lse, sums the float32 values.
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float e0 = exp2f(x[j] - mref), e1 = exp2f(x[j + 1] - mref);
+          pk[gi][j >> 1] = pack2(e0, e1);
+          ps += e0 + e1;
+        }
+        lrun[gi] = lrun[gi] * alpha + ps;
+        mrun[gi] = mnew;
+        if (__ballot(alpha != 1.f)) {  // some column's maximum moved
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt][gi] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vr = &vt[buf][(dt * 16 + (lane & 15)) * VSTR + 4 * (lane >> 4)];
+        const u32x2 lo = *(const u32x2*)vr;
+        const u32x2 hi = *(const u32x2*)(vr + 16);
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int gi = 0; gi < GS; ++gi) {
+          const bf16x8_t B = __builtin_bit_cast(
+              bf16x8_t, u32x4{pk[gi][0], pk[gi][1], pk[gi][2], pk[gi][3]});
+          o[dt][gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
+        }
+      }
+    }
+    // The other buffer was last read before the previous barrier.
+    if (kb + 1 < nkb) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: normalise and store this lane's column (4 rows per d tile).
+#pragma unroll
+  for (int gi = 0; gi < GS; ++gi) {
+    const int g = sub * GS + gi;
+    float l = lrun[gi];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (g >= p.G || qpos >= p.n) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* orow = p.out + (((size_t)b * hq + h * p.G + g) * p.n + qpos) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4_t v = o[dt][gi] * inv;
+      *(float4*)(orow + dt * 16 + 4 * (lane >> 4)) = float4{v[0], v[1], v[2], v[3]};
+    }
+    if (p.lse && (lane >> 4) == 0)
+      p.lse[((size_t)b * hq + h * p.G + g) * p.n + qpos] =
+          l > 0.f ? 0.6931471805599453f * (mrun[gi] + log2f(l)) : -__builtin_inff();
+  }
+}
+
+}  // namespace
+
+size_t prefill_ws_bytes(long long slices, int n) {
+  const long long npad = (n + kSortChunk - 1) / kSortChunk * kSortChunk;
+  return (size_t)(slices * npad) * sizeof(uint64_t);
+}
+
+hipError_t launch_prefill_select(const float* score, const float* lg, int H,
+                                 int slices, int cap, int n, int S, int W,
+                                 int k, void* ws, int32_t* rank, int32_t* tau,
+                                 hipStream_t s) {
+  const int npad = (n + kSortChunk - 1) / kSortChunk * kSortChunk;
+  uint64_t* sorted = (uint64_t*)ws;
+  hipLaunchKernelGGL(rank_sort_kernel, dim3(npad / kSortChunk, slices),
+                     dim3(kSortThreads), 0, s, score, lg, H, cap, n, npad, sorted);
+  hipLaunchKernelGGL(rank_count_kernel, dim3((n + 255) / 256, slices), dim3(256),
+                     0, s, score, lg, H, cap, n, npad, (const uint64_t*)sorted,
+                     rank);
+  hipLaunchKernelGGL(cutoff_kernel, dim3(slices), dim3(64), 0, s,
+                     (const int32_t*)rank, n, S, W, k, tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const PrefillAttnLaunch& a, hipStream_t s) {
+  const int nqb = (a.n + kQB - 1) / kQB;
+  const dim3 grid(nqb, a.H * a.nsub, a.batch);
+#define KVE_PA(DD, GG)                                                       \
+  if (a.D == DD && a.gsub == GG) {                                           \
+    hipLaunchKernelGGL((prefill_attn_kernel<DD, GG>), grid, dim3(256), 0, s, a); \
+    return hipGetLastError();                                                \
+  }
+  KVE_PA(128, 1) KVE_PA(128, 2) KVE_PA(128, 3) KVE_PA(128, 4)
+  KVE_PA(64, 1) KVE_PA(64, 2) KVE_PA(64, 3) KVE_PA(64, 4)
+#undef KVE_PA
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kve

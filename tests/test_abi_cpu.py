@@ -255,3 +255,36 @@ def test_mlstm_rejects_bad_arguments():
 
     assert step(_mlstm(delay=64)) == 2          # delay != window
     assert step(_mlstm(), cache=no_state) == 1
+
+
+def test_prefill_workspace_and_validation():
+    lib = _lib()
+    s = _shape(capacity=10000)
+    n = lib.kve_prefill_workspace_bytes(ctypes.byref(s), 9000)
+    assert n == 2 * 8 * 12288 * 8            # slices x chunk-rounded len x u64
+    assert lib.kve_prefill_workspace_bytes(ctypes.byref(s), 0) == 0
+    assert lib.kve_prefill_workspace_bytes(ctypes.byref(s), 262145) == 0
+    c = _cache()
+    p = kve._Policy(1024, 4, 128, 128)
+
+    def sel(length, rank=FAKE, ws_bytes=1 << 30, shape=s):
+        return lib.kve_prefill_select(ctypes.byref(shape), ctypes.byref(p),
+                                      ctypes.byref(c), length, rank, FAKE,
+                                      FAKE, ws_bytes, None)
+
+    assert sel(0) == 1
+    assert sel(10001) == 3
+    assert sel(100, rank=None) == 1
+    assert sel(9000, ws_bytes=1000) == 5
+    big = _shape(capacity=300000)
+    assert sel(262145, shape=big) == 4
+
+    def attn(length, shape=s, q=FAKE):
+        return lib.kve_prefill_attn(ctypes.byref(shape), ctypes.byref(p),
+                                    ctypes.byref(c), length, FAKE, FAKE, q,
+                                    FAKE, None, None)
+
+    assert attn(0) == 1
+    assert attn(10001) == 3
+    assert attn(100, q=None) == 1
+    assert attn(100, shape=_shape(capacity=10000, kv_dtype=kve.F32)) == 4

@@ -1,0 +1,168 @@
+"""Prefill selection and masked prefill attention (KVpop section 3.2
+"Running top-k sparse attention", Appendix C.1-C.2, Eq. 26) through the C
+ABI, against the float64 oracle.
+
+Ranks and cutoffs are integers decided from the same float32 keys on both
+sides: bit-exact. Attention: the GPU rounds the softmax weights to bf16 for
+the P.V contraction and normalises by the float32 sum, so each weight
+carries a relative error of at most 2^-9 and the output lies within
+2^-9 * max|V| of the exact one; the test allows 2^-8 * max|V| per tensor.
+lse is float32 math on unrounded weights: within 1e-4 absolute.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as syn
+from kvharness import kve
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 1e-4
+
+
+def scores_for(rng, b, H, n, kind):
+    if kind == "ties":
+        s = rng.integers(0, 5, (b, H, n)).astype(np.float32)
+        s[..., ::11] = -0.0
+        return s
+    return rng.standard_normal((b, H, n)).astype(np.float32)
+
+
+def run_select(b, H, n, S, W, k, kind, decay, seed, cap=None):
+    import torch
+    k_ = kve()
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(seed)
+    cap = cap or n
+    shape = k_.Shape(b, H, 1, 64, cap, k_.BF16)
+    cache = k_.CacheTensors.empty(shape, dev)
+    s = scores_for(rng, b, H, n, kind)
+    cache.score[:, :, :n] = torch.from_numpy(s).to(dev)
+    cache.score[:, :, n:] = float("nan")  # beyond the prompt: never read
+    lg = None
+    if decay:
+        lg = np.log(np.linspace(0.9, 0.999999, H)).astype(np.float32)
+    pol = k_.Policy(S + W + k, S, W, 1,
+                    log_gamma=None if lg is None else torch.from_numpy(lg).to(dev))
+    rank = torch.full((b, H, n), -7, dtype=torch.int32, device=dev)
+    tau = torch.full((b, H, n), -7, dtype=torch.int32, device=dev)
+    k_.kve_prefill_select(shape, pol, cache, n, rank, tau)
+    torch.cuda.synchronize()
+    return s, lg, rank.cpu().numpy(), tau.cpu().numpy(), cache, shape, pol
+
+
+SELECT_CASES = [
+    # b, H, n, S, W, k, scores, decay
+    (1, 2, 1, 4, 8, 16, "normal", False),
+    (2, 3, 7, 1, 2, 2, "ties", False),
+    (1, 2, 300, 4, 16, 40, "ties", False),
+    (2, 2, 300, 4, 16, 40, "normal", True),
+    (1, 2, 4113, 4, 64, 500, "normal", False),   # two sort chunks, ragged
+    (1, 1, 2000, 0, 0, 100, "ties", False),
+    (1, 2, 500, 3, 5, 0, "normal", False),         # k = 0
+    (1, 2, 500, 3, 5, 600, "normal", False),       # k > n: nothing cut
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=[
+    f"b{c[0]}H{c[1]}n{c[2]}S{c[3]}W{c[4]}k{c[5]}-{c[6]}{'-decay' if c[7] else ''}"
+    for c in SELECT_CASES])
+def test_prefill_select_exact(case):
+    b, H, n, S, W, k, kind, decay = case
+    print(f"[prefill-select] {case}", flush=True)
+    s, lg, rank, tau, *_ = run_select(b, H, n, S, W, k, kind, decay,
+                                      seed=n + S + W + k)
+    for bi in range(b):
+        for h in range(H):
+            r = O.prefill_ranks(s[bi, h], None if lg is None else float(lg[h]))
+            assert np.array_equal(rank[bi, h], r), (bi, h)
+            t = O.prefill_cutoffs(r, S, W, k)
+            assert np.array_equal(tau[bi, h], t), (bi, h)
+
+
+def test_prefill_last_row_is_one_shot_compression():
+    """The mask row of the last prompt position keeps what the one-shot
+    compression (kve_select_evict down to B) keeps."""
+    import torch
+    k_ = kve()
+    b, H, n, S, W, k = 2, 4, 3000, 4, 128, 700
+    s, lg, rank, tau, cache, shape, pol = run_select(b, H, n, S, W, k,
+                                                     "ties", True, seed=9)
+    cache.pos[:, :, :n] = torch.arange(n, dtype=torch.int32, device="cuda")
+    keep = torch.zeros((b, H, S + W + k), dtype=torch.int32, device="cuda")
+    k_.kve_select_evict(shape, pol, cache, n, S + W + k, keep)
+    kept = keep.cpu().numpy()
+    for bi in range(b):
+        for h in range(H):
+            M = O.prefill_mask(rank[bi, h], tau[bi, h], S, W)
+            assert np.flatnonzero(M[n - 1]).tolist() == kept[bi, h].tolist()
+
+
+ATTN_CASES = [
+    # b, H, G, d, n, S, W, k
+    (1, 2, 4, 128, 200, 4, 16, 40),
+    (2, 1, 1, 128, 45, 2, 3, 10),
+    (1, 2, 5, 128, 333, 4, 32, 64),      # G = 5: two head subsets
+    (1, 2, 2, 64, 257, 1, 8, 100),
+    (1, 1, 8, 128, 130, 0, 1, 20),
+    (1, 2, 4, 128, 100, 4, 16, 200),     # k >= n: causal attention
+    (1, 1, 3, 128, 1, 4, 8, 16),         # one token
+]
+
+
+def run_attn(b, H, G, d, n, S, W, k, seed, decay=False):
+    import torch
+    k_ = kve()
+    dev = torch.device("cuda")
+    s, lg, rank, tau, cache, shape, pol = run_select(b, H, n, S, W, k, "normal",
+                                                     decay, seed)
+    shape = k_.Shape(b, H, G, d, n, k_.BF16)
+    cache2 = k_.CacheTensors.empty(shape, dev)
+    rng = np.random.default_rng(seed + 1)
+    K = syn.Stored(rng.standard_normal((b, H, n, d)).astype(np.float32), "bf16")
+    V = syn.Stored(rng.standard_normal((b, H, n, d)).astype(np.float32), "bf16")
+    Q = syn.Stored((1.5 * rng.standard_normal((b, H * G, n, d))).astype(np.float32),
+                   "bf16")
+    cache2.k.copy_(K.torch(dev))
+    cache2.v.copy_(V.torch(dev))
+    out = torch.full((b, H * G, n, d), float("nan"), device=dev)
+    lse = torch.full((b, H * G, n), float("nan"), device=dev)
+    k_.kve_prefill_attn(shape, pol, cache2, n,
+                        torch.from_numpy(rank).to(dev),
+                        torch.from_numpy(tau).to(dev), Q.torch(dev), out, lse)
+    torch.cuda.synchronize()
+    return rank, tau, K, V, Q, out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[
+    f"b{c[0]}H{c[1]}G{c[2]}d{c[3]}n{c[4]}S{c[5]}W{c[6]}k{c[7]}"
+    for c in ATTN_CASES])
+def test_prefill_attention(case):
+    b, H, G, d, n, S, W, k = case
+    print(f"[prefill-attn] {case}", flush=True)
+    rank, tau, K, V, Q, out, lse = run_attn(*case, seed=sum(case))
+    for bi in range(b):
+        masks = np.stack([O.prefill_mask(rank[bi, h], tau[bi, h], S, W)
+                          for h in range(H)])
+        ref, ref_lse = O.prefill_attention(Q.f64[bi], K.f64[bi], V.f64[bi],
+                                           masks, G)
+        tol = 2.0 ** -8 * np.abs(V.f64[bi]).max()
+        err = np.abs(out[bi] - ref).max()
+        print(f"[prefill-attn] max |err| {err:.3g} (tol {tol:.3g})", flush=True)
+        np.testing.assert_allclose(out[bi], ref, rtol=0, atol=tol)
+        np.testing.assert_allclose(lse[bi], ref_lse, rtol=0, atol=LSE_TOL)
+
+
+def test_prefill_attention_with_decay_and_skipped_blocks():
+    """Decay orders eligible tokens by age as well as score: whole key
+    blocks fall below the cutoff and are skipped."""
+    b, H, G, d, n, S, W, k = 1, 2, 4, 128, 1500, 4, 64, 96
+    rank, tau, K, V, Q, out, lse = run_attn(b, H, G, d, n, S, W, k, seed=3,
+                                            decay=True)
+    masks = np.stack([O.prefill_mask(rank[0, h], tau[0, h], S, W)
+                      for h in range(H)])
+    ref, ref_lse = O.prefill_attention(Q.f64[0], K.f64[0], V.f64[0], masks, G)
+    np.testing.assert_allclose(out[0], ref, rtol=0,
+                               atol=2.0 ** -8 * np.abs(V.f64[0]).max())
+    np.testing.assert_allclose(lse[0], ref_lse, rtol=0, atol=LSE_TOL)
