@@ -332,6 +332,139 @@ def cpu_baseline_mlstm(w, seed, sample_batch, sample_steps, threads) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# Prefill: running top-k selection and Eq. 26 masked prefill attention
+# ---------------------------------------------------------------------------
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def prefill_kept_pairs(n: int, budget: int) -> int:
+    """(query, key) pairs the Eq. 26 mask keeps for an n-token prompt: every
+    causal pair while q + 1 <= B, then B per query."""
+    return sum(min(q + 1, budget) for q in range(n))
+
+
+def run_prefill(args, w, dev) -> dict:
+    """Time one layer's prefill: kve_prefill_select (ranks, cutoffs) and
+    kve_prefill_attn over the workload's prompt for the whole batch, with
+    the library's MLP scores."""
+    import torch
+    import learned_kv_cache_head_amd as kve
+    import synthetic as syn
+    T = syn.TENSOR_IDS
+    b, H, G, d, n = w.batch, w.n_kv, w.group, w.head_dim, w.n0
+    cfg, l, seed = w.cfg_id, 0, args.seed
+    shape = kve.Shape(b, H, G, d, n, kve.BF16)
+    pol = kve.Policy(w.budget, w.sinks, w.window, w.evict_len)
+    dn = syn.device_normal
+    c = kve.CacheTensors.empty(shape, dev)
+    c.k.copy_(dn((b, H, n, d), seed, (cfg, l, 0, T["k0"]), torch.bfloat16, dev))
+    c.v.copy_(dn((b, H, n, d), seed, (cfg, l, 0, T["v0"]), torch.bfloat16, dev))
+    c.pos.copy_(torch.arange(n, dtype=torch.int32, device=dev).expand(b, H, n))
+    w1 = dn((H, w.hidden, 2 * d), seed, (cfg, l, 0, T["w1"]), torch.bfloat16,
+            dev, scale=(2 * d) ** -0.5)
+    w2 = dn((H, w.hidden), seed, (cfg, l, 0, T["w2"]), torch.float32, dev,
+            scale=w.hidden ** -0.5)
+    kve.kve_score(shape, kve.Scorer.mlp(w1, w2), c, 0, n)
+    q = dn((b, H * G, n, d), seed, (cfg, l, 2, T["q"]), torch.bfloat16, dev)
+    rank = torch.empty((b, H, n), dtype=torch.int32, device=dev)
+    tau = torch.empty_like(rank)
+    out = torch.empty((b, H * G, n, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((b, H * G, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(kve.kve_prefill_workspace_bytes(shape, n) // 8,
+                     dtype=torch.int64, device=dev)
+    steps = args.steps if args.steps is not None else 3
+    warmup = args.warmup if args.warmup is not None else 1
+    for _ in range(warmup):
+        kve.kve_prefill_select(shape, pol, c, n, rank, tau, ws)
+        kve.kve_prefill_attn(shape, pol, c, n, rank, tau, q, out, lse)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        kve.kve_prefill_select(shape, pol, c, n, rank, tau, ws)
+        ev[2 * i + 1].record()
+        kve.kve_prefill_attn(shape, pol, c, n, rank, tau, q, out, lse)
+        ev[2 * i + 2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sel_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+    attn_ms = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2])
+                  for i in range(steps)) / steps
+    kept = prefill_kept_pairs(n, w.budget)
+    flops = kept * 4 * d * H * G * b  # q.k and p.v over the kept pairs
+    causal = n * (n + 1) // 2
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": ("prefill tokens/s of one layer: running top-k selection "
+                   "(KVpop Eq. 26) + masked prefill attention"),
+        "value": round(b * n * steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload + "-prefill-1layer", "batch": b,
+                   "prompt_len": n, "n_kv_heads": H, "n_q_heads": H * G,
+                   "head_dim": d, "budget": w.budget, "sinks": w.sinks,
+                   "window": w.window, "scorer": "mlp", "parallelism": "none"},
+        "select_ms": round(sel_ms, 3),
+        "attn_ms": round(attn_ms, 3),
+        "mask_density": round(kept / causal, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "prefill_attn_kernel (Eq. 26 masked attention)",
+                     "algorithmic_flops_per_launch": int(flops),
+                     "mean_launch_ms": round(attn_ms, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(w, seed)
+    return result
+
+
+def cpu_baseline_prefill(w, seed) -> dict:
+    """The oracle's prefill (ranks, cutoffs, Eq. 26 mask, float64 masked
+    attention) for one sequence and one KV head of the same prompt; scaled
+    to tokens/s of the layer as n / (time x KV heads)."""
+    import numpy as np
+    import oracle as O
+    import synthetic as syn
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    n, d, G = w.n0, w.head_dim, w.group
+    rng = syn.rng_for(seed, w.cfg_id, 0, -1, "misc")
+    K = rng.standard_normal((1, n, d))
+    V = rng.standard_normal((1, n, d))
+    Q = rng.standard_normal((G, n, d))
+    s = rng.standard_normal(n).astype(np.float32)
+    t0 = time.perf_counter()
+    r = O.prefill_ranks(s)
+    tau = O.prefill_cutoffs(r, w.sinks, w.window, w.budget - w.sinks - w.window)
+    M = O.prefill_mask(r, tau, w.sinks, w.window)[None]
+    O.prefill_attention(Q, K, V, M, G)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / (dt * w.n_kv), 3), "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 oracle prefill (ranks, cutoffs, mask, masked "
+                       f"attention) of one {n}-token sequence and one of "
+                       f"{w.n_kv} KV heads ({G} query heads); {dt:.1f} s wall; "
+                       f"scaled to the layer as n / (time x KV heads)")}
+
+
+# ---------------------------------------------------------------------------
 # Recorded rocprofv3 traffic of the attention kernel
 # ---------------------------------------------------------------------------
 
@@ -380,6 +513,9 @@ def main() -> int:
     ap.add_argument("--cpu-batch", type=int, default=None,
                     help="oracle sample sequences (default 16; 2 for mLSTM)")
     ap.add_argument("--cpu-steps", type=int, default=None)
+    ap.add_argument("--prefill", action="store_true",
+                    help="time one layer's prefill (running top-k selection "
+                         "and Eq. 26 masked attention) instead of decode")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, run a plain 1 GiB "
                          "elementwise copy (counter calibration)")
@@ -400,6 +536,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = syn.workload(WORKLOAD_BY_NAME[args.workload])
+    if args.prefill:
+        log(f"prefill {args.workload}: batch={w.batch} prompt={w.n0} B={w.budget}")
+        print(json.dumps(run_prefill(args, w, dev)), flush=True)
+        return 0
     L = w.evict_len
     steps = args.steps if args.steps is not None else 2 * L
     warmup = args.warmup if args.warmup is not None else L

@@ -189,6 +189,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 constexpr int kQB = 64;   // query positions per workgroup
 constexpr int kKB = 32;   // keys per block
+constexpr float kLazy = 8.f;  // log2 headroom of the softmax reference
 
 template <int D, int GS>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) {
@@ -344,21 +345,26 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun[gi], mx);
+        // Lazy rescaling: the reference maximum moves only when a logit
+        // passes it by more than 2^kLazy (or on the first kept key), so
+        // weights stay below 2^kLazy and the accumulators are rarely scaled.
+        const bool move = mx > mrun[gi] + kLazy;
+        const float mnew = move ? mx : mrun[gi];
+        const float alpha = move ? __builtin_amdgcn_exp2f(mrun[gi] - mnew) : 1.f;
         const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-        const float alpha = exp2f(mrun[gi] - mref);
         // p goes to the MFMA in bf16 (relative error <= 2^-9 per weight);
         // the normaliser, and so lse, sums the float32 values.
         float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          const float e0 = exp2f(x[j] - mref), e1 = exp2f(x[j + 1] - mref);
+          const float e0 = __builtin_amdgcn_exp2f(x[j] - mref);
+          const float e1 = __builtin_amdgcn_exp2f(x[j + 1] - mref);
           pk[gi][j >> 1] = pack2(e0, e1);
           ps += e0 + e1;
         }
         lrun[gi] = lrun[gi] * alpha + ps;
         mrun[gi] = mnew;
-        if (__ballot(alpha != 1.f)) {  // some column's maximum moved
+        if (__ballot(move)) {  // some column's reference moved
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) o[dt][gi] *= alpha;
         }

@@ -166,3 +166,67 @@ def test_prefill_attention_with_decay_and_skipped_blocks():
     np.testing.assert_allclose(out[0], ref, rtol=0,
                                atol=2.0 ** -8 * np.abs(V.f64[0]).max())
     np.testing.assert_allclose(lse[0], ref_lse, rtol=0, atol=LSE_TOL)
+
+
+FULL_CASES = [
+    # b, H, G, n, S, W, B: a Qwen3-4B layer (8192-token prompt, B = 1024)
+    # and a Qwen2.5-14B layer (131072-token prompt, 30% budget)
+    (2, 8, 4, 8192, 4, 128, 1024),
+    (1, 8, 5, 131072, 4, 512, 39321),
+]
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[f"n{c[3]}" for c in FULL_CASES])
+def test_prefill_full_size_sampled(case):
+    """Full-size prompts in the launch shape the benchmark uses: ranks exact
+    for every token, cutoffs exact at sampled positions (the definition:
+    sort of the eligible ranks), attention rows at sampled (position, head)
+    pairs against decode attention over the tokens the mask keeps."""
+    import torch
+    k_ = kve()
+    dev = torch.device("cuda")
+    b, H, G, n, S, W, B = case
+    d, kk = 128, B - S - W
+    print(f"[prefill-full] {case}", flush=True)
+    shape = k_.Shape(b, H, G, d, n, k_.BF16)
+    c = k_.CacheTensors.empty(shape, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(n)
+    c.k.copy_(torch.randn(c.k.shape, generator=g, device=dev).to(torch.bfloat16))
+    c.v.copy_(torch.randn(c.v.shape, generator=g, device=dev).to(torch.bfloat16))
+    c.score.copy_(torch.randn(c.score.shape, generator=g, device=dev))
+    q = torch.randn((b, H * G, n, d), generator=g, device=dev).to(torch.bfloat16)
+    pol = k_.Policy(B, S, W, 1)
+    rank = torch.empty((b, H, n), dtype=torch.int32, device=dev)
+    tau = torch.empty_like(rank)
+    out = torch.empty((b, H * G, n, d), device=dev)
+    lse = torch.empty((b, H * G, n), device=dev)
+    k_.kve_prefill_select(shape, pol, c, n, rank, tau)
+    k_.kve_prefill_attn(shape, pol, c, n, rank, tau, q, out, lse)
+    torch.cuda.synchronize()
+    print("[prefill-full] kernels done", flush=True)
+    rng = np.random.default_rng(n)
+    qs = sorted(set(rng.integers(0, n, 24).tolist()) |
+                {0, S + W + kk - 1, S + W + kk, n - 1})
+    for bi in range(b):
+        for h in (0, H - 1):
+            s = c.score[bi, h].cpu().numpy()
+            r = O.prefill_ranks(s)
+            assert np.array_equal(rank[bi, h].cpu().numpy(), r)
+            t_gpu = tau[bi, h].cpu().numpy()
+            K = c.k[bi, h].float().cpu().numpy().astype(np.float64)
+            V = c.v[bi, h].float().cpu().numpy().astype(np.float64)
+            for qq in qs:
+                elig = r[S:max(qq - W + 1, S)]
+                t_ref = n if elig.shape[0] < kk else np.partition(elig, kk - 1)[kk - 1]
+                assert t_gpu[qq] == t_ref, (bi, h, qq)
+                t = np.arange(qq + 1)
+                keep = t[(t < S) | (qq - t < W) | ((t <= qq - W) & (r[:qq + 1] <= t_ref))]
+                for gq in (0, G - 1):
+                    j = h * G + gq
+                    qv = q[bi, j, qq].float().cpu().numpy().astype(np.float64)
+                    o_ref, l_ref = O.decode_attention(qv[None], K[keep], V[keep])
+                    o = out[bi, j, qq].cpu().numpy()
+                    np.testing.assert_allclose(o, o_ref[0], rtol=0,
+                                               atol=2.0 ** -8 * np.abs(V).max())
+                    assert abs(float(lse[bi, j, qq]) - float(l_ref[0])) <= LSE_TOL
