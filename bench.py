@@ -373,11 +373,13 @@ def run_prefill(args, w, dev) -> dict:
     lse = torch.empty((b, H * G, n), dtype=torch.float32, device=dev)
     ws = torch.empty(kve.kve_prefill_workspace_bytes(shape, n) // 8,
                      dtype=torch.int64, device=dev)
+    wsa = torch.empty(kve.kve_prefill_attn_workspace_bytes(shape, pol, n) // 4,
+                      dtype=torch.int32, device=dev)
     steps = args.steps if args.steps is not None else 3
     warmup = args.warmup if args.warmup is not None else 1
     for _ in range(warmup):
         kve.kve_prefill_select(shape, pol, c, n, rank, tau, ws)
-        kve.kve_prefill_attn(shape, pol, c, n, rank, tau, q, out, lse)
+        kve.kve_prefill_attn(shape, pol, c, n, rank, tau, q, out, lse, wsa)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
     t0 = time.perf_counter()
@@ -385,7 +387,7 @@ def run_prefill(args, w, dev) -> dict:
     for i in range(steps):
         kve.kve_prefill_select(shape, pol, c, n, rank, tau, ws)
         ev[2 * i + 1].record()
-        kve.kve_prefill_attn(shape, pol, c, n, rank, tau, q, out, lse)
+        kve.kve_prefill_attn(shape, pol, c, n, rank, tau, q, out, lse, wsa)
         ev[2 * i + 2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -421,7 +423,7 @@ def run_prefill(args, w, dev) -> dict:
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": "prefill_attn_kernel (Eq. 26 masked attention)",
+                     "kernel": "key lists + prefill_attn_kernel (Eq. 26 masked attention)",
                      "algorithmic_flops_per_launch": int(flops),
                      "mean_launch_ms": round(attn_ms, 3)},
         "cpu_baseline": None,

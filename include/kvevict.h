@@ -285,12 +285,17 @@ kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
  * rank and tau from kve_prefill_select. q [batch][H*G][len][d] bf16; out
  * [batch][H*G][len][d] float32; lse [batch][H*G][len] float32 natural-log
  * normaliser or NULL. bf16 caches only; MFMA (bf16 inputs, float32
- * accumulation and softmax). */
+ * accumulation and softmax). ws: kve_prefill_attn_workspace_bytes bytes of
+ * scratch: per 64-position query block, the at most k long-range keys any
+ * of its queries keeps (the attention visits only those, the sinks and the
+ * block's recent windows). */
+size_t kve_prefill_attn_workspace_bytes(const kve_shape* shape,
+                                        const kve_policy* policy, int32_t len);
 kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
                             const kve_cache* cache, int32_t len,
                             const int32_t* rank, const int32_t* tau,
-                            const void* q, float* out, float* lse,
-                            hipStream_t stream);
+                            const void* q, float* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* Static string naming a status. */
 const char* kve_status_str(kve_status status);

@@ -22,6 +22,7 @@ __all__ = [
     "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "SCORER_MLSTM",
     "kve_scorer_state_bytes", "alloc_workspace", "LayerStep",
     "kve_prefill_workspace_bytes", "kve_prefill_select", "kve_prefill_attn",
+    "kve_prefill_attn_workspace_bytes",
 ]
 
 F32, BF16 = 0, 1
@@ -89,9 +90,11 @@ _SIGS = {
     "kve_prefill_select": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
                                 ctypes.POINTER(_Cache), _I, _P, _P, _P,
                                 ctypes.c_size_t, _P]),
+    "kve_prefill_attn_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.POINTER(_Shape), ctypes.POINTER(_Policy), _I]),
     "kve_prefill_attn": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
                               ctypes.POINTER(_Cache), _I, _P, _P, _P, _P, _P,
-                              _P]),
+                              _P, ctypes.c_size_t, _P]),
     "kve_step": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
                       ctypes.POINTER(_Scorer), ctypes.POINTER(_Cache),
                       ctypes.POINTER(_State), _P, _P, _P, _P, _P, _P, _P, _P,
@@ -379,14 +382,29 @@ def kve_prefill_select(shape: Shape, policy: Policy, cache: CacheTensors,
         _stream(stream)), "kve_prefill_select")
 
 
+def kve_prefill_attn_workspace_bytes(shape: Shape, policy: Policy,
+                                     length: int) -> int:
+    cs, cp = shape.c(), policy.c()
+    return load_library().kve_prefill_attn_workspace_bytes(
+        ctypes.byref(cs), ctypes.byref(cp), length)
+
+
 def kve_prefill_attn(shape: Shape, policy: Policy, cache: CacheTensors,
-                     length: int, rank, tau, q, out, lse=None,
+                     length: int, rank, tau, q, out, lse=None, ws=None,
                      stream=None) -> None:
+    """Eq. 26 masked prefill attention; allocates the key-list workspace
+    with torch when none is given."""
+    import torch
+    if ws is None:
+        n = kve_prefill_attn_workspace_bytes(shape, policy, length)
+        if n == 0:
+            raise ValueError("invalid shape, policy or length")
+        ws = torch.empty((n + 3) // 4, dtype=torch.int32, device=q.device)
     cs, cp, cc = shape.c(), policy.c(), cache.c()
     _check(load_library().kve_prefill_attn(
         ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(cc), length,
-        _ptr(rank), _ptr(tau), _ptr(q), _ptr(out), _ptr(lse),
-        _stream(stream)), "kve_prefill_attn")
+        _ptr(rank), _ptr(tau), _ptr(q), _ptr(out), _ptr(lse), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "kve_prefill_attn")
 
 
 class LayerStep:

@@ -130,7 +130,11 @@ struct PrefillAttnLaunch {
   float* lse;            // [batch][H*G][n] or null
   int batch, H, G, D, cap, n, S, W;
   int gsub, nsub;        // query heads per workgroup, head subsets per KV head
+  int32_t* list;         // [batch*H][query blocks][kmax] long-range keys
+  int32_t* count;        // [batch*H][query blocks]
+  int kmax;              // max(k, 1)
 };
+size_t prefill_attn_ws_bytes(long long slices, int n, int kmax);
 hipError_t launch_prefill_attn(const PrefillAttnLaunch& a, hipStream_t s);
 size_t mlstm_state_floats(int D);  // 0 for an unsupported head_dim
 

@@ -277,11 +277,21 @@ kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
       policy->window, k, ws, rank, tau, stream));
 }
 
+size_t kve_prefill_attn_workspace_bytes(const kve_shape* shape,
+                                        const kve_policy* policy, int32_t len) {
+  if (check_shape(shape) != KVE_OK || check_policy(policy) != KVE_OK ||
+      len < 1 || len > kve::kMaxPrefillLen)
+    return 0;
+  const int k = policy->budget - policy->sinks - policy->window;
+  return kve::prefill_attn_ws_bytes((long long)shape->batch * shape->n_kv_heads,
+                                    len, k > 0 ? k : 1);
+}
+
 kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
                             const kve_cache* cache, int32_t len,
                             const int32_t* rank, const int32_t* tau,
-                            const void* q, float* out, float* lse,
-                            hipStream_t stream) {
+                            const void* q, float* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   kve_status st = check_shape(shape);
   if (st != KVE_OK) return st;
   if ((st = check_policy(policy)) != KVE_OK) return st;
@@ -291,7 +301,17 @@ kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
   if (len > shape->capacity) return KVE_ERR_CAPACITY;
   if (len > kve::kMaxPrefillLen) return KVE_ERR_UNSUPPORTED;
   if (shape->kv_dtype != KVE_BF16) return KVE_ERR_UNSUPPORTED;
+  const size_t need = kve_prefill_attn_workspace_bytes(shape, policy, len);
+  if (!ws || ws_bytes < need) return KVE_ERR_WORKSPACE;
+  if ((long long)shape->batch * shape->n_kv_heads > 65535)
+    return KVE_ERR_UNSUPPORTED;  // one grid row per slice (key lists)
+  const int k = policy->budget - policy->sinks - policy->window;
+  const long long nqb = (len + 63) / 64;
+  const long long slices = (long long)shape->batch * shape->n_kv_heads;
   kve::PrefillAttnLaunch a{};
+  a.kmax = k > 0 ? k : 1;
+  a.list = (int32_t*)ws;
+  a.count = (int32_t*)((char*)ws + (need - (size_t)(slices * nqb) * sizeof(int32_t)));
   a.k = cache->k;
   a.v = cache->v;
   a.rank = rank;

@@ -40,6 +40,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSortChunk = 4096;   // pairs sorted per workgroup
+constexpr int kQBlock = 64;        // query positions per attention workgroup
 constexpr int kSortThreads = 512;
 
 // Orderable 32-bit key of a token's static priority (KVpop Eq. 20),
@@ -176,6 +177,45 @@ __global__ __launch_bounds__(64) void cutoff_kernel(const int32_t* rank, int n,
 }
 
 // ---------------------------------------------------------------------------
+// Long-range key lists: for the query block starting at q0, the eligible
+// tokens t in [S, q0 - W] with rank(t) <= tau_q0, in position order. The
+// cutoff only tightens as q grows, so these hold every long-range key any
+// query of the block keeps (at most k of them: the top-k of E(q0)).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void keylist_kernel(const int32_t* rank,
+                                                      const int32_t* tau, int n,
+                                                      int S, int W, int kmax,
+                                                      int32_t* list,
+                                                      int32_t* count) {
+  __shared__ int wsum[4];
+  const int qb = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int nqb = gridDim.x;
+  const int q0 = qb * kQBlock;
+  const int32_t* rk = rank + (size_t)slice * n;
+  const int t0 = tau[(size_t)slice * n + q0];
+  int32_t* out = list + ((size_t)slice * nqb + qb) * kmax;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lim = q0 - W;  // last eligible position at q0
+  int base = 0;
+  for (int c = S; c <= lim; c += 256) {
+    const int t = c + threadIdx.x;
+    const bool f = t <= lim && rk[t] <= t0;
+    const uint64_t m = __ballot(f);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (f && off + before < kmax) out[off + before] = t;
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) count[(size_t)slice * nqb + qb] = min(base, kmax);
+}
+
+// ---------------------------------------------------------------------------
 // Masked prefill attention.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
@@ -187,7 +227,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-constexpr int kQB = 64;   // query positions per workgroup
+constexpr int kQB = kQBlock;
 constexpr int kKB = 32;   // keys per block
 constexpr float kLazy = 8.f;  // log2 headroom of the softmax reference
 
@@ -199,7 +239,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
   constexpr int VSTR = kKB + 4;   // bf16 per staged V^T row
   __shared__ __align__(16) uint16_t ks[2][kKB * KSTR];
   __shared__ __align__(16) uint16_t vt[2][D * VSTR];
-  __shared__ int rks[2][kKB];
+  __shared__ int rks[2][kKB];   // rank of each staged key
+  __shared__ int tps[2][kKB];   // its position (INT_MAX: padding)
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -243,27 +284,42 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
   }
   const float qscale = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
 
+  // Keys of this workgroup in position order: the sinks, the long-range
+  // list of this query block, then the span of its recent windows. Every
+  // other key is masked for all of its queries.
+  const int last_q = min(q0 + kQB, p.n) - 1;
+  const int nS = min(p.S, last_q + 1);
+  const int qbi = q0 / kQB;
+  const int nL = p.count[slice * nqb + qbi];
+  const int32_t* lst = p.list + (slice * nqb + qbi) * p.kmax;
+  const int w0 = max(p.S, q0 - p.W + 1);
+  const int nWin = max(0, last_q - w0 + 1);
+  const int nkeys = nS + nL + nWin;
+  auto key_pos = [&](int j) {
+    return j < nS ? j : (j < nS + nL ? lst[j - nS] : w0 + (j - nS - nL));
+  };
+
   // Staging: each of the 256 threads moves 16 B of K and 16 B of V per
   // 32-key block (32 rows of D bf16 = D/8 chunks per row).
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   u32x4 kreg[kKB * CPR / 256], vreg[kKB * CPR / 256];
-  int rreg = 0;
-  const int last_q = min(q0 + kQB, p.n) - 1;
-  const int nkb = last_q / kKB + 1;
+  int rreg = 0, treg = 0;
+  const int nkb = (nkeys + kKB - 1) / kKB;
   auto fetch = [&](int kb) {
-    const int t0 = kb * kKB;
 #pragma unroll
     for (int c = 0; c < kKB * CPR / 256; ++c) {
       const int idx = threadIdx.x + c * 256;
       const int row = idx / CPR;
       const int ch = idx % CPR;
-      const int t = min(t0 + row, p.n - 1);
+      const int j = kb * kKB + row;
+      const int t = j < nkeys ? key_pos(j) : 0;  // padding reads row 0
       kreg[c] = *(const u32x4*)(kc + (size_t)t * D + ch * 8);
       vreg[c] = *(const u32x4*)(vc + (size_t)t * D + ch * 8);
     }
     if (threadIdx.x < kKB) {
-      const int t = t0 + threadIdx.x;
-      rreg = t < p.n ? rk[t] : 0x7fffffff;
+      const int j = kb * kKB + threadIdx.x;
+      treg = j < nkeys ? key_pos(j) : 0x7fffffff;
+      rreg = j < nkeys ? rk[treg] : 0x7fffffff;
     }
   };
   auto stage = [&](int buf) {
@@ -279,7 +335,10 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
         vt[buf][(ch * 8 + e) * VSTR + row] =
             (uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
     }
-    if (threadIdx.x < kKB) rks[buf][threadIdx.x] = rreg;
+    if (threadIdx.x < kKB) {
+      rks[buf][threadIdx.x] = rreg;
+      tps[buf][threadIdx.x] = treg;
+    }
   };
 
   fetch(0);
@@ -287,20 +346,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
-    const int t0 = kb * kKB;
     if (kb + 1 < nkb) fetch(kb + 1);
-
-    // A block whose keys are all eligible for every query of this wave and
-    // all ranked below the wave's loosest cutoff (tau at its first
-    // position: tau only tightens as q grows) contributes nothing.
-    bool skip = false;
-    const int qmin = q0 + wave * 16;
-    if (t0 >= p.S && t0 + kKB - 1 <= qmin - p.W) {
-      int mn = rks[buf][lane & 31];
-      for (int off = 16; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off));
-      skip = mn > __shfl(tau, 0);
-    }
-    if (!skip) {
+    {
       // S^T = K Q^T: two 16-key tiles x GS query tiles.
       f32x4_t s[2][GS];
 #pragma unroll
@@ -325,7 +372,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kr = kt * 16 + 4 * (lane >> 4) + i;
-          const int t = t0 + kr;
+          const int t = tps[buf][kr];
           keep[kt][i] = t <= qpos &&
                         (t < p.S || t > qpos - p.W || rks[buf][kr] <= tau);
         }
@@ -432,8 +479,17 @@ hipError_t launch_prefill_select(const float* score, const float* lg, int H,
   return hipGetLastError();
 }
 
+size_t prefill_attn_ws_bytes(long long slices, int n, int kmax) {
+  const long long nqb = (n + kQB - 1) / kQB;
+  const size_t lists = (size_t)(slices * nqb) * kmax * sizeof(int32_t);
+  const size_t counts = (size_t)(slices * nqb) * sizeof(int32_t);
+  return (lists + 255) / 256 * 256 + counts;
+}
+
 hipError_t launch_prefill_attn(const PrefillAttnLaunch& a, hipStream_t s) {
   const int nqb = (a.n + kQB - 1) / kQB;
+  hipLaunchKernelGGL(keylist_kernel, dim3(nqb, a.batch * a.H), dim3(256), 0, s,
+                     a.rank, a.tau, a.n, a.S, a.W, a.kmax, a.list, a.count);
   const dim3 grid(nqb, a.H * a.nsub, a.batch);
 #define KVE_PA(DD, GG)                                                       \
   if (a.D == DD && a.gsub == GG) {                                           \

@@ -279,12 +279,20 @@ def test_prefill_workspace_and_validation():
     big = _shape(capacity=300000)
     assert sel(262145, shape=big) == 4
 
-    def attn(length, shape=s, q=FAKE):
+    def attn(length, shape=s, q=FAKE, ws_bytes=1 << 30):
         return lib.kve_prefill_attn(ctypes.byref(shape), ctypes.byref(p),
                                     ctypes.byref(c), length, FAKE, FAKE, q,
-                                    FAKE, None, None)
+                                    FAKE, None, FAKE, ws_bytes, None)
 
     assert attn(0) == 1
     assert attn(10001) == 3
     assert attn(100, q=None) == 1
     assert attn(100, shape=_shape(capacity=10000, kv_dtype=kve.F32)) == 4
+    assert attn(9000, ws_bytes=100) == 5
+    # key lists: k = 892 ints per 64-position query block and slice, then
+    # one count per block
+    wsb = lib.kve_prefill_attn_workspace_bytes(ctypes.byref(s), ctypes.byref(p),
+                                               9000)
+    nqb = (9000 + 63) // 64
+    lists = 2 * 8 * nqb * 892 * 4
+    assert wsb == (lists + 255) // 256 * 256 + 2 * 8 * nqb * 4
