@@ -24,9 +24,10 @@
 //
 // Attention: a flash-attention forward on MFMA (v_mfma_f32_16x16x32_bf16,
 // float32 accumulation) with the Eq. 26 predicate applied to each logit. A
-// workgroup owns 64 query positions of one KV head and up to 4 of its query
-// heads; the 4 waves take 16 positions each. Each 32-key block of K and V
-// is staged in LDS (V transposed) and shared by all of them. The kernel
+// workgroup owns 64 query positions of one KV head and up to 2 of its query
+// heads (two waves per SIMD fit); the 4 waves take 16 positions each. Each
+// 64-key block of K and V is staged in LDS, row-major, and shared by all of
+// them; the V^T operand comes from LDS transpose reads. The kernel
 // computes S^T = K Q^T, so a lane's accumulators hold 8 keys of one query
 // column: those are exactly the operand of P^T that O^T = V^T P^T needs,
 // and the online-softmax state is one value per lane and head.
@@ -38,6 +39,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kSortChunk = 4096;   // pairs sorted per workgroup
 constexpr int kQBlock = 64;        // query positions per attention workgroup
@@ -228,17 +231,21 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 constexpr int kQB = kQBlock;
-constexpr int kKB = 32;   // keys per block
+constexpr int kKB = 64;   // keys per block (measured faster than 32)
 constexpr float kLazy = 8.f;  // log2 headroom of the softmax reference
 
 template <int D, int GS>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_attn_kernel(PrefillAttnLaunch p) {
   constexpr int KS = D / 32;      // contraction steps of S^T
   constexpr int DT = D / 16;      // 16-row tiles of O^T
+  constexpr int KT = kKB / 16;    // 16-key tiles per block
   constexpr int KSTR = D + 8;     // bf16 per staged K row
-  constexpr int VSTR = kKB + 4;   // bf16 per staged V^T row
+  // bf16 per staged V row: a row stride of 8 words (mod 32 banks) keeps the
+  // 16 lanes of a transpose read (4 rows x 4 column chunks) on distinct banks
+  constexpr int VSTR = D + 16;
   __shared__ __align__(16) uint16_t ks[2][kKB * KSTR];
-  __shared__ __align__(16) uint16_t vt[2][D * VSTR];
+  __shared__ __align__(16) uint16_t vs[2][kKB * VSTR];
   __shared__ int rks[2][kKB];   // rank of each staged key
   __shared__ int tps[2][kKB];   // its position (INT_MAX: padding)
 
@@ -329,11 +336,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
       const int row = idx / CPR;
       const int ch = idx % CPR;
       *(u32x4*)(&ks[buf][row * KSTR + ch * 8]) = kreg[c];
-      const uint32_t w[4] = {vreg[c].x, vreg[c].y, vreg[c].z, vreg[c].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vt[buf][(ch * 8 + e) * VSTR + row] =
-            (uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+      *(u32x4*)(&vs[buf][row * VSTR + ch * 8]) = vreg[c];
     }
     if (threadIdx.x < kKB) {
       rks[buf][threadIdx.x] = rreg;
@@ -348,10 +351,10 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
     const int buf = kb & 1;
     if (kb + 1 < nkb) fetch(kb + 1);
     {
-      // S^T = K Q^T: two 16-key tiles x GS query tiles.
-      f32x4_t s[2][GS];
+      // S^T = K Q^T: KT 16-key tiles x GS query tiles.
+      f32x4_t s[KT][GS];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
         for (int gi = 0; gi < GS; ++gi) s[kt][gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -365,10 +368,10 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
                                                                 s[kt][gi], 0, 0, 0);
         }
       }
-      // Eq. 26 predicate for this lane's 8 keys and its query position.
-      bool keep[2][4];
+      // Eq. 26 predicate for this lane's keys and its query position.
+      bool keep[KT][4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kr = kt * 16 + 4 * (lane >> 4) + i;
@@ -376,14 +379,15 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
           keep[kt][i] = t <= qpos &&
                         (t < p.S || t > qpos - p.W || rks[buf][kr] <= tau);
         }
-      // Online softmax per query column, then O^T += V^T P^T.
-      uint32_t pk[GS][4];
+      // Online softmax per query column, then O^T += V^T P^T, 32 keys per
+      // contraction step: half hh holds key tiles 2hh and 2hh+1.
+      uint32_t pk[GS][KT / 2][4];
 #pragma unroll
       for (int gi = 0; gi < GS; ++gi) {
-        float x[8];
+        float x[KT * 4];
         float mx = -__builtin_inff();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float v = keep[kt][i] ? s[kt][gi][i] * qscale : -__builtin_inff();
@@ -403,10 +407,10 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
         // the normaliser, and so lse, sums the float32 values.
         float ps = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
+        for (int j = 0; j < KT * 4; j += 2) {
           const float e0 = __builtin_amdgcn_exp2f(x[j] - mref);
           const float e1 = __builtin_amdgcn_exp2f(x[j + 1] - mref);
-          pk[gi][j >> 1] = pack2(e0, e1);
+          pk[gi][j >> 3][(j >> 1) & 3] = pack2(e0, e1);
           ps += e0 + e1;
         }
         lrun[gi] = lrun[gi] * alpha + ps;
@@ -416,17 +420,31 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnLaunch p) 
           for (int dt = 0; dt < DT; ++dt) o[dt][gi] *= alpha;
         }
       }
+      // V^T operand by LDS transpose reads (ds_read_b64_tr_b16): in each
+      // 16-lane group, lane 4j + s points at the 4 columns 4s.. of key row
+      // j, and lane m receives column m of the 4 rows. Lane l thus gets
+      // V[keys pi(l/16, 0..3)][dt * 16 + l % 16], the A rows of O^T.
+      const int trow = 4 * (lane >> 4) + ((lane & 15) >> 2);
+      const int tcol = 4 * (lane & 3);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vr = &vt[buf][(dt * 16 + (lane & 15)) * VSTR + 4 * (lane >> 4)];
-        const u32x2 lo = *(const u32x2*)vr;
-        const u32x2 hi = *(const u32x2*)(vr + 16);
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+      for (int hh = 0; hh < KT / 2; ++hh) {
 #pragma unroll
-        for (int gi = 0; gi < GS; ++gi) {
-          const bf16x8_t B = __builtin_bit_cast(
-              bf16x8_t, u32x4{pk[gi][0], pk[gi][1], pk[gi][2], pk[gi][3]});
-          o[dt][gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* v0 = &vs[buf][(hh * 32 + trow) * VSTR + dt * 16 + tcol];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)v0);
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 16 * VSTR));
+          const bf16x8_t A = __builtin_bit_cast(
+              bf16x8_t, u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                              __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y});
+#pragma unroll
+          for (int gi = 0; gi < GS; ++gi) {
+            const bf16x8_t B = __builtin_bit_cast(
+                bf16x8_t,
+                u32x4{pk[gi][hh][0], pk[gi][hh][1], pk[gi][hh][2], pk[gi][hh][3]});
+            o[dt][gi] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
+          }
         }
       }
     }
@@ -496,8 +514,7 @@ hipError_t launch_prefill_attn(const PrefillAttnLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL((prefill_attn_kernel<DD, GG>), grid, dim3(256), 0, s, a); \
     return hipGetLastError();                                                \
   }
-  KVE_PA(128, 1) KVE_PA(128, 2) KVE_PA(128, 3) KVE_PA(128, 4)
-  KVE_PA(64, 1) KVE_PA(64, 2) KVE_PA(64, 3) KVE_PA(64, 4)
+  KVE_PA(128, 1) KVE_PA(128, 2) KVE_PA(64, 1) KVE_PA(64, 2)
 #undef KVE_PA
   return hipErrorInvalidValue;
 }
