@@ -233,6 +233,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 constexpr int kQB = kQBlock;
 constexpr int kKB = 64;   // keys per block (measured faster than 32)
 constexpr float kLazy = 8.f;  // log2 headroom of the softmax reference
+constexpr int kWin = 1024;    // key positions held in LDS ahead of the loads
 
 template <int D, int GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -248,6 +249,7 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
   __shared__ __align__(16) uint16_t vs[2][kKB * VSTR];
   __shared__ int rks[2][kKB];   // rank of each staged key
   __shared__ int tps[2][kKB];   // its position (INT_MAX: padding)
+  __shared__ int kpos[kWin];    // positions of key indices [wbase, wbase + kWin)
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -312,21 +314,30 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
   u32x4 kreg[kKB * CPR / 256], vreg[kKB * CPR / 256];
   int rreg = 0, treg = 0;
   const int nkb = (nkeys + kKB - 1) / kKB;
+  // The K/V loads take their row positions from LDS, so they never wait on
+  // the key-list loads (a wait on those would drain every load in flight).
+  int wbase = 0;
+  auto refill = [&](int j0) {
+    wbase = j0;
+    for (int i = threadIdx.x; i < kWin; i += 256) {
+      const int j = j0 + i;
+      kpos[i] = j < nkeys ? key_pos(j) : 0x7fffffff;
+    }
+  };
   auto fetch = [&](int kb) {
 #pragma unroll
     for (int c = 0; c < kKB * CPR / 256; ++c) {
       const int idx = threadIdx.x + c * 256;
       const int row = idx / CPR;
       const int ch = idx % CPR;
-      const int j = kb * kKB + row;
-      const int t = j < nkeys ? key_pos(j) : 0;  // padding reads row 0
+      const int t0 = kpos[kb * kKB + row - wbase];
+      const int t = t0 == 0x7fffffff ? 0 : t0;  // padding reads row 0
       kreg[c] = *(const u32x4*)(kc + (size_t)t * D + ch * 8);
       vreg[c] = *(const u32x4*)(vc + (size_t)t * D + ch * 8);
     }
     if (threadIdx.x < kKB) {
-      const int j = kb * kKB + threadIdx.x;
-      treg = j < nkeys ? key_pos(j) : 0x7fffffff;
-      rreg = j < nkeys ? rk[treg] : 0x7fffffff;
+      treg = kpos[kb * kKB + threadIdx.x - wbase];
+      rreg = treg == 0x7fffffff ? 0x7fffffff : rk[treg];
     }
   };
   auto stage = [&](int buf) {
@@ -344,12 +355,20 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
     }
   };
 
+  refill(0);
+  __syncthreads();
   fetch(0);
   stage(0);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
-    if (kb + 1 < nkb) fetch(kb + 1);
+    if (kb + 1 < nkb) {
+      if ((kb + 2) * kKB > wbase + kWin) {  // uniform; last read of kpos
+        refill((kb + 1) * kKB);             // was before the last barrier
+        __syncthreads();
+      }
+      fetch(kb + 1);
+    }
     {
       // S^T = K Q^T: KT 16-key tiles x GS query tiles.
       f32x4_t s[KT][GS];
