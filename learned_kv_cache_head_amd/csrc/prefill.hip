@@ -247,8 +247,8 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
   constexpr int VSTR = D + 16;
   __shared__ __align__(16) uint16_t ks[2][kKB * KSTR];
   __shared__ __align__(16) uint16_t vs[2][kKB * VSTR];
-  __shared__ int rks[2][kKB];   // rank of each staged key
-  __shared__ int tps[2][kKB];   // its position (INT_MAX: padding)
+  __shared__ __align__(16) int rks[2][kKB];   // rank of each staged key
+  __shared__ __align__(16) int tps[2][kKB];   // its position (INT_MAX: padding)
   __shared__ int kpos[kWin];    // positions of key indices [wbase, wbase + kWin)
 
   const int lane = threadIdx.x & 63;
@@ -388,16 +388,21 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
         }
       }
       // Eq. 26 predicate for this lane's keys and its query position.
+      // (Evaluated without short-circuits: every operand is loaded, so no
+      // branches split the block.)
       bool keep[KT][4];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+      for (int kt = 0; kt < KT; ++kt) {
+        const int kr = kt * 16 + 4 * (lane >> 4);
+        const int4 t4 = *(const int4*)&tps[buf][kr];
+        const int4 r4 = *(const int4*)&rks[buf][kr];
+        const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
+        const int rv[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kr = kt * 16 + 4 * (lane >> 4) + i;
-          const int t = tps[buf][kr];
-          keep[kt][i] = t <= qpos &&
-                        (t < p.S || t > qpos - p.W || rks[buf][kr] <= tau);
-        }
+        for (int i = 0; i < 4; ++i)
+          keep[kt][i] = (tv[i] <= qpos) &
+                        ((tv[i] < p.S) | (tv[i] > qpos - p.W) | (rv[i] <= tau));
+      }
       // Online softmax per query column, then O^T += V^T P^T, 32 keys per
       // contraction step: half hh holds key tiles 2hh and 2hh+1.
       uint32_t pk[GS][KT / 2][4];
