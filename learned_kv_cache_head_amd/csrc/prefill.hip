@@ -388,38 +388,50 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
         }
       }
       // Eq. 26 predicate for this lane's keys and its query position.
+      // Blocks made only of long-range list keys (t <= q0 - W for every
+      // query of the workgroup, never sinks) need only the rank test.
       // (Evaluated without short-circuits: every operand is loaded, so no
       // branches split the block.)
+      const int j0 = kb * kKB;
+      const bool list_only = j0 >= nS && j0 + kKB <= nS + nL;  // uniform
       bool keep[KT][4];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         const int kr = kt * 16 + 4 * (lane >> 4);
-        const int4 t4 = *(const int4*)&tps[buf][kr];
         const int4 r4 = *(const int4*)&rks[buf][kr];
-        const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
         const int rv[4] = {r4.x, r4.y, r4.z, r4.w};
+        if (list_only) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          keep[kt][i] = (tv[i] <= qpos) &
-                        ((tv[i] < p.S) | (tv[i] > qpos - p.W) | (rv[i] <= tau));
+          for (int i = 0; i < 4; ++i) keep[kt][i] = rv[i] <= tau;
+        } else {
+          const int4 t4 = *(const int4*)&tps[buf][kr];
+          const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            keep[kt][i] = (tv[i] <= qpos) &
+                          ((tv[i] < p.S) | (tv[i] > qpos - p.W) | (rv[i] <= tau));
+        }
       }
       // Online softmax per query column, then O^T += V^T P^T, 32 keys per
       // contraction step: half hh holds key tiles 2hh and 2hh+1.
       uint32_t pk[GS][KT / 2][4];
 #pragma unroll
       for (int gi = 0; gi < GS; ++gi) {
+        // Raw logits (the scale is positive, so the maximum commutes with
+        // it); the scale folds into the exponent's FMA below.
         float x[KT * 4];
         float mx = -__builtin_inff();
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = keep[kt][i] ? s[kt][gi][i] * qscale : -__builtin_inff();
+            const float v = keep[kt][i] ? s[kt][gi][i] : -__builtin_inff();
             x[kt * 4 + i] = v;
             mx = fmaxf(mx, v);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx *= qscale;
         // Lazy rescaling: the reference maximum moves only when a logit
         // passes it by more than 2^kLazy (or on the first kept key), so
         // weights stay below 2^kLazy and the accumulators are rarely scaled.
@@ -432,8 +444,8 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
         float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < KT * 4; j += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(x[j] - mref);
-          const float e1 = __builtin_amdgcn_exp2f(x[j + 1] - mref);
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(x[j], qscale, -mref));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(x[j + 1], qscale, -mref));
           pk[gi][j >> 3][(j >> 1) & 3] = pack2(e0, e1);
           ps += e0 + e1;
         }
