@@ -224,10 +224,13 @@ __global__ __launch_bounds__(256) void keylist_kernel(const int32_t* rank,
 __device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two floats to packed bf16 (round to nearest even), a in the low half:
+// one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 constexpr int kQB = kQBlock;
@@ -332,8 +335,11 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
       const int ch = idx % CPR;
       const int t0 = kpos[kb * kKB + row - wbase];
       const int t = t0 == 0x7fffffff ? 0 : t0;  // padding reads row 0
-      kreg[c] = *(const u32x4*)(kc + (size_t)t * D + ch * 8);
-      vreg[c] = *(const u32x4*)(vc + (size_t)t * D + ch * 8);
+      // 32-bit byte offset from the slice base (a slice holds at most
+      // 262144 rows of 256 B), so the loads use a scalar base address
+      const uint32_t off = (uint32_t)(t * D + ch * 8) * 2u;
+      kreg[c] = *(const u32x4*)((const char*)kc + off);
+      vreg[c] = *(const u32x4*)((const char*)vc + off);
     }
     if (threadIdx.x < kKB) {
       treg = kpos[kb * kKB + threadIdx.x - wbase];
