@@ -25,6 +25,10 @@ What it computes, step by step, in the pages' notation:
   small projections of x = [k; v], a gated matrix memory C and normaliser z
   updated by every token, and a delayed read-out: after absorbing position q
   the token at q - W is scored from the state that has seen q.
+* Sink-attention gate. Fast KVzip section 3.4 "Low-Rank Sink Attention":
+  low-rank normalised projections of the hidden state give per-KV-head keys
+  and per-query-head queries; each query weighs the token's key against a
+  fixed set of sink keys and a learnable denominator term.
 * Retention rule. KVpop section 3, Eq. (1) B = s + w + k; section 3.1 Eq. (4)
   eligible set E(q) = {t | s <= t <= q - w}; Appendix C.1 Eq. (26) retained
   set = sinks, recent window, and the top-k eligible tokens.
@@ -55,6 +59,12 @@ Readings where the pages leave a step open (also listed in the design notes):
 * Temporal decay (optional, per KV head): decay step n = 1 only (KVpop Table
   3 uses n = 1), ranking by the static priority of Eq. (20) in float32.
 * Query head j reads KV head floor(j / G) (contiguous GQA groups).
+* Sink-attention gate (the page's equation is not legible; these follow its
+  prose): RMS normalisation with eps 1e-6 after each projection, logits
+  scaled by 1/sqrt(D'), the token's own term in the denominator (so the
+  gate lies in [0, 1] for b >= 0 and the no-denominator variant is a
+  sigmoid), one shared set of sink keys per layer, and the maximum over the
+  G query heads of a KV head.
 * Stateful scorer: the Hedgehog variant with projection width P = d/2
   (features of 2P entries), scalar affine gate preactivations with biases, no
   output gate, soft-cap, norm or skip connection; the read-out delay equals
@@ -77,6 +87,7 @@ __all__ = [
     "hedgehog", "MlstmWeights", "mlstm_features", "mlstm_readout",
     "MlstmScorer", "mlstm_scores_parallel",
     "prefill_ranks", "prefill_cutoffs", "prefill_mask", "prefill_attention",
+    "rms_norm", "SinkGateWeights", "sink_gate_score",
     "eligible_mask",
     "select_keep", "compaction_sources", "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
     "closed_form_retained", "cache_bytes_per_token",
@@ -246,6 +257,55 @@ def mlstm_scores_parallel(x: np.ndarray, w: MlstmWeights, window: int
         out[u] = float(np.dot(np.asarray(w.a, np.float64),
                               h / (1.0 + np.exp(-h))) + w.b)
     return out
+
+
+def rms_norm(y: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """Weighted normalisation over the last axis (the per-head RMS norm with
+    a learnable per-feature weight that Fast KVzip section 3.4 applies after
+    the gate projections): weight * y / sqrt(mean(y^2) + eps)."""
+    y = np.asarray(y, np.float64)
+    return np.asarray(weight, np.float64) * y / np.sqrt(
+        np.mean(y * y, axis=-1, keepdims=True) + eps)
+
+
+@dataclass
+class SinkGateWeights:
+    """One layer's low-rank sink-attention gate (Fast KVzip section 3.4,
+    "Low-Rank Sink Attention"): projections W_k [H][D'][D] and
+    W_q [H][G][D'][D] of the hidden state, the normalisation weights
+    g_k, g_q [D'], the layer's S sink keys [S][D'] and the learnable
+    denominator terms b [H][G]."""
+
+    wk: np.ndarray
+    wq: np.ndarray
+    gk: np.ndarray
+    gq: np.ndarray
+    sinks: np.ndarray
+    b: np.ndarray
+    eps: float = 1e-6
+
+
+def sink_gate_score(hidden: np.ndarray, w: SinkGateWeights) -> np.ndarray:
+    """Per-KV-head gate scores of tokens with hidden states hidden [n][D]
+    (Fast KVzip section 3.4): k_h = norm(W_k[h] x), q_j = norm(W_q[j] x);
+    with logits a_j = q_j . k_h / sqrt(D') and c_jr = q_j . k_sink^r /
+    sqrt(D'), query head j gives exp(a_j) / (exp(a_j) + sum_r exp(c_jr) +
+    b_j) in [0, 1] (the variant without a learnable denominator sets
+    sum_r exp(c_jr) + b_j = 1, i.e. sigmoid(a_j)); the KV head's score is the
+    maximum over its G query heads. Returns [n][H]."""
+    x = np.asarray(hidden, np.float64)
+    wk = np.asarray(w.wk, np.float64)
+    wq = np.asarray(w.wq, np.float64)
+    H, G, dp = wq.shape[0], wq.shape[1], wq.shape[2]
+    k = rms_norm(np.einsum("hpd,nd->nhp", wk, x), w.gk, w.eps)      # [n][H][D']
+    q = rms_norm(np.einsum("hgpd,nd->nhgp", wq, x), w.gq, w.eps)    # [n][H][G][D']
+    a = np.einsum("nhgp,nhp->nhg", q, k) / np.sqrt(dp)
+    c = np.einsum("nhgp,rp->nhgr", q, np.asarray(w.sinks, np.float64)) / np.sqrt(dp)
+    m = np.maximum(a, c.max(axis=-1) if c.shape[-1] else -np.inf)
+    ea = np.exp(a - m)
+    den = ea + np.exp(c - m[..., None]).sum(axis=-1) + \
+        np.asarray(w.b, np.float64)[None] * np.exp(-m)
+    return (ea / den).max(axis=-1)
 
 
 def score_to_f32(s: np.ndarray) -> np.ndarray:

@@ -284,3 +284,46 @@ def test_prefill_mutants_fail(fns):
         except AssertionError:
             failed += 1
     assert failed >= 1
+
+
+# --- sink-attention gate mutants --------------------------------------------
+
+def sink_gate_mean(hidden, w):
+    """Mean over the query heads instead of the maximum."""
+    G = np.asarray(w.wq).shape[1]
+    total = 0.0
+    for g in range(G):
+        wg = O.SinkGateWeights(w.wk, np.asarray(w.wq)[:, g:g + 1], w.gk, w.gq,
+                               w.sinks, np.asarray(w.b)[:, g:g + 1], w.eps)
+        total = total + O.sink_gate_score(hidden, wg)
+    return total / G
+
+
+def sink_gate_no_own_term(hidden, w):
+    """exp(a) / (sum_r exp(c_r) + b): the token's term left out of the
+    denominator."""
+    g = O.sink_gate_score(hidden, w)
+    return g / (1.0 - g)
+
+
+def sink_gate_unscaled(hidden, w):
+    """Logits without the 1/sqrt(D') scale."""
+    dp = np.asarray(w.wq).shape[2]
+    return O.sink_gate_score(hidden, O.SinkGateWeights(
+        w.wk, np.asarray(w.wq) * np.sqrt(dp) ** 0, w.gk,
+        np.asarray(w.gq) * np.sqrt(dp), w.sinks, w.b, w.eps))
+
+
+@pytest.mark.parametrize("fn", [sink_gate_mean, sink_gate_no_own_term,
+                                sink_gate_unscaled],
+                         ids=["mean", "no-own-term", "unscaled"])
+def test_sink_gate_mutants_fail(fn):
+    failed = 0
+    for check in (P.check_sink_gate_hand,
+                  P.check_sink_gate_without_denominator_is_sigmoid,
+                  P.check_sink_gate_sinks_equal_to_key):
+        try:
+            check(fn)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1

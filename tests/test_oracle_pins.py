@@ -820,3 +820,100 @@ def test_prefill_attention_rows_are_decode_attention():
                                       V[j // G, keep])
             np.testing.assert_allclose(out[j, q], o[0], rtol=1e-12, atol=1e-14)
             assert lse[j, q] == pytest.approx(float(l[0]), rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Sink-attention gate (Fast KVzip section 3.4)
+# ---------------------------------------------------------------------------
+
+def _sink_weights(rng, D, H, G, dp, S, b=None):
+    return O.SinkGateWeights(rng.standard_normal((H, dp, D)) / np.sqrt(D),
+                             rng.standard_normal((H, G, dp, D)) / np.sqrt(D),
+                             0.5 + rng.random(dp), 0.5 + rng.random(dp),
+                             rng.standard_normal((S, dp)),
+                             rng.random((H, G)) if b is None else b)
+
+
+def _torch_qk(x, w):
+    """q [n][H][G][D'], k [n][H][D'] by torch float64 linear + rms_norm."""
+    import torch
+    X = torch.from_numpy(np.asarray(x, np.float64))
+    Wk = torch.from_numpy(np.asarray(w.wk, np.float64))
+    Wq = torch.from_numpy(np.asarray(w.wq, np.float64))
+    H, G, dp, D = Wq.shape
+    k = torch.nn.functional.rms_norm(
+        (X @ Wk.reshape(H * dp, D).T).reshape(-1, H, dp), (dp,),
+        torch.from_numpy(np.asarray(w.gk, np.float64)), w.eps)
+    q = torch.nn.functional.rms_norm(
+        (X @ Wq.reshape(H * G * dp, D).T).reshape(-1, H, G, dp), (dp,),
+        torch.from_numpy(np.asarray(w.gq, np.float64)), w.eps)
+    return q.numpy(), k.numpy()
+
+
+def check_sink_gate_hand(score_fn):
+    g = golden()["sink_gate"]
+    w = O.SinkGateWeights(np.eye(2)[None], np.eye(2)[None, None], np.ones(2),
+                          np.ones(2), np.asarray([g["sink"]]),
+                          np.full((1, 1), g["b"]), eps=0.0)
+    got = score_fn(np.asarray([g["hidden"]]), w)
+    assert got.shape == (1, 1)
+    assert got[0, 0] == pytest.approx(g["expected"], rel=1e-12)
+
+
+def check_sink_gate_without_denominator_is_sigmoid(score_fn):
+    """No sink keys and b = 1 (the variant with sum_r exp(c_jr) + b_j = 1):
+    each query head gives sigmoid(q_j . k_h / sqrt(D')); the KV head takes
+    the largest."""
+    rng = np.random.default_rng(61)
+    D, H, G, dp = 24, 3, 2, 4
+    w = _sink_weights(rng, D, H, G, dp, 0, b=np.ones((H, G)))
+    x = rng.standard_normal((7, D))
+    q, k = _torch_qk(x, w)
+    a = np.einsum("nhgp,nhp->nhg", q, k) / np.sqrt(dp)
+    np.testing.assert_allclose(score_fn(x, w),
+                               scipy.special.expit(a).max(axis=-1),
+                               rtol=1e-12)
+
+
+def check_sink_gate_sinks_equal_to_key(score_fn):
+    """Sink keys all equal to the token's own key and b = 0: the token's
+    term competes with S identical terms, so every gate is 1 / (1 + S)."""
+    rng = np.random.default_rng(62)
+    D, dp, S = 16, 4, 5
+    w = _sink_weights(rng, D, 1, 3, dp, S, b=np.zeros((1, 3)))
+    x = rng.standard_normal((1, D))
+    _, k = _torch_qk(x, w)
+    w.sinks = np.repeat(k[0], S, axis=0)
+    assert score_fn(x, w)[0, 0] == pytest.approx(1.0 / (1 + S), rel=1e-12)
+
+
+def test_rms_norm_matches_torch():
+    import torch
+    rng = np.random.default_rng(60)
+    y = rng.standard_normal((5, 3, 8))
+    wt = rng.random(8)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(y), (8,),
+                                       torch.from_numpy(wt), 1e-6).numpy()
+    np.testing.assert_allclose(O.rms_norm(y, wt, 1e-6), ref, rtol=1e-13)
+
+
+def test_sink_gate_hand_case():
+    check_sink_gate_hand(O.sink_gate_score)
+
+
+def test_sink_gate_without_denominator_is_sigmoid():
+    check_sink_gate_without_denominator_is_sigmoid(O.sink_gate_score)
+
+
+def test_sink_gate_sinks_equal_to_key():
+    check_sink_gate_sinks_equal_to_key(O.sink_gate_score)
+
+
+def test_sink_gate_range_and_monotone_in_b():
+    rng = np.random.default_rng(63)
+    w = _sink_weights(rng, 32, 2, 4, 16, 16)
+    x = rng.standard_normal((20, 32))
+    g1 = O.sink_gate_score(x, w)
+    assert np.all((g1 > 0) & (g1 < 1))
+    w.b = w.b + 1.0
+    assert np.all(O.sink_gate_score(x, w) < g1)
