@@ -74,7 +74,8 @@ typedef enum { KVE_ACT_RELU = 0, KVE_ACT_SILU = 1 } kve_act;
 typedef enum {
   KVE_SCORER_MLP_KV = 0,
   KVE_SCORER_GATE_HIDDEN = 1,
-  KVE_SCORER_MLSTM = 2
+  KVE_SCORER_MLSTM = 2,
+  KVE_SCORER_SINK_GATE = 3
 } kve_scorer_kind;
 
 /* Shape of one layer's cache. head_dim in {64, 128}; group in [1, 8];
@@ -133,7 +134,17 @@ typedef struct {
  *    float32 or NULL its bias. delay = W: after absorbing the token at
  *    position q the scorer scores position q - W (no score while fewer than
  *    W tokens precede q in the state). kv_dtype and wdtype bf16; act unused.
- *  delay is read for MLSTM only. */
+ *  SINK_GATE, low-rank sink attention on hidden states (Fast KVzip section
+ *    3.4): in_dim = D (a multiple of 32), hidden = D' = 16, n_sink = S in
+ *    [0, 16]. w1 [H*16 + H*G*16][D] bf16 holds the rows of W_k (16 per KV
+ *    head) then W_q (16 per query head j = h*G + g); b1 [32] float32 the
+ *    normalisation weights of k then q, or NULL (ones); w2 [S][16] float32
+ *    the layer's sink keys; b2 [H*G] float32 the denominator terms b_j, or
+ *    NULL (zeros). With k = norm(W_k[h] x), q_j = norm(W_q[j] x) (RMS,
+ *    eps 1e-6), a_j = q_j . k / 4 and c_jr = q_j . sink_r / 4:
+ *    score_h = max_g exp(a_j) / (exp(a_j) + sum_r exp(c_jr) + b_j).
+ *    Hidden states are passed as for GATE.
+ *  delay is read for MLSTM only, n_sink for SINK_GATE only. */
 typedef struct {
   int32_t kind;   /* kve_scorer_kind */
   int32_t act;    /* kve_act (MLP only) */
@@ -145,6 +156,7 @@ typedef struct {
   const float* w2;
   const float* b2;
   int32_t delay;
+  int32_t n_sink;
 } kve_scorer;
 
 /* Host-side decode state of one layer for kve_step (in/out).
@@ -187,7 +199,7 @@ kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
  * cache->score (float32). MLP reads the cached K, V rows of those slots
  * (KVpop Eq. 35-36). GATE reads `hidden` [batch][slot_end-slot_begin][D]
  * bf16, the hidden states of those tokens (Fast KVzip section 3.1);
- * `hidden` must be NULL for MLP and MLSTM. Runs as a bf16 MFMA GEMM with
+ * `hidden` must be NULL for MLP and MLSTM; SINK_GATE reads it as GATE does. Runs as a bf16 MFMA GEMM with
  * float32 accumulation (float32 VALU for float32 weights).
  * MLSTM absorbs the cached tokens of those slots into cache->scorer_state in
  * slot order and writes the score of every token it reads out, into that
@@ -247,7 +259,8 @@ kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
  * attend over the cache. Updates *state on the host.
  * GATE scorers: hidden_new [batch][D] is the new token's hidden state and
  * hidden_buf [batch][L][D] (bf16, caller-owned) holds the pending tokens'
- * hidden states between calls; both must be NULL for MLP and MLSTM.
+ * hidden states between calls (SINK_GATE likewise); both must be NULL for
+ * MLP and MLSTM.
  * MLSTM scorers absorb the pending tokens at that point (the same scores as
  * absorbing every token as it arrives) and need scorer->delay equal to the
  * policy window.

@@ -19,7 +19,7 @@ __all__ = [
     "kve_workspace_bytes", "kve_append", "kve_score",
     "kve_select_evict", "kve_compact", "kve_decode_attn", "kve_step",
     "F32", "BF16", "ACT_RELU", "ACT_SILU",
-    "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "SCORER_MLSTM",
+    "SCORER_MLP_KV", "SCORER_GATE_HIDDEN", "SCORER_MLSTM", "SCORER_SINK_GATE",
     "kve_scorer_state_bytes", "alloc_workspace", "LayerStep",
     "kve_prefill_workspace_bytes", "kve_prefill_select", "kve_prefill_attn",
     "kve_prefill_attn_workspace_bytes",
@@ -27,7 +27,7 @@ __all__ = [
 
 F32, BF16 = 0, 1
 ACT_RELU, ACT_SILU = 0, 1
-SCORER_MLP_KV, SCORER_GATE_HIDDEN, SCORER_MLSTM = 0, 1, 2
+SCORER_MLP_KV, SCORER_GATE_HIDDEN, SCORER_MLSTM, SCORER_SINK_GATE = 0, 1, 2, 3
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 
@@ -59,7 +59,8 @@ class _Scorer(ctypes.Structure):
                 ("wdtype", ctypes.c_int32), ("in_dim", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("w1", ctypes.c_void_p),
                 ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("b2", ctypes.c_void_p), ("delay", ctypes.c_int32)]
+                ("b2", ctypes.c_void_p), ("delay", ctypes.c_int32),
+                ("n_sink", ctypes.c_int32)]
 
 
 class _State(ctypes.Structure):
@@ -225,9 +226,10 @@ class Scorer:
 
     def __init__(self, kind: int, w1, b1=None, w2=None, b2=None,
                  act: int = ACT_RELU, hidden: int = 0, in_dim: int = 0,
-                 wdtype: Optional[int] = None, delay: int = 0):
+                 wdtype: Optional[int] = None, delay: int = 0,
+                 n_sink: int = 0):
         import torch
-        self.kind, self.act, self.delay = kind, act, delay
+        self.kind, self.act, self.delay, self.n_sink = kind, act, delay, n_sink
         self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
         self.hidden, self.in_dim = hidden, in_dim
         if wdtype is None:
@@ -253,10 +255,18 @@ class Scorer:
         return cls(SCORER_MLSTM, w, gate_b, a, b, hidden=a.shape[1],
                    in_dim=w.shape[2], delay=delay)
 
+    @classmethod
+    def sink_gate(cls, w, sinks, norm=None, b=None):
+        """Low-rank sink-attention gate: w [H*16 + H*G*16][D] bf16 (rows of
+        W_k then W_q), sinks [S][16] float32, norm [32] float32 (k then q
+        normalisation weights), b [H*G] float32."""
+        return cls(SCORER_SINK_GATE, w, norm, sinks, b, hidden=16,
+                   in_dim=w.shape[1], n_sink=sinks.shape[0])
+
     def c(self) -> _Scorer:
         return _Scorer(self.kind, self.act, self.wdtype, self.in_dim,
                        self.hidden, _ptr(self.w1), _ptr(self.b1),
-                       _ptr(self.w2), _ptr(self.b2), self.delay)
+                       _ptr(self.w2), _ptr(self.b2), self.delay, self.n_sink)
 
 
 @dataclass

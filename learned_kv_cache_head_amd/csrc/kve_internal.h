@@ -97,6 +97,19 @@ struct GateLaunch {
 };
 hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s);
 
+struct SinkGateLaunch {
+  const void* hidden;      // bf16 [batch][rows_stride][in_dim]
+  long long batch_stride;  // elements between batches of `hidden`
+  float* score;            // [batch][H][cap]
+  const void* w;           // bf16 [H*16 + H*G*16][in_dim]: W_k, then W_q
+  const float* norm;       // [32] (g_k, g_q) or null
+  const float* sinks;      // [n_sink][16]
+  const float* b;          // [H*G] or null
+  int batch, H, G, cap, in_dim, n_sink;
+  int slot_begin, slot_end;
+};
+hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s);
+
 struct MlstmLaunch {
   const void* k;         // cache base (bf16)
   const void* v;

@@ -168,6 +168,15 @@ kve_status check_scorer(const kve_shape* shape, const kve_scorer* sc) {
     if (shape->n_kv_heads > 16) return KVE_ERR_UNSUPPORTED;
     return KVE_OK;
   }
+  if (sc->kind == KVE_SCORER_SINK_GATE) {
+    if (sc->wdtype != KVE_BF16) return KVE_ERR_UNSUPPORTED;
+    if (sc->in_dim < 32 || sc->in_dim % 32 != 0) return KVE_ERR_UNSUPPORTED;
+    if (sc->hidden != 16) return KVE_ERR_UNSUPPORTED;
+    if (shape->group < 1 || shape->group > 8) return KVE_ERR_UNSUPPORTED;
+    if (sc->n_sink < 0 || sc->n_sink > 16) return KVE_ERR_UNSUPPORTED;
+    if (sc->n_sink > 0 && !sc->w2) return KVE_ERR_INVALID_ARG;
+    return KVE_OK;
+  }
   if (sc->kind == KVE_SCORER_MLSTM) {
     if (shape->kv_dtype != KVE_BF16 || sc->wdtype != KVE_BF16)
       return KVE_ERR_UNSUPPORTED;
@@ -226,6 +235,25 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
     m.slot_begin = slot_begin;
     m.slot_end = slot_end;
     return from_hip(kve::launch_score_mlp(m, stream));
+  }
+  if (sc->kind == KVE_SCORER_SINK_GATE) {
+    kve::SinkGateLaunch q{};
+    q.hidden = hidden;
+    q.batch_stride = hidden_batch_stride;
+    q.score = cache->score;
+    q.w = sc->w1;
+    q.norm = sc->b1;
+    q.sinks = sc->w2;
+    q.b = sc->b2;
+    q.batch = shape->batch;
+    q.H = shape->n_kv_heads;
+    q.G = shape->group;
+    q.cap = shape->capacity;
+    q.in_dim = sc->in_dim;
+    q.n_sink = sc->n_sink;
+    q.slot_begin = slot_begin;
+    q.slot_end = slot_end;
+    return from_hip(kve::launch_score_sink_gate(q, stream));
   }
   kve::GateLaunch g{};
   g.hidden = hidden;
@@ -388,7 +416,8 @@ kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
   if ((st = check_scorer(shape, scorer)) != KVE_OK) return st;
   if (slot_begin < 0 || slot_end < slot_begin) return KVE_ERR_INVALID_ARG;
   if (slot_end > shape->capacity) return KVE_ERR_CAPACITY;
-  const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN;
+  const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN ||
+                    scorer->kind == KVE_SCORER_SINK_GATE;
   if (gate != (hidden != nullptr)) return KVE_ERR_INVALID_ARG;
   if (scorer->kind == KVE_SCORER_MLSTM && !cache->scorer_state)
     return KVE_ERR_INVALID_ARG;
@@ -464,7 +493,8 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
     return KVE_ERR_INVALID_ARG;
   const int B = policy->budget, L = policy->evict_len;
   if ((long long)B + L > shape->capacity) return KVE_ERR_CAPACITY;
-  const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN;
+  const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN ||
+                    scorer->kind == KVE_SCORER_SINK_GATE;
   if (gate != (hidden_new != nullptr) || gate != (hidden_buf != nullptr))
     return KVE_ERR_INVALID_ARG;
   if (scorer->kind == KVE_SCORER_MLSTM) {

@@ -235,6 +235,164 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Low-rank sink-attention gate (Fast KVzip section 3.4): one wave scores 64
+// tokens of one KV head. The projections k = W_k x (D' = 16 outputs) and
+// q_j = W_q[j] x (G x 16) of the hidden states run on MFMA, four 16-token
+// tiles per wave so each weight fragment serves 64 tokens. In the
+// accumulator layout a token's 16 features sit in one 16-lane row, so the
+// RMS normalisations and dot products are DPP row sums; the S sink logits
+// of a query come from a reduce-scatter over the row (lane c ends with
+// sink c's logit).
+// ---------------------------------------------------------------------------
+constexpr int kSgTiles = 4;        // 16-token tiles per wave
+constexpr float kSgEps = 1e-6f;    // RMS normalisation epsilon
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                         0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dppf<0xB1>(x);
+  x += dppf<0x4E>(x);
+  x += dppf<0x141>(x);
+  return x + dppf<0x140>(x);
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dppf<0xB1>(x));
+  x = fmaxf(x, dppf<0x4E>(x));
+  x = fmaxf(x, dppf<0x141>(x));
+  return fmaxf(x, dppf<0x140>(x));
+}
+// p[r] in every lane c of a 16-lane row -> sum over the row of p[c], in
+// lane c. The partners c^8, c^7 (row_half_mirror), c^2, c^1 flip bits 3, 2,
+// 1, 0 in turn; each step keeps the half of the vector that the lane's bit
+// selects and adds the partner's copy of it.
+__device__ __forceinline__ float reduce_scatter16(const float (&p)[16], int c) {
+  float a8[8], a4[4], a2[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool up = c & 8;
+    const float keep = up ? p[8 + j] : p[j];
+    const float send = up ? p[j] : p[8 + j];
+    a8[j] = keep + dppf<0x128>(send);      // row_ror:8 = lane c^8
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool up = c & 4;
+    const float keep = up ? a8[4 + j] : a8[j];
+    const float send = up ? a8[j] : a8[4 + j];
+    a4[j] = keep + dppf<0x141>(send);      // row_half_mirror = lane c^7
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bool up = c & 2;
+    const float keep = up ? a4[2 + j] : a4[j];
+    const float send = up ? a4[j] : a4[2 + j];
+    a2[j] = keep + dppf<0x4E>(send);       // lane c^2
+  }
+  const bool up = c & 1;
+  const float keep = up ? a2[1] : a2[0];
+  const float send = up ? a2[0] : a2[1];
+  return keep + dppf<0xB1>(send);          // lane c^1
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void sink_gate_kernel(SinkGateLaunch g) {
+  constexpr int NT = 1 + G;  // k tile, then one q tile per query head
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.y * 4 + wave;
+  const int b = blockIdx.z;
+  const int rows = g.slot_end - g.slot_begin;
+  const int r0 = blockIdx.x * (16 * kSgTiles);
+  if (h >= g.H || r0 >= rows) return;  // no barriers below
+  const int c = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const uint16_t* xb = (const uint16_t*)g.hidden + (size_t)b * g.batch_stride;
+  const uint16_t* xr[kSgTiles];
+#pragma unroll
+  for (int t = 0; t < kSgTiles; ++t) {
+    const int r = min(r0 + t * 16 + c, rows - 1);
+    xr[t] = xb + (size_t)r * g.in_dim + kq;
+  }
+  const uint16_t* wr[NT];
+  wr[0] = (const uint16_t*)g.w + ((size_t)h * 16 + c) * g.in_dim + kq;
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    wr[1 + j] = (const uint16_t*)g.w +
+                ((size_t)g.H * 16 + (size_t)(h * G + j) * 16 + c) * g.in_dim + kq;
+  f32x4_t acc[kSgTiles][NT];
+#pragma unroll
+  for (int t = 0; t < kSgTiles; ++t)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[t][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ksteps = g.in_dim / 32;
+#pragma unroll 2
+  for (int ks = 0; ks < ksteps; ++ks) {
+    bf16x8_t A[kSgTiles], B[NT];
+#pragma unroll
+    for (int t = 0; t < kSgTiles; ++t) A[t] = load8(xr[t] + ks * 32);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) B[j] = load8(wr[j] + ks * 32);
+#pragma unroll
+    for (int t = 0; t < kSgTiles; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B[j], acc[t][j],
+                                                            0, 0, 0);
+  }
+
+  // Epilogue: lane c holds feature c of 4 tokens per tile.
+  const float gk = g.norm ? g.norm[c] : 1.f;
+  const float gq = g.norm ? g.norm[16 + c] : 1.f;
+  float ks16[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ks16[r] = r < g.n_sink ? g.sinks[r * 16 + c] : 0.f;
+  float bj[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) bj[j] = g.b ? g.b[h * G + j] : 0.f;
+  const float inv_sqrt = 0.25f;  // 1 / sqrt(16)
+  float* out = g.score + ((size_t)b * g.H + h) * g.cap + g.slot_begin;
+  // One token (row i of tile t) at a time; the accumulator values are
+  // copied out first so that no register array is indexed dynamically.
+  auto token = [&](const f32x4_t (&tile)[NT], int t, int i) {
+    float kc = tile[0][0], qv[G];
+    if (i == 1) kc = tile[0][1];
+    if (i == 2) kc = tile[0][2];
+    if (i == 3) kc = tile[0][3];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const f32x4_t v = tile[1 + j];
+      qv[j] = i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+    }
+    const float kn = gk * kc * rsqrtf(row_sum16(kc * kc) * (1.f / 16.f) + kSgEps);
+    float best = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float qc = qv[j];
+      const float qn = gq * qc * rsqrtf(row_sum16(qc * qc) * (1.f / 16.f) + kSgEps);
+      const float a = row_sum16(qn * kn) * inv_sqrt;
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = qn * ks16[r];
+      float cs = reduce_scatter16(pr, c) * inv_sqrt;  // sink c's logit
+      cs = c < g.n_sink ? cs : -__builtin_inff();
+      const float m = fmaxf(a, row_max16(cs));
+      const float ssum = row_sum16(__expf(cs - m));
+      const float ea = __expf(a - m);
+      best = fmaxf(best, ea / (ea + ssum + bj[j] * __expf(-m)));
+    }
+    const int r = r0 + t * 16 + 4 * (lane >> 4) + i;
+    if (c == 0 && r < rows) out[r] = best;
+  };
+#pragma unroll
+  for (int t = 0; t < kSgTiles; ++t)
+    for (int i = 0; i < 4; ++i) token(acc[t], t, i);
+}
+
 }  // namespace
 
 hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
@@ -264,6 +422,21 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
     hipLaunchKernelGGL((mlp_valu_kernel<true>), grid, dim3(64), lds, s, m);
   } else {
     hipLaunchKernelGGL((mlp_valu_kernel<false>), grid, dim3(64), lds, s, m);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
+  const int rows = g.slot_end - g.slot_begin;
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + 16 * kSgTiles - 1) / (16 * kSgTiles), (g.H + 3) / 4,
+                  g.batch);
+  switch (g.G) {
+#define KVE_SG(GG) \
+    case GG: hipLaunchKernelGGL((sink_gate_kernel<GG>), grid, dim3(256), 0, s, g); break;
+    KVE_SG(1) KVE_SG(2) KVE_SG(3) KVE_SG(4) KVE_SG(5) KVE_SG(6) KVE_SG(7) KVE_SG(8)
+#undef KVE_SG
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

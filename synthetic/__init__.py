@@ -24,7 +24,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "rng_for", "round_to_bf16_bits",
     "bf16_bits_to_f32", "draw_rows", "draw_mlp_weights", "draw_gate_weights",
-    "draw_mlstm_weights",
+    "draw_mlstm_weights", "draw_sink_gate_weights",
     "initial_context", "step_inputs", "TENSOR_IDS",
 ]
 
@@ -47,8 +47,9 @@ class Workload:
     evict_len: int     # L
     steps: int         # decode steps
     layers: int
-    scorer: str        # "mlp" ([k;v] MLP), "gate" (hidden-state gate) or
-                       # "mlstm" (stateful scorer over [k;v])
+    scorer: str        # "mlp" ([k;v] MLP), "gate" (hidden-state gate),
+                       # "sink_gate" (low-rank sink-attention gate on hidden
+                       # states) or "mlstm" (stateful scorer over [k;v])
     hidden: int        # MLP hidden width, gate input dim D, or the mLSTM
                        # projection width P = d / 2
     act: str           # "relu" or "silu" (MLP only)
@@ -62,7 +63,8 @@ class Workload:
 
     @property
     def in_dim(self) -> int:
-        return self.hidden if self.scorer == "gate" else 2 * self.head_dim
+        return (self.hidden if self.scorer in ("gate", "sink_gate")
+                else 2 * self.head_dim)
 
     @property
     def capacity(self) -> int:
@@ -114,6 +116,7 @@ TENSOR_IDS = {
     "dir_k": 7, "dir_v": 8, "w1": 9, "w2": 10, "b1": 11, "b2": 12,
     "gate_w": 13, "hidden0": 14, "hidden_new": 15, "misc": 16,
     "mlstm_w": 17, "mlstm_gb": 18, "mlstm_a": 19,
+    "sg_w": 20, "sg_norm": 21, "sg_sinks": 22, "sg_b": 23,
 }
 
 
@@ -281,6 +284,25 @@ def draw_mlstm_weights(w: Workload, seed: int, layer: int) -> dict:
             "b": Stored(b.astype(np.float32), "f32")}
 
 
+def draw_sink_gate_weights(w: Workload, seed: int, layer: int,
+                           n_sink: int = 16) -> dict:
+    """Low-rank sink-attention gate of one layer, D' = 16 (Fast KVzip
+    section 3.4, S = D' = 16): w [H*16 + H*G*16][D] bf16, N(0, 1/D) (rows of
+    W_k, then W_q); norm [32] float32, 0.5 + U(0, 1) (k then q weights);
+    sinks [S][16] float32, N(0, 1); b [H*G] float32, U(0, 1)."""
+    D, H, G = w.hidden, w.n_kv, w.group
+    g = rng_for(seed, w.cfg_id, layer, -1, "sg_w")
+    wt = g.standard_normal((H * 16 + H * G * 16, D)) / np.sqrt(D)
+    norm = 0.5 + rng_for(seed, w.cfg_id, layer, -1, "sg_norm").random(32)
+    sinks = rng_for(seed, w.cfg_id, layer, -1, "sg_sinks").standard_normal(
+        (n_sink, 16))
+    b = rng_for(seed, w.cfg_id, layer, -1, "sg_b").random(H * G)
+    return {"w": Stored(wt.astype(np.float32), "bf16"),
+            "norm": Stored(norm.astype(np.float32), "f32"),
+            "sinks": Stored(sinks.astype(np.float32), "f32"),
+            "b": Stored(b.astype(np.float32), "f32")}
+
+
 def initial_context(w: Workload, seed: int, layer: int) -> dict:
     """The prefill cache of one layer: positions 0..n0-1 in every head.
 
@@ -294,7 +316,7 @@ def initial_context(w: Workload, seed: int, layer: int) -> dict:
         "v0": Stored(draw_rows(w, seed, layer, -1, "v0", w.n0, heavy),
                      w.kv_dtype),
     }
-    if w.scorer == "gate":
+    if w.scorer in ("gate", "sink_gate"):
         g = rng_for(seed, w.cfg_id, layer, -1, "hidden0")
         out["hidden0"] = Stored(
             g.standard_normal((w.batch, w.n0, w.hidden)).astype(np.float32),
@@ -315,7 +337,7 @@ def step_inputs(w: Workload, seed: int, layer: int, step: int) -> dict:
     q = gq.standard_normal((w.batch, w.n_q, w.head_dim)).astype(np.float32)
     out = {"k_new": Stored(k, w.kv_dtype), "v_new": Stored(v, w.kv_dtype),
            "q": Stored(q, w.kv_dtype)}
-    if w.scorer == "gate":
+    if w.scorer in ("gate", "sink_gate"):
         g = rng_for(seed, w.cfg_id, layer, step, "hidden_new")
         out["hidden_new"] = Stored(
             g.standard_normal((w.batch, w.hidden)).astype(np.float32), "bf16")

@@ -173,3 +173,21 @@ class Tracker:
                 self.lay.V[bi, h] = self.V[bi, h, g]
                 self.lay.score[bi, h] = self.S[bi, h, g]
                 self.lay.pos[bi, h] = g
+
+
+def oracle_sink_gate_weights(wts: dict, H: int, G: int) -> O.SinkGateWeights:
+    """synthetic.draw_sink_gate_weights output in the oracle's form."""
+    w = wts["w"].f64
+    D = w.shape[1]
+    return O.SinkGateWeights(w[:H * 16].reshape(H, 16, D),
+                             w[H * 16:].reshape(H, G, 16, D),
+                             wts["norm"].f64[:16], wts["norm"].f64[16:],
+                             wts["sinks"].f64, wts["b"].f64.reshape(H, G))
+
+
+def oracle_sink_gate_scores(hidden64, wts, H, G) -> np.ndarray:
+    """hidden [b][n][D] -> float32 scores [b][H][n]."""
+    w = oracle_sink_gate_weights(wts, H, G)
+    out = np.stack([O.sink_gate_score(hidden64[bi], w).T
+                    for bi in range(hidden64.shape[0])])
+    return O.score_to_f32(out)

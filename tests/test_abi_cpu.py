@@ -203,6 +203,7 @@ def test_cache_and_scorer_struct_layout_matches_header():
     assert kve._Cache.scorer_state.offset == 32
     assert kve._Scorer.w1.offset == 24
     assert kve._Scorer.delay.offset == 56
+    assert kve._Scorer.n_sink.offset == 60
     assert ctypes.sizeof(kve._Scorer) == 64
 
 
@@ -296,3 +297,20 @@ def test_prefill_workspace_and_validation():
     nqb = (9000 + 63) // 64
     lists = 2 * 8 * nqb * 892 * 4
     assert wsb == (lists + 255) // 256 * 256 + 2 * 8 * nqb * 4
+
+
+def test_sink_gate_rejects_bad_scorers():
+    lib = _lib()
+    s, c = _shape(), _cache()
+
+    def score(hidden_dim=5120, hid=16, n_sink=16, w2=FAKE, hidden=FAKE):
+        sc = kve._Scorer(3, 0, kve.BF16, hidden_dim, hid, FAKE, None, w2, None,
+                         0, n_sink)
+        return lib.kve_score(ctypes.byref(s), ctypes.byref(sc),
+                             ctypes.byref(c), 0, 10, hidden, None)
+
+    assert score(hidden=None) == 1      # hidden states required
+    assert score(hid=8) == 4            # D' must be 16
+    assert score(n_sink=17) == 4
+    assert score(hidden_dim=5000) == 4
+    assert score(w2=None) == 1          # sink keys missing
