@@ -467,6 +467,134 @@ def cpu_baseline_prefill(w, seed) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# Prefill scoring with the low-rank sink-attention gate
+# ---------------------------------------------------------------------------
+
+SINK_GATE_WORKLOAD = 5  # Qwen2.5-14B layer, 131072-token prompt
+SINK_GATE_RANK = 16     # D' = S = 16 (Fast KVzip section 3.4)
+
+
+def sink_gate_flops(n: int, D: int, H: int, G: int) -> int:
+    """MFMA work of the gate over n hidden states: the W_k and W_q
+    projections, 2 n D (H + H G) D' flops (the normalisations, logits and
+    softmax are O(n H G D') and not counted)."""
+    return 2 * n * D * H * (1 + G) * SINK_GATE_RANK
+
+
+def sink_gate_bytes(n: int, D: int, H: int, G: int) -> int:
+    """Algorithmic HBM bytes: the n bf16 hidden states read once, the bf16
+    projection weights once, one float32 score per (token, KV head)."""
+    return n * D * 2 + H * (1 + G) * SINK_GATE_RANK * D * 2 + n * H * 4
+
+
+def run_sink_gate(args, dev) -> dict:
+    """Time one layer's gate scoring of a whole prompt (kve_score with the
+    sink-attention gate over all n hidden states)."""
+    import torch
+    import learned_kv_cache_head_amd as kve
+    import synthetic as syn
+    T = syn.TENSOR_IDS
+    w = syn.workload(SINK_GATE_WORKLOAD, scorer="sink_gate")
+    b, H, G, D, n = w.batch, w.n_kv, w.group, w.hidden, w.n0
+    cfg, l, seed = w.cfg_id, 0, args.seed
+    dn = syn.device_normal
+    shape = kve.Shape(b, H, G, w.head_dim, n, kve.BF16)
+    cache = kve.CacheTensors.empty(shape, dev)
+    hidden = dn((b, n, D), seed, (cfg, l, 0, T["hidden0"]), torch.bfloat16, dev)
+    wt = dn((H * (1 + G) * SINK_GATE_RANK, D), seed, (cfg, l, 0, T["sg_w"]),
+            torch.bfloat16, dev, scale=D ** -0.5)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    norm = 0.5 + torch.rand(32, generator=gen, device=dev)
+    sinks = torch.randn((SINK_GATE_RANK, SINK_GATE_RANK), generator=gen,
+                        device=dev)
+    bias = torch.rand(H * G, generator=gen, device=dev)
+    sc = kve.Scorer.sink_gate(wt, sinks, norm=norm, b=bias)
+    steps = args.steps if args.steps is not None else 20
+    warmup = args.warmup if args.warmup is not None else 3
+    for _ in range(warmup):
+        kve.kve_score(shape, sc, cache, 0, n, hidden=hidden)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        kve.kve_score(shape, sc, cache, 0, n, hidden=hidden)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+    flops = sink_gate_flops(b * n, D, H, G)
+    nbytes = sink_gate_bytes(b * n, D, H, G)
+    achieved = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": ("prefill gate tokens/s of one layer: low-rank "
+                   "sink-attention gate scores of every prompt token"),
+        "value": round(b * n * steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen2.5-14b-1layer-131k-sink-gate",
+                   "batch": b, "prompt_len": n, "hidden_dim": D,
+                   "n_kv_heads": H, "n_q_heads": H * G,
+                   "gate_rank": SINK_GATE_RANK, "n_sink": SINK_GATE_RANK,
+                   "parallelism": "none"},
+        "hbm_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "sink_gate_kernel (projections + gate)",
+                     "algorithmic_flops_per_launch": int(flops),
+                     "algorithmic_bytes_per_launch": int(nbytes),
+                     "mean_launch_ms": round(ms, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_sink_gate(w, seed)
+    return result
+
+
+def cpu_baseline_sink_gate(w, seed, sample: int = 8192) -> dict:
+    """The oracle's gate on ``sample`` tokens of the same layer shape, scaled
+    to tokens/s."""
+    import numpy as np
+    import oracle as O
+    import synthetic as syn
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    H, G, D = w.n_kv, w.group, w.hidden
+    wts = syn.draw_sink_gate_weights(w, seed, 0)
+    wt = wts["w"].f64
+    ow = O.SinkGateWeights(wt[:H * 16].reshape(H, 16, D),
+                           wt[H * 16:].reshape(H, G, 16, D),
+                           wts["norm"].f64[:16], wts["norm"].f64[16:],
+                           wts["sinks"].f64, wts["b"].f64.reshape(H, G))
+    rng = syn.rng_for(seed, w.cfg_id, 0, -1, "hidden0")
+    x = syn.Stored(rng.standard_normal((sample, D)).astype(np.float32),
+                   "bf16").f64
+    t0 = time.perf_counter()
+    O.sink_gate_score(x, ow)
+    dt = time.perf_counter() - t0
+    return {"value": round(sample / dt, 1), "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 oracle gate over {sample} of {w.n0} prompt "
+                       f"tokens of one layer (D = {D}, {H} KV heads, "
+                       f"{H * G} query heads); {dt:.1f} s wall")}
+
+
+# ---------------------------------------------------------------------------
 # Recorded rocprofv3 traffic of the attention kernel
 # ---------------------------------------------------------------------------
 
@@ -518,6 +646,10 @@ def main() -> int:
     ap.add_argument("--prefill", action="store_true",
                     help="time one layer's prefill (running top-k selection "
                          "and Eq. 26 masked attention) instead of decode")
+    ap.add_argument("--sink-gate", action="store_true",
+                    help="time one layer's prompt scoring with the low-rank "
+                         "sink-attention gate (Qwen2.5-14B, 131072 tokens) "
+                         "instead of decode")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, run a plain 1 GiB "
                          "elementwise copy (counter calibration)")
@@ -537,6 +669,10 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sink_gate:
+        log("sink gate: qwen2.5-14b layer, 131072-token prompt")
+        print(json.dumps(run_sink_gate(args, dev)), flush=True)
+        return 0
     w = syn.workload(WORKLOAD_BY_NAME[args.workload])
     if args.prefill:
         log(f"prefill {args.workload}: batch={w.batch} prompt={w.n0} B={w.budget}")

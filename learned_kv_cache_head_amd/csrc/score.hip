@@ -299,18 +299,57 @@ __device__ __forceinline__ float reduce_scatter16(const float (&p)[16], int c) {
   return keep + dppf<0xB1>(send);          // lane c^1
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void sink_gate_kernel(SinkGateLaunch g) {
-  constexpr int NT = 1 + G;  // k tile, then one q tile per query head
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.y * 4 + wave;
-  const int b = blockIdx.z;
-  const int rows = g.slot_end - g.slot_begin;
-  const int r0 = blockIdx.x * (16 * kSgTiles);
-  if (h >= g.H || r0 >= rows) return;  // no barriers below
+// One workgroup: 256 tokens (64 per wave, four 16-token tiles) x HP KV
+// heads, i.e. NT = HP (1 + G) 16-column tiles of the projection [k_h; q_j].
+// The weight rows of those tiles are staged through LDS in 64-wide k chunks
+// (double-buffered, shared by the four waves); each wave reads its own token
+// rows straight from global memory one chunk ahead. Workgroup ids are
+// mapped so that the head groups of one token block run back to back on the
+// same XCD and share its hidden states in that XCD's L2.
+constexpr int kSgRowsWG = 256;
+constexpr int kSgKC = 64;                    // k chunk
+constexpr int kSgRowB = kSgKC * 2 + 16;      // LDS bytes per weight row
+// Heads per workgroup for group size G: about 6 column tiles (96
+// accumulators a lane), so that two workgroups fit on a CU.
+constexpr int sg_heads(int G) { return G >= 5 ? 1 : 6 / (1 + G); }
+
+template <int G, int HP, int WPE = (HP * (1 + G) <= 7 ? 2 : 1)>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void sink_gate_kernel(SinkGateLaunch g, int nb, int ncg) {
+  constexpr int NT = HP * (1 + G);
+  constexpr int NROWS = NT * 16;
+  constexpr int SEGS = NROWS * (kSgKC / 8);  // 16-byte pieces per chunk
+  constexpr int SPT = (SEGS + 255) / 256;
+  // Rows past NROWS take the stores of the pieces past SEGS (never read),
+  // so every thread stores unconditionally.
+  constexpr int LROWS = SPT * 256 / (kSgKC / 8);
+  __shared__ __attribute__((aligned(16))) uint8_t wl[2][LROWS * kSgRowB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int c = lane & 15;
   const int kq = (lane >> 4) * 8;
+
+  // Block id -> (token block, head group). Within each run of 8 * ncg ids,
+  // the ncg head groups of a token block share id % 8 (the XCD).
+  const int id = blockIdx.x;
+  const int grp = 8 * ncg;
+  const int base = id - id % grp;
+  const int rr = id - base;
+  const int total = nb * g.batch * ncg;
+  int blk, cg;
+  if (base + grp <= total) {
+    blk = base / ncg + rr % 8;
+    cg = rr / 8;
+  } else {
+    blk = base / ncg + rr / ncg;
+    cg = rr % ncg;
+  }
+  const int b = blk / nb;
+  const int tb = blk - b * nb;
+  const int rows = g.slot_end - g.slot_begin;
+  const int r0 = tb * kSgRowsWG + wave * 64;
+
   const uint16_t* xb = (const uint16_t*)g.hidden + (size_t)b * g.batch_stride;
   const uint16_t* xr[kSgTiles];
 #pragma unroll
@@ -318,31 +357,118 @@ __global__ __launch_bounds__(256) void sink_gate_kernel(SinkGateLaunch g) {
     const int r = min(r0 + t * 16 + c, rows - 1);
     xr[t] = xb + (size_t)r * g.in_dim + kq;
   }
-  const uint16_t* wr[NT];
-  wr[0] = (const uint16_t*)g.w + ((size_t)h * 16 + c) * g.in_dim + kq;
+  // Weight pieces this thread stages: LDS row R <- global row of tile R/16.
+  const uint16_t* wsrc[SPT];
+  int wdst[SPT];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
-    wr[1 + j] = (const uint16_t*)g.w +
-                ((size_t)g.H * 16 + (size_t)(h * G + j) * 16 + c) * g.in_dim + kq;
+  for (int s = 0; s < SPT; ++s) {
+    const int seg = min(tid + s * 256, SEGS - 1);
+    const int R = seg / (kSgKC / 8);
+    const int part = seg % (kSgKC / 8);
+    const int Rs = (tid + s * 256) / (kSgKC / 8);  // LDS row of the store
+    const int tile = R / 16;
+    const int hp = tile / (1 + G);
+    const int j = tile % (1 + G);
+    const int h = min(cg * HP + hp, g.H - 1);
+    const size_t grow = j == 0 ? (size_t)h * 16 + (R & 15)
+                               : (size_t)g.H * 16 + (size_t)(h * G + j - 1) * 16 + (R & 15);
+    wsrc[s] = (const uint16_t*)g.w + grow * g.in_dim + part * 8;
+    wdst[s] = Rs * kSgRowB + part * 16;
+  }
+  const int nch = (g.in_dim + kSgKC - 1) / kSgKC;
+  // A chunk is 64 wide except possibly the last (in_dim % 64 == 32).
+  auto full = [&](int ch) { return ch * kSgKC + kSgKC <= g.in_dim; };
+  u32x4 wreg[SPT];
+  // In a half chunk (in_dim % 64 == 32) the upper 32 columns of the staged
+  // weights are zero, so the second k step adds nothing.
+  auto load_w = [&](int ch) {
+    const int back = full(ch) ? 0 : 32;
+#pragma unroll
+    for (int s = 0; s < SPT; ++s) {
+      const int part = (wdst[s] % kSgRowB) / 16;
+      wreg[s] = *(const u32x4*)(wsrc[s] + ch * kSgKC - (part < 4 ? 0 : back));
+    }
+  };
+  auto store_w = [&](int ch, int buf) {
+    const bool f = full(ch);
+#pragma unroll
+    for (int s = 0; s < SPT; ++s) {
+      const int part = (wdst[s] % kSgRowB) / 16;
+      const u32x4 v = (f || part < 4) ? wreg[s] : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(&wl[buf][wdst[s]]) = v;
+    }
+  };
+  bf16x8_t A[2][kSgTiles], An[2][kSgTiles];
+  auto load_a = [&](bf16x8_t (&a)[2][kSgTiles], int ch) {
+    // In a half chunk the second half repeats the first (in bounds, unused).
+    const int hi = full(ch) ? 32 : 0;
+#pragma unroll
+    for (int t = 0; t < kSgTiles; ++t) {
+      a[0][t] = load8(xr[t] + ch * kSgKC);
+      a[1][t] = load8(xr[t] + ch * kSgKC + hi);
+    }
+  };
+
   f32x4_t acc[kSgTiles][NT];
 #pragma unroll
   for (int t = 0; t < kSgTiles; ++t)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[t][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int ksteps = g.in_dim / 32;
-#pragma unroll 2
-  for (int ks = 0; ks < ksteps; ++ks) {
-    bf16x8_t A[kSgTiles], B[NT];
+
+  // The first chunk's token rows are requested before its weights, so that
+  // the weight store's wait leaves no load in flight when the loop starts.
+  load_a(A, 0);
+  load_w(0);
+  store_w(0, 0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    // Request the next chunk; the last chunk requests itself again (in
+    // bounds, unused), so the loads carry no branch and the wait counts
+    // stay exact.
+    const int nx = min(ch + 1, nch - 1);
+    load_w(nx);
+    load_a(An, nx);
+    // Weight fragments of the second k step are read from LDS while the
+    // first step's MFMAs run.
+    const uint8_t* wb = wl[ch & 1] + c * kSgRowB + kq * 2;
+    bf16x8_t B0[NT], B1[NT];
 #pragma unroll
-    for (int t = 0; t < kSgTiles; ++t) A[t] = load8(xr[t] + ks * 32);
+    for (int j = 0; j < NT; ++j)
+      B0[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(wb + j * 16 * kSgRowB));
 #pragma unroll
-    for (int j = 0; j < NT; ++j) B[j] = load8(wr[j] + ks * 32);
+    for (int j = 0; j < NT; ++j) {
+      B1[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(wb + j * 16 * kSgRowB + 64));
 #pragma unroll
-    for (int t = 0; t < kSgTiles; ++t)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B[j], acc[t][j],
+      for (int t = 0; t < kSgTiles; ++t)
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][t], B0[j], acc[t][j],
                                                             0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int t = 0; t < kSgTiles; ++t)
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][t], B1[j], acc[t][j],
+                                                            0, 0, 0);
+    // Into the buffer no wave reads in this chunk (after the last chunk, a
+    // copy nobody reads).
+    store_w(nx, (ch + 1) & 1);
+    // Order: next chunk's global loads, first-step weight reads, first-step
+    // MFMAs interleaved with the second step's reads, second-step MFMAs,
+    // weight stores.
+    __builtin_amdgcn_sched_group_barrier(0x020, SPT + 2 * kSgTiles, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kSgTiles, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kSgTiles * NT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, SPT, 0);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int t = 0; t < kSgTiles; ++t) A[ks][t] = An[ks][t];
   }
 
   // Epilogue: lane c holds feature c of 4 tokens per tile.
@@ -351,46 +477,55 @@ __global__ __launch_bounds__(256) void sink_gate_kernel(SinkGateLaunch g) {
   float ks16[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) ks16[r] = r < g.n_sink ? g.sinks[r * 16 + c] : 0.f;
-  float bj[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) bj[j] = g.b ? g.b[h * G + j] : 0.f;
   const float inv_sqrt = 0.25f;  // 1 / sqrt(16)
-  float* out = g.score + ((size_t)b * g.H + h) * g.cap + g.slot_begin;
-  // One token (row i of tile t) at a time; the accumulator values are
-  // copied out first so that no register array is indexed dynamically.
-  auto token = [&](const f32x4_t (&tile)[NT], int t, int i) {
-    float kc = tile[0][0], qv[G];
-    if (i == 1) kc = tile[0][1];
-    if (i == 2) kc = tile[0][2];
-    if (i == 3) kc = tile[0][3];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const f32x4_t v = tile[1 + j];
-      qv[j] = i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+  for (int hp = 0; hp < HP; ++hp) {
+    const int h = min(cg * HP + hp, g.H - 1);
+    const bool live = cg * HP + hp < g.H;
+    float bj[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) bj[j] = g.b ? g.b[h * G + j] : 0.f;
+    float* out = g.score + ((size_t)b * g.H + h) * g.cap + g.slot_begin;
+    // One token (row i of tile t) at a time; the accumulator values are
+    // copied out first so that no register array is indexed dynamically.
+    auto token = [&](const f32x4_t (&tile)[1 + G], int t, int i) {
+      float kc = tile[0][0], qv[G];
+      if (i == 1) kc = tile[0][1];
+      if (i == 2) kc = tile[0][2];
+      if (i == 3) kc = tile[0][3];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const f32x4_t v = tile[1 + j];
+        qv[j] = i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+      }
+      const float kn = gk * kc * rsqrtf(row_sum16(kc * kc) * (1.f / 16.f) + kSgEps);
+      float best = 0.f;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float qc = qv[j];
+        const float qn = gq * qc * rsqrtf(row_sum16(qc * qc) * (1.f / 16.f) + kSgEps);
+        const float a = row_sum16(qn * kn) * inv_sqrt;
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = qn * ks16[r];
+        float cs = reduce_scatter16(pr, c) * inv_sqrt;  // sink c's logit
+        cs = c < g.n_sink ? cs : -__builtin_inff();
+        const float m = fmaxf(a, row_max16(cs));
+        const float ssum = row_sum16(__expf(cs - m));
+        const float ea = __expf(a - m);
+        best = fmaxf(best, ea / (ea + ssum + bj[j] * __expf(-m)));
+      }
+      const int r = r0 + t * 16 + 4 * (lane >> 4) + i;
+      if (live && c == 0 && r < rows) out[r] = best;
+    };
+#pragma unroll
+    for (int t = 0; t < kSgTiles; ++t) {
+      f32x4_t ht[1 + G];
+#pragma unroll
+      for (int j = 0; j <= G; ++j) ht[j] = acc[t][hp * (1 + G) + j];
+      for (int i = 0; i < 4; ++i) token(ht, t, i);
     }
-    const float kn = gk * kc * rsqrtf(row_sum16(kc * kc) * (1.f / 16.f) + kSgEps);
-    float best = 0.f;
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float qc = qv[j];
-      const float qn = gq * qc * rsqrtf(row_sum16(qc * qc) * (1.f / 16.f) + kSgEps);
-      const float a = row_sum16(qn * kn) * inv_sqrt;
-      float pr[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = qn * ks16[r];
-      float cs = reduce_scatter16(pr, c) * inv_sqrt;  // sink c's logit
-      cs = c < g.n_sink ? cs : -__builtin_inff();
-      const float m = fmaxf(a, row_max16(cs));
-      const float ssum = row_sum16(__expf(cs - m));
-      const float ea = __expf(a - m);
-      best = fmaxf(best, ea / (ea + ssum + bj[j] * __expf(-m)));
-    }
-    const int r = r0 + t * 16 + 4 * (lane >> 4) + i;
-    if (c == 0 && r < rows) out[r] = best;
-  };
-#pragma unroll
-  for (int t = 0; t < kSgTiles; ++t)
-    for (int i = 0; i < 4; ++i) token(acc[t], t, i);
+  }
 }
 
 }  // namespace
@@ -429,11 +564,17 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
 hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
   const int rows = g.slot_end - g.slot_begin;
   if (rows <= 0) return hipSuccess;
-  const dim3 grid((rows + 16 * kSgTiles - 1) / (16 * kSgTiles), (g.H + 3) / 4,
-                  g.batch);
+  const int nb = (rows + kSgRowsWG - 1) / kSgRowsWG;
+  const int hp = sg_heads(g.G);
+  const int ncg = (g.H + hp - 1) / hp;
+  const long long wgs = (long long)nb * g.batch * ncg;
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   switch (g.G) {
-#define KVE_SG(GG) \
-    case GG: hipLaunchKernelGGL((sink_gate_kernel<GG>), grid, dim3(256), 0, s, g); break;
+#define KVE_SG(GG)                                                           \
+    case GG:                                                                 \
+      hipLaunchKernelGGL((sink_gate_kernel<GG, sg_heads(GG)>),               \
+                         dim3((unsigned)wgs), dim3(256), 0, s, g, nb, ncg);  \
+      break;
     KVE_SG(1) KVE_SG(2) KVE_SG(3) KVE_SG(4) KVE_SG(5) KVE_SG(6) KVE_SG(7) KVE_SG(8)
 #undef KVE_SG
     default: return hipErrorInvalidValue;

@@ -25,6 +25,8 @@ CASES = [
     (2, 3, 2, 256, 77, 10, 100, 5),
     (1, 2, 1, 64, 130, 0, 130, 0),           # no sink keys
     (1, 4, 8, 1024, 200, 0, 200, 16),        # G = 8
+    (1, 5, 3, 96, 517, 3, 600, 7),           # D % 64 == 32: a half k chunk
+    (3, 7, 7, 160, 33, 0, 40, 16),           # G = 7, one partial block
 ]
 
 
@@ -119,3 +121,32 @@ def test_sink_gate_step_end_to_end():
         ref_out, _ = tr.lay.attend(st["q"].f64)
         attn_close(out.cpu().double().numpy(), ref_out, f"step {i}")
     assert evictions == 3
+
+
+def test_sink_gate_full_prompt_sampled():
+    """The whole 131072-token Qwen2.5-14B prompt (D = 5120, 8 KV heads, 40
+    query heads, S = 16) in one launch, as the gate benchmark times it; 600
+    sampled tokens, the last 64 among them, against the oracle."""
+    import torch
+    k = kve()
+    dev = torch.device("cuda")
+    w = syn.workload(5, scorer="sink_gate")
+    H, G, D, n = w.n_kv, w.group, w.hidden, w.n0
+    print(f"[sink-gate-full] n={n} D={D} H={H} G={G}", flush=True)
+    T = syn.TENSOR_IDS
+    hid = syn.device_normal((1, n, D), 3, (5, 0, 0, T["hidden0"]),
+                            torch.bfloat16, dev)
+    wts = syn.draw_sink_gate_weights(w, 3, 0)
+    shape = k.Shape(1, H, G, w.head_dim, n, k.BF16)
+    cache = k.CacheTensors.empty(shape, dev)
+    sc = k.Scorer.sink_gate(wts["w"].torch(dev), wts["sinks"].torch(dev),
+                            norm=wts["norm"].torch(dev), b=wts["b"].torch(dev))
+    k.kve_score(shape, sc, cache, 0, n, hidden=hid)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([rng.choice(n - 64, 536, replace=False),
+                                     np.arange(n - 64, n)]))
+    idx = torch.from_numpy(rows).to(dev)
+    x64 = hid[0].index_select(0, idx).float().cpu().double().numpy()
+    ref = oracle_sink_gate_scores(x64[None], wts, H, G)
+    got = cache.score[:, :, rows].cpu().numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=SINK_GATE_ATOL)
