@@ -236,102 +236,62 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
 }
 
 // ---------------------------------------------------------------------------
-// Low-rank sink-attention gate (Fast KVzip section 3.4): one wave scores 64
-// tokens of one KV head. The projections k = W_k x (D' = 16 outputs) and
-// q_j = W_q[j] x (G x 16) of the hidden states run on MFMA, four 16-token
-// tiles per wave so each weight fragment serves 64 tokens. In the
-// accumulator layout a token's 16 features sit in one 16-lane row, so the
-// RMS normalisations and dot products are DPP row sums; the S sink logits
-// of a query come from a reduce-scatter over the row (lane c ends with
-// sink c's logit).
+// Low-rank sink-attention gate (Fast KVzip section 3.4) over hidden states.
+//
+// The projections P = W x for the rows of W_k (16 per KV head) and W_q (16
+// per query head) are one GEMM. A workgroup of 8 waves computes 256 tokens x
+// 2 HPW KV heads: waves (wr, wc) own tokens 64 wr .. 64 wr + 63 and the
+// NTW = HPW (1 + G) 16-row weight tiles of head column wc. The operands move
+// from global memory straight into LDS (global_load_lds_dwordx4: lane l's 16
+// bytes land at base + 16 l), one 1 KB block per 16-row x 32-k MFMA
+// fragment, so the fragment reads are linear and conflict-free. Chunks of
+// 32 k go through a 3-stage ring: chunk ch + 2 is requested while chunk ch
+// is multiplied. Workgroup ids are mapped so that the head groups of a token
+// block run back to back on one XCD and share its hidden states in L2.
+//
+// The MFMA takes W as A and x as B, so a lane ends with 4 features (rows
+// 4 (l / 16) + v) of token l % 16: per-token sums over the 16 features are
+// 4 in-lane terms plus two cross-lane steps (lanes l ^ 16, l ^ 32). The 16
+// sink logits of a query are a 16 x 16 x 16 fp32 MFMA with the raw q tile as
+// B, so lane l gets sinks 4 (l / 16) + i of its token.
 // ---------------------------------------------------------------------------
-constexpr int kSgTiles = 4;        // 16-token tiles per wave
-constexpr float kSgEps = 1e-6f;    // RMS normalisation epsilon
+constexpr int kSgTok = 256;       // tokens per workgroup
+constexpr int kSgStages = 3;
+constexpr float kSgEps = 1e-6f;   // RMS normalisation epsilon
 
-template <int CTRL>
-__device__ __forceinline__ float dppf(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                         0xF, 0xF, false));
+template <int G>
+struct SgCfg {
+  static constexpr int HPW = 12 / (1 + G);    // heads per wave column
+  static constexpr int NTW = HPW * (1 + G);   // weight tiles per wave
+  static constexpr int NB = 16 + 2 * NTW;     // 1 KB blocks per chunk
+  static constexpr int LPW = (NB + 7) / 8;    // blocks each wave loads
+  static constexpr int NBP = 8 * LPW;         // padded: every wave loads LPW
+};
+
+__device__ __forceinline__ float xsum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dppf<0xB1>(x);
-  x += dppf<0x4E>(x);
-  x += dppf<0x141>(x);
-  return x + dppf<0x140>(x);
-}
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dppf<0xB1>(x));
-  x = fmaxf(x, dppf<0x4E>(x));
-  x = fmaxf(x, dppf<0x141>(x));
-  return fmaxf(x, dppf<0x140>(x));
-}
-// p[r] in every lane c of a 16-lane row -> sum over the row of p[c], in
-// lane c. The partners c^8, c^7 (row_half_mirror), c^2, c^1 flip bits 3, 2,
-// 1, 0 in turn; each step keeps the half of the vector that the lane's bit
-// selects and adds the partner's copy of it.
-__device__ __forceinline__ float reduce_scatter16(const float (&p)[16], int c) {
-  float a8[8], a4[4], a2[2];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const bool up = c & 8;
-    const float keep = up ? p[8 + j] : p[j];
-    const float send = up ? p[j] : p[8 + j];
-    a8[j] = keep + dppf<0x128>(send);      // row_ror:8 = lane c^8
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool up = c & 4;
-    const float keep = up ? a8[4 + j] : a8[j];
-    const float send = up ? a8[j] : a8[4 + j];
-    a4[j] = keep + dppf<0x141>(send);      // row_half_mirror = lane c^7
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const bool up = c & 2;
-    const float keep = up ? a4[2 + j] : a4[j];
-    const float send = up ? a4[j] : a4[2 + j];
-    a2[j] = keep + dppf<0x4E>(send);       // lane c^2
-  }
-  const bool up = c & 1;
-  const float keep = up ? a2[1] : a2[0];
-  const float send = up ? a2[0] : a2[1];
-  return keep + dppf<0xB1>(send);          // lane c^1
+__device__ __forceinline__ float xmax(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
 }
 
-// One workgroup: 256 tokens (64 per wave, four 16-token tiles) x HP KV
-// heads, i.e. NT = HP (1 + G) 16-column tiles of the projection [k_h; q_j].
-// The weight rows of those tiles are staged through LDS in 64-wide k chunks
-// (double-buffered, shared by the four waves); each wave reads its own token
-// rows straight from global memory one chunk ahead. Workgroup ids are
-// mapped so that the head groups of one token block run back to back on the
-// same XCD and share its hidden states in that XCD's L2.
-constexpr int kSgRowsWG = 256;
-constexpr int kSgKC = 64;                    // k chunk
-constexpr int kSgRowB = kSgKC * 2 + 16;      // LDS bytes per weight row
-// Heads per workgroup for group size G: about 6 column tiles (96
-// accumulators a lane), so that two workgroups fit on a CU.
-constexpr int sg_heads(int G) { return G >= 5 ? 1 : 6 / (1 + G); }
-
-template <int G, int HP, int WPE = (HP * (1 + G) <= 7 ? 2 : 1)>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+template <int G>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sink_gate_kernel(SinkGateLaunch g, int nb, int ncg) {
-  constexpr int NT = HP * (1 + G);
-  constexpr int NROWS = NT * 16;
-  constexpr int SEGS = NROWS * (kSgKC / 8);  // 16-byte pieces per chunk
-  constexpr int SPT = (SEGS + 255) / 256;
-  // Rows past NROWS take the stores of the pieces past SEGS (never read),
-  // so every thread stores unconditionally.
-  constexpr int LROWS = SPT * 256 / (kSgKC / 8);
-  __shared__ __attribute__((aligned(16))) uint8_t wl[2][LROWS * kSgRowB];
+  using C = SgCfg<G>;
+  constexpr int NTW = C::NTW, LPW = C::LPW;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kSgStages][C::NBP * 1024];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave & 3;   // token quarter
+  const int wc = wave >> 2;  // head column
   const int c = lane & 15;
   const int kq = (lane >> 4) * 8;
 
-  // Block id -> (token block, head group). Within each run of 8 * ncg ids,
-  // the ncg head groups of a token block share id % 8 (the XCD).
+  // Block id -> (token block, head group); see the comment above.
   const int id = blockIdx.x;
   const int grp = 8 * ncg;
   const int base = id - id % grp;
@@ -346,184 +306,142 @@ void sink_gate_kernel(SinkGateLaunch g, int nb, int ncg) {
     cg = rr % ncg;
   }
   const int b = blk / nb;
-  const int tb = blk - b * nb;
+  const int tok0 = (blk - b * nb) * kSgTok;
   const int rows = g.slot_end - g.slot_begin;
-  const int r0 = tb * kSgRowsWG + wave * 64;
+  const int h0 = cg * 2 * C::HPW;  // first head of the workgroup
 
+  // Source of each block this wave loads (chunk 0). Blocks 0..15: token
+  // tiles; 16..NB-1: weight tiles of head columns 0 and 1; past NB: padding
+  // (a copy of block 16's source into an unread slot).
   const uint16_t* xb = (const uint16_t*)g.hidden + (size_t)b * g.batch_stride;
-  const uint16_t* xr[kSgTiles];
+  const uint16_t* src[LPW];
 #pragma unroll
-  for (int t = 0; t < kSgTiles; ++t) {
-    const int r = min(r0 + t * 16 + c, rows - 1);
-    xr[t] = xb + (size_t)r * g.in_dim + kq;
+  for (int s = 0; s < LPW; ++s) {
+    const int bi = wave * LPW + s;
+    if (bi < 16) {
+      const int r = min(tok0 + bi * 16 + c, rows - 1);
+      src[s] = xb + (size_t)r * g.in_dim + kq;
+    } else {
+      const int q = bi < C::NB ? bi - 16 : 0;
+      const int col = q / NTW, j = q % NTW;
+      const int h = min(h0 + col * C::HPW + j / (1 + G), g.H - 1);
+      const int jj = j % (1 + G);
+      const size_t grow = jj == 0 ? (size_t)h * 16 + c
+                                  : (size_t)g.H * 16 + (size_t)(h * G + jj - 1) * 16 + c;
+      src[s] = (const uint16_t*)g.w + grow * g.in_dim + kq;
+    }
   }
-  // Weight pieces this thread stages: LDS row R <- global row of tile R/16.
-  const uint16_t* wsrc[SPT];
-  int wdst[SPT];
+  const int nch = g.in_dim / 32;
+  auto issue = [&](int ch, int stage) {
 #pragma unroll
-  for (int s = 0; s < SPT; ++s) {
-    const int seg = min(tid + s * 256, SEGS - 1);
-    const int R = seg / (kSgKC / 8);
-    const int part = seg % (kSgKC / 8);
-    const int Rs = (tid + s * 256) / (kSgKC / 8);  // LDS row of the store
-    const int tile = R / 16;
-    const int hp = tile / (1 + G);
-    const int j = tile % (1 + G);
-    const int h = min(cg * HP + hp, g.H - 1);
-    const size_t grow = j == 0 ? (size_t)h * 16 + (R & 15)
-                               : (size_t)g.H * 16 + (size_t)(h * G + j - 1) * 16 + (R & 15);
-    wsrc[s] = (const uint16_t*)g.w + grow * g.in_dim + part * 8;
-    wdst[s] = Rs * kSgRowB + part * 16;
-  }
-  const int nch = (g.in_dim + kSgKC - 1) / kSgKC;
-  // A chunk is 64 wide except possibly the last (in_dim % 64 == 32).
-  auto full = [&](int ch) { return ch * kSgKC + kSgKC <= g.in_dim; };
-  u32x4 wreg[SPT];
-  // In a half chunk (in_dim % 64 == 32) the upper 32 columns of the staged
-  // weights are zero, so the second k step adds nothing.
-  auto load_w = [&](int ch) {
-    const int back = full(ch) ? 0 : 32;
-#pragma unroll
-    for (int s = 0; s < SPT; ++s) {
-      const int part = (wdst[s] % kSgRowB) / 16;
-      wreg[s] = *(const u32x4*)(wsrc[s] + ch * kSgKC - (part < 4 ? 0 : back));
-    }
-  };
-  auto store_w = [&](int ch, int buf) {
-    const bool f = full(ch);
-#pragma unroll
-    for (int s = 0; s < SPT; ++s) {
-      const int part = (wdst[s] % kSgRowB) / 16;
-      const u32x4 v = (f || part < 4) ? wreg[s] : u32x4{0u, 0u, 0u, 0u};
-      *(u32x4*)(&wl[buf][wdst[s]]) = v;
-    }
-  };
-  bf16x8_t A[2][kSgTiles], An[2][kSgTiles];
-  auto load_a = [&](bf16x8_t (&a)[2][kSgTiles], int ch) {
-    // In a half chunk the second half repeats the first (in bounds, unused).
-    const int hi = full(ch) ? 32 : 0;
-#pragma unroll
-    for (int t = 0; t < kSgTiles; ++t) {
-      a[0][t] = load8(xr[t] + ch * kSgKC);
-      a[1][t] = load8(xr[t] + ch * kSgKC + hi);
-    }
+    for (int s = 0; s < LPW; ++s)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[s] + ch * 32),
+          (__attribute__((address_space(3))) void*)&lds[stage][(wave * LPW + s) * 1024],
+          16, 0, 0);
   };
 
-  f32x4_t acc[kSgTiles][NT];
+  f32x4_t acc[NTW][4];
 #pragma unroll
-  for (int t = 0; t < kSgTiles; ++t)
+  for (int j = 0; j < NTW; ++j)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[t][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) acc[j][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // The first chunk's token rows are requested before its weights, so that
-  // the weight store's wait leaves no load in flight when the loop starts.
-  load_a(A, 0);
-  load_w(0);
-  store_w(0, 0);
-  __syncthreads();
+  // Chunks past the last one re-request the last chunk into a stage nobody
+  // reads, so every wave always has LPW loads per chunk in flight and the
+  // wait count below is exact.
+  issue(0, 0);
+  issue(min(1, nch - 1), 1);
+  int st = 0;
   for (int ch = 0; ch < nch; ++ch) {
-    // Request the next chunk; the last chunk requests itself again (in
-    // bounds, unused), so the loads carry no branch and the wait counts
-    // stay exact.
-    const int nx = min(ch + 1, nch - 1);
-    load_w(nx);
-    load_a(An, nx);
-    // Weight fragments of the second k step are read from LDS while the
-    // first step's MFMAs run.
-    const uint8_t* wb = wl[ch & 1] + c * kSgRowB + kq * 2;
-    bf16x8_t B0[NT], B1[NT];
+    // Own loads of chunk ch done (those of ch + 1 may still fly), then
+    // everyone's: the block is complete and the stage read at ch - 1 free.
+    // (A bare s_barrier: a fence here would wait for every load.)
+    __builtin_amdgcn_s_waitcnt((LPW & 15) | ((LPW >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();
+    const int st2 = st == 0 ? 2 : st - 1;  // (ch + 2) % 3
+    issue(min(ch + 2, nch - 1), st2);
+    const uint8_t* sb = &lds[st][lane * 16];
+    bf16x8_t xa[4];
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      B0[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(wb + j * 16 * kSgRowB));
+    for (int t = 0; t < 4; ++t)
+      xa[t] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(sb + (wr * 4 + t) * 1024));
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      B1[j] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(wb + j * 16 * kSgRowB + 64));
+    for (int j = 0; j < NTW; ++j) {
+      const bf16x8_t wf = __builtin_bit_cast(
+          bf16x8_t, *(const u32x4*)(sb + (16 + wc * NTW + j) * 1024));
 #pragma unroll
-      for (int t = 0; t < kSgTiles; ++t)
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][t], B0[j], acc[t][j],
-                                                            0, 0, 0);
+      for (int t = 0; t < 4; ++t)
+        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xa[t], acc[j][t], 0, 0, 0);
     }
+    // Fragment reads run two weight tiles ahead of the MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int t = 0; t < kSgTiles; ++t)
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][t], B1[j], acc[t][j],
-                                                            0, 0, 0);
-    // Into the buffer no wave reads in this chunk (after the last chunk, a
-    // copy nobody reads).
-    store_w(nx, (ch + 1) & 1);
-    // Order: next chunk's global loads, first-step weight reads, first-step
-    // MFMAs interleaved with the second step's reads, second-step MFMAs,
-    // weight stores.
-    __builtin_amdgcn_sched_group_barrier(0x020, SPT + 2 * kSgTiles, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, kSgTiles, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int j = 0; j < NTW; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (j + 2 < NTW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kSgTiles * NT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, SPT, 0);
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int t = 0; t < kSgTiles; ++t) A[ks][t] = An[ks][t];
+    st = st == 2 ? 0 : st + 1;
   }
+  // No load may still be writing this workgroup's LDS when it exits.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
-  // Epilogue: lane c holds feature c of 4 tokens per tile.
-  const float gk = g.norm ? g.norm[c] : 1.f;
-  const float gq = g.norm ? g.norm[16 + c] : 1.f;
-  float ks16[16];
+  // Epilogue. Lane l: features f_v = 4 (l / 16) + v of token l % 16.
+  const int f0 = (lane >> 4) * 4;
+  float gk[4], gq[4], sp[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ks16[r] = r < g.n_sink ? g.sinks[r * 16 + c] : 0.f;
-  const float inv_sqrt = 0.25f;  // 1 / sqrt(16)
+  for (int v = 0; v < 4; ++v) {
+    gk[v] = g.norm ? g.norm[f0 + v] : 1.f;
+    gq[v] = g.norm ? g.norm[16 + f0 + v] : 1.f;
+    // A operand of the sink MFMA v: row c (sink), k = l / 16 (feature f_v).
+    sp[v] = c < g.n_sink ? gq[v] * g.sinks[c * 16 + f0 + v] : 0.f;
+  }
+  bool sink_ok[4];
 #pragma unroll
-  for (int hp = 0; hp < HP; ++hp) {
-    const int h = min(cg * HP + hp, g.H - 1);
-    const bool live = cg * HP + hp < g.H;
+  for (int i = 0; i < 4; ++i) sink_ok[i] = f0 + i < g.n_sink;
+#pragma unroll
+  for (int hp = 0; hp < C::HPW; ++hp) {
+    const int hv = h0 + wc * C::HPW + hp;
+    const bool live = hv < g.H;
+    const int h = min(hv, g.H - 1);
     float bj[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) bj[j] = g.b ? g.b[h * G + j] : 0.f;
     float* out = g.score + ((size_t)b * g.H + h) * g.cap + g.slot_begin;
-    // One token (row i of tile t) at a time; the accumulator values are
-    // copied out first so that no register array is indexed dynamically.
-    auto token = [&](const f32x4_t (&tile)[1 + G], int t, int i) {
-      float kc = tile[0][0], qv[G];
-      if (i == 1) kc = tile[0][1];
-      if (i == 2) kc = tile[0][2];
-      if (i == 3) kc = tile[0][3];
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const f32x4_t v = tile[1 + j];
-        qv[j] = i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-      }
-      const float kn = gk * kc * rsqrtf(row_sum16(kc * kc) * (1.f / 16.f) + kSgEps);
+    for (int t = 0; t < 4; ++t) {
+      const f32x4_t kt = acc[hp * (1 + G)][t];
+      const float ik = rsqrtf(xsum(kt[0] * kt[0] + kt[1] * kt[1] + kt[2] * kt[2] +
+                                   kt[3] * kt[3]) * (1.f / 16.f) + kSgEps);
+      float kg[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) kg[v] = gq[v] * gk[v] * kt[v] * ik;
       float best = 0.f;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const float qc = qv[j];
-        const float qn = gq * qc * rsqrtf(row_sum16(qc * qc) * (1.f / 16.f) + kSgEps);
-        const float a = row_sum16(qn * kn) * inv_sqrt;
-        float pr[16];
+        const f32x4_t qt = acc[hp * (1 + G) + 1 + j][t];
+        const float iq = rsqrtf(xsum(qt[0] * qt[0] + qt[1] * qt[1] + qt[2] * qt[2] +
+                                     qt[3] * qt[3]) * (1.f / 16.f) + kSgEps);
+        const float a = xsum(qt[0] * kg[0] + qt[1] * kg[1] + qt[2] * kg[2] +
+                             qt[3] * kg[3]) * iq * 0.25f;
+        f32x4_t cs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = qn * ks16[r];
-        float cs = reduce_scatter16(pr, c) * inv_sqrt;  // sink c's logit
-        cs = c < g.n_sink ? cs : -__builtin_inff();
-        const float m = fmaxf(a, row_max16(cs));
-        const float ssum = row_sum16(__expf(cs - m));
+        for (int v = 0; v < 4; ++v)
+          cs = __builtin_amdgcn_mfma_f32_16x16x4f32(sp[v], qt[v], cs, 0, 0, 0);
+        float cl[4], m = a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cl[i] = sink_ok[i] ? cs[i] * iq * 0.25f : -__builtin_inff();
+          m = fmaxf(m, cl[i]);
+        }
+        m = xmax(m);
+        const float e = xsum(__expf(cl[0] - m) + __expf(cl[1] - m) + __expf(cl[2] - m) +
+                             __expf(cl[3] - m));
         const float ea = __expf(a - m);
-        best = fmaxf(best, ea / (ea + ssum + bj[j] * __expf(-m)));
+        best = fmaxf(best, ea / (ea + e + bj[j] * __expf(-m)));
       }
-      const int r = r0 + t * 16 + 4 * (lane >> 4) + i;
-      if (live && c == 0 && r < rows) out[r] = best;
-    };
-#pragma unroll
-    for (int t = 0; t < kSgTiles; ++t) {
-      f32x4_t ht[1 + G];
-#pragma unroll
-      for (int j = 0; j <= G; ++j) ht[j] = acc[t][hp * (1 + G) + j];
-      for (int i = 0; i < 4; ++i) token(ht, t, i);
+      const int r = tok0 + wr * 64 + t * 16 + c;
+      if (live && lane < 16 && r < rows) out[r] = best;
     }
   }
 }
@@ -564,17 +482,17 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
 hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
   const int rows = g.slot_end - g.slot_begin;
   if (rows <= 0) return hipSuccess;
-  const int nb = (rows + kSgRowsWG - 1) / kSgRowsWG;
-  const int hp = sg_heads(g.G);
-  const int ncg = (g.H + hp - 1) / hp;
-  const long long wgs = (long long)nb * g.batch * ncg;
-  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int nb = (rows + kSgTok - 1) / kSgTok;
   switch (g.G) {
 #define KVE_SG(GG)                                                           \
-    case GG:                                                                 \
-      hipLaunchKernelGGL((sink_gate_kernel<GG, sg_heads(GG)>),               \
-                         dim3((unsigned)wgs), dim3(256), 0, s, g, nb, ncg);  \
-      break;
+    case GG: {                                                               \
+      const int ncg = (g.H + 2 * SgCfg<GG>::HPW - 1) / (2 * SgCfg<GG>::HPW); \
+      const long long wgs = (long long)nb * g.batch * ncg;                   \
+      if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;                   \
+      hipLaunchKernelGGL((sink_gate_kernel<GG>), dim3((unsigned)wgs),        \
+                         dim3(512), 0, s, g, nb, ncg);                       \
+      break;                                                                 \
+    }
     KVE_SG(1) KVE_SG(2) KVE_SG(3) KVE_SG(4) KVE_SG(5) KVE_SG(6) KVE_SG(7) KVE_SG(8)
 #undef KVE_SG
     default: return hipErrorInvalidValue;
