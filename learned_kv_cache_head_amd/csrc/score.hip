@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
 // bytes land at base + 16 l), one 1 KB block per 16-row x 32-k MFMA
 // fragment, so the fragment reads are linear and conflict-free. Chunks of
 // 32 k go through a 3-stage ring: chunk ch + 2 is requested while chunk ch
-// is multiplied. Workgroup ids are mapped so that the head groups of a token
+// is multiplied (a fourth stage, all 160 KB of LDS, measured no faster). Workgroup ids are mapped so that the head groups of a token
 // block run back to back on one XCD and share its hidden states in L2.
 //
 // The MFMA takes W as A and x as B, so a lane ends with 4 features (rows
@@ -350,17 +350,19 @@ void sink_gate_kernel(SinkGateLaunch g, int nb, int ncg) {
   // Chunks past the last one re-request the last chunk into a stage nobody
   // reads, so every wave always has LPW loads per chunk in flight and the
   // wait count below is exact.
-  issue(0, 0);
-  issue(min(1, nch - 1), 1);
+  constexpr int AHEAD = kSgStages - 1;        // chunks in flight
+  constexpr int NWAIT = (AHEAD - 1) * LPW;     // loads allowed to fly on
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) issue(min(i, nch - 1), i);
   int st = 0;
   for (int ch = 0; ch < nch; ++ch) {
-    // Own loads of chunk ch done (those of ch + 1 may still fly), then
+    // Own loads of chunk ch done (later chunks' may still fly), then
     // everyone's: the block is complete and the stage read at ch - 1 free.
     // (A bare s_barrier: a fence here would wait for every load.)
-    __builtin_amdgcn_s_waitcnt((LPW & 15) | ((LPW >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((NWAIT & 15) | ((NWAIT >> 4) << 14) | (7 << 4) | (15 << 8));
     __builtin_amdgcn_s_barrier();
-    const int st2 = st == 0 ? 2 : st - 1;  // (ch + 2) % 3
-    issue(min(ch + 2, nch - 1), st2);
+    const int st2 = st == 0 ? kSgStages - 1 : st - 1;  // (ch + AHEAD) % stages
+    issue(min(ch + AHEAD, nch - 1), st2);
     const uint8_t* sb = &lds[st][lane * 16];
     bf16x8_t xa[4];
 #pragma unroll
@@ -381,7 +383,7 @@ void sink_gate_kernel(SinkGateLaunch g, int nb, int ncg) {
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       if (j + 2 < NTW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    st = st == 2 ? 0 : st + 1;
+    st = st == kSgStages - 1 ? 0 : st + 1;
   }
   // No load may still be writing this workgroup's LDS when it exits.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
