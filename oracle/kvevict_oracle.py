@@ -65,6 +65,12 @@ Readings where the pages leave a step open (also listed in the design notes):
   gate lies in [0, 1] for b >= 0 and the no-denominator variant is a
   sigmoid), one shared set of sink keys per layer, and the maximum over the
   G query heads of a KV head.
+* Stochastic eviction (ForesightKV): the pool is the 2r lowest-ranked
+  candidates for r evictions; the page weights the draws by the negated
+  scores, read here as a softmax over -key (a multinomial over logits, the
+  form its policy-gradient training needs, defined for any real score); the
+  r draws without replacement are realised by Gumbel-top-k with the noise
+  passed in, sums rounded to float32, equal sums evicting the older token.
 * Stateful scorer: the Hedgehog variant with projection width P = d/2
   (features of 2P entries), scalar affine gate preactivations with biases, no
   output gate, soft-cap, norm or skip connection; the read-out delay equals
@@ -87,7 +93,7 @@ __all__ = [
     "hedgehog", "MlstmWeights", "mlstm_features", "mlstm_readout",
     "MlstmScorer", "mlstm_scores_parallel",
     "prefill_ranks", "prefill_cutoffs", "prefill_mask", "prefill_attention",
-    "rms_norm", "SinkGateWeights", "sink_gate_score",
+    "rms_norm", "SinkGateWeights", "sink_gate_score", "select_keep_stochastic",
     "eligible_mask",
     "select_keep", "compaction_sources", "compact_slice", "attention_probs", "decode_attention", "OracleLayer",
     "closed_form_retained", "cache_bytes_per_token",
@@ -374,6 +380,48 @@ def select_keep(score32: np.ndarray, pos: np.ndarray, length: int,
     order = np.lexsort((pos[cand], s))      # ascending score, then position
     evicted = np.zeros(length, dtype=bool)
     evicted[cand[order[:r]]] = True
+    return np.nonzero(~evicted)[0].astype(np.int64)
+
+
+def select_keep_stochastic(score32: np.ndarray, pos: np.ndarray,
+                           length: int, n_keep: int, sinks: int, window: int,
+                           gumbel: np.ndarray,
+                           log_gamma: Optional[float] = None) -> np.ndarray:
+    """Slots kept under ForesightKV's stochastic eviction (summary page,
+    "Key Contributions" item 4 and "Methodology in Plain English"): with
+    r = length - n_keep entries to evict, the 2r lowest-ranked candidates
+    (the order of ``select_keep``; all candidates if fewer) form the pool,
+    and r of them are drawn without replacement with probability
+    proportional to exp(-key), key being the ranking key of
+    ``select_keep``.
+
+    The draw is the Gumbel-top-k realisation of that sampling (successive
+    draws without replacement from a softmax equal the r largest of
+    logit + independent standard Gumbel noise): ``gumbel[slot]`` is the
+    noise of the entry in that slot, passed in. Each pool entry gets the
+    float32 sum -key + gumbel; the r largest are evicted, equal sums taking
+    the lower position first. Zero noise evicts the r lowest keys, i.e.
+    ``select_keep``.
+
+    Returns the kept slot indices in ascending order (int64).
+    """
+    pos = np.asarray(pos)[:length]
+    key = static_priority(np.asarray(score32, dtype=np.float32)[:length],
+                          pos, log_gamma) + np.float32(0.0)
+    if n_keep >= length:
+        return np.arange(length, dtype=np.int64)
+    r = length - n_keep
+    cand = np.nonzero(eligible_mask(pos, sinks, window))[0]
+    if cand.size < r:
+        raise ValueError("not enough eligible entries to evict")
+    order = np.lexsort((pos[cand], key[cand]))   # ascending key, then position
+    pool = cand[order[:min(2 * r, cand.size)]]
+    perturbed = (-key[pool]).astype(np.float32) + \
+        np.asarray(gumbel, dtype=np.float32)[pool]
+    perturbed = perturbed.astype(np.float32) + np.float32(0.0)
+    draw = np.lexsort((pos[pool], -perturbed.astype(np.float64)))
+    evicted = np.zeros(length, dtype=bool)
+    evicted[pool[draw[:r]]] = True
     return np.nonzero(~evicted)[0].astype(np.int64)
 
 

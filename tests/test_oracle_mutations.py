@@ -327,3 +327,69 @@ def test_sink_gate_mutants_fail(fn):
         except AssertionError:
             failed += 1
     assert failed >= 1
+
+
+# --- stochastic eviction mutants ---------------------------------------------
+
+def _stoch(score32, pos, length, n_keep, sinks, window, gumbel, log_gamma=None,
+           pool_mult=2, sign=-1.0, newer_first=False):
+    pos = np.asarray(pos)[:length]
+    key = O.static_priority(np.asarray(score32, np.float32)[:length], pos,
+                            log_gamma)
+    if n_keep >= length:
+        return np.arange(length)
+    r = length - n_keep
+    cand = np.nonzero(O.eligible_mask(pos, sinks, window))[0]
+    order = np.lexsort((pos[cand], key[cand]))
+    pool = cand[order[:min(pool_mult * r, cand.size)]]
+    pert = (np.float32(sign) * key[pool]).astype(np.float32) + \
+        np.asarray(gumbel, np.float32)[pool]
+    tie = -pos[pool] if newer_first else pos[pool]
+    draw = np.lexsort((tie, -pert.astype(np.float64)))
+    ev = np.zeros(length, bool)
+    ev[pool[draw[:r]]] = True
+    return np.nonzero(~ev)[0]
+
+
+def stoch_greedy_pool(*a, **k):
+    """Pool of r: plain greedy eviction, no sampling."""
+    return _stoch(*a, pool_mult=1, **k)
+
+
+def stoch_all_candidates(*a, **k):
+    """Draws over every candidate instead of the 2r lowest."""
+    return _stoch(*a, pool_mult=10 ** 9, **k)
+
+
+def stoch_sign_flipped(*a, **k):
+    """Weights exp(+score): the highest-scoring pool entries go first."""
+    return _stoch(*a, sign=1.0, **k)
+
+
+def stoch_ties_newer_first(*a, **k):
+    """Equal perturbed sums evict the newer token first."""
+    return _stoch(*a, newer_first=True, **k)
+
+
+def test_stochastic_reference_mutant_passes():
+    """The helper with the oracle's settings passes every check (so the
+    mutants below fail for their planted change alone)."""
+    for check in (P.check_stochastic_zero_noise_is_greedy,
+                  P.check_stochastic_pool, P.check_stochastic_hand):
+        check(_stoch)
+
+
+@pytest.mark.parametrize("fn", [stoch_greedy_pool, stoch_all_candidates,
+                                stoch_sign_flipped, stoch_ties_newer_first],
+                         ids=["greedy-pool", "all-candidates", "sign-flipped",
+                              "ties-newer-first"])
+def test_stochastic_mutants_fail(fn):
+    failed = 0
+    for check in (P.check_stochastic_zero_noise_is_greedy,
+                  P.check_stochastic_pool, P.check_stochastic_hand,
+                  P.check_stochastic_distribution):
+        try:
+            check(fn)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1

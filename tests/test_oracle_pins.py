@@ -917,3 +917,99 @@ def test_sink_gate_range_and_monotone_in_b():
     assert np.all((g1 > 0) & (g1 < 1))
     w.b = w.b + 1.0
     assert np.all(O.sink_gate_score(x, w) < g1)
+
+
+# ---------------------------------------------------------------------------
+# Stochastic eviction (ForesightKV's Top-K multinomial rule)
+# ---------------------------------------------------------------------------
+
+def check_stochastic_zero_noise_is_greedy(fn):
+    """Zero noise evicts the r lowest keys of the pool, which are the r
+    lowest of all candidates: the deterministic rule (itself pinned by brute
+    force above), over 3-valued scores with ties at the cut and decay."""
+    rng = np.random.default_rng(71)
+    for trial in range(300):
+        n = int(rng.integers(4, 24))
+        sc = rng.integers(0, 3, n).astype(np.float32)
+        pos = rng.permutation(n + 5)[:n]
+        S, W = int(rng.integers(0, 3)), int(rng.integers(0, 4))
+        lg = None if trial % 3 else -0.25
+        n_cand = int(O.eligible_mask(pos, S, W).sum())
+        if n_cand == 0:
+            continue
+        n_keep = n - int(rng.integers(1, n_cand + 1))
+        got = fn(sc, pos, n, n_keep, S, W, np.zeros(n, np.float32),
+                 log_gamma=lg)
+        ref = O.select_keep(sc, pos, n, n_keep, S, W, log_gamma=lg)
+        np.testing.assert_array_equal(got, ref)
+
+
+def check_stochastic_pool(fn):
+    """Whatever the noise: exactly r candidates are evicted, all from the 2r
+    lowest (brute-force count of candidates ranked below each), and the
+    sinks and the window stay."""
+    rng = np.random.default_rng(72)
+    for _ in range(300):
+        n = int(rng.integers(6, 30))
+        sc = rng.integers(0, 4, n).astype(np.float32)
+        pos = rng.permutation(n)
+        S, W = 2, 3
+        cand = np.nonzero(O.eligible_mask(pos, S, W))[0]
+        r = int(rng.integers(1, cand.size + 1))
+        g = (rng.standard_normal(n) * 50).astype(np.float32)
+        keep = fn(sc, pos, n, n - r, S, W, g)
+        evicted = np.setdiff1d(np.arange(n), keep)
+        assert evicted.size == r and np.all(np.isin(evicted, cand))
+        for e in evicted:
+            below = sum(1 for c in cand if (sc[c], pos[c]) < (sc[e], pos[e]))
+            assert below < 2 * r
+
+
+def check_stochastic_distribution(fn):
+    """The draw follows successive sampling without replacement with
+    probability proportional to exp(-score) over the pool: frequencies of
+    each evicted pair over 20000 numpy Gumbel draws against the exact
+    two-draw probabilities p_a p_b (1/(1 - p_a) + 1/(1 - p_b))."""
+    sc = np.array([9.0, 0.3, -0.5, 1.2, 0.0, 2.0, 9.0], np.float32)
+    pos = np.arange(7)
+    pool = [1, 2, 3, 4]        # the 4 lowest of candidates 1..5 (S = W = 1)
+    w = np.exp(-sc[pool].astype(np.float64))
+    p = dict(zip(pool, w / w.sum()))
+    rng = np.random.default_rng(73)
+    N = 20000
+    counts = {}
+    for _ in range(N):
+        keep = fn(sc, pos, 7, 5, 1, 1, rng.gumbel(size=7).astype(np.float32))
+        ev = tuple(np.setdiff1d(pos, keep))
+        counts[ev] = counts.get(ev, 0) + 1
+    assert set(counts) <= set(itertools.combinations(pool, 2))
+    for a, b in itertools.combinations(pool, 2):
+        exact = p[a] * p[b] * (1 / (1 - p[a]) + 1 / (1 - p[b]))
+        sigma = math.sqrt(exact * (1 - exact) / N)
+        assert abs(counts.get((a, b), 0) / N - exact) < 5 * sigma + 1e-4
+
+
+def check_stochastic_hand(fn):
+    """Hand case: scores [5, 1, 2, 0, 3, 4] at positions 0..5, S = 1, W = 1,
+    keep 4 (r = 2). Candidates 1..4, pool = the 4 lowest = {3 (0), 1 (1),
+    2 (2), 4 (3)}. Noise [0, 0.5, 3.5, 0.25, 1.0, 0]: sums -key + g = 1: -0.5,
+    2: 1.5, 3: 0.25, 4: -2.0. The two largest, slots 2 and 3, are evicted."""
+    keep = fn(np.array([5, 1, 2, 0, 3, 4], np.float32), np.arange(6), 6, 4, 1,
+              1, np.array([0, 0.5, 3.5, 0.25, 1.0, 0], np.float32))
+    np.testing.assert_array_equal(keep, [0, 1, 4, 5])
+
+
+def test_stochastic_zero_noise_is_greedy():
+    check_stochastic_zero_noise_is_greedy(O.select_keep_stochastic)
+
+
+def test_stochastic_pool():
+    check_stochastic_pool(O.select_keep_stochastic)
+
+
+def test_stochastic_distribution():
+    check_stochastic_distribution(O.select_keep_stochastic)
+
+
+def test_stochastic_hand_case():
+    check_stochastic_hand(O.select_keep_stochastic)
