@@ -94,13 +94,25 @@ typedef struct {
  * log_gamma: NULL, or a device array [n_kv_heads] of float32 log decay
  * factors (KVpop Eq. 5 with decay step 1, gamma in (0, 1)): eligible entries
  * are then ranked by the static priority score - position * log_gamma[h]
- * (KVpop Appendix B.3, Eq. 20), both operations rounded to float32. */
+ * (KVpop Appendix B.3, Eq. 20), both operations rounded to float32.
+ * gumbel: NULL (deterministic eviction), or a device array
+ * [batch][n_kv_heads][capacity] of float32 standard Gumbel noise, one value
+ * per cache slot, for ForesightKV's stochastic eviction (summary page, "Key
+ * Contributions" item 4): to evict r entries, the 2r lowest-ranked
+ * candidates (all candidates if fewer) form a pool and r of them are drawn
+ * without replacement with probability proportional to exp(-key). The draw
+ * is the Gumbel-top-k one: the r pool entries with the largest float32 sum
+ * -key + gumbel[slot] are evicted, equal sums taking the lower position
+ * first. Zero noise gives the deterministic rule. The caller refreshes the
+ * noise before each evicting call; it must be finite. Used by
+ * kve_select_evict and kve_step; the prefill entry points reject it. */
 typedef struct {
   int32_t budget;
   int32_t sinks;
   int32_t window;
   int32_t evict_len;
   const float* log_gamma;
+  const float* gumbel;
 } kve_policy;
 
 /* Device pointers of one layer's cache (layouts above). scorer_state is

@@ -45,7 +45,7 @@ class _Shape(ctypes.Structure):
 class _Policy(ctypes.Structure):
     _fields_ = [("budget", ctypes.c_int32), ("sinks", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("evict_len", ctypes.c_int32),
-                ("log_gamma", ctypes.c_void_p)]
+                ("log_gamma", ctypes.c_void_p), ("gumbel", ctypes.c_void_p)]
 
 
 class _Cache(ctypes.Structure):
@@ -174,16 +174,19 @@ class Shape:
 @dataclass(frozen=True)
 class Policy:
     """Budget B, sinks S, window W, eviction length L; optional per-KV-head
-    float32 log decay factors (a device tensor [n_kv_heads])."""
+    float32 log decay factors (a device tensor [n_kv_heads]); optional
+    float32 Gumbel noise per cache slot (a device tensor
+    [batch][n_kv_heads][capacity]) for stochastic eviction."""
     budget: int
     sinks: int
     window: int
     evict_len: int
     log_gamma: object = None
+    gumbel: object = None
 
     def c(self) -> _Policy:
         return _Policy(self.budget, self.sinks, self.window, self.evict_len,
-                       _ptr(self.log_gamma))
+                       _ptr(self.log_gamma), _ptr(self.gumbel))
 
 
 class CacheTensors:

@@ -152,11 +152,13 @@ __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const float* score, const int32_t* pos, const float* log_gamma, int H,
-    int cap, int len, int n_keep, int S, int W, int32_t* keep) {
+    const float* score, const int32_t* pos, const float* log_gamma,
+    const float* gumbel, int H, int cap, int len, int n_keep, int S, int W,
+    int32_t* keep) {
   const size_t slice = blockIdx.x;
   const float* sc = score + slice * (size_t)cap;
   const int32_t* ps = pos + slice * (size_t)cap;
+  const float* gs = gumbel ? gumbel + slice * (size_t)cap : nullptr;
   int32_t* out = keep + slice * (size_t)n_keep;
   const int tid = threadIdx.x;
 
@@ -191,26 +193,62 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // float32 separately (no fused multiply-add).
   const float lg = log_gamma ? log_gamma[slice % H] : 0.f;
   const bool decay = log_gamma != nullptr;
-  auto skey = [&](int c) {
+  auto fkey = [&](int c) {
     float r = sc[c];
     if (decay) r = __fsub_rn(r, __fmul_rn((float)ps[c], lg));
-    return score_key(r);
+    return r;
+  };
+  auto skey = [&](int c) { return score_key(fkey(c)); };
+  auto pkey = [&](int c) { return (uint32_t)ps[c]; };
+
+  // The `count` entries with take() that come first in (key, position)
+  // order: cut key `thr`, and among entries with key thr those at positions
+  // <= `pthr` (all of them unless the cut falls inside a tie).
+  auto cut = [&](uint32_t count, auto key_of, auto take, uint32_t* thr_out,
+                 uint32_t* pthr_out) {
+    uint32_t thr, need, count_eq;
+    radix_select(len, count, key_of, take, hist, wsum, sh, &thr, &need,
+                 &count_eq);
+    uint32_t pthr = 0xffffffffu;
+    if (need < count_eq) {
+      auto tied = [&](int c) { return take(c) && key_of(c) == thr; };
+      uint32_t pneed, pcount;
+      radix_select(len, need, pkey, tied, hist, wsum, sh, &pthr, &pneed,
+                   &pcount);
+    }
+    *thr_out = thr;
+    *pthr_out = pthr;
+  };
+  auto before = [&](uint32_t k, int c, uint32_t thr, uint32_t pthr) {
+    return k < thr || (k == thr && (uint32_t)ps[c] <= pthr);
   };
 
-  // 2. Cut score key.
-  uint32_t thr, need, count_eq;
-  radix_select(len, r, skey, is_cand, hist, wsum, sh, &thr, &need, &count_eq);
-
-  // 3. Among candidates with key thr, evict the `need` (>= 1) oldest: all of
-  // them unless the cut falls inside the tie.
-  uint32_t pthr = 0xffffffffu;
-  if (need < count_eq) {
-    auto tied = [&](int c) { return is_cand(c) && skey(c) == thr; };
-    auto pkey = [&](int c) { return (uint32_t)ps[c]; };
-    uint32_t pneed, pcount;
-    radix_select(len, need, pkey, tied, hist, wsum, sh, &pthr, &pneed,
-                 &pcount);
+  // 2-3. Deterministic: evict the r lowest candidates.
+  uint32_t thr, pthr;
+  // Stochastic (ForesightKV): the pool is the 2r lowest candidates; evict
+  // the r pool entries with the largest float32 sum -key + noise, i.e. the
+  // smallest descending key, equal sums the lower position first.
+  uint32_t gthr = 0, gpthr = 0;
+  auto dkey = [&](int c) { return ~score_key(__fadd_rn(-fkey(c), gs[c])); };
+  if (!gs) {
+    cut(r, skey, is_cand, &thr, &pthr);
+  } else {
+    __shared__ uint32_t ncand_sh;
+    if (tid == 0) ncand_sh = 0;
+    __syncthreads();
+    uint32_t nc = 0;
+    for (int c = tid; c < len; c += kSelThreads) nc += is_cand(c) ? 1u : 0u;
+    atomicAdd(&ncand_sh, nc);
+    __syncthreads();
+    const uint32_t pool = min(2u * r, ncand_sh);
+    cut(pool, skey, is_cand, &thr, &pthr);
+    auto in_pool = [&](int c) { return is_cand(c) && before(skey(c), c, thr, pthr); };
+    cut(r, dkey, in_pool, &gthr, &gpthr);
   }
+  auto evicted = [&](int c) {
+    if (!is_cand(c) || !before(skey(c), c, thr, pthr)) return false;
+    return !gs || before(dkey(c), c, gthr, gpthr);
+  };
 
   // 4. Kept slots, ascending.
   __shared__ uint32_t scan_sh[kSelWaves];
@@ -218,15 +256,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   for (int base = 0; base < len; base += kSelThreads) {
     const int c = base + tid;
     bool kept = false;
-    if (c < len) {
-      kept = true;
-      if (is_cand(c)) {
-        const uint32_t k = skey(c);
-        if (k < thr) kept = false;
-        else if (k == thr && (uint32_t)ps[c] <= pthr)
-          kept = false;
-      }
-    }
+    if (c < len) kept = !evicted(c);
     uint32_t tot;
     const uint32_t idx = carry + block_excl_count(kept, scan_sh, &tot);
     if (kept && idx < (uint32_t)n_keep) out[idx] = c;
@@ -328,11 +358,12 @@ hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
 }
 
 hipError_t launch_select(const float* score, const int32_t* pos,
-                         const float* log_gamma, int H, int slices, int cap,
-                         int len, int n_keep, int S, int W, int32_t* keep,
-                         hipStream_t s) {
+                         const float* log_gamma, const float* gumbel, int H,
+                         int slices, int cap, int len, int n_keep, int S,
+                         int W, int32_t* keep, hipStream_t s) {
   hipLaunchKernelGGL(select_kernel, dim3(slices), dim3(kSelThreads), 0, s,
-                     score, pos, log_gamma, H, cap, len, n_keep, S, W, keep);
+                     score, pos, log_gamma, gumbel, H, cap, len, n_keep, S, W,
+                     keep);
   return hipGetLastError();
 }
 

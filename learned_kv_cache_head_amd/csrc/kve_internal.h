@@ -65,9 +65,9 @@ hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
                          hipStream_t s);
 
 hipError_t launch_select(const float* score, const int32_t* pos,
-                         const float* log_gamma, int H, int slices, int cap,
-                         int len, int n_keep, int S, int W, int32_t* keep,
-                         hipStream_t s);
+                         const float* log_gamma, const float* gumbel, int H,
+                         int slices, int cap, int len, int n_keep, int S,
+                         int W, int32_t* keep, hipStream_t s);
 
 hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
                           int slices, int cap, int row_bytes, int len,

@@ -289,6 +289,7 @@ kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
   kve_status st = check_shape(shape);
   if (st != KVE_OK) return st;
   if ((st = check_policy(policy)) != KVE_OK) return st;
+  if (policy->gumbel) return KVE_ERR_UNSUPPORTED;  // deterministic ranks only
   if ((st = check_cache(cache)) != KVE_OK) return st;
   if (!rank || !tau) return KVE_ERR_INVALID_ARG;
   if (len < 1) return KVE_ERR_INVALID_ARG;
@@ -323,6 +324,7 @@ kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
   kve_status st = check_shape(shape);
   if (st != KVE_OK) return st;
   if ((st = check_policy(policy)) != KVE_OK) return st;
+  if (policy->gumbel) return KVE_ERR_UNSUPPORTED;  // deterministic ranks only
   if ((st = check_cache(cache)) != KVE_OK) return st;
   if (!rank || !tau || !q || !out) return KVE_ERR_INVALID_ARG;
   if (len < 1) return KVE_ERR_INVALID_ARG;
@@ -442,7 +444,8 @@ kve_status kve_select_evict(const kve_shape* shape, const kve_policy* policy,
     return KVE_ERR_POLICY;
   if (len == 0) return KVE_OK;
   return from_hip(kve::launch_select(
-      cache->score, cache->pos, policy->log_gamma, shape->n_kv_heads,
+      cache->score, cache->pos, policy->log_gamma, policy->gumbel,
+      shape->n_kv_heads,
       shape->batch * shape->n_kv_heads, shape->capacity, len, n_keep,
       policy->sinks, policy->window, keep_slots, stream));
 }
@@ -538,7 +541,8 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   }
   if (evict) {
     st = from_hip(kve::launch_select(
-        cache->score, cache->pos, policy->log_gamma, shape->n_kv_heads,
+        cache->score, cache->pos, policy->log_gamma, policy->gumbel,
+        shape->n_kv_heads,
         shape->batch * shape->n_kv_heads, shape->capacity, len, B,
         policy->sinks, policy->window, keep_slots, stream));
     if (st != KVE_OK) return st;

@@ -520,17 +520,26 @@ class OracleLayer:
     def n(self) -> int:
         return self.K.shape[2]
 
-    def _evict_to(self, n_keep: int) -> np.ndarray:
+    def _evict_to(self, n_keep: int,
+                  gumbel: Optional[np.ndarray] = None) -> np.ndarray:
+        """Cut every slice to n_keep entries: the deterministic rule, or
+        with ``gumbel`` ([b][H][>= n] noise by slot) the stochastic one."""
         b, H = self.K.shape[:2]
         keeps = np.empty((b, H, n_keep), dtype=np.int64)
         srcs = np.empty((b, H, n_keep), dtype=np.int64)
         lg = self.policy.log_gamma
         for bi in range(b):
             for h in range(H):
-                keeps[bi, h] = select_keep(self.score[bi, h], self.pos[bi, h],
-                                           self.n, n_keep, self.policy.sinks,
-                                           self.policy.window,
-                                           None if lg is None else lg[h])
+                lgh = None if lg is None else lg[h]
+                if gumbel is None:
+                    keeps[bi, h] = select_keep(
+                        self.score[bi, h], self.pos[bi, h], self.n, n_keep,
+                        self.policy.sinks, self.policy.window, lgh)
+                else:
+                    keeps[bi, h] = select_keep_stochastic(
+                        self.score[bi, h], self.pos[bi, h], self.n, n_keep,
+                        self.policy.sinks, self.policy.window,
+                        gumbel[bi, h], lgh)
                 srcs[bi, h] = compaction_sources(keeps[bi, h])
         idx = srcs[..., None]
         self.K = np.take_along_axis(self.K, idx, axis=2)
@@ -569,11 +578,13 @@ class OracleLayer:
         sc = np.asarray(score_32, np.float32)
         self.score[hit] = np.broadcast_to(sc[:, :, None], hit.shape)[hit]
 
-    def maybe_evict(self) -> Optional[np.ndarray]:
-        """Evict n - B entries once the cache reaches B + L."""
+    def maybe_evict(self, gumbel: Optional[np.ndarray] = None
+                    ) -> Optional[np.ndarray]:
+        """Evict n - B entries once the cache reaches B + L (with
+        ``gumbel``, by ForesightKV's stochastic rule)."""
         p = self.policy
         if self.n >= p.budget + p.evict_len:
-            return self._evict_to(p.budget)
+            return self._evict_to(p.budget, gumbel)
         return None
 
     def attend(self, q: np.ndarray):

@@ -25,7 +25,7 @@ __all__ = [
     "Workload", "WORKLOADS", "workload", "rng_for", "round_to_bf16_bits",
     "bf16_bits_to_f32", "draw_rows", "draw_mlp_weights", "draw_gate_weights",
     "draw_mlstm_weights", "draw_sink_gate_weights",
-    "initial_context", "step_inputs", "TENSOR_IDS",
+    "initial_context", "step_inputs", "TENSOR_IDS", "gumbel_noise",
 ]
 
 
@@ -301,6 +301,12 @@ def draw_sink_gate_weights(w: Workload, seed: int, layer: int,
             "norm": Stored(norm.astype(np.float32), "f32"),
             "sinks": Stored(sinks.astype(np.float32), "f32"),
             "b": Stored(b.astype(np.float32), "f32")}
+
+
+def gumbel_noise(rng: np.random.Generator, shape) -> np.ndarray:
+    """Standard Gumbel noise (numpy's generator), rounded once to float32:
+    the random input of stochastic eviction."""
+    return rng.gumbel(size=shape).astype(np.float32)
 
 
 def initial_context(w: Workload, seed: int, layer: int) -> dict:

@@ -139,17 +139,17 @@ class Tracker:
         if self.lay.prefill_compress() is not None:
             self._record_cut()
 
-    def step(self, pos, k, v, s, delayed=None):
+    def step(self, pos, k, v, s, delayed=None, gumbel=None):
         """Append the token at ``pos``; ``delayed`` = (u, scores [b][H])
         gives an earlier token its score (stateful scorers) before the
-        eviction check."""
+        eviction check; ``gumbel`` (noise by slot) makes it stochastic."""
         self.K[:, :, pos], self.V[:, :, pos], self.S[:, :, pos] = k, v, s
         self.lay.append(k, v, s)
         if delayed is not None:
             u, su = delayed
             self.S[:, :, u] = su
             self.lay.set_scores(u, su)
-        if self.lay.maybe_evict() is not None:
+        if self.lay.maybe_evict(gumbel) is not None:
             self._record_cut()
 
     def check_and_sync(self, gpu_pos):

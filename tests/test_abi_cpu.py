@@ -189,11 +189,13 @@ def test_step_rejects_bad_state():
 
 
 def test_policy_struct_layout_matches_header():
-    """kve_policy: four int32 fields, then the log_gamma pointer."""
-    assert ctypes.sizeof(kve._Policy) == 24
+    """kve_policy: four int32 fields, then the log_gamma and gumbel
+    pointers."""
+    assert ctypes.sizeof(kve._Policy) == 32
     assert kve._Policy.log_gamma.offset == 16
+    assert kve._Policy.gumbel.offset == 24
     p = kve.Policy(1024, 4, 128, 128).c()
-    assert p.log_gamma is None
+    assert p.log_gamma is None and p.gumbel is None
 
 
 def test_cache_and_scorer_struct_layout_matches_header():
@@ -297,6 +299,10 @@ def test_prefill_workspace_and_validation():
     nqb = (9000 + 63) // 64
     lists = 2 * 8 * nqb * 892 * 4
     assert wsb == (lists + 255) // 256 * 256 + 2 * 8 * nqb * 4
+    # stochastic eviction noise: the prefill ranks are deterministic only
+    p.gumbel = FAKE
+    assert sel(100) == 4
+    assert attn(100) == 4
 
 
 def test_sink_gate_rejects_bad_scorers():
