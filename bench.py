@@ -39,8 +39,22 @@ WORKLOAD_BY_NAME = {
 DEFAULT_WORKLOAD = "qwen3-4b-36layer-b96-B1024"
 ATTN_SOURCE = os.path.join(ROOT, "learned_kv_cache_head_amd", "csrc",
                            "attention.hip")
+SCORE_SOURCE = os.path.join(ROOT, "learned_kv_cache_head_amd", "csrc",
+                            "score.hip")
 METRIC = ("evict+decode tokens/s at budget B and achieved HBM GB/s vs "
           "MI355X peak")
+
+
+def calib_copy(dev) -> None:
+    """A plain elementwise copy of known size (1 GiB read, 1 GiB written),
+    the reference that scales the HBM byte counters."""
+    import torch
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def log(msg: str) -> None:
@@ -112,7 +126,7 @@ class Stack:
     """Per-layer caches, scorer weights, step runners and input pools."""
 
     def __init__(self, w, seed: int, pool_steps: int, dev, decay=False,
-                 scorer="mlp"):
+                 scorer="mlp", stochastic=False):
         import torch
         import learned_kv_cache_head_amd as kve
         import synthetic as syn
@@ -180,8 +194,17 @@ class Stack:
             st = kve.DecodeState(B, B, w.n0)
             self.caches.append(c)
             self.scorers.append(sc)
-            self.runners.append(kve.LayerStep(self.shape, self.policy, sc, c,
-                                              st, self.ws))
+            pol = self.policy
+            if stochastic:
+                # ForesightKV's stochastic eviction: standard Gumbel noise
+                # per slot, drawn once per layer (resident input).
+                u = torch.rand((b, H, self.shape.capacity), generator=torch.Generator(
+                    device=dev).manual_seed(seed * 1000 + l), device=dev)
+                gum = -torch.log(-torch.log(u.clamp_(1e-7, 1 - 1e-7)))
+                pol = kve.Policy(w.budget, w.sinks, w.window, w.evict_len,
+                                 log_gamma=self.policy.log_gamma, gumbel=gum)
+            self.runners.append(kve.LayerStep(self.shape, pol, sc, c, st,
+                                              self.ws))
             self.k_pool.append(dn((pool_steps, b, H, d), seed,
                                   (cfg, l, 1, T["k_new"]), torch.bfloat16, dev))
             self.v_pool.append(dn((pool_steps, b, H, d), seed,
@@ -472,6 +495,7 @@ def cpu_baseline_prefill(w, seed) -> dict:
 
 SINK_GATE_WORKLOAD = 5  # Qwen2.5-14B layer, 131072-token prompt
 SINK_GATE_RANK = 16     # D' = S = 16 (Fast KVzip section 3.4)
+SINK_GATE_WORKLOAD_NAME = "qwen2.5-14b-1layer-131k-sink-gate"
 
 
 def sink_gate_flops(n: int, D: int, H: int, G: int) -> int:
@@ -524,9 +548,13 @@ def run_sink_gate(args, dev) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+    if args.calib_copy:
+        calib_copy(dev)
     flops = sink_gate_flops(b * n, D, H, G)
     nbytes = sink_gate_bytes(b * n, D, H, G)
     achieved = flops / (ms * 1e-3) / 1e12
+    ratio = recorded_ratio(f"sink_gate_{SINK_GATE_WORKLOAD_NAME}.txt",
+                           SCORE_SOURCE, "score_source_sha256")
     result = {
         "metric": ("prefill gate tokens/s of one layer: low-rank "
                    "sink-attention gate scores of every prompt token"),
@@ -541,7 +569,7 @@ def run_sink_gate(args, dev) -> dict:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen2.5-14b-1layer-131k-sink-gate",
+        "config": {"workload": SINK_GATE_WORKLOAD_NAME,
                    "batch": b, "prompt_len": n, "hidden_dim": D,
                    "n_kv_heads": H, "n_q_heads": H * G,
                    "gate_rank": SINK_GATE_RANK, "n_sink": SINK_GATE_RANK,
@@ -550,7 +578,7 @@ def run_sink_gate(args, dev) -> dict:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": None if ratio is None else int(ratio * nbytes),
                      "kernel": "sink_gate_kernel (projections + gate)",
                      "algorithmic_flops_per_launch": int(flops),
                      "algorithmic_bytes_per_launch": int(nbytes),
@@ -598,12 +626,12 @@ def cpu_baseline_sink_gate(w, seed, sample: int = 8192) -> dict:
 # Recorded rocprofv3 traffic of the attention kernel
 # ---------------------------------------------------------------------------
 
-def traffic_ratio(workload: str):
-    """Measured HBM bytes over algorithmic bytes of one attention launch, from
-    the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE passes,
+def recorded_ratio(profile: str, source: str, sha_key: str):
+    """Measured HBM bytes over algorithmic bytes of one launch, from a
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE passes,
     each scaled by what the counter reads for a plain copy of known size), or
     None if there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     rec = {}
@@ -611,13 +639,19 @@ def traffic_ratio(workload: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             rec[k.strip()] = v.strip()
-    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    if rec.get("attention_source_sha256") != src:
+    src = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    if rec.get(sha_key) != src:
         return None
     try:
         return float(rec["traffic_over_algorithmic"])
     except (KeyError, ValueError):
         return None
+
+
+def traffic_ratio(workload: str):
+    """Recorded traffic ratio of the decode attention kernel."""
+    return recorded_ratio(f"decode_attn_{workload}_traffic.txt", ATTN_SOURCE,
+                          "attention_source_sha256")
 
 
 # ---------------------------------------------------------------------------
@@ -637,6 +671,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decay", action="store_true",
                     help="rank with KVpop temporal decay (static priority)")
+    ap.add_argument("--stochastic", action="store_true",
+                    help="ForesightKV stochastic eviction (Gumbel noise per "
+                         "slot in the policy)")
     ap.add_argument("--scorer", default="mlp", choices=["mlp", "mlstm"],
                     help="stateless MLP over [k; v], or the stateful mLSTM "
                          "scorer with delayed read-out")
@@ -686,7 +723,7 @@ def main() -> int:
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")
     t0 = time.perf_counter()
     stack = Stack(w, args.seed, pool, dev, decay=args.decay,
-                  scorer=args.scorer)
+                  scorer=args.scorer, stochastic=args.stochastic)
     log(f"set-up {time.perf_counter() - t0:.1f} s")
 
     for i in range(warmup):
@@ -739,12 +776,7 @@ def main() -> int:
     log(f"timed {steps} steps in {wall * 1e3:.1f} ms")
 
     if args.calib_copy:
-        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(dev)
 
     # Algorithmic bytes over the timed region.
     moved = {}
@@ -809,6 +841,7 @@ def main() -> int:
                               f"mlstm P={w.head_dim // 2} hedgehog, delayed "
                               f"read-out W={w.window}"),
                    "decay": bool(args.decay),
+                   "stochastic_eviction": bool(args.stochastic),
                    "parallelism": "none"},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
