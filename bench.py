@@ -35,6 +35,7 @@ WORKLOAD_BY_NAME = {
     "qwen3-4b-36layer-b96-B1024": 4,
     "qwen3-4b-36layer-b8-B2048": 3,
     "qwen3-4b-1layer-b16": 2,
+    "qwen2.5-14b-48layer-131k-gate": 5,
 }
 DEFAULT_WORKLOAD = "qwen3-4b-36layer-b96-B1024"
 ATTN_SOURCE = os.path.join(ROOT, "learned_kv_cache_head_amd", "csrc",
@@ -93,6 +94,9 @@ def score_bytes(w, scorer: str) -> int:
     weights once."""
     d, e, L, hid = w.head_dim, w.elem_bytes, w.evict_len, w.hidden
     slices = w.batch * w.n_kv
+    if scorer == "gate":
+        # the L buffered hidden states read, L scores written, weights once
+        return w.batch * L * (w.hidden * 2) + slices * L * 4 + w.n_kv * w.hidden * 2
     if scorer == "mlstm":
         P = d // 2
         scans = -(-min(w.window, L) // 32) if w.window else 0
@@ -149,6 +153,7 @@ class Stack:
         self.ws = kve.alloc_workspace(self.shape, self.shape.capacity, dev)
         self.caches, self.scorers, self.runners = [], [], []
         self.k_pool, self.v_pool, self.q_pool = [], [], []
+        self.h_pool, self.h_buf = [], []  # gate scorer: hidden states
         cfg = w.cfg_id
         for l in range(w.layers):
             dn = syn.device_normal
@@ -166,6 +171,12 @@ class Stack:
                 sc = kve.Scorer.mlstm(wq.to(torch.bfloat16), a, gate_b=gb,
                                       delay=w.window)
                 scratch.attach_scorer_state(pre_shape, sc)
+            elif scorer == "gate":
+                # Fast KVzip gate on the hidden state: linear D -> 1 per KV
+                # head, sigmoid; weights N(0, 1/D).
+                gw = dn((H, w.hidden), seed, (cfg, l, 0, T["gate_w"]),
+                        torch.bfloat16, dev, scale=w.hidden ** -0.5)
+                sc = kve.Scorer.gate(gw)
             else:
                 w1 = dn((H, w.hidden, 2 * d), seed, (cfg, l, 0, T["w1"]),
                         torch.bfloat16, dev, scale=(2 * d) ** -0.5)
@@ -178,7 +189,13 @@ class Stack:
             scratch.v.copy_(dn((b, H, w.n0, d), seed, (cfg, l, 0, T["v0"]),
                                torch.bfloat16, dev))
             scratch.pos.copy_(scratch_pos.expand(b, H, w.n0))
-            kve.kve_score(pre_shape, sc, scratch, 0, w.n0)
+            if scorer == "gate":
+                hid0 = dn((b, w.n0, w.hidden), seed, (cfg, l, 0, T["hidden0"]),
+                          torch.bfloat16, dev)
+                kve.kve_score(pre_shape, sc, scratch, 0, w.n0, hidden=hid0)
+                del hid0
+            else:
+                kve.kve_score(pre_shape, sc, scratch, 0, w.n0)
             kve.kve_select_evict(pre_shape, self.policy, scratch, w.n0,
                                  w.budget, keep_pre)
             kve.kve_compact(pre_shape, scratch, w.n0, keep_pre, w.budget)
@@ -211,6 +228,12 @@ class Stack:
                                   (cfg, l, 1, T["v_new"]), torch.bfloat16, dev))
             self.q_pool.append(dn((pool_steps, b, H * G, d), seed,
                                   (cfg, l, 1, T["q"]), torch.bfloat16, dev))
+            if scorer == "gate":
+                self.h_pool.append(dn((pool_steps, b, w.hidden), seed,
+                                      (cfg, l, 1, T["hidden_new"]),
+                                      torch.bfloat16, dev))
+                self.h_buf.append(torch.zeros((b, w.evict_len, w.hidden),
+                                              dtype=torch.bfloat16, device=dev))
         del scratch
         self.pool_steps = pool_steps
         self.out = torch.empty((b, H * G, d), dtype=torch.float32, device=dev)
@@ -227,8 +250,13 @@ class Stack:
             keep = self.keep_scratch[l]
             if keep_for is not None and r.evicts_next():
                 keep = keep_for(l)
-            r(self.k_pool[l][j], self.v_pool[l][j], self.q_pool[l][j],
-              self.out, None, keep)
+            if self.h_pool:
+                r(self.k_pool[l][j], self.v_pool[l][j], self.q_pool[l][j],
+                  self.out, None, keep, hidden_new=self.h_pool[l][j],
+                  hidden_buf=self.h_buf[l])
+            else:
+                r(self.k_pool[l][j], self.v_pool[l][j], self.q_pool[l][j],
+                  self.out, None, keep)
 
 
 # ---------------------------------------------------------------------------
@@ -252,6 +280,8 @@ def cpu_baseline(w, seed: int, sample_batch: int, sample_steps: int,
         threads = 1
     if scorer == "mlstm":
         return cpu_baseline_mlstm(w, seed, sample_batch, sample_steps, threads)
+    if scorer == "gate":
+        return cpu_baseline_gate(w, seed, sample_steps, threads)
     ws = syn.workload(w.cfg_id, batch=sample_batch)
     ctx = syn.initial_context(ws, seed, 0)
     wts = syn.draw_mlp_weights(ws, seed, 0)
@@ -288,6 +318,47 @@ def cpu_baseline(w, seed: int, sample_batch: int, sample_steps: int,
                    f"({sample_steps // w.evict_len} eviction cycles) from a "
                    f"compressed {w.n0}-token prompt; {dt:.1f} s wall; scaled "
                    f"to the {w.layers}-layer step as tokens/(time x layers)"),
+    }
+
+
+def cpu_baseline_gate(w, seed, sample_steps, threads) -> dict:
+    """The oracle's decode loop with the hidden-state gate, one layer of the
+    batch-1 stack, from a random cache of B entries (the prompt's one-shot
+    compression is not timed and not run: its product is a cache of B)."""
+    import numpy as np
+    import oracle as O
+    import synthetic as syn
+    ws = syn.workload(w.cfg_id, batch=1, n0=w.budget)
+    ctx = syn.initial_context(ws, seed, 0)
+    gw = syn.draw_gate_weights(ws, seed, 0)
+
+    def scores(hid64):
+        return np.stack([np.stack([O.score_to_f32(O.gate_score(
+            hid64[bi], gw["w"].f64[h], gw["b"].f64[h]))
+            for h in range(ws.n_kv)]) for bi in range(hid64.shape[0])])
+
+    s0 = scores(ctx["hidden0"].f64)
+    lay = O.OracleLayer(ctx["k0"].f64, ctx["v0"].f64, s0,
+                        O.Policy(ws.budget, ws.sinks, ws.window, ws.evict_len),
+                        ws.group)
+    del ctx
+    inputs = [syn.step_inputs(ws, seed, 0, i) for i in range(sample_steps)]
+    t0 = time.perf_counter()
+    for x in inputs:
+        sn = scores(x["hidden_new"].f64[:, None])[:, :, 0]
+        lay.step(x["k_new"].f64, x["v_new"].f64, sn, x["q"].f64)
+    dt = time.perf_counter() - t0
+    return {
+        "value": sample_steps / (dt * w.layers),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 oracle with the hidden-state gate, 1 of "
+                   f"{w.layers} layers, batch 1, {sample_steps} decode steps "
+                   f"({sample_steps // w.evict_len} eviction cycles) from a "
+                   f"random cache of B = {w.budget} entries; {dt:.1f} s wall; "
+                   f"scaled to the {w.layers}-layer step as "
+                   f"tokens/(time x layers)"),
     }
 
 
@@ -722,8 +793,9 @@ def main() -> int:
     log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")
     t0 = time.perf_counter()
+    scorer = "gate" if w.scorer == "gate" else args.scorer
     stack = Stack(w, args.seed, pool, dev, decay=args.decay,
-                  scorer=args.scorer, stochastic=args.stochastic)
+                  scorer=scorer, stochastic=args.stochastic)
     log(f"set-up {time.perf_counter() - t0:.1f} s")
 
     for i in range(warmup):
@@ -792,7 +864,7 @@ def main() -> int:
                 c = ev_count.get(l, 0)
                 ev_count[l] = c + 1
                 total_bytes += evict_extra_bytes(w, n, moved[(l, c)],
-                                                 args.scorer)
+                                                 scorer)
                 total_bytes += attn_launch_bytes(w, w.budget, False)
             else:
                 total_bytes += attn_launch_bytes(w, n, True)
@@ -837,7 +909,9 @@ def main() -> int:
                    "budget": w.budget, "sinks": w.sinks, "window": w.window,
                    "evict_len": w.evict_len, "prompt_len": w.n0,
                    "scorer": (f"mlp {2 * w.head_dim}-{w.hidden}-1 relu"
-                              if args.scorer == "mlp" else
+                              if scorer == "mlp" else
+                              f"gate {w.hidden}-1 sigmoid on hidden states"
+                              if scorer == "gate" else
                               f"mlstm P={w.head_dim // 2} hedgehog, delayed "
                               f"read-out W={w.window}"),
                    "decay": bool(args.decay),
@@ -856,7 +930,9 @@ def main() -> int:
         if cbatch is None:
             cbatch = 2 if args.scorer == "mlstm" else 16
         log(f"cpu baseline: oracle on {cbatch} sequences x {cs} steps")
-        cb = cpu_baseline(w, args.seed, cbatch, cs, args.scorer)
+        if scorer == "gate":
+            cbatch = min(cbatch, w.batch)
+        cb = cpu_baseline(w, args.seed, cbatch, cs, scorer)
         cb["value"] = round(cb["value"], 3)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)

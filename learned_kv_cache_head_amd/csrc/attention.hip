@@ -164,6 +164,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
       } else if (tid == 2 * NV) {
         a.pos[slice * (size_t)a.cap + new_slot] = a.new_pos;
       }
+      // The same workgroup of KV head 0 copies the token's hidden state
+      // into the pending-token buffer of its batch row.
+      if (a.hidden_new && h == 0) {
+        const char* hs = (const char*)a.hidden_new + (size_t)b * a.hidden_bytes;
+        char* hd = (char*)a.hidden_buf +
+                   ((size_t)b * a.hidden_rows + a.hidden_row) * a.hidden_bytes;
+        for (int i = tid; i < a.hidden_bytes / 16; i += kThreads)
+          ((u32x4*)hd)[i] = ((const u32x4*)hs)[i];
+      }
     }
   }
 

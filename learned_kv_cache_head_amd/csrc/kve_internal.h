@@ -53,6 +53,12 @@ struct AttnLaunch {
   void* k_store;        // cache base pointers for the append (same as k, v)
   void* v_store;
   int32_t* pos;         // [batch][H][cap]
+  // Optional fused copy of the new token's hidden state (hidden-state
+  // scorers): hidden_new [batch][hidden_bytes] -> row hidden_row of
+  // hidden_buf [batch][hidden_rows][hidden_bytes]. Null: none.
+  const void* hidden_new;
+  void* hidden_buf;
+  int hidden_bytes, hidden_rows, hidden_row;
 };
 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);

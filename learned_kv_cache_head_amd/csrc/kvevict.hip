@@ -117,7 +117,10 @@ kve_status from_hip(hipError_t e) { return e == hipSuccess ? KVE_OK : KVE_ERR_LA
 kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
                      const void* q, float* out, float* lse, void* ws,
                      size_t ws_bytes, int new_slot, int new_pos,
-                     const void* k_new, const void* v_new, hipStream_t stream) {
+                     const void* k_new, const void* v_new, hipStream_t stream,
+                     const void* hidden_new = nullptr, void* hidden_buf = nullptr,
+                     int hidden_bytes = 0, int hidden_rows = 0,
+                     int hidden_row = 0) {
   // The attention kernel reads the appended row from k_new / v_new only in
   // the last stage of the last split, so it must be the slice's last row.
   if (new_slot >= 0 && new_slot != len - 1) return KVE_ERR_INVALID_ARG;
@@ -148,6 +151,13 @@ kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
   a.k_store = cache->k;
   a.v_store = cache->v;
   a.pos = cache->pos;
+  if (new_slot >= 0 && hidden_new) {
+    a.hidden_new = hidden_new;
+    a.hidden_buf = hidden_buf;
+    a.hidden_bytes = hidden_bytes;
+    a.hidden_rows = hidden_rows;
+    a.hidden_row = hidden_row;
+  }
   return from_hip(kve::launch_attention(a, stream));
 }
 
@@ -522,8 +532,9 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
 
   state->evicted = 0;
   bool appended = false;
-  if (score_now || gate) {
-    // The new row must be in the cache before scoring or selection.
+  if (score_now) {
+    // The new row (and hidden state) must be in place before scoring or
+    // selection. Otherwise the attention launch appends them.
     st = from_hip(kve::launch_append(
         cache->k, cache->v, cache->pos, shape->batch, shape->n_kv_heads,
         shape->head_dim, shape->capacity, elem_bytes(shape->kv_dtype), slot,
@@ -557,7 +568,9 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
     state->evicted = 1;
   }
   st = attn_impl(shape, cache, len, q, out, lse, ws, ws_bytes,
-                 appended ? -1 : slot, position, k_new, v_new, stream);
+                 appended ? -1 : slot, position, k_new, v_new, stream,
+                 gate ? hidden_new : nullptr, hidden_buf, scorer->in_dim * 2,
+                 L, slot - scored);
   if (st != KVE_OK) return st;
   state->len = len;
   state->scored_upto = scored;
