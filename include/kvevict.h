@@ -30,7 +30,13 @@
  *    KV Eviction"): per-KV-head gate on the layer's hidden state with output
  *    in [0, 1] (section 3.1 "Formulation"); buffered scoring of the pending
  *    tokens in parallel, then eviction of as many entries (section 3.1 and
- *    Appendix A.5).
+ *    Appendix A.5); the low-rank sink-attention gate (section 3.4).
+ *  - Optional parts of the path: KVpop's temporal decay in the ranking
+ *    (Appendix B.3, Eq. 20), its stateful mLSTM scorer with delayed read-out
+ *    (section 3.3, Appendix A and E.3-E.4), its running top-k selection and
+ *    masked prefill attention (section 3.2, Appendix C.1-C.2, Eq. 26), and
+ *    ForesightKV's stochastic eviction from the 2L lowest-scored candidates
+ *    (summary page, "Key Contributions" item 4).
  *
  * Tensor layouts (row-major, innermost last):
  *   K, V        [batch][n_kv_heads][capacity][head_dim]   kv_dtype
@@ -209,10 +215,11 @@ kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
 
 /* a2 Score the slots [slot_begin, slot_end) of every slice into
  * cache->score (float32). MLP reads the cached K, V rows of those slots
- * (KVpop Eq. 35-36). GATE reads `hidden` [batch][slot_end-slot_begin][D]
- * bf16, the hidden states of those tokens (Fast KVzip section 3.1);
- * `hidden` must be NULL for MLP and MLSTM; SINK_GATE reads it as GATE does. Runs as a bf16 MFMA GEMM with
- * float32 accumulation (float32 VALU for float32 weights).
+ * (KVpop Eq. 35-36). GATE and SINK_GATE read `hidden`
+ * [batch][slot_end-slot_begin][D] bf16, the hidden states of those tokens
+ * (Fast KVzip sections 3.1 and 3.4); `hidden` must be NULL for MLP and
+ * MLSTM. MLP, GATE and SINK_GATE run as bf16 MFMA GEMMs with float32
+ * accumulation (float32 VALU for float32 MLP weights).
  * MLSTM absorbs the cached tokens of those slots into cache->scorer_state in
  * slot order and writes the score of every token it reads out, into that
  * token's slot (KVpop Eq. 41-42). The slots must hold consecutive positions
@@ -235,7 +242,9 @@ kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
  * Requires 0 <= n_keep <= len <= capacity, and S + W <= n_keep when
  * n_keep < len; n_keep == len writes the identity. Scores must be finite;
  * positions distinct, with the S oldest and W newest present (as the
- * library's own appends and compaction keep them). */
+ * library's own appends and compaction keep them). With policy->gumbel the
+ * evicted entries are drawn by ForesightKV's stochastic rule instead (see
+ * kve_policy); the same noise and scores give the same kept slots. */
 kve_status kve_select_evict(const kve_shape* shape, const kve_policy* policy,
                             const kve_cache* cache, int32_t len,
                             int32_t n_keep, int32_t* keep_slots,
@@ -275,7 +284,8 @@ kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
  * MLP and MLSTM.
  * MLSTM scorers absorb the pending tokens at that point (the same scores as
  * absorbing every token as it arrives) and need scorer->delay equal to the
- * policy window.
+ * policy window. With policy->gumbel the eviction is stochastic, as in
+ * kve_select_evict.
  * Requires capacity >= B + L and state->len < capacity. */
 kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
                     const kve_scorer* scorer, kve_cache* cache,
@@ -296,7 +306,9 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
  *    k-th best token of E(q) = {S <= t <= q - W}, k = B - S - W; len when
  *    E(q) holds fewer than k tokens, -1 when k = 0.
  * ws: kve_prefill_workspace_bytes(shape, len) bytes of scratch (sorted
- * keys). Requires 1 <= len <= min(capacity, 262144); scores finite. */
+ * keys). Requires 1 <= len <= min(capacity, 262144); scores finite;
+ * policy->gumbel NULL (KVE_ERR_UNSUPPORTED otherwise: the running top-k is
+ * deterministic). */
 size_t kve_prefill_workspace_bytes(const kve_shape* shape, int32_t len);
 kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
                               const kve_cache* cache, int32_t len,
@@ -313,7 +325,8 @@ kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
  * accumulation and softmax). ws: kve_prefill_attn_workspace_bytes bytes of
  * scratch: per 64-position query block, the at most k long-range keys any
  * of its queries keeps (the attention visits only those, the sinks and the
- * block's recent windows). */
+ * block's recent windows). policy->gumbel must be NULL, as for
+ * kve_prefill_select. */
 size_t kve_prefill_attn_workspace_bytes(const kve_shape* shape,
                                         const kve_policy* policy, int32_t len);
 kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,

@@ -284,7 +284,7 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
 
 extern "C" {
 
-int32_t kve_version(void) { return 100; }
+int32_t kve_version(void) { return 10400; }  // 1.4.0
 
 size_t kve_prefill_workspace_bytes(const kve_shape* shape, int32_t len) {
   if (check_shape(shape) != KVE_OK || len < 1 || len > kve::kMaxPrefillLen)
