@@ -142,6 +142,74 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _dev(t, nbytes: int, name: str, optional: bool = False) -> Optional[int]:
+    """Pointer of a device tensor that must hold at least ``nbytes``
+    contiguous bytes. The C ABI takes bare pointers and cannot see buffer
+    sizes, so a tensor that is too small, strided or on the host is refused
+    here instead of reaching a kernel."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name}: a device tensor is required")
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, needs at least {nbytes}")
+    return t.data_ptr()
+
+
+def _check_cache(shape: "Shape", cache: "CacheTensors", kv: bool = True,
+                 score: bool = True, pos: bool = True) -> None:
+    """The cache tensors a call reads or writes (kv: K and V)."""
+    rows = shape.batch * shape.n_kv_heads * shape.capacity
+    eb = 4 if shape.kv_dtype == F32 else 2
+    if kv:
+        _dev(cache.k, rows * shape.head_dim * eb, "cache.k")
+        _dev(cache.v, rows * shape.head_dim * eb, "cache.v")
+    if score:
+        _dev(cache.score, rows * 4, "cache.score")
+    if pos:
+        _dev(cache.pos, rows * 4, "cache.pos")
+
+
+def _check_policy(shape: "Shape", policy: "Policy") -> None:
+    _dev(policy.log_gamma, shape.n_kv_heads * 4, "policy.log_gamma", True)
+    _dev(policy.gumbel, shape.batch * shape.n_kv_heads * shape.capacity * 4,
+         "policy.gumbel", True)
+
+
+def _eb(shape: "Shape") -> int:
+    return 4 if shape.kv_dtype == F32 else 2
+
+
+def _check_scorer(shape: "Shape", sc: "Scorer") -> None:
+    """Weight buffers large enough for the scorer kind (layouts as in
+    kvevict.h)."""
+    H, G, n = shape.n_kv_heads, shape.group, sc.in_dim
+    web = 4 if sc.wdtype == F32 else 2
+    if sc.kind == SCORER_MLP_KV:
+        _dev(sc.w1, H * sc.hidden * n * web, "scorer.w1")
+        _dev(sc.b1, H * sc.hidden * 4, "scorer.b1", True)
+        _dev(sc.w2, H * sc.hidden * 4, "scorer.w2")
+        _dev(sc.b2, H * 4, "scorer.b2", True)
+    elif sc.kind == SCORER_GATE_HIDDEN:
+        _dev(sc.w1, H * n * web, "scorer.w1")
+        _dev(sc.b1, H * 4, "scorer.b1", True)
+    elif sc.kind == SCORER_MLSTM:
+        _dev(sc.w1, H * (3 * sc.hidden + 2) * n * web, "scorer.w1")
+        _dev(sc.b1, H * 2 * 4, "scorer.b1", True)
+        _dev(sc.w2, H * sc.hidden * 4, "scorer.w2")
+        _dev(sc.b2, H * 4, "scorer.b2", True)
+    elif sc.kind == SCORER_SINK_GATE:
+        _dev(sc.w1, (H * 16 + H * G * 16) * n * web, "scorer.w1")
+        _dev(sc.b1, 32 * 4, "scorer.b1", True)
+        _dev(sc.w2, sc.n_sink * 16 * 4, "scorer.w2", sc.n_sink == 0)
+        _dev(sc.b2, H * G * 4, "scorer.b2", True)
+
+
 def _stream(stream=None) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -314,45 +382,93 @@ def alloc_workspace(shape: Shape, max_len: int, device="cuda"):
 
 def kve_append(shape: Shape, cache: CacheTensors, slot: int, position: int,
                k_new, v_new, stream=None) -> None:
+    _check_cache(shape, cache, score=False)
+    row = shape.batch * shape.n_kv_heads * shape.head_dim * _eb(shape)
     cs, cc = shape.c(), cache.c()
     _check(load_library().kve_append(
-        ctypes.byref(cs), ctypes.byref(cc), slot, position, _ptr(k_new),
-        _ptr(v_new), _stream(stream)), "kve_append")
+        ctypes.byref(cs), ctypes.byref(cc), slot, position,
+        _dev(k_new, row, "k_new"), _dev(v_new, row, "v_new"),
+        _stream(stream)), "kve_append")
 
 
 def kve_score(shape: Shape, scorer: Scorer, cache: CacheTensors,
               slot_begin: int, slot_end: int, hidden=None,
               stream=None) -> None:
+    on_kv = scorer.kind in (SCORER_MLP_KV, SCORER_MLSTM)
+    _check_cache(shape, cache, kv=on_kv, pos=scorer.kind == SCORER_MLSTM)
+    _check_scorer(shape, scorer)
+    if scorer.kind == SCORER_MLSTM:
+        _dev(cache.scorer_state, kve_scorer_state_bytes(shape, scorer),
+             "cache.scorer_state")
+    rows = max(slot_end - slot_begin, 0)
     cs, csc, cc = shape.c(), scorer.c(), cache.c()
     _check(load_library().kve_score(
         ctypes.byref(cs), ctypes.byref(csc), ctypes.byref(cc), slot_begin,
-        slot_end, _ptr(hidden), _stream(stream)), "kve_score")
+        slot_end, _dev(hidden, shape.batch * rows * scorer.in_dim * 2,
+                       "hidden", True), _stream(stream)), "kve_score")
 
 
 def kve_select_evict(shape: Shape, policy: Policy, cache: CacheTensors,
                      length: int, n_keep: int, keep_slots,
                      stream=None) -> None:
+    _check_cache(shape, cache, kv=False)
+    _check_policy(shape, policy)
     cs, cp, cc = shape.c(), policy.c(), cache.c()
+    keep = _dev(keep_slots, shape.batch * shape.n_kv_heads * max(n_keep, 0) * 4,
+                "keep_slots")
     _check(load_library().kve_select_evict(
         ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(cc), length, n_keep,
-        _ptr(keep_slots), _stream(stream)), "kve_select_evict")
+        keep, _stream(stream)), "kve_select_evict")
 
 
 def kve_compact(shape: Shape, cache: CacheTensors, length: int, keep_slots,
                 n_keep: int, stream=None) -> None:
+    _check_cache(shape, cache)
     cs, cc = shape.c(), cache.c()
+    keep = _dev(keep_slots, shape.batch * shape.n_kv_heads * max(n_keep, 0) * 4,
+                "keep_slots")
     _check(load_library().kve_compact(
-        ctypes.byref(cs), ctypes.byref(cc), length, _ptr(keep_slots), n_keep,
+        ctypes.byref(cs), ctypes.byref(cc), length, keep, n_keep,
         _stream(stream)), "kve_compact")
+
+
+def _check_attn_io(shape: Shape, q, out, lse) -> None:
+    hq = shape.batch * shape.n_kv_heads * shape.group
+    _dev(q, hq * shape.head_dim * _eb(shape), "q")
+    _dev(out, hq * shape.head_dim * 4, "out")
+    _dev(lse, hq * 4, "lse", True)
 
 
 def kve_decode_attn(shape: Shape, cache: CacheTensors, length: int, q, out,
                     lse, ws, stream=None) -> None:
+    _check_cache(shape, cache, score=False, pos=False)
+    _check_attn_io(shape, q, out, lse)
     cs, cc = shape.c(), cache.c()
     _check(load_library().kve_decode_attn(
         ctypes.byref(cs), ctypes.byref(cc), length, _ptr(q), _ptr(out),
-        _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(lse), _dev(ws, 0, "ws", True),
+        0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)), "kve_decode_attn")
+
+
+def _check_step_args(shape, policy, scorer, cache, k_new, v_new, q, out, lse,
+                     keep_slots, ws, hidden_new, hidden_buf) -> None:
+    _check_cache(shape, cache)
+    _check_policy(shape, policy)
+    _check_scorer(shape, scorer)
+    if scorer.kind == SCORER_MLSTM:
+        _dev(cache.scorer_state, kve_scorer_state_bytes(shape, scorer),
+             "cache.scorer_state")
+    _check_attn_io(shape, q, out, lse)
+    row = shape.batch * shape.n_kv_heads * shape.head_dim * _eb(shape)
+    _dev(k_new, row, "k_new")
+    _dev(v_new, row, "v_new")
+    _dev(keep_slots, shape.batch * shape.n_kv_heads * policy.budget * 4,
+         "keep_slots")
+    _dev(ws, 0, "ws")
+    _dev(hidden_new, shape.batch * scorer.in_dim * 2, "hidden_new", True)
+    _dev(hidden_buf, shape.batch * policy.evict_len * scorer.in_dim * 2,
+         "hidden_buf", True)
 
 
 def kve_step(shape: Shape, policy: Policy, scorer: Scorer,
@@ -360,6 +476,8 @@ def kve_step(shape: Shape, policy: Policy, scorer: Scorer,
              lse, keep_slots, ws, hidden_new=None, hidden_buf=None,
              stream=None) -> DecodeState:
     """One decode step of one layer; updates and returns ``state``."""
+    _check_step_args(shape, policy, scorer, cache, k_new, v_new, q, out, lse,
+                     keep_slots, ws, hidden_new, hidden_buf)
     cs, cp, csc, cc = shape.c(), policy.c(), scorer.c(), cache.c()
     st = _State(state.len, state.scored_upto, state.next_position, 0)
     _check(load_library().kve_step(
@@ -388,11 +506,14 @@ def kve_prefill_select(shape: Shape, policy: Policy, cache: CacheTensors,
         if n == 0:
             raise ValueError("invalid shape or length for prefill selection")
         ws = torch.empty(n // 8, dtype=torch.int64, device=rank.device)
+    _check_cache(shape, cache, kv=False, pos=False)
+    _check_policy(shape, policy)
+    per = shape.batch * shape.n_kv_heads * max(length, 0) * 4
     cs, cp, cc = shape.c(), policy.c(), cache.c()
     _check(load_library().kve_prefill_select(
         ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(cc), length,
-        _ptr(rank), _ptr(tau), _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(stream)), "kve_prefill_select")
+        _dev(rank, per, "rank"), _dev(tau, per, "tau"), _dev(ws, 0, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)), "kve_prefill_select")
 
 
 def kve_prefill_attn_workspace_bytes(shape: Shape, policy: Policy,
@@ -413,10 +534,18 @@ def kve_prefill_attn(shape: Shape, policy: Policy, cache: CacheTensors,
         if n == 0:
             raise ValueError("invalid shape, policy or length")
         ws = torch.empty((n + 3) // 4, dtype=torch.int32, device=q.device)
+    _check_cache(shape, cache, score=False, pos=False)
+    _check_policy(shape, policy)
+    n = max(length, 0)
+    per = shape.batch * shape.n_kv_heads * n * 4
+    hq = shape.batch * shape.n_kv_heads * shape.group * n
     cs, cp, cc = shape.c(), policy.c(), cache.c()
     _check(load_library().kve_prefill_attn(
         ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(cc), length,
-        _ptr(rank), _ptr(tau), _ptr(q), _ptr(out), _ptr(lse), _ptr(ws),
+        _dev(rank, per, "rank"), _dev(tau, per, "tau"),
+        _dev(q, hq * shape.head_dim * 2, "q"),
+        _dev(out, hq * shape.head_dim * 4, "out"),
+        _dev(lse, hq * 4, "lse", True), _dev(ws, 0, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)), "kve_prefill_attn")
 
 
@@ -444,6 +573,8 @@ class LayerStep:
         self._keepalive = (scorer, cache, ws, policy)
         self.state = state
         self.budget, self.evict_len = policy.budget, policy.evict_len
+        self._args = (shape, policy, scorer, cache, ws)
+        self._checked = False
 
     def evicts_next(self) -> bool:
         """True if the next call reaches B + L and evicts."""
@@ -451,7 +582,14 @@ class LayerStep:
 
     def __call__(self, k_new, v_new, q, out, lse, keep_slots,
                  hidden_new=None, hidden_buf=None) -> int:
-        """One decode step; returns 1 if it evicted, else 0."""
+        """One decode step; returns 1 if it evicted, else 0. The tensors of
+        the first call are checked as by ``kve_step``; later calls are
+        trusted to pass tensors of the same shapes."""
+        if not self._checked:
+            shape, policy, scorer, cache, ws = self._args
+            _check_step_args(shape, policy, scorer, cache, k_new, v_new, q,
+                             out, lse, keep_slots, ws, hidden_new, hidden_buf)
+            self._checked = True
         r = self._refs
         status = self._fn(r[0], r[1], r[2], r[3], r[4], k_new.data_ptr(),
                           v_new.data_ptr(), _ptr(hidden_new), _ptr(hidden_buf),

@@ -320,3 +320,58 @@ def test_sink_gate_rejects_bad_scorers():
     assert score(n_sink=17) == 4
     assert score(hidden_dim=5000) == 4
     assert score(w2=None) == 1          # sink keys missing
+
+
+class _FakeDev:
+    """Stands in for a device tensor in the binding's buffer checks."""
+
+    def __init__(self, nbytes, contiguous=True, cuda=True):
+        self.nbytes, self.contig, self.is_cuda = nbytes, contiguous, cuda
+
+    def is_contiguous(self):
+        return self.contig
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return FAKE
+
+
+def test_binding_refuses_host_small_or_strided_buffers():
+    """The C ABI sees bare pointers, so the binding checks every device
+    buffer's size, placement and contiguity before a call."""
+    import torch
+    s = kve.Shape(2, 8, 4, 128, 1152, kve.BF16)
+    rows = 2 * 8 * 1152
+    good = kve.CacheTensors(_FakeDev(rows * 256), _FakeDev(rows * 256),
+                            _FakeDev(rows * 4), _FakeDev(rows * 4))
+    kve._check_cache(s, good)
+    for bad in (kve.CacheTensors(_FakeDev(rows * 256 - 1), _FakeDev(rows * 256),
+                                 _FakeDev(rows * 4), _FakeDev(rows * 4)),
+                kve.CacheTensors(_FakeDev(rows * 256), _FakeDev(rows * 256),
+                                 _FakeDev(rows * 4, contiguous=False),
+                                 _FakeDev(rows * 4)),
+                kve.CacheTensors(torch.zeros(rows * 128, dtype=torch.bfloat16),
+                                 _FakeDev(rows * 256), _FakeDev(rows * 4),
+                                 _FakeDev(rows * 4))):
+        with pytest.raises(ValueError):
+            kve._check_cache(s, bad)
+    pol = kve.Policy(1024, 4, 128, 128, gumbel=_FakeDev(rows * 4 - 4))
+    with pytest.raises(ValueError):
+        kve._check_policy(s, pol)
+    kve._check_policy(s, kve.Policy(1024, 4, 128, 128,
+                                    gumbel=_FakeDev(rows * 4)))
+    # keep_slots of a select needs batch * H * n_keep int32
+    with pytest.raises(ValueError):
+        kve.kve_select_evict(s, kve.Policy(1024, 4, 128, 128), good, 1152,
+                             1024, _FakeDev(2 * 8 * 1024 * 4 - 1))
+    # scorer weights: MLP w1 [H][hidden][2d] bf16
+    sc = kve.Scorer(kve.SCORER_MLP_KV, _FakeDev(8 * 64 * 256 * 2 - 2),
+                    w2=_FakeDev(8 * 64 * 4), hidden=64, in_dim=256,
+                    wdtype=kve.BF16)
+    with pytest.raises(ValueError):
+        kve._check_scorer(s, sc)
