@@ -118,65 +118,137 @@ __global__ __launch_bounds__(256) void rank_count_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Running cutoffs, one wave per slice.
+// Running cutoffs, one workgroup per (slice, 64-query block). tau_q is the
+// k-th smallest rank in E(q) = {S <= t <= q - W}; ranks are distinct
+// (0..n-1), so a bitmap over rank values holds E. For its first query q0
+// the workgroup sets the bits of E(q0) (positions S..q0 - W, in parallel)
+// and finds the k-th set bit by a block scan of word popcounts; then one
+// wave inserts t = q - W for the block's other queries in order: while
+// |E| < k, tau = n (all kept) and the largest rank so far is tracked; at
+// |E| = k the cut is that largest rank; after that, an entering rank below
+// the cut moves the cut to the largest set rank below it (a predecessor
+// search over the bitmap words, 64 words per wave ballot).
+// Dynamic LDS: ceil(n / 32) words.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void cutoff_kernel(const int32_t* rank, int n,
-                                                    int S, int W, int k,
-                                                    int32_t* tau) {
-  __shared__ uint32_t bm[kMaxPrefillLen / 32];
-  const int slice = blockIdx.x;
-  const int lane = threadIdx.x;
+constexpr int kCutThreads = 256;
+
+__global__ __launch_bounds__(kCutThreads) void cutoff_kernel(
+    const int32_t* rank, int n, int S, int W, int k, int32_t* tau) {
+  extern __shared__ uint32_t bm[];
+  __shared__ uint32_t wpart[kCutThreads / 64];
+  __shared__ int sh_cut, sh_maxr;
+  const int qb = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int q0 = qb * kQBlock;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int32_t* rk = rank + (size_t)slice * n;
   int32_t* out = tau + (size_t)slice * n;
-  const int words = (n + 31) >> 5;
-  for (int w = lane; w < words; w += 64) bm[w] = 0u;
-  __syncthreads();
-  int count = 0;   // tokens in E(q)
-  int cut = n;     // tau while count >= k
-  int maxr = -1;   // largest inserted rank (tau when count reaches k)
-  for (int q0 = 0; q0 < n; q0 += 64) {
-    const int ql = q0 + lane;
-    const int tl = ql - W;
-    const int rl = (ql < n && tl >= S) ? rk[tl] : -1;  // rank entering at ql
-    int mine = 0;
-    const int m = min(64, n - q0);
-    for (int i = 0; i < m; ++i) {
-      const int r = __builtin_amdgcn_readlane(rl, i);
-      if (r >= 0 && k > 0) {
-        if (lane == 0) bm[r >> 5] |= 1u << (r & 31);
-        ++count;
-        maxr = max(maxr, r);
-        if (count == k) {
-          cut = maxr;
-        } else if (count > k && r < cut) {
-          // next smaller inserted rank below cut
-          int w0 = (cut - 1) >> 5;
-          const uint32_t below = (cut & 31) ? ((1u << (cut & 31)) - 1u) : ~0u;
-          int found = -1;
-          while (found < 0) {
-            const int w = w0 - lane;
-            uint32_t word = 0u;
-            if (w >= 0) {
-              word = bm[w];
-              if (w == (cut >> 5)) word &= below;
-            }
-            const uint64_t nz = __ballot(word != 0u);
-            if (nz) {
-              const int l = __ffsll((unsigned long long)nz) - 1;  // highest word
-              const uint32_t wv = __shfl(word, l);
-              found = (w0 - l) * 32 + 31 - __clz(wv);
-            } else {
-              w0 -= 64;
-            }
-          }
-          cut = found;
-        }
-      }
-      const int t = k == 0 ? -1 : (count >= k ? cut : n);
-      mine = lane == i ? t : mine;
-    }
-    if (lane < m) out[q0 + lane] = mine;
+  const int m = min(kQBlock, n - q0);
+  if (k == 0) {  // no long-range budget: every tau is -1
+    if (tid < m) out[q0 + tid] = -1;
+    return;
   }
+  const int words = (n + 31) >> 5;
+  for (int w = tid; w < words; w += kCutThreads) bm[w] = 0u;
+  if (tid == 0) {
+    sh_cut = n;
+    sh_maxr = -1;
+  }
+  __syncthreads();
+  // E(q0): positions S .. q0 - W.
+  const int lim = q0 - W;
+  int lmax = -1;
+  for (int t = S + tid; t <= lim; t += kCutThreads) {
+    const int r = rk[t];
+    atomicOr(&bm[r >> 5], 1u << (r & 31));
+    lmax = max(lmax, r);
+  }
+  const int count0 = max(0, lim - S + 1);
+  // Largest rank of E(q0) (the cut once |E| reaches k).
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, __shfl_xor(lmax, off));
+  if (lane == 0) atomicMax(&sh_maxr, lmax);
+  __syncthreads();
+  if (count0 >= k) {
+    // k-th set bit: thread i counts its run of words, block exclusive scan.
+    const int per = (words + kCutThreads - 1) / kCutThreads;
+    const int wb = tid * per, we = min(words, wb + per);
+    uint32_t c = 0;
+    for (int w = wb; w < we; ++w) c += __popc(bm[w]);
+    uint32_t incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wpart[wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - c;
+    for (int w = 0; w < wave; ++w) before += wpart[w];
+    const uint32_t kk = (uint32_t)k;
+    if (before < kk && before + c >= kk) {
+      uint32_t need = kk - before;  // the need-th set bit of this run
+      for (int w = wb; w < we; ++w) {
+        uint32_t word = bm[w];
+        const uint32_t pc = __popc(word);
+        if (need > pc) {
+          need -= pc;
+          continue;
+        }
+        for (uint32_t j = 1; j < need; ++j) word &= word - 1u;  // drop lowest
+        sh_cut = w * 32 + __ffs(word) - 1;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // One wave: the block's queries in order; lane i keeps tau of q0 + i.
+  int count = count0;
+  int cut = sh_cut;
+  int maxr = sh_maxr;
+  const int ql = q0 + lane;
+  const int tl = ql - W;
+  const int rl = (lane > 0 && ql < n && tl >= S) ? rk[tl] : -1;  // entering rank
+  int mine = 0;
+  for (int i = 0; i < m; ++i) {
+    const int r = __builtin_amdgcn_readlane(rl, i);
+    if (r >= 0) {
+      if (lane == 0) bm[r >> 5] |= 1u << (r & 31);
+      ++count;
+      maxr = max(maxr, r);
+      if (count == k) {
+        cut = maxr;
+      } else if (count > k && r < cut) {
+        // largest set rank below cut (r itself at worst)
+        int w0 = (cut - 1) >> 5;
+        const uint32_t below = (cut & 31) ? ((1u << (cut & 31)) - 1u) : ~0u;
+        int found = -1;
+        while (found < 0) {
+          const int w = w0 - lane;
+          uint32_t word = 0u;
+          if (w >= 0) {
+            word = bm[w];
+            if (w == (cut >> 5)) word &= below;
+          }
+          const uint64_t nz = __ballot(word != 0u);
+          if (nz) {
+            const int l = __ffsll((unsigned long long)nz) - 1;  // highest word
+            const uint32_t wv = __shfl(word, l);
+            found = (w0 - l) * 32 + 31 - __clz(wv);
+          } else {
+            w0 -= 64;
+          }
+        }
+        cut = found;
+      }
+    }
+    const int t = count >= k ? cut : n;
+    mine = lane == i ? t : mine;
+  }
+  if (lane < m) out[q0 + lane] = mine;
 }
 
 // ---------------------------------------------------------------------------
@@ -534,8 +606,10 @@ hipError_t launch_prefill_select(const float* score, const float* lg, int H,
   hipLaunchKernelGGL(rank_count_kernel, dim3((n + 255) / 256, slices), dim3(256),
                      0, s, score, lg, H, cap, n, npad, (const uint64_t*)sorted,
                      rank);
-  hipLaunchKernelGGL(cutoff_kernel, dim3(slices), dim3(64), 0, s,
-                     (const int32_t*)rank, n, S, W, k, tau);
+  const int nqb = (n + kQBlock - 1) / kQBlock;
+  const size_t bm_bytes = (size_t)((n + 31) / 32) * sizeof(uint32_t);
+  hipLaunchKernelGGL(cutoff_kernel, dim3(nqb, slices), dim3(kCutThreads),
+                     bm_bytes, s, (const int32_t*)rank, n, S, W, k, tau);
   return hipGetLastError();
 }
 
