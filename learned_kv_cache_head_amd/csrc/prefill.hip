@@ -274,16 +274,35 @@ __global__ __launch_bounds__(256) void keylist_kernel(const int32_t* rank,
   const int wave = threadIdx.x >> 6;
   const int lim = q0 - W;  // last eligible position at q0
   int base = 0;
-  for (int c = S; c <= lim; c += 256) {
-    const int t = c + threadIdx.x;
-    const bool f = t <= lim && rk[t] <= t0;
-    const uint64_t m = __ballot(f);
-    const int before = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(m);
+  // 1024 positions per pass, 4 consecutive ones per thread; kept positions
+  // are written in order at their exclusive-scan offsets.
+  for (int c = S; c <= lim; c += 1024) {
+    const int tb = c + 4 * threadIdx.x;
+    bool f[4];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tb + j;
+      f[j] = t <= lim && rk[t] <= t0;
+      cnt += f[j] ? 1 : 0;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (f && off + before < kmax) out[off + before] = t;
+    int at = base + incl - cnt;
+    for (int w = 0; w < wave; ++w) at += wsum[w];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (f[j]) {
+        if (at < kmax) out[at] = tb + j;
+        ++at;
+      }
+    }
     base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
