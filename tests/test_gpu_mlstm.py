@@ -244,3 +244,50 @@ def test_mlstm_step_qwen3_layer():
     print(f"[mlstm-step] {w.name} batch=2", flush=True)
     ev = run_e2e_mlstm(w, check_stride=16)
     assert ev == 2
+
+
+def test_mlstm_full_size_prompt_and_flush_sampled():
+    """The batch-96 Qwen3-4B layer in the benchmark's launch configuration:
+    all 768 slices absorb an 8192-token prompt in one launch, then one
+    buffered-scoring flush absorbs 128 more tokens and reads 128 out; six
+    sampled slices (first, last and four others) against the oracle's
+    float64 recurrence, every read-out score."""
+    import torch
+    k = kve()
+    dev = torch.device("cuda")
+    w = syn.workload(4, scorer="mlstm", hidden=64)
+    b, H, d, n0, L, W = w.batch, w.n_kv, w.head_dim, w.n0, w.evict_len, w.window
+    n = n0 + L
+    print(f"[mlstm-full] b={b} H={H} n0={n0} L={L}", flush=True)
+    T = syn.TENSOR_IDS
+    K = syn.device_normal((b, H, n, d), 4, (4, 0, 0, T["k0"]), torch.bfloat16, dev)
+    V = syn.device_normal((b, H, n, d), 4, (4, 0, 0, T["v0"]), torch.bfloat16, dev)
+    wts = syn.draw_mlstm_weights(w, 4, 0)
+    shape = k.Shape(b, H, w.group, d, n, k.BF16)
+    cache = k.CacheTensors.empty(shape, dev)
+    cache.k.copy_(K)
+    cache.v.copy_(V)
+    cache.pos.copy_(torch.arange(n, dtype=torch.int32, device=dev).expand(b, H, n))
+    cache.score.fill_(UNSET)
+    sc = mlstm_device_scorer(wts, W, dev)
+    cache.attach_scorer_state(shape, sc)
+    k.kve_score(shape, sc, cache, 0, n0)       # prompt absorption
+    k.kve_score(shape, sc, cache, n0, n)       # one flush of L tokens
+    torch.cuda.synchronize()
+    sampled = [(0, 0), (b - 1, H - 1), (17, 3), (40, 6), (63, 1), (90, 5)]
+    for bi, h in sampled:
+        Kh = K[bi, h].float().cpu().double().numpy()
+        Vh = V[bi, h].float().cpu().double().numpy()
+        scorer = O.MlstmScorer(oracle_mlstm_weights(wts, h), W)
+        ref = np.full(n, np.nan)
+        for t in range(n):
+            r = scorer.push(np.concatenate([Kh[t], Vh[t]]))
+            if r is not None:
+                ref[r[0]] = r[1]
+        got = cache.score[bi, h].cpu().numpy()
+        read = ~np.isnan(ref)
+        assert read.sum() == n - W
+        err = float(np.max(np.abs(got[read] - ref[read])))
+        print(f"[mlstm-full] slice ({bi},{h}) max |err| {err:.3g}", flush=True)
+        np.testing.assert_allclose(got[read], ref[read], rtol=0, atol=MLSTM_ATOL)
+        assert np.all(got[~read] == UNSET)
