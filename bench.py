@@ -46,6 +46,26 @@ METRIC = ("evict+decode tokens/s at budget B and achieved HBM GB/s vs "
           "MI355X peak")
 
 
+def achievable_copy_gbps(dev) -> float:
+    """Best of three timed 1 GiB device-to-device copies (1 GiB read + 1 GiB
+    written), in GB/s: the achievable-bandwidth reference."""
+    import torch
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
+
+
 def calib_copy(dev) -> None:
     """A plain elementwise copy of known size (1 GiB read, 1 GiB written),
     the reference that scales the HBM byte counters."""
@@ -130,7 +150,7 @@ class Stack:
     """Per-layer caches, scorer weights, step runners and input pools."""
 
     def __init__(self, w, seed: int, pool_steps: int, dev, decay=False,
-                 scorer="mlp", stochastic=False):
+                 scorer="mlp", stochastic=False, start_pos=None):
         import torch
         import learned_kv_cache_head_amd as kve
         import synthetic as syn
@@ -208,7 +228,9 @@ class Stack:
             # The recurrent state does not depend on the capacity.
             c.scorer_state = scratch.scorer_state
             scratch.scorer_state = None
-            st = kve.DecodeState(B, B, w.n0)
+            # Decoding continues at position start_pos (default: right after
+            # the prompt); the compressed cache is the same either way.
+            st = kve.DecodeState(B, B, w.n0 if start_pos is None else start_pos)
             self.caches.append(c)
             self.scorers.append(sc)
             pol = self.policy
@@ -742,6 +764,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decay", action="store_true",
                     help="rank with KVpop temporal decay (static priority)")
+    ap.add_argument("--start-pos", type=int, default=None,
+                    help="position of the first decoded token (default: the "
+                         "prompt length); the cache is the prompt compressed "
+                         "to B, relabelled as a cache at that position")
     ap.add_argument("--stochastic", action="store_true",
                     help="ForesightKV stochastic eviction (Gumbel noise per "
                          "slot in the policy)")
@@ -787,15 +813,20 @@ def main() -> int:
         print(json.dumps(run_prefill(args, w, dev)), flush=True)
         return 0
     L = w.evict_len
-    steps = args.steps if args.steps is not None else 2 * L
+    steps = args.steps if args.steps is not None else 4 * L
     warmup = args.warmup if args.warmup is not None else L
     pool = min(warmup + steps, 3 * L)
     log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")
     t0 = time.perf_counter()
     scorer = "gate" if w.scorer == "gate" else args.scorer
+    if args.start_pos is not None and args.start_pos < w.n0:
+        print(json.dumps({"error": "--start-pos must be at least the prompt "
+                          f"length {w.n0}"}))
+        return 2
     stack = Stack(w, args.seed, pool, dev, decay=args.decay,
-                  scorer=scorer, stochastic=args.stochastic)
+                  scorer=scorer, stochastic=args.stochastic,
+                  start_pos=args.start_pos)
     log(f"set-up {time.perf_counter() - t0:.1f} s")
 
     for i in range(warmup):
@@ -908,6 +939,8 @@ def main() -> int:
                    "n_q_heads": w.n_q, "head_dim": w.head_dim,
                    "budget": w.budget, "sinks": w.sinks, "window": w.window,
                    "evict_len": w.evict_len, "prompt_len": w.n0,
+                   "start_pos": (w.n0 if args.start_pos is None
+                                 else args.start_pos),
                    "scorer": (f"mlp {2 * w.head_dim}-{w.hidden}-1 relu"
                               if scorer == "mlp" else
                               f"gate {w.hidden}-1 sigmoid on hidden states"
@@ -919,12 +952,14 @@ def main() -> int:
                    "parallelism": "none"},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "achievable_copy_gbps": None,
         "roofline": roof,
         "cpu_baseline": None,
     }
+    del stack
+    torch.cuda.empty_cache()
+    result["achievable_copy_gbps"] = round(achievable_copy_gbps(dev), 1)
     if not args.no_cpu_baseline:
-        del stack
-        torch.cuda.empty_cache()
         cs = args.cpu_steps if args.cpu_steps is not None else 2 * L
         cbatch = args.cpu_batch
         if cbatch is None:
