@@ -147,31 +147,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
   const int new_slot = a.new_slot;
   const char* knew = nullptr;
   const char* vnew = nullptr;
+  // Fused append: the workgroup whose rows contain the new slot stores the
+  // new row into the cache (and, for hidden-state scorers, the workgroup of
+  // KV head 0 copies the token's hidden state into the pending-token buffer
+  // of its batch row). No thread of this launch reads that slot from the
+  // cache: the row is read straight from k_new / v_new below. The row is
+  // loaded here and stored after the output, so its memory latency overlaps
+  // the stream instead of delaying it; the hidden state (kilobytes, too many
+  // registers to hold through the stream) is copied after the output.
+  constexpr int NV = ROWB / 16;
+  const bool appends = new_slot >= 0 && new_slot >= r_begin && new_slot < r_end;
+  u32x4 app = {0u, 0u, 0u, 0u};
   if (new_slot >= 0) {
     knew = (const char*)a.k_new + slice * ROWB;
     vnew = (const char*)a.v_new + slice * ROWB;
-    // Fused append: the workgroup whose rows contain the new slot stores the
-    // new row into the cache. No thread of this launch reads that slot from
-    // the cache: the row is read straight from k_new / v_new below.
-    if (new_slot >= r_begin && new_slot < r_end) {
-      constexpr int NV = ROWB / 16;
-      char* ks = (char*)a.k_store + (slice * (size_t)a.cap + new_slot) * ROWB;
-      char* vs = (char*)a.v_store + (slice * (size_t)a.cap + new_slot) * ROWB;
+    if (appends) {
       if (tid < NV) {
-        ((u32x4*)ks)[tid] = ((const u32x4*)knew)[tid];
+        app = ((const u32x4*)knew)[tid];
       } else if (tid < 2 * NV) {
-        ((u32x4*)vs)[tid - NV] = ((const u32x4*)vnew)[tid - NV];
-      } else if (tid == 2 * NV) {
-        a.pos[slice * (size_t)a.cap + new_slot] = a.new_pos;
-      }
-      // The same workgroup of KV head 0 copies the token's hidden state
-      // into the pending-token buffer of its batch row.
-      if (a.hidden_new && h == 0) {
-        const char* hs = (const char*)a.hidden_new + (size_t)b * a.hidden_bytes;
-        char* hd = (char*)a.hidden_buf +
-                   ((size_t)b * a.hidden_rows + a.hidden_row) * a.hidden_bytes;
-        for (int i = tid; i < a.hidden_bytes / 16; i += kThreads)
-          ((u32x4*)hd)[i] = ((const u32x4*)hs)[i];
+        app = ((const u32x4*)vnew)[tid - NV];
       }
     }
   }
@@ -510,6 +504,42 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
       if (d == 0) {
         part[D] = M;
         part[D + 1] = L;
+      }
+    }
+  }
+
+  // Stores of the fused append (payload loaded at the start).
+  if (appends) {
+    char* ks = (char*)a.k_store + (slice * (size_t)a.cap + new_slot) * ROWB;
+    char* vs = (char*)a.v_store + (slice * (size_t)a.cap + new_slot) * ROWB;
+    if (tid < NV) {
+      ((u32x4*)ks)[tid] = app;
+    } else if (tid < 2 * NV) {
+      ((u32x4*)vs)[tid - NV] = app;
+    } else if (tid == 2 * NV) {
+      a.pos[slice * (size_t)a.cap + new_slot] = a.new_pos;
+    }
+    if (a.hidden_new && h == 0) {
+      // Four chunks per thread in flight before their stores.
+      constexpr int kHidRegs = 4;
+      const int n = a.hidden_bytes / 16;
+      const u32x4* hs =
+          (const u32x4*)((const char*)a.hidden_new + (size_t)b * a.hidden_bytes);
+      u32x4* hd = (u32x4*)((char*)a.hidden_buf +
+                           ((size_t)b * a.hidden_rows + a.hidden_row) *
+                               a.hidden_bytes);
+      for (int i0 = tid; i0 < n; i0 += kHidRegs * kThreads) {
+        u32x4 t[kHidRegs];
+#pragma unroll
+        for (int r = 0; r < kHidRegs; ++r) {
+          const int i = i0 + r * kThreads;
+          if (i < n) t[r] = hs[i];
+        }
+#pragma unroll
+        for (int r = 0; r < kHidRegs; ++r) {
+          const int i = i0 + r * kThreads;
+          if (i < n) hd[i] = t[r];
+        }
       }
     }
   }
