@@ -137,9 +137,51 @@ def evict_extra_bytes(w, n_before: int, moved: int, scorer: str = "mlp") -> int:
     append = slices * (2 * d * e * 2 + 4)
     score = score_bytes(w, scorer)
     cand = n_before - w.sinks - w.window
-    select = slices * (cand * 4 + w.budget * 4)
+    select = slices * (cand * 8 + w.budget * 4)
     compact = moved * 2 * (2 * d * e + 8)
     return append + score + select + compact
+
+
+def compress_summary(w, stack, scorer: str) -> dict:
+    """Per-layer time and bytes of the one-shot prompt compression that
+    set-up runs in every layer (score all n0 prompt tokens, select B, compact
+    in place): median over the layers after the first, from HIP events on
+    the launch stream. Bytes: scoring reads every prompt row (the K and V
+    rows for the MLP scorer, the hidden states for the gate) and writes a
+    score per row and KV head; select reads each entry's score and position
+    and writes B kept slots; compaction reads and writes each moved row."""
+    import statistics
+    d, e = w.head_dim, w.elem_bytes
+    slices = w.batch * w.n_kv
+    if scorer == "gate":
+        score_b = w.batch * w.n0 * w.hidden * 2 + slices * w.n0 * 4 + \
+            w.n_kv * w.hidden * 2
+    elif scorer == "mlp":
+        score_b = slices * w.n0 * (2 * d * e + 4) + \
+            w.n_kv * (2 * d * w.hidden * 2 + w.hidden * 4)
+    else:
+        score_b = None
+    select_b = slices * (w.n0 * 8 + w.budget * 4)
+    evs = stack.compress_events[1:] or stack.compress_events
+    moved = [int(m.item()) for m in stack.compress_moved]
+    moved = moved[1:] if len(moved) > 1 else moved
+    parts = [statistics.median(ev[i].elapsed_time(ev[i + 1]) * 1e3
+                               for ev in evs) for i in range(3)]
+    total = statistics.median(ev[0].elapsed_time(ev[3]) * 1e3 for ev in evs)
+    compact_b = int(statistics.median(moved)) * 2 * (2 * d * e + 8)
+    out = {"per_layer_us": round(total, 1), "score_us": round(parts[0], 1),
+           "select_us": round(parts[1], 1), "compact_us": round(parts[2], 1),
+           "prompt_tokens": w.n0, "batch": w.batch, "budget": w.budget,
+           "layers_timed": len(evs)}
+    if score_b is not None:
+        tot_b = score_b + select_b + compact_b
+        out.update({"bytes": tot_b, "gbps": round(tot_b / total / 1e3, 1),
+                    "score_gbps": round(score_b / parts[0] / 1e3, 1),
+                    "compact_gbps": round(compact_b / parts[2] / 1e3, 1)})
+    out["tokens_per_s"] = round(w.batch * w.n0 / (total * 1e-6), 1)
+    out["note"] = ("one-shot compression of the prompt in one layer during "
+                   "set-up, median over layers 2..L, HIP events")
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -172,6 +214,8 @@ class Stack:
         keep_pre = torch.empty((b, H, w.budget), dtype=torch.int32, device=dev)
         self.ws = kve.alloc_workspace(self.shape, self.shape.capacity, dev)
         self.caches, self.scorers, self.runners = [], [], []
+        self.compress_events, self.compress_moved = [], []
+        keep_idx = torch.arange(w.budget, dtype=torch.int32, device=dev)
         self.k_pool, self.v_pool, self.q_pool = [], [], []
         self.h_pool, self.h_buf = [], []  # gate scorer: hidden states
         cfg = w.cfg_id
@@ -209,16 +253,27 @@ class Stack:
             scratch.v.copy_(dn((b, H, w.n0, d), seed, (cfg, l, 0, T["v0"]),
                                torch.bfloat16, dev))
             scratch.pos.copy_(scratch_pos.expand(b, H, w.n0))
+            # The one-shot compression of the prompt (score every prompt
+            # token, select, compact), timed per layer with events.
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             if scorer == "gate":
                 hid0 = dn((b, w.n0, w.hidden), seed, (cfg, l, 0, T["hidden0"]),
                           torch.bfloat16, dev)
+                ev[0].record()
                 kve.kve_score(pre_shape, sc, scratch, 0, w.n0, hidden=hid0)
+                ev[1].record()
                 del hid0
             else:
+                ev[0].record()
                 kve.kve_score(pre_shape, sc, scratch, 0, w.n0)
+                ev[1].record()
             kve.kve_select_evict(pre_shape, self.policy, scratch, w.n0,
                                  w.budget, keep_pre)
+            ev[2].record()
             kve.kve_compact(pre_shape, scratch, w.n0, keep_pre, w.budget)
+            ev[3].record()
+            self.compress_events.append(ev)
+            self.compress_moved.append((keep_pre != keep_idx).sum())
             c = kve.CacheTensors.empty(self.shape, dev)
             B = w.budget
             c.k[:, :, :B].copy_(scratch.k[:, :, :B])
@@ -954,6 +1009,7 @@ def main() -> int:
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "achievable_copy_gbps": None,
         "roofline": roof,
+        "prompt_compress": compress_summary(w, stack, scorer),
         "cpu_baseline": None,
     }
     del stack

@@ -62,6 +62,13 @@ __global__ __launch_bounds__(64) void append_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
+// Every pass over a slice's entries runs in sweeps of kSelV entries per
+// thread (entry c = base + v * kSelThreads + tid): the index is clamped to
+// len - 1, so all loads of a sweep are in bounds and unconditional and are in
+// flight together, and entries past len are masked afterwards. A pass over
+// 131072 entries is 16 sweeps instead of 256 dependent load round trips.
+constexpr int kSelV = 16;
+constexpr int kSelSweep = kSelThreads * kSelV;
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
   // Number of set bits of `mask` in lanes below this one.
@@ -69,32 +76,11 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), lo);
 }
 
-// Exclusive block-wide prefix count of `flag` (slot order = thread order);
-// returns the prefix and writes the block total to *total.
-__device__ __forceinline__ uint32_t block_excl_count(bool flag, uint32_t* sh,
-                                                     uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint64_t mask = __builtin_amdgcn_ballot_w64(flag);
-  const uint32_t in_wave = lane_prefix(mask);
-  if (lane == 0) sh[wave] = (uint32_t)__builtin_popcountll(mask);
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const uint32_t c = sh[w];
-    before += (w < wave) ? c : 0u;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + in_wave;
-}
-
 // Radix select over 32-bit keys: the value of the `rank`-th smallest key
 // (1-based) among the entries i < len with take(i), and how many of those
 // keys equal it must still be taken (`rank` minus the number of smaller
 // keys). `count_eq` receives how many such entries have exactly that key.
+// take and key_of must be safe to call on any index below len.
 template <typename KeyFn, typename TakeFn>
 __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
                              TakeFn take, uint32_t* hist, uint32_t* wsum,
@@ -110,10 +96,20 @@ __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
       sh[2] = 0u;
     }
     __syncthreads();
-    for (int c = tid; c < len; c += kSelThreads) {
-      if (!take(c)) continue;
-      const uint32_t k = key_of(c);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    for (int base = 0; base < len; base += kSelSweep) {
+      bool t[kSelV];
+      uint32_t k[kSelV];
+#pragma unroll
+      for (int v = 0; v < kSelV; ++v) {
+        const int c = base + v * kSelThreads + tid;
+        const int cc = min(c, len - 1);
+        t[v] = (c < len) & take(cc);
+        k[v] = key_of(cc);
+      }
+#pragma unroll
+      for (int v = 0; v < kSelV; ++v)
+        if (t[v] && (k[v] & mask) == prefix)
+          atomicAdd(&hist[(k[v] >> shift) & 255u], 1u);
     }
     __syncthreads();
     // Inclusive scan of the 256 bins by threads 0..255 (4 waves).
@@ -161,6 +157,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const float* gs = gumbel ? gumbel + slice * (size_t)cap : nullptr;
   int32_t* out = keep + slice * (size_t)n_keep;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
 
   if (n_keep >= len) {  // nothing to evict: identity
     for (int i = tid; i < len; i += kSelThreads) out[i] = i;
@@ -175,10 +173,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   // 1. Newest position present.
   int32_t mx = INT32_MIN;
-  for (int c = tid; c < len; c += kSelThreads) mx = max(mx, ps[c]);
+  for (int base = 0; base < len; base += kSelSweep) {
+#pragma unroll
+    for (int v = 0; v < kSelV; ++v)
+      mx = max(mx, ps[min(base + v * kSelThreads + tid, len - 1)]);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
-  if ((tid & 63) == 0) sh_max[tid >> 6] = mx;
+  if (lane == 0) sh_max[wave] = mx;
   __syncthreads();
   int32_t newest = sh_max[0];
 #pragma unroll
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const long long last_eligible = (long long)newest - W;
   auto is_cand = [&](int c) {
     const int32_t p = ps[c];
-    return p >= S && (long long)p <= last_eligible;
+    return (p >= S) & ((long long)p <= last_eligible);
   };
   // Ranking key: the score, or under temporal decay the static priority
   // score - position * log(gamma) (KVpop Eq. 20), each operation rounded to
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                  &count_eq);
     uint32_t pthr = 0xffffffffu;
     if (need < count_eq) {
-      auto tied = [&](int c) { return take(c) && key_of(c) == thr; };
+      auto tied = [&](int c) { return take(c) & (key_of(c) == thr); };
       uint32_t pneed, pcount;
       radix_select(len, need, pkey, tied, hist, wsum, sh, &pthr, &pneed,
                    &pcount);
@@ -219,8 +221,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     *thr_out = thr;
     *pthr_out = pthr;
   };
+  // Non-short-circuit forms, so the loads of both operands are always made.
   auto before = [&](uint32_t k, int c, uint32_t thr, uint32_t pthr) {
-    return k < thr || (k == thr && (uint32_t)ps[c] <= pthr);
+    return (k < thr) | ((k == thr) & ((uint32_t)ps[c] <= pthr));
   };
 
   // 2-3. Deterministic: evict the r lowest candidates.
@@ -237,30 +240,61 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (tid == 0) ncand_sh = 0;
     __syncthreads();
     uint32_t nc = 0;
-    for (int c = tid; c < len; c += kSelThreads) nc += is_cand(c) ? 1u : 0u;
+    for (int base = 0; base < len; base += kSelSweep) {
+#pragma unroll
+      for (int v = 0; v < kSelV; ++v) {
+        const int c = base + v * kSelThreads + tid;
+        nc += ((c < len) & is_cand(min(c, len - 1))) ? 1u : 0u;
+      }
+    }
     atomicAdd(&ncand_sh, nc);
     __syncthreads();
     const uint32_t pool = min(2u * r, ncand_sh);
     cut(pool, skey, is_cand, &thr, &pthr);
-    auto in_pool = [&](int c) { return is_cand(c) && before(skey(c), c, thr, pthr); };
+    auto in_pool = [&](int c) {
+      return is_cand(c) & before(skey(c), c, thr, pthr);
+    };
     cut(r, dkey, in_pool, &gthr, &gpthr);
   }
   auto evicted = [&](int c) {
-    if (!is_cand(c) || !before(skey(c), c, thr, pthr)) return false;
-    return !gs || before(dkey(c), c, gthr, gpthr);
+    const bool low = is_cand(c) & before(skey(c), c, thr, pthr);
+    return gs ? (low & before(dkey(c), c, gthr, gpthr)) : low;
   };
 
-  // 4. Kept slots, ascending.
-  __shared__ uint32_t scan_sh[kSelWaves];
+  // 4. Kept slots, ascending. A sweep holds kSelV slabs of kSelThreads
+  // consecutive slots (slab v, slot base + v * kSelThreads + tid): one
+  // ballot count per wave and slab, one barrier, then every kept entry's
+  // rank is the kept count of the earlier slabs, of the earlier waves of its
+  // slab and of the lower lanes of its wave.
+  __shared__ uint32_t cnt_sh[kSelV][kSelWaves];
   uint32_t carry = 0;
-  for (int base = 0; base < len; base += kSelThreads) {
-    const int c = base + tid;
-    bool kept = false;
-    if (c < len) kept = !evicted(c);
-    uint32_t tot;
-    const uint32_t idx = carry + block_excl_count(kept, scan_sh, &tot);
-    if (kept && idx < (uint32_t)n_keep) out[idx] = c;
-    carry += tot;
+  for (int base = 0; base < len; base += kSelSweep) {
+    uint64_t m[kSelV];
+#pragma unroll
+    for (int v = 0; v < kSelV; ++v) {
+      const int c = base + v * kSelThreads + tid;
+      const bool kept = (c < len) & !evicted(min(c, len - 1));
+      m[v] = __builtin_amdgcn_ballot_w64(kept);
+      if (lane == 0) cnt_sh[v][wave] = (uint32_t)__builtin_popcountll(m[v]);
+    }
+    __syncthreads();
+    uint32_t before_slab = carry;
+#pragma unroll
+    for (int v = 0; v < kSelV; ++v) {
+      uint32_t in_slab = 0, slab_total = 0;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) {
+        const uint32_t cw = cnt_sh[v][w];
+        in_slab += (w < wave) ? cw : 0u;
+        slab_total += cw;
+      }
+      const int c = base + v * kSelThreads + tid;
+      const uint32_t idx = before_slab + in_slab + lane_prefix(m[v]);
+      if (((m[v] >> lane) & 1ull) && idx < (uint32_t)n_keep) out[idx] = c;
+      before_slab += slab_total;
+    }
+    carry = before_slab;
+    __syncthreads();  // cnt_sh is rewritten by the next sweep
   }
 }
 
