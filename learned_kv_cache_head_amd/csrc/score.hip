@@ -197,41 +197,88 @@ __global__ __launch_bounds__(64) void mlp_valu_kernel(MlpLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate scorer on MFMA: one wave = 16 tokens x all H heads.
+// Gate scorer on MFMA (Fast KVzip section 3.1: a linear map of the token's
+// hidden state per KV head, then a sigmoid). The contraction is
+// (tokens x D) x (D x H), H <= 16 padded to the 16 columns of
+// v_mfma_f32_16x16x32_bf16. One wave = kGateRG groups of 16 tokens x all H
+// heads: each 16-byte weight load feeds kGateRG MFMAs, so the weight reads
+// (from L2) are a quarter of the hidden-state stream, and a k step keeps
+// kGateRG hidden-state loads per lane in flight, kGateUnroll steps ahead.
 // ---------------------------------------------------------------------------
+constexpr int kGateRG = 4;                       // 16-token groups per wave
+constexpr int kGateRowsPerWG = 4 * 16 * kGateRG;  // 4 waves
+
 __global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rows = g.slot_end - g.slot_begin;
-  const int r0 = blockIdx.x * 64 + wave * 16;
+  const int r0 = blockIdx.x * kGateRowsPerWG + wave * 16 * kGateRG;
   if (r0 >= rows) return;
-  const int rrow = r0 + (lane & 15);
-  const int rc = rrow < rows ? rrow : rows - 1;
-  const uint16_t* x =
-      (const uint16_t*)g.hidden + (size_t)b * g.batch_stride + (size_t)rc * g.in_dim;
+  const uint16_t* x[kGateRG];
+#pragma unroll
+  for (int gi = 0; gi < kGateRG; ++gi) {
+    const int rrow = r0 + gi * 16 + (lane & 15);
+    const int rc = rrow < rows ? rrow : rows - 1;  // clamp: in bounds
+    x[gi] = (const uint16_t*)g.hidden + (size_t)b * g.batch_stride +
+            (size_t)rc * g.in_dim;
+  }
   const int n = lane & 15;
   const bool has_w = n < g.H;
   const uint16_t* w = (const uint16_t*)g.w + (size_t)(has_w ? n : 0) * g.in_dim;
+  // Lanes of columns n >= H load weight row 0 (in bounds, no branch): an
+  // MFMA output column depends only on its own B column, and those columns
+  // are never stored.
   const int kq = (lane >> 4) * 8;
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, u32x4{0u, 0u, 0u, 0u});
+  f32x4_t acc[kGateRG];
+#pragma unroll
+  for (int gi = 0; gi < kGateRG; ++gi) acc[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const u32x4& wb, const u32x4& xa, int gi) {
+    acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, wb),
+        acc[gi], 0, 0, 0);
+  };
+  auto wload = [&](int kidx) { return *(const u32x4*)(w + kidx); };
+  // k blocks of kGateKU steps: every load of a block is issued before its
+  // MFMAs.
+  constexpr int kGateKU = 4;
   const int ksteps = g.in_dim / 32;
-#pragma unroll 8
-  for (int ks = 0; ks < ksteps; ++ks) {
+  int ks = 0;
+  for (; ks + kGateKU <= ksteps; ks += kGateKU) {
+    u32x4 wb[kGateKU], xa[kGateKU][kGateRG];
+#pragma unroll
+    for (int u = 0; u < kGateKU; ++u) {
+      const int kidx = (ks + u) * 32 + kq;
+      wb[u] = wload(kidx);
+#pragma unroll
+      for (int gi = 0; gi < kGateRG; ++gi)
+        xa[u][gi] = *(const u32x4*)(x[gi] + kidx);
+    }
+    // Keep the scheduler from interleaving the block's loads with its MFMAs
+    // (it would reuse the registers and leave few loads in flight).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kGateKU; ++u)
+#pragma unroll
+      for (int gi = 0; gi < kGateRG; ++gi) step(wb[u], xa[u][gi], gi);
+  }
+  for (; ks < ksteps; ++ks) {
     const int kidx = ks * 32 + kq;
-    const bf16x8_t A = load8(x + kidx);
-    const bf16x8_t B = has_w ? load8(w + kidx) : zero;
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+    const u32x4 wb = wload(kidx);
+#pragma unroll
+    for (int gi = 0; gi < kGateRG; ++gi)
+      step(wb, *(const u32x4*)(x[gi] + kidx), gi);
   }
   if (has_w) {
     const float bias = g.b ? g.b[n] : 0.f;
     float* out = g.score + ((size_t)b * g.H + n) * g.cap + g.slot_begin;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 4 * (lane >> 4) + i;
-      if (row < rows) out[row] = 1.f / (1.f + __expf(-(acc[i] + bias)));
-    }
+    for (int gi = 0; gi < kGateRG; ++gi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + gi * 16 + 4 * (lane >> 4) + i;
+        if (row < rows) out[row] = 1.f / (1.f + __expf(-(acc[gi][i] + bias)));
+      }
   }
 }
 
@@ -505,7 +552,7 @@ hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
 hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s) {
   const int rows = g.slot_end - g.slot_begin;
   if (rows <= 0) return hipSuccess;
-  const dim3 grid((rows + 63) / 64, g.batch);
+  const dim3 grid((rows + kGateRowsPerWG - 1) / kGateRowsPerWG, g.batch);
   hipLaunchKernelGGL(gate_mfma_kernel, grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
