@@ -41,7 +41,7 @@ __device__ __forceinline__ float activate(float a, int act) {
 // operands before the MFMAs of the current one.
 // ---------------------------------------------------------------------------
 constexpr int kMlpWaves = 4;
-constexpr int kMlpTiles = 4;                       // tiles per wave
+constexpr int kMlpTiles = 8;                       // tiles per wave
 constexpr int kMlpRowsPerWG = kMlpWaves * kMlpTiles * 16;
 
 template <int D, int NB>
