@@ -282,6 +282,92 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
   }
 }
 
+// Few rows (the L pending tokens of a decode eviction): one workgroup of
+// kGateSmallWaves waves per batch row scores up to 64 tokens, each wave
+// taking a slice of the D contraction for all four 16-token groups; the
+// partial sums meet in LDS before the sigmoid. A single wave walking the whole
+// contraction would chain D / 128 dependent load blocks.
+constexpr int kGateSmallWaves = 16;
+constexpr int kGateSmallRows = 16 * kGateRG;  // 64
+
+__global__ __launch_bounds__(64 * kGateSmallWaves) void gate_mfma_small_kernel(
+    GateLaunch g) {
+  __shared__ f32x4_t red[kGateSmallWaves][kGateRG][64];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rows = g.slot_end - g.slot_begin;
+  const int r0 = blockIdx.x * kGateSmallRows;
+  const uint16_t* x[kGateRG];
+#pragma unroll
+  for (int gi = 0; gi < kGateRG; ++gi) {
+    const int rrow = r0 + gi * 16 + (lane & 15);
+    const int rc = rrow < rows ? rrow : rows - 1;  // clamp: in bounds
+    x[gi] = (const uint16_t*)g.hidden + (size_t)b * g.batch_stride +
+            (size_t)rc * g.in_dim;
+  }
+  const int n = lane & 15;
+  const uint16_t* w =
+      (const uint16_t*)g.w + (size_t)(n < g.H ? n : 0) * g.in_dim;
+  const int kq = (lane >> 4) * 8;
+  const int ksteps = g.in_dim / 32;
+  const int per = (ksteps + kGateSmallWaves - 1) / kGateSmallWaves;
+  const int k0 = wave * per;
+  const int k1 = min(ksteps, k0 + per);
+  f32x4_t acc[kGateRG];
+#pragma unroll
+  for (int gi = 0; gi < kGateRG; ++gi) acc[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const u32x4& wb, const u32x4& xa, int gi) {
+    acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, wb),
+        acc[gi], 0, 0, 0);
+  };
+  // Blocks of four steps, every load of a block ahead of its MFMAs.
+  constexpr int KU = 4;
+  int ks = k0;
+  for (; ks + KU <= k1; ks += KU) {
+    u32x4 wb[KU], xa[KU][kGateRG];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int kidx = (ks + u) * 32 + kq;
+      wb[u] = *(const u32x4*)(w + kidx);
+#pragma unroll
+      for (int gj = 0; gj < kGateRG; ++gj)
+        xa[u][gj] = *(const u32x4*)(x[gj] + kidx);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int gj = 0; gj < kGateRG; ++gj) step(wb[u], xa[u][gj], gj);
+  }
+  for (; ks < k1; ++ks) {
+    const int kidx = ks * 32 + kq;
+    const u32x4 wb = *(const u32x4*)(w + kidx);
+#pragma unroll
+    for (int gj = 0; gj < kGateRG; ++gj)
+      step(wb, *(const u32x4*)(x[gj] + kidx), gj);
+  }
+#pragma unroll
+  for (int gi = 0; gi < kGateRG; ++gi) red[wave][gi][lane] = acc[gi];
+  __syncthreads();
+  // Thread t: group t / 256, lane (t / 4) % 64, element t % 4.
+  const int gi = tid >> 8;
+  const int ol = (tid >> 2) & 63;
+  const int i = tid & 3;
+  float sum = 0.f;
+#pragma unroll
+  for (int wv = 0; wv < kGateSmallWaves; ++wv) sum += red[wv][gi][ol][i];
+  const int col = ol & 15;
+  const int row = r0 + gi * 16 + 4 * (ol >> 4) + i;
+  if (col < g.H && row < rows) {
+    const float bias = g.b ? g.b[col] : 0.f;
+    g.score[((size_t)b * g.H + col) * g.cap + g.slot_begin + row] =
+        1.f / (1.f + __expf(-(sum + bias)));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Low-rank sink-attention gate (Fast KVzip section 3.4) over hidden states.
 //
@@ -552,6 +638,11 @@ hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
 hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s) {
   const int rows = g.slot_end - g.slot_begin;
   if (rows <= 0) return hipSuccess;
+  if (rows <= kGateSmallRows) {
+    hipLaunchKernelGGL(gate_mfma_small_kernel, dim3(1, g.batch),
+                       dim3(64 * kGateSmallWaves), 0, s, g);
+    return hipGetLastError();
+  }
   const dim3 grid((rows + kGateRowsPerWG - 1) / kGateRowsPerWG, g.batch);
   hipLaunchKernelGGL(gate_mfma_kernel, grid, dim3(256), 0, s, g);
   return hipGetLastError();

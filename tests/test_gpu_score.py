@@ -70,6 +70,11 @@ GATE_CASES = [
     (1, 8, 5120, 64, 39321, 39385),  # a decode buffer of L = 64 tokens
     (2, 3, 256, 77, 10, 100),
     (1, 16, 1024, 130, 0, 130),
+    # at most 64 rows: the contraction split over 16 waves
+    (3, 16, 32, 1, 5, 10),           # one k step, one row
+    (2, 5, 1056, 50, 3, 60),         # 33 k steps: 3 per wave, no full block
+    (1, 8, 5120, 63, 0, 64),         # ragged group
+    (2, 8, 8192, 64, 0, 64),         # 16 k steps per wave: four full blocks
 ]
 
 
