@@ -105,12 +105,22 @@ _SIGS = {
 _lib = None
 
 
+_lib_path = None
+
+
 def load_library(path: Optional[str] = None):
-    """Load libkvevict.so (built by ``__graft_entry__.build()``)."""
-    global _lib
-    if _lib is not None and path is None:
-        return _lib
-    p = path or library_path()
+    """Load libkvevict.so (built by ``__graft_entry__.build()``), or the
+    build at ``path``; every call of this module then goes to it. One process
+    holds one build: two copies of the library's device code in one process
+    fail to launch, so asking for a second path raises."""
+    global _lib, _lib_path
+    p = os.path.abspath(path or library_path())
+    if _lib is not None:
+        if path is None or p == _lib_path:
+            return _lib
+        raise RuntimeError(
+            f"libkvevict is already loaded from {_lib_path}; one process "
+            f"cannot also load {p}")
     if not os.path.exists(p):
         raise RuntimeError(
             f"libkvevict is not built ({p} missing); run "
@@ -120,8 +130,7 @@ def load_library(path: Optional[str] = None):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if path is None:
-        _lib = lib
+    _lib, _lib_path = lib, p
     return lib
 
 

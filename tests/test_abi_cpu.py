@@ -375,3 +375,13 @@ def test_binding_refuses_host_small_or_strided_buffers():
                     wdtype=kve.BF16)
     with pytest.raises(ValueError):
         kve._check_scorer(s, sc)
+
+
+def test_one_library_per_process(tmp_path):
+    """Every call goes to the one loaded build; a second build is refused
+    (two copies of the device code in one process fail to launch)."""
+    lib = _lib()
+    assert kve.load_library() is lib
+    assert kve.load_library(kve.library_path()) is lib
+    with pytest.raises(RuntimeError, match="already loaded"):
+        kve.load_library(str(tmp_path / "libkvevict.so"))
