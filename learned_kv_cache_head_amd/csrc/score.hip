@@ -283,25 +283,26 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
 }
 
 // Few rows (the L pending tokens of a decode eviction): one workgroup of
-// kGateSmallWaves waves per batch row scores up to 64 tokens, each wave
-// taking a slice of the D contraction for all four 16-token groups; the
-// partial sums meet in LDS before the sigmoid. A single wave walking the whole
-// contraction would chain D / 128 dependent load blocks.
+// kGateSmallWaves waves per 16 tokens, each wave taking a slice of the D
+// contraction; the partial sums meet in LDS before the sigmoid. A single wave
+// walking the whole contraction would chain D / 128 dependent load blocks,
+// and one workgroup for all the tokens would be held to one CU's bandwidth.
 constexpr int kGateSmallWaves = 16;
-constexpr int kGateSmallRows = 16 * kGateRG;  // 64
+constexpr int kGateSmallMaxRows = 64;  // row counts served by this kernel
 
 __global__ __launch_bounds__(64 * kGateSmallWaves) void gate_mfma_small_kernel(
     GateLaunch g) {
-  __shared__ f32x4_t red[kGateSmallWaves][kGateRG][64];
+  constexpr int RG = 1;  // 16-token groups per workgroup
+  __shared__ f32x4_t red[kGateSmallWaves][RG][64];
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int rows = g.slot_end - g.slot_begin;
-  const int r0 = blockIdx.x * kGateSmallRows;
-  const uint16_t* x[kGateRG];
+  const int r0 = blockIdx.x * 16 * RG;
+  const uint16_t* x[RG];
 #pragma unroll
-  for (int gi = 0; gi < kGateRG; ++gi) {
+  for (int gi = 0; gi < RG; ++gi) {
     const int rrow = r0 + gi * 16 + (lane & 15);
     const int rc = rrow < rows ? rrow : rows - 1;  // clamp: in bounds
     x[gi] = (const uint16_t*)g.hidden + (size_t)b * g.batch_stride +
@@ -315,9 +316,9 @@ __global__ __launch_bounds__(64 * kGateSmallWaves) void gate_mfma_small_kernel(
   const int per = (ksteps + kGateSmallWaves - 1) / kGateSmallWaves;
   const int k0 = wave * per;
   const int k1 = min(ksteps, k0 + per);
-  f32x4_t acc[kGateRG];
+  f32x4_t acc[RG];
 #pragma unroll
-  for (int gi = 0; gi < kGateRG; ++gi) acc[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int gi = 0; gi < RG; ++gi) acc[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto step = [&](const u32x4& wb, const u32x4& xa, int gi) {
     acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
         __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, wb),
@@ -327,32 +328,33 @@ __global__ __launch_bounds__(64 * kGateSmallWaves) void gate_mfma_small_kernel(
   constexpr int KU = 4;
   int ks = k0;
   for (; ks + KU <= k1; ks += KU) {
-    u32x4 wb[KU], xa[KU][kGateRG];
+    u32x4 wb[KU], xa[KU][RG];
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int kidx = (ks + u) * 32 + kq;
       wb[u] = *(const u32x4*)(w + kidx);
 #pragma unroll
-      for (int gj = 0; gj < kGateRG; ++gj)
+      for (int gj = 0; gj < RG; ++gj)
         xa[u][gj] = *(const u32x4*)(x[gj] + kidx);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < KU; ++u)
 #pragma unroll
-      for (int gj = 0; gj < kGateRG; ++gj) step(wb[u], xa[u][gj], gj);
+      for (int gj = 0; gj < RG; ++gj) step(wb[u], xa[u][gj], gj);
   }
   for (; ks < k1; ++ks) {
     const int kidx = ks * 32 + kq;
     const u32x4 wb = *(const u32x4*)(w + kidx);
 #pragma unroll
-    for (int gj = 0; gj < kGateRG; ++gj)
+    for (int gj = 0; gj < RG; ++gj)
       step(wb, *(const u32x4*)(x[gj] + kidx), gj);
   }
 #pragma unroll
-  for (int gi = 0; gi < kGateRG; ++gi) red[wave][gi][lane] = acc[gi];
+  for (int gi = 0; gi < RG; ++gi) red[wave][gi][lane] = acc[gi];
   __syncthreads();
-  // Thread t: group t / 256, lane (t / 4) % 64, element t % 4.
+  // Thread t < 256 * RG: group t / 256, lane (t / 4) % 64, element t % 4.
+  if (tid >= 256 * RG) return;
   const int gi = tid >> 8;
   const int ol = (tid >> 2) & 63;
   const int i = tid & 3;
@@ -638,8 +640,8 @@ hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
 hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s) {
   const int rows = g.slot_end - g.slot_begin;
   if (rows <= 0) return hipSuccess;
-  if (rows <= kGateSmallRows) {
-    hipLaunchKernelGGL(gate_mfma_small_kernel, dim3(1, g.batch),
+  if (rows <= kGateSmallMaxRows) {
+    hipLaunchKernelGGL(gate_mfma_small_kernel, dim3((rows + 15) / 16, g.batch),
                        dim3(64 * kGateSmallWaves), 0, s, g);
     return hipGetLastError();
   }

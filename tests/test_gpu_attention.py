@@ -29,6 +29,7 @@ CASES = [
     ("bf16", 128, 4, 2, 1, 1, 64, 1.0),         # single retained row
     ("bf16", 128, 4, 2, 1, 33, 64, 1.0),        # ragged tail
     ("bf16", 128, 5, 8, 1, 5000, 5000, 1.0),    # group 5, many splits
+    ("bf16", 128, 5, 8, 1, 39353, 39385, 1.0),  # Qwen2.5-14B decode layer
     ("bf16", 64, 1, 3, 2, 300, 320, 1.0),
     ("f32", 128, 8, 2, 1, 700, 700, 1.0),
     ("bf16", 128, 3, 4, 3, 4097, 4100, 1.0),
