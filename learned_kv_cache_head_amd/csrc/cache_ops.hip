@@ -69,6 +69,14 @@ constexpr int kSelWaves = kSelThreads / 64;
 // 131072 entries is 16 sweeps instead of 256 dependent load round trips.
 constexpr int kSelV = 16;
 constexpr int kSelSweep = kSelThreads * kSelV;
+// Slices of up to kSelCacheMax entries (when few enough slices run that one
+// workgroup per CU fills the chip) keep every entry's ranking key in LDS,
+// with kSelNoCand marking entries that are not candidates: the radix passes
+// and the ordered pass then read LDS, and only the newest-position pass and
+// the pass that fills the keys read HBM. kSelNoCand is the key of a NaN
+// score, outside the contract.
+constexpr int kSelCacheMax = 40000;  // 160,000 bytes of LDS
+constexpr uint32_t kSelNoCand = 0xffffffffu;
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
   // Number of set bits of `mask` in lanes below this one.
@@ -147,6 +155,7 @@ __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
   *count_eq_out = count_eq;
 }
 
+template <bool CACHE>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* score, const int32_t* pos, const float* log_gamma,
     const float* gumbel, int H, int cap, int len, int n_keep, int S, int W,
@@ -170,6 +179,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ uint32_t wsum[kSelWaves];
   __shared__ uint32_t sh[4];
   __shared__ int32_t sh_max[kSelWaves];
+  __shared__ uint32_t kc[CACHE ? kSelCacheMax : 1];  // keys (CACHE)
 
   // 1. Newest position present.
   int32_t mx = INT32_MIN;
@@ -234,7 +244,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   uint32_t gthr = 0, gpthr = 0;
   auto dkey = [&](int c) { return ~score_key(__fadd_rn(-fkey(c), gs[c])); };
   if (!gs) {
-    cut(r, skey, is_cand, &thr, &pthr);
+    if constexpr (CACHE) {
+      for (int base = 0; base < len; base += kSelSweep) {
+        uint32_t kv[kSelV];
+#pragma unroll
+        for (int v = 0; v < kSelV; ++v) {
+          const int cc = min(base + v * kSelThreads + tid, len - 1);
+          const uint32_t k = skey(cc);  // loaded whether or not a candidate
+          kv[v] = is_cand(cc) ? k : kSelNoCand;
+        }
+#pragma unroll
+        for (int v = 0; v < kSelV; ++v) {
+          const int c = base + v * kSelThreads + tid;
+          if (c < len) kc[c] = kv[v];
+        }
+      }
+      __syncthreads();
+      auto ckey = [&](int c) { return kc[c]; };
+      auto ccand = [&](int c) { return kc[c] != kSelNoCand; };
+      cut(r, ckey, ccand, &thr, &pthr);
+    } else {
+      cut(r, skey, is_cand, &thr, &pthr);
+    }
   } else {
     __shared__ uint32_t ncand_sh;
     if (tid == 0) ncand_sh = 0;
@@ -257,6 +288,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     cut(r, dkey, in_pool, &gthr, &gpthr);
   }
   auto evicted = [&](int c) {
+    if constexpr (CACHE) {
+      if (!gs) {
+        // Positions are read only when the cut falls inside a tie.
+        const uint32_t k = kc[c];
+        return (k != kSelNoCand) &
+               ((k < thr) | ((k == thr) & (pthr == 0xffffffffu ||
+                                            (uint32_t)ps[c] <= pthr)));
+      }
+    }
     const bool low = is_cand(c) & before(skey(c), c, thr, pthr);
     return gs ? (low & before(dkey(c), c, gthr, gpthr)) : low;
   };
@@ -395,9 +435,17 @@ hipError_t launch_select(const float* score, const int32_t* pos,
                          const float* log_gamma, const float* gumbel, int H,
                          int slices, int cap, int len, int n_keep, int S,
                          int W, int32_t* keep, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(slices), dim3(kSelThreads), 0, s,
-                     score, pos, log_gamma, gumbel, H, cap, len, n_keep, S, W,
-                     keep);
+  // The key cache takes all of a CU's LDS: used when few slices run.
+  const bool cache = !gumbel && len > 2048 && len <= kSelCacheMax &&
+                     slices <= 256;
+  if (cache)
+    hipLaunchKernelGGL(select_kernel<true>, dim3(slices), dim3(kSelThreads), 0,
+                       s, score, pos, log_gamma, gumbel, H, cap, len, n_keep,
+                       S, W, keep);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3(slices), dim3(kSelThreads),
+                       0, s, score, pos, log_gamma, gumbel, H, cap, len,
+                       n_keep, S, W, keep);
   return hipGetLastError();
 }
 

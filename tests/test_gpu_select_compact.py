@@ -40,6 +40,10 @@ SELECT_CASES = [
     (2, 3, 10, 5, 2, 2),           # k = 0: sinks + window only
     (3, 5, 40, 40, 1, 2),          # nothing to evict
     (4, 512, 39385, 39321, 1, 8),  # Qwen2.5-14B decode eviction
+    # keys held in LDS up to 40000 entries (few slices), global beyond
+    (4, 128, 40000, 30000, 1, 2),
+    (4, 128, 40001, 30000, 1, 2),
+    (4, 64, 4096, 1024, 32, 8),    # 256 slices, LDS keys
 ]
 
 
