@@ -111,3 +111,60 @@ def test_decode_attention_deterministic_and_len_sweep():
             ref, _ = O.decode_attention(Qs.f64[0, h * G:(h + 1) * G],
                                         Ks.f64[0, h, :n], Vs.f64[0, h, :n])
             attn_close(got[0, h * G:(h + 1) * G], ref, f"len {n} h{h}")
+
+
+@pytest.mark.parametrize("batch,n", [(96, 1088), (2, 1087)],
+                         ids=["unsplit-b96", "split-b2"])
+def test_decode_attention_in_hip_graph(batch, n):
+    """The decode-attention launches (attention, and the split merge when
+    the rows are split) replay from a captured HIP graph: the library
+    allocates nothing and records no memset, so every replay, with eager
+    launches and synchronisations between replays, equals the eager result
+    bitwise and the oracle within tolerance."""
+    import torch
+    k = kve()
+    B, H, G, D, cap = batch, 8, 4, 128, 1152
+    print(f"[attn-graph] batch {B} len {n}", flush=True)
+    rng = np.random.default_rng(B * 1000 + n)
+    Ks = _rows(rng, (B, H, cap, D), "bf16", 1.0)
+    Vs = _rows(rng, (B, H, cap, D), "bf16", 1.0)
+    Qs = _rows(rng, (B, H * G, D), "bf16", 1.0)
+    Q2 = _rows(rng, (B, H * G, D), "bf16", 1.0)
+    shape = k.Shape(B, H, G, D, cap, k.BF16)
+    dev = torch.device("cuda")
+    cache = k.CacheTensors.empty(shape, dev)
+    cache.k.copy_(Ks.torch(dev))
+    cache.v.copy_(Vs.torch(dev))
+    q, q2 = Qs.torch(dev), Q2.torch(dev)
+    out = torch.empty((B, H * G, D), device=dev)
+    lse = torch.empty((B, H * G), device=dev)
+    out2 = torch.empty_like(out)
+    ws = k.alloc_workspace(shape, cap, dev)
+    k.kve_decode_attn(shape, cache, n, q, out, lse, ws)
+    torch.cuda.synchronize()
+    eager, eager_lse = out.clone(), lse.clone()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            k.kve_decode_attn(shape, cache, n, q, out, lse, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}: output differs"
+        assert torch.equal(lse, eager_lse), f"replay {rep}: lse differs"
+        # eager work on the same workspace between replays
+        k.kve_decode_attn(shape, cache, n, q2, out2, None, ws)
+        torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    for b in range(0, B, max(1, B // 4)):
+        for h in range(H):
+            ref, _ = O.decode_attention(Qs.f64[b, h * G:(h + 1) * G],
+                                        Ks.f64[b, h, :n], Vs.f64[b, h, :n])
+            attn_close(got[b, h * G:(h + 1) * G], ref, f"b{b} h{h}")
