@@ -839,6 +839,10 @@ def main() -> int:
                     help="time one layer's prompt scoring with the low-rank "
                          "sink-attention gate (Qwen2.5-14B, 131072 tokens) "
                          "instead of decode")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="copy this many MB before every timed step (not "
+                         "timed) so the cache is read from HBM, not the "
+                         "Infinity Cache; steps are timed alone by events")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, run a plain 1 GiB "
                          "elementwise copy (counter calibration)")
@@ -849,6 +853,10 @@ def main() -> int:
                           f"{args.gpus} is not supported (the step shards "
                           "by batch or KV head with no exchange, but only "
                           "the one-GPU path is built)"}))
+        return 2
+    if args.flush_mb > 0 and args.no_kernel_events:
+        print(json.dumps({"error": "--flush-mb times every step with events; "
+                          "it cannot be combined with --no-kernel-events"}))
         return 2
 
     import torch
@@ -921,17 +929,35 @@ def main() -> int:
     if use_events:
         events = [torch.cuda.Event(enable_timing=True)
                   for _ in range(steps + 1)]
+    # --flush-mb: a plain copy of that many bytes before every step pushes the
+    # cache out of the Infinity Cache (a single layer at batch 16 fits in
+    # it); each step is then timed alone with events and the flush excluded.
+    flush = None
+    if args.flush_mb > 0:
+        nb = args.flush_mb * (1 << 20) // 2
+        flush = (torch.ones(nb, dtype=torch.uint8, device=dev),
+                 torch.empty(nb, dtype=torch.uint8, device=dev))
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     if use_events:
         events[0].record()
     for s in range(steps):
+        if flush is not None:
+            flush[1].copy_(flush[0])
+            starts[s].record()
         stack.run_step(warmup + s, keep_for)
         if use_events:
             events[s + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {steps} steps in {wall * 1e3:.1f} ms")
+    step_ms_list = None
+    if flush is not None:
+        step_ms_list = [starts[s].elapsed_time(events[s + 1])
+                        for s in range(steps)]
+        wall = sum(step_ms_list) * 1e-3
+        log(f"steps alone (flush excluded): {wall * 1e3:.1f} ms")
 
     if args.calib_copy:
         calib_copy(dev)
@@ -955,7 +981,8 @@ def main() -> int:
             else:
                 total_bytes += attn_launch_bytes(w, n, True)
         if use_events and not ev:
-            step_ms = events[s].elapsed_time(events[s + 1])
+            step_ms = (step_ms_list[s] if step_ms_list is not None
+                       else events[s].elapsed_time(events[s + 1]))
             attn_bytes += [attn_launch_bytes(w, n, True)] * n_layers
             attn_ms += [step_ms / n_layers] * n_layers
 
@@ -1004,11 +1031,16 @@ def main() -> int:
                               f"read-out W={w.window}"),
                    "decay": bool(args.decay),
                    "stochastic_eviction": bool(args.stochastic),
+                   "flush_mb": args.flush_mb,
                    "parallelism": "none"},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "achievable_copy_gbps": None,
         "roofline": roof,
+        "timing": ("wall clock over the timed steps" if flush is None else
+                   f"sum of per-step HIP event times; a {args.flush_mb} MB "
+                   "copy before every step, outside the timed spans, keeps "
+                   "the cache out of the Infinity Cache"),
         "prompt_compress": compress_summary(w, stack, scorer),
         "cpu_baseline": None,
     }

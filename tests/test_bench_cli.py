@@ -31,3 +31,9 @@ def test_no_visible_gpu_reports_an_error():
     rc, lines = _run("--steps", "1", "--warmup", "0", "--no-cpu-baseline")
     assert rc == 1
     assert "error" in json.loads(lines[-1])
+
+
+def test_flush_needs_per_step_events():
+    rc, lines = _run("--flush-mb", "512", "--no-kernel-events")
+    assert rc == 2
+    assert "--flush-mb" in json.loads(lines[-1])["error"]
