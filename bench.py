@@ -36,6 +36,7 @@ WORKLOAD_BY_NAME = {
     "qwen3-4b-36layer-b8-B2048": 3,
     "qwen3-4b-1layer-b16": 2,
     "qwen2.5-14b-48layer-131k-gate": 5,
+    "tiny-1layer-fp32": 1,
 }
 DEFAULT_WORKLOAD = "qwen3-4b-36layer-b96-B1024"
 ATTN_SOURCE = os.path.join(ROOT, "learned_kv_cache_head_amd", "csrc",
@@ -180,7 +181,9 @@ def compress_summary(w, stack, scorer: str) -> dict:
                     "compact_gbps": round(compact_b / parts[2] / 1e3, 1)})
     out["tokens_per_s"] = round(w.batch * w.n0 / (total * 1e-6), 1)
     out["note"] = ("one-shot compression of the prompt in one layer during "
-                   "set-up, median over layers 2..L, HIP events")
+                   "set-up, median over layers 2..L (the only layer of a "
+                   "one-layer workload, first launches included), HIP "
+                   "events")
     return out
 
 
@@ -199,7 +202,11 @@ class Stack:
         self.w, self.dev = w, dev
         T = syn.TENSOR_IDS
         b, H, d, G = w.batch, w.n_kv, w.head_dim, w.group
-        self.shape = kve.Shape(b, H, G, d, w.budget + w.evict_len, kve.BF16)
+        # K, V, Q and the MLP's W1 in the workload's dtype (float32 for the
+        # tiny single-layer workload, bf16 otherwise)
+        kd = kve.F32 if w.kv_dtype == "f32" else kve.BF16
+        kt = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
+        self.shape = kve.Shape(b, H, G, d, w.budget + w.evict_len, kd)
         log_gamma = None
         if decay:
             # per-KV-head decay factors spread over KVpop's range (Table 3:
@@ -208,7 +215,7 @@ class Stack:
             log_gamma = torch.log(g).to(torch.float32).to(dev)
         self.policy = kve.Policy(w.budget, w.sinks, w.window, w.evict_len,
                                  log_gamma=log_gamma)
-        pre_shape = kve.Shape(b, H, G, d, w.n0, kve.BF16)
+        pre_shape = kve.Shape(b, H, G, d, w.n0, kd)
         scratch = kve.CacheTensors.empty(pre_shape, dev)
         scratch_pos = torch.arange(w.n0, dtype=torch.int32, device=dev)
         keep_pre = torch.empty((b, H, w.budget), dtype=torch.int32, device=dev)
@@ -243,15 +250,15 @@ class Stack:
                 sc = kve.Scorer.gate(gw)
             else:
                 w1 = dn((H, w.hidden, 2 * d), seed, (cfg, l, 0, T["w1"]),
-                        torch.bfloat16, dev, scale=(2 * d) ** -0.5)
+                        kt, dev, scale=(2 * d) ** -0.5)
                 w2 = dn((H, w.hidden), seed, (cfg, l, 0, T["w2"]),
                         torch.float32, dev, scale=w.hidden ** -0.5)
                 sc = kve.Scorer.mlp(w1, w2)
             # Prompt of n0 tokens, scored and compressed to B by the library.
             scratch.k.copy_(dn((b, H, w.n0, d), seed, (cfg, l, 0, T["k0"]),
-                               torch.bfloat16, dev))
+                               kt, dev))
             scratch.v.copy_(dn((b, H, w.n0, d), seed, (cfg, l, 0, T["v0"]),
-                               torch.bfloat16, dev))
+                               kt, dev))
             scratch.pos.copy_(scratch_pos.expand(b, H, w.n0))
             # The one-shot compression of the prompt (score every prompt
             # token, select, compact), timed per layer with events.
@@ -300,11 +307,11 @@ class Stack:
             self.runners.append(kve.LayerStep(self.shape, pol, sc, c, st,
                                               self.ws))
             self.k_pool.append(dn((pool_steps, b, H, d), seed,
-                                  (cfg, l, 1, T["k_new"]), torch.bfloat16, dev))
+                                  (cfg, l, 1, T["k_new"]), kt, dev))
             self.v_pool.append(dn((pool_steps, b, H, d), seed,
-                                  (cfg, l, 1, T["v_new"]), torch.bfloat16, dev))
+                                  (cfg, l, 1, T["v_new"]), kt, dev))
             self.q_pool.append(dn((pool_steps, b, H * G, d), seed,
-                                  (cfg, l, 1, T["q"]), torch.bfloat16, dev))
+                                  (cfg, l, 1, T["q"]), kt, dev))
             if scorer == "gate":
                 self.h_pool.append(dn((pool_steps, b, w.hidden), seed,
                                       (cfg, l, 1, T["hidden_new"]),
@@ -876,8 +883,10 @@ def main() -> int:
         print(json.dumps(run_prefill(args, w, dev)), flush=True)
         return 0
     L = w.evict_len
-    steps = args.steps if args.steps is not None else 4 * L
-    warmup = args.warmup if args.warmup is not None else L
+    # four eviction cycles after one, at least 64 steps (the tiny workload
+    # evicts one entry every step)
+    steps = args.steps if args.steps is not None else max(4 * L, 64)
+    warmup = args.warmup if args.warmup is not None else max(L, 8)
     pool = min(warmup + steps, 3 * L)
     log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")
@@ -1014,7 +1023,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if w.kv_dtype == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "layers": w.layers,
                    "batch": w.batch, "n_kv_heads": w.n_kv,
@@ -1048,13 +1057,12 @@ def main() -> int:
     torch.cuda.empty_cache()
     result["achievable_copy_gbps"] = round(achievable_copy_gbps(dev), 1)
     if not args.no_cpu_baseline:
-        cs = args.cpu_steps if args.cpu_steps is not None else 2 * L
+        cs = args.cpu_steps if args.cpu_steps is not None else max(2 * L, 64)
         cbatch = args.cpu_batch
         if cbatch is None:
             cbatch = 2 if args.scorer == "mlstm" else 16
+        cbatch = min(cbatch, w.batch)
         log(f"cpu baseline: oracle on {cbatch} sequences x {cs} steps")
-        if scorer == "gate":
-            cbatch = min(cbatch, w.batch)
         cb = cpu_baseline(w, args.seed, cbatch, cs, scorer)
         cb["value"] = round(cb["value"], 3)
         result["cpu_baseline"] = cb
