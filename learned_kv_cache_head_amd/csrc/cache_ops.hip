@@ -413,6 +413,140 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(
   }
 }
 
+// Slices with n_keep <= kCompSmallKeep: a workgroup handles holes
+// [blockIdx.y * hpw, +hpw) of one slice. The kept list goes to LDS with
+// coalesced loads, the kept slots below n_keep become
+// a bitmap, and the holes are the bitmap's zero bits in ascending order
+// (word popcounts and one prefix scan), so no thread runs a dependent
+// search through global memory. The same placement rule as compact_kernel:
+// the j-th hole below n_keep receives keep[i0 + j].
+constexpr int kCompSmallKeep = 4096;
+constexpr int kCompSmallWords = kCompSmallKeep / 32;
+
+__global__ __launch_bounds__(kCompThreads) void compact_small_kernel(
+    char* k, char* v, float* score, int32_t* pos, int cap, int row_bytes,
+    const int32_t* keep, int n_keep, int hpw) {
+  const size_t slice = blockIdx.x;
+  const int32_t* kp = keep + slice * (size_t)n_keep;
+  const int tid = threadIdx.x;
+  __shared__ int32_t ks[kCompSmallKeep];        // kept slots, then sources
+  __shared__ uint32_t bits[kCompSmallWords];    // kept slots below n_keep
+  __shared__ uint32_t zpre[kCompSmallWords];    // holes before each word
+  __shared__ int32_t dst[kCompSmallKeep];       // hole j -> slot
+  __shared__ int i0_sh;
+  for (int w = tid; w < kCompSmallWords; w += kCompThreads) bits[w] = 0u;
+  if (tid == 0) i0_sh = n_keep;
+  __syncthreads();
+  // Kept list into LDS; i0 = first index whose slot is >= n_keep (the list
+  // ascends); kept slots below n_keep set their bits.
+  for (int i = tid; i < n_keep; i += kCompThreads) {
+    const int32_t sl = kp[i];
+    ks[i] = sl;
+    if (sl < n_keep) {
+      atomicOr(&bits[sl >> 5], 1u << (sl & 31));
+    } else if (i == 0 || kp[i - 1] < n_keep) {
+      i0_sh = i;  // the one index where the list crosses n_keep
+    }
+  }
+  __syncthreads();
+  const int i0 = i0_sh;
+  const int j_begin = blockIdx.y * hpw;
+  const int j_end = min(n_keep - i0, j_begin + hpw);  // holes: n_keep - i0
+  if (j_begin >= j_end) return;  // uniform
+  const int nwords = (n_keep + 31) >> 5;
+  // Exclusive prefix of the words' zero counts (bits past n_keep excluded),
+  // by the first wave.
+  if (tid < 64) {
+    uint32_t carry = 0;
+    for (int w0 = 0; w0 < nwords; w0 += 64) {
+      const int w = w0 + tid;
+      uint32_t z = 0;
+      if (w < nwords) {
+        const int valid = min(32, n_keep - (w << 5));
+        const uint32_t vmask = valid == 32 ? 0xffffffffu : ((1u << valid) - 1u);
+        z = (uint32_t)__builtin_popcount(~bits[w] & vmask);
+      }
+      uint32_t incl = z;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (tid >= off) incl += o;
+      }
+      if (w < nwords) zpre[w] = carry + incl - z;
+      carry += __shfl(incl, 63);
+    }
+  }
+  __syncthreads();
+  // Hole j: the word holding zero number j (binary search over zpre in
+  // LDS), then that zero bit within the word.
+  for (int j = j_begin + tid; j < j_end; j += kCompThreads) {
+    int lo = 0, hi = nwords - 1;  // last word with zpre <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)zpre[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    uint32_t zeros = ~bits[lo];
+    for (int r = j - (int)zpre[lo]; r > 0; --r) zeros &= zeros - 1u;
+    // A kept list that breaks the contract (not ascending, repeated slots)
+    // can leave no such zero: the hole is then skipped, never written.
+    dst[j - j_begin] = zeros ? (lo << 5) + __builtin_ctz(zeros) : -1;
+  }
+  __syncthreads();
+  // Copies: 8 lanes per row, 16-byte accesses, RB rows per thread loaded
+  // before any of them is stored (sources lie at or above
+  // n_keep and destinations below it, so no load reads a row stored here).
+  constexpr int RB = 4;                  // rows in flight per thread
+  constexpr int NC = 4;                  // 128-byte chunks per row, at most
+  const int nc = row_bytes >> 7;         // 1..4
+  const int sub = tid & 7;
+  const size_t base = slice * (size_t)cap;
+  for (int j0 = j_begin + (tid >> 3); j0 < j_end;
+       j0 += RB * (kCompThreads / 8)) {
+    u32x4 kb[RB][NC], vb[RB][NC];
+    float sv[RB];
+    int32_t pv[RB];
+    int dr[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int j = j0 + r * (kCompThreads / 8);
+      int d = -1, src = 0;
+      if (j < j_end) {
+        d = dst[j - j_begin];
+        src = ks[i0 + j];
+        if (src < n_keep || src >= cap) d = -1;
+      }
+      dr[r] = d;
+      if (d >= 0) {
+        const size_t srow = (base + src) * (size_t)row_bytes + sub * 16;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          if (c < nc) {
+            kb[r][c] = *(const u32x4*)(k + srow + c * 128);
+            vb[r][c] = *(const u32x4*)(v + srow + c * 128);
+          }
+        sv[r] = score[base + src];
+        pv[r] = pos[base + src];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int d = dr[r];
+      if (d < 0) continue;
+      const size_t drow = (base + d) * (size_t)row_bytes + sub * 16;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c < nc) {
+          *(u32x4*)(k + drow + c * 128) = kb[r][c];
+          *(u32x4*)(v + drow + c * 128) = vb[r][c];
+        }
+      if (sub == 0) {
+        score[base + d] = sv[r];
+        pos[base + d] = pv[r];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
@@ -457,6 +591,18 @@ hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
   // the holes below it.
   const int max_moves = n_keep < len - n_keep ? n_keep : len - n_keep;
   if (max_moves <= 0) return hipSuccess;
+  if (n_keep <= kCompSmallKeep) {
+    // About 1024 workgroups in all, at least 32 holes each.
+    int groups = (1024 + slices - 1) / slices;
+    const int by_rows = (max_moves + 31) / 32;
+    if (groups > by_rows) groups = by_rows;
+    if (groups < 1) groups = 1;
+    const int hpw = (max_moves + groups - 1) / groups;
+    hipLaunchKernelGGL(compact_small_kernel, dim3(slices, groups),
+                       dim3(kCompThreads), 0, s, (char*)k, (char*)v, score, pos,
+                       cap, row_bytes, keep, n_keep, hpw);
+    return hipGetLastError();
+  }
   const int groups = (max_moves + kCompRows - 1) / kCompRows;
   if (groups > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(compact_kernel, dim3(slices, groups), dim3(kCompThreads),

@@ -187,6 +187,11 @@ COMPACT_CASES = [
     ("bf16", 64, 2, 3, 1000, 517, "random"),
     ("f32", 128, 1, 2, 900, 450, "random"),
     ("bf16", 128, 1, 8, 131072, 39321, "random"),
+    # one workgroup per slice up to n_keep = 4096, the grouped kernel beyond
+    ("bf16", 128, 4, 8, 8192, 1024, "random"),     # prompt compression
+    ("bf16", 128, 1, 2, 9000, 4096, "random"),
+    ("bf16", 128, 1, 2, 9000, 4097, "random"),
+    ("f32", 128, 1, 2, 5000, 4000, "hole_at_0"),
 ]
 
 
