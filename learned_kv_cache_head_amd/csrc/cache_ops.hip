@@ -415,11 +415,11 @@ __global__ __launch_bounds__(kCompThreads) void compact_kernel(
 
 // Slices with n_keep <= kCompSmallKeep: a workgroup handles holes
 // [blockIdx.y * hpw, +hpw) of one slice. The kept list goes to LDS with
-// coalesced loads, the kept slots below n_keep become
-// a bitmap, and the holes are the bitmap's zero bits in ascending order
-// (word popcounts and one prefix scan), so no thread runs a dependent
-// search through global memory. The same placement rule as compact_kernel:
-// the j-th hole below n_keep receives keep[i0 + j].
+// coalesced loads, the kept slots below n_keep become a bitmap, and the
+// holes are the bitmap's zero bits in ascending order (word popcounts and
+// one prefix scan), so no thread runs a dependent search through global
+// memory. The same placement rule as compact_kernel: the j-th hole below
+// n_keep receives keep[i0 + j].
 constexpr int kCompSmallKeep = 4096;
 constexpr int kCompSmallWords = kCompSmallKeep / 32;
 
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kCompThreads) void compact_small_kernel(
   __shared__ int32_t ks[kCompSmallKeep];        // kept slots, then sources
   __shared__ uint32_t bits[kCompSmallWords];    // kept slots below n_keep
   __shared__ uint32_t zpre[kCompSmallWords];    // holes before each word
-  __shared__ int32_t dst[kCompSmallKeep];       // hole j -> slot
+  __shared__ int32_t dst[kCompSmallKeep];       // hole j_begin + i -> slot
   __shared__ int i0_sh;
   for (int w = tid; w < kCompSmallWords; w += kCompThreads) bits[w] = 0u;
   if (tid == 0) i0_sh = n_keep;
