@@ -85,7 +85,10 @@ typedef enum {
 } kve_scorer_kind;
 
 /* Shape of one layer's cache. head_dim in {64, 128}; group in [1, 8];
- * kv_dtype is a kve_dtype. capacity = slots per (batch, KV head) slice. */
+ * kv_dtype is a kve_dtype. capacity = slots per (batch, KV head) slice.
+ * Limits (KVE_ERR_UNSUPPORTED beyond them): batch and n_kv_heads at most
+ * 65535, batch * n_kv_heads below 2^31, and one slice's K (or V) rows,
+ * capacity * head_dim * element bytes, below 4 GiB. */
 typedef struct {
   int32_t batch;
   int32_t n_kv_heads;
@@ -286,7 +289,16 @@ kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
  * absorbing every token as it arrives) and need scorer->delay equal to the
  * policy window. With policy->gumbel the eviction is stochastic, as in
  * kve_select_evict.
- * Requires capacity >= B + L and state->len < capacity. */
+ * Requires capacity >= B + L and state->len < capacity.
+ * Failure: the step validates its arguments and the launch configuration of
+ * every kernel it will enqueue (append, scorer, select, compaction,
+ * attention) on the host before it enqueues the first one; any such error
+ * is returned with *state, the cache and the outputs untouched, so the
+ * call may be corrected and repeated. Only a launch that the HIP runtime
+ * itself refuses after that check (KVE_ERR_LAUNCH; the device or the
+ * stream is already in an error state) can leave the step part-way: *state
+ * is then unchanged, but the layer's cache contents are undefined and it
+ * must be rebuilt before the next step. */
 kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
                     const kve_scorer* scorer, kve_cache* cache,
                     kve_decode_state* state, const void* k_new,

@@ -572,7 +572,8 @@ __global__ __launch_bounds__(D) void combine_kernel(AttnLaunch a) {
 }
 
 template <bool BF16, int D, int G>
-hipError_t launch_one(const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_one(const AttnLaunch& a, hipStream_t s, bool check_only) {
+  if (check_only) return hipSuccess;
   hipLaunchKernelGGL((attn_kernel<BF16, D, G>), dim3(a.nsplit, a.H, a.batch),
                      dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -583,30 +584,31 @@ hipError_t launch_one(const AttnLaunch& a, hipStream_t s) {
 }
 
 template <bool BF16, int D>
-hipError_t launch_g(const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_g(const AttnLaunch& a, hipStream_t s, bool check_only) {
   switch (a.G) {
-    case 1: return launch_one<BF16, D, 1>(a, s);
-    case 2: return launch_one<BF16, D, 2>(a, s);
-    case 3: return launch_one<BF16, D, 3>(a, s);
-    case 4: return launch_one<BF16, D, 4>(a, s);
-    case 5: return launch_one<BF16, D, 5>(a, s);
-    case 6: return launch_one<BF16, D, 6>(a, s);
-    case 7: return launch_one<BF16, D, 7>(a, s);
-    case 8: return launch_one<BF16, D, 8>(a, s);
+    case 1: return launch_one<BF16, D, 1>(a, s, check_only);
+    case 2: return launch_one<BF16, D, 2>(a, s, check_only);
+    case 3: return launch_one<BF16, D, 3>(a, s, check_only);
+    case 4: return launch_one<BF16, D, 4>(a, s, check_only);
+    case 5: return launch_one<BF16, D, 5>(a, s, check_only);
+    case 6: return launch_one<BF16, D, 6>(a, s, check_only);
+    case 7: return launch_one<BF16, D, 7>(a, s, check_only);
+    case 8: return launch_one<BF16, D, 8>(a, s, check_only);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t s,
+                            bool check_only) {
   if (a.nsplit < 1 || a.nsplit > kMaxSplit) return hipErrorInvalidValue;
   if (a.is_bf16) {
-    if (a.D == 128) return launch_g<true, 128>(a, s);
-    if (a.D == 64) return launch_g<true, 64>(a, s);
+    if (a.D == 128) return launch_g<true, 128>(a, s, check_only);
+    if (a.D == 64) return launch_g<true, 64>(a, s, check_only);
   } else {
-    if (a.D == 128) return launch_g<false, 128>(a, s);
-    if (a.D == 64) return launch_g<false, 64>(a, s);
+    if (a.D == 128) return launch_g<false, 128>(a, s, check_only);
+    if (a.D == 64) return launch_g<false, 64>(a, s, check_only);
   }
   return hipErrorInvalidValue;
 }

@@ -554,9 +554,10 @@ hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
                          int position, const void* k_new, const void* v_new,
                          const void* hidden_new, void* hidden_buf,
                          int hidden_dim, int hidden_rows, int hidden_row,
-                         hipStream_t s) {
+                         hipStream_t s, bool check_only) {
   const int slices = batch * H;
   const int extra = hidden_new ? batch : 0;
+  if (check_only) return hipSuccess;
   hipLaunchKernelGGL(append_kernel, dim3(slices + extra), dim3(64), 0, s,
                      (char*)k, (char*)v, pos, H, D * elem_bytes, cap, slot,
                      position, (const char*)k_new, (const char*)v_new, batch,
@@ -568,10 +569,12 @@ hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
 hipError_t launch_select(const float* score, const int32_t* pos,
                          const float* log_gamma, const float* gumbel, int H,
                          int slices, int cap, int len, int n_keep, int S,
-                         int W, int32_t* keep, hipStream_t s) {
+                         int W, int32_t* keep, hipStream_t s,
+                         bool check_only) {
   // The key cache takes all of a CU's LDS: used when few slices run.
   const bool cache = !gumbel && len > 2048 && len <= kSelCacheMax &&
                      slices <= 256;
+  if (check_only) return hipSuccess;
   if (cache)
     hipLaunchKernelGGL(select_kernel<true>, dim3(slices), dim3(kSelThreads), 0,
                        s, score, pos, log_gamma, gumbel, H, cap, len, n_keep,
@@ -585,7 +588,8 @@ hipError_t launch_select(const float* score, const int32_t* pos,
 
 hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
                           int slices, int cap, int row_bytes, int len,
-                          const int32_t* keep, int n_keep, hipStream_t s) {
+                          const int32_t* keep, int n_keep, hipStream_t s,
+                          bool check_only) {
   if (row_bytes % 128 != 0) return hipErrorInvalidValue;
   // Moved rows per slice: at most the slots at or above n_keep, and at most
   // the holes below it.
@@ -598,6 +602,7 @@ hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
     if (groups > by_rows) groups = by_rows;
     if (groups < 1) groups = 1;
     const int hpw = (max_moves + groups - 1) / groups;
+    if (check_only) return hipSuccess;
     hipLaunchKernelGGL(compact_small_kernel, dim3(slices, groups),
                        dim3(kCompThreads), 0, s, (char*)k, (char*)v, score, pos,
                        cap, row_bytes, keep, n_keep, hpw);
@@ -605,6 +610,7 @@ hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
   }
   const int groups = (max_moves + kCompRows - 1) / kCompRows;
   if (groups > 65535) return hipErrorInvalidValue;
+  if (check_only) return hipSuccess;
   hipLaunchKernelGGL(compact_kernel, dim3(slices, groups), dim3(kCompThreads),
                      0, s, (char*)k, (char*)v, score, pos, cap, row_bytes,
                      keep, n_keep);

@@ -61,23 +61,30 @@ struct AttnLaunch {
   int hidden_bytes, hidden_rows, hidden_row;
 };
 
-hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+// Every launcher validates its launch configuration on the host first and
+// returns hipErrorInvalidValue if the kernel cannot run it. With check_only
+// it stops there and launches nothing: kve_step checks every launch of a
+// step this way before it enqueues the first one.
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t s,
+                            bool check_only = false);
 
 hipError_t launch_append(void* k, void* v, int32_t* pos, int batch, int H,
                          int D, int cap, int elem_bytes, int slot,
                          int position, const void* k_new, const void* v_new,
                          const void* hidden_new, void* hidden_buf,
                          int hidden_dim, int hidden_rows, int hidden_row,
-                         hipStream_t s);
+                         hipStream_t s, bool check_only = false);
 
 hipError_t launch_select(const float* score, const int32_t* pos,
                          const float* log_gamma, const float* gumbel, int H,
                          int slices, int cap, int len, int n_keep, int S,
-                         int W, int32_t* keep, hipStream_t s);
+                         int W, int32_t* keep, hipStream_t s,
+                         bool check_only = false);
 
 hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
                           int slices, int cap, int row_bytes, int len,
-                          const int32_t* keep, int n_keep, hipStream_t s);
+                          const int32_t* keep, int n_keep, hipStream_t s,
+                          bool check_only = false);
 
 struct MlpLaunch {
   const void* k;         // cache base
@@ -90,7 +97,8 @@ struct MlpLaunch {
   int batch, H, D, cap, hidden, act, is_bf16;
   int slot_begin, slot_end;
 };
-hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s);
+hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s,
+                            bool check_only = false);
 
 struct GateLaunch {
   const void* hidden;    // bf16 [batch][rows_stride][in_dim]
@@ -101,7 +109,8 @@ struct GateLaunch {
   int batch, H, cap, in_dim;
   int slot_begin, slot_end;
 };
-hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s);
+hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s,
+                             bool check_only = false);
 
 struct SinkGateLaunch {
   const void* hidden;      // bf16 [batch][rows_stride][in_dim]
@@ -114,7 +123,8 @@ struct SinkGateLaunch {
   int batch, H, G, cap, in_dim, n_sink;
   int slot_begin, slot_end;
 };
-hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s);
+hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s,
+                                  bool check_only = false);
 
 struct MlstmLaunch {
   const void* k;         // cache base (bf16)
@@ -130,7 +140,8 @@ struct MlstmLaunch {
   int slot_begin, slot_end;
   int delay;             // read-out delay W
 };
-hipError_t launch_score_mlstm(const MlstmLaunch& m, hipStream_t s);
+hipError_t launch_score_mlstm(const MlstmLaunch& m, hipStream_t s,
+                              bool check_only = false);
 
 // Prefill selection and masked prefill attention.
 constexpr int kMaxPrefillLen = 262144;  // the cutoff bitmap lives in LDS

@@ -28,6 +28,13 @@ kve_status check_shape(const kve_shape* s) {
   if (s->head_dim != 64 && s->head_dim != 128) return KVE_ERR_UNSUPPORTED;
   if (s->kv_dtype != KVE_F32 && s->kv_dtype != KVE_BF16)
     return KVE_ERR_UNSUPPORTED;
+  // Kernels address the rows of one slice with 32-bit byte offsets and count
+  // slices in an int.
+  const long long row_bytes = (long long)s->head_dim * elem_bytes(s->kv_dtype);
+  if ((long long)s->capacity * row_bytes >= (1LL << 32))
+    return KVE_ERR_UNSUPPORTED;
+  if ((long long)s->batch * s->n_kv_heads > 0x7fffffffLL)
+    return KVE_ERR_UNSUPPORTED;
   return KVE_OK;
 }
 
@@ -114,13 +121,18 @@ size_t ws_bytes_for(const kve_shape* s, int nsplit) {
 
 kve_status from_hip(hipError_t e) { return e == hipSuccess ? KVE_OK : KVE_ERR_LAUNCH; }
 
+// Status of a launcher's host-side configuration check (check_only).
+kve_status from_check(hipError_t e) {
+  return e == hipSuccess ? KVE_OK : KVE_ERR_UNSUPPORTED;
+}
+
 kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
                      const void* q, float* out, float* lse, void* ws,
                      size_t ws_bytes, int new_slot, int new_pos,
                      const void* k_new, const void* v_new, hipStream_t stream,
                      const void* hidden_new = nullptr, void* hidden_buf = nullptr,
                      int hidden_bytes = 0, int hidden_rows = 0,
-                     int hidden_row = 0) {
+                     int hidden_row = 0, bool check_only = false) {
   // The attention kernel reads the appended row from k_new / v_new only in
   // the last stage of the last split, so it must be the slice's last row.
   if (new_slot >= 0 && new_slot != len - 1) return KVE_ERR_INVALID_ARG;
@@ -158,6 +170,7 @@ kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
     a.hidden_rows = hidden_rows;
     a.hidden_row = hidden_row;
   }
+  if (check_only) return from_check(kve::launch_attention(a, stream, true));
   return from_hip(kve::launch_attention(a, stream));
 }
 
@@ -203,8 +216,11 @@ kve_status check_scorer(const kve_shape* shape, const kve_scorer* sc) {
 kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
                       kve_cache* cache, int slot_begin, int slot_end,
                       const void* hidden, long long hidden_batch_stride,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool check_only = false) {
   if (slot_end == slot_begin) return KVE_OK;
+  auto done = [check_only](hipError_t e) {
+    return check_only ? from_check(e) : from_hip(e);
+  };
   if (sc->kind == KVE_SCORER_MLSTM) {
     if (!cache->scorer_state) return KVE_ERR_INVALID_ARG;
     kve::MlstmLaunch m{};
@@ -224,7 +240,7 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
     m.slot_begin = slot_begin;
     m.slot_end = slot_end;
     m.delay = sc->delay;
-    return from_hip(kve::launch_score_mlstm(m, stream));
+    return done(kve::launch_score_mlstm(m, stream, check_only));
   }
   if (sc->kind == KVE_SCORER_MLP_KV) {
     kve::MlpLaunch m{};
@@ -244,7 +260,7 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
     m.is_bf16 = shape->kv_dtype == KVE_BF16;
     m.slot_begin = slot_begin;
     m.slot_end = slot_end;
-    return from_hip(kve::launch_score_mlp(m, stream));
+    return done(kve::launch_score_mlp(m, stream, check_only));
   }
   if (sc->kind == KVE_SCORER_SINK_GATE) {
     kve::SinkGateLaunch q{};
@@ -263,7 +279,7 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
     q.n_sink = sc->n_sink;
     q.slot_begin = slot_begin;
     q.slot_end = slot_end;
-    return from_hip(kve::launch_score_sink_gate(q, stream));
+    return done(kve::launch_score_sink_gate(q, stream, check_only));
   }
   kve::GateLaunch g{};
   g.hidden = hidden;
@@ -277,7 +293,7 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
   g.in_dim = sc->in_dim;
   g.slot_begin = slot_begin;
   g.slot_end = slot_end;
-  return from_hip(kve::launch_score_gate(g, stream));
+  return done(kve::launch_score_gate(g, stream, check_only));
 }
 
 }  // namespace
@@ -529,49 +545,53 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   const int new_len = len + 1;
   const bool evict = new_len >= B + L;
   const bool score_now = evict || (new_len - scored) >= L;
-
-  state->evicted = 0;
-  bool appended = false;
-  if (score_now) {
-    // The new row (and hidden state) must be in place before scoring or
-    // selection. Otherwise the attention launch appends them.
-    st = from_hip(kve::launch_append(
-        cache->k, cache->v, cache->pos, shape->batch, shape->n_kv_heads,
-        shape->head_dim, shape->capacity, elem_bytes(shape->kv_dtype), slot,
-        position, k_new, v_new, hidden_new, hidden_buf, scorer->in_dim, L,
-        slot - scored, stream));
+  const int slices = shape->batch * shape->n_kv_heads;
+  const int row_bytes = shape->head_dim * elem_bytes(shape->kv_dtype);
+  // Launches of this step, in order: append (when a scoring is due: the new
+  // row must be in place before it is scored or selected; otherwise the
+  // attention launch appends it), scoring of the pending rows, select and
+  // compaction (when the count reaches B + L), attention. Pass 0 checks
+  // every launch configuration on the host and launches nothing, so a step
+  // the kernels cannot run fails before it touches the device; pass 1
+  // enqueues them.
+  const int att_len = evict ? B : new_len;
+  const int att_scored = score_now ? (evict ? B : new_len) : scored;
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool chk = pass == 0;
+    auto done = [chk](hipError_t e) {
+      return chk ? from_check(e) : from_hip(e);
+    };
+    if (score_now) {
+      st = done(kve::launch_append(
+          cache->k, cache->v, cache->pos, shape->batch, shape->n_kv_heads,
+          shape->head_dim, shape->capacity, elem_bytes(shape->kv_dtype), slot,
+          position, k_new, v_new, hidden_new, hidden_buf, scorer->in_dim, L,
+          slot - scored, stream, chk));
+      if (st != KVE_OK) return st;
+      st = score_impl(shape, scorer, cache, scored, new_len, hidden_buf,
+                      (long long)L * scorer->in_dim, stream, chk);
+      if (st != KVE_OK) return st;
+    }
+    if (evict) {
+      st = done(kve::launch_select(
+          cache->score, cache->pos, policy->log_gamma, policy->gumbel,
+          shape->n_kv_heads, slices, shape->capacity, new_len, B,
+          policy->sinks, policy->window, keep_slots, stream, chk));
+      if (st != KVE_OK) return st;
+      st = done(kve::launch_compact(
+          cache->k, cache->v, cache->score, cache->pos, slices,
+          shape->capacity, row_bytes, new_len, keep_slots, B, stream, chk));
+      if (st != KVE_OK) return st;
+    }
+    st = attn_impl(shape, cache, att_len, q, out, lse, ws, ws_bytes,
+                   score_now ? -1 : slot, position, k_new, v_new, stream,
+                   gate ? hidden_new : nullptr, hidden_buf, scorer->in_dim * 2,
+                   L, slot - att_scored, chk);
     if (st != KVE_OK) return st;
-    appended = true;
   }
-  len = new_len;
-  if (score_now) {
-    st = score_impl(shape, scorer, cache, scored, len, hidden_buf,
-                    (long long)L * scorer->in_dim, stream);
-    if (st != KVE_OK) return st;
-    scored = len;
-  }
-  if (evict) {
-    st = from_hip(kve::launch_select(
-        cache->score, cache->pos, policy->log_gamma, policy->gumbel,
-        shape->n_kv_heads,
-        shape->batch * shape->n_kv_heads, shape->capacity, len, B,
-        policy->sinks, policy->window, keep_slots, stream));
-    if (st != KVE_OK) return st;
-    st = from_hip(kve::launch_compact(
-        cache->k, cache->v, cache->score, cache->pos,
-        shape->batch * shape->n_kv_heads, shape->capacity,
-        shape->head_dim * elem_bytes(shape->kv_dtype), len, keep_slots, B,
-        stream));
-    if (st != KVE_OK) return st;
-    len = B;
-    scored = B;
-    state->evicted = 1;
-  }
-  st = attn_impl(shape, cache, len, q, out, lse, ws, ws_bytes,
-                 appended ? -1 : slot, position, k_new, v_new, stream,
-                 gate ? hidden_new : nullptr, hidden_buf, scorer->in_dim * 2,
-                 L, slot - scored);
-  if (st != KVE_OK) return st;
+  state->evicted = evict ? 1 : 0;
+  len = att_len;
+  scored = att_scored;
   state->len = len;
   state->scored_upto = scored;
   state->next_position = position + 1;

@@ -487,9 +487,12 @@ size_t mlstm_state_floats(int D) {
   return 0;
 }
 
-hipError_t launch_score_mlstm(const MlstmLaunch& m, hipStream_t s) {
+hipError_t launch_score_mlstm(const MlstmLaunch& m, hipStream_t s,
+                              bool check_only) {
   if (m.slot_end <= m.slot_begin) return hipSuccess;
   const dim3 grid((unsigned)(m.batch * m.H));
+  if (m.D != 128 && m.D != 64) return hipErrorInvalidValue;
+  if (check_only) return hipSuccess;
   if (m.D == 128) {
     hipLaunchKernelGGL((mlstm_kernel<128>), grid, dim3(256), 0, s, m);
   } else if (m.D == 64) {

@@ -585,7 +585,8 @@ void sink_gate_kernel(SinkGateLaunch g, int nb, int ncg) {
 
 }  // namespace
 
-hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
+hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s,
+                            bool check_only) {
   const int rows = m.slot_end - m.slot_begin;
   if (rows <= 0) return hipSuccess;
   const dim3 grid((rows + 63) / 64, m.H, m.batch);
@@ -598,6 +599,7 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
     const dim3 mgrid((unsigned)wgs, m.H);
 #define KVE_MLP(DD, NBB)                                                     \
   if (m.D == DD && m.hidden == NBB * 16) {                                   \
+    if (check_only) return hipSuccess;                                       \
     hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB>), mgrid, dim3(256), 0, s, m); \
     return hipGetLastError();                                                \
   }
@@ -608,6 +610,7 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
 #undef KVE_MLP
   }
   const size_t lds = (size_t)64 * (2 * m.D + 1) * sizeof(float);
+  if (check_only) return hipSuccess;
   if (m.is_bf16) {
     hipLaunchKernelGGL((mlp_valu_kernel<true>), grid, dim3(64), lds, s, m);
   } else {
@@ -616,7 +619,8 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
+hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s,
+                                  bool check_only) {
   const int rows = g.slot_end - g.slot_begin;
   if (rows <= 0) return hipSuccess;
   const int nb = (rows + kSgTok - 1) / kSgTok;
@@ -626,6 +630,7 @@ hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
       const int ncg = (g.H + 2 * SgCfg<GG>::HPW - 1) / (2 * SgCfg<GG>::HPW); \
       const long long wgs = (long long)nb * g.batch * ncg;                   \
       if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;                   \
+      if (check_only) return hipSuccess;                                     \
       hipLaunchKernelGGL((sink_gate_kernel<GG>), dim3((unsigned)wgs),        \
                          dim3(512), 0, s, g, nb, ncg);                       \
       break;                                                                 \
@@ -637,9 +642,11 @@ hipError_t launch_score_sink_gate(const SinkGateLaunch& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s) {
+hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s,
+                             bool check_only) {
   const int rows = g.slot_end - g.slot_begin;
   if (rows <= 0) return hipSuccess;
+  if (check_only) return hipSuccess;
   if (rows <= kGateSmallMaxRows) {
     hipLaunchKernelGGL(gate_mfma_small_kernel, dim3((rows + 15) / 16, g.batch),
                        dim3(64 * kGateSmallWaves), 0, s, g);

@@ -188,6 +188,53 @@ def test_step_rejects_bad_state():
     assert call(kve._State(1030, 1024, 9000, 0), ws_bytes=64) == 5
 
 
+def test_shape_limits():
+    """One slice's K rows must stay below 4 GiB (the kernels address a
+    slice with 32-bit byte offsets) and batch * n_kv_heads below 2^31."""
+    lib = _lib()
+    ok = _shape(batch=1, n_kv_heads=1, capacity=(1 << 24) - 1)  # 256 B rows
+    assert lib.kve_workspace_bytes(ctypes.byref(ok), 64) > 0
+    big = _shape(batch=1, n_kv_heads=1, capacity=1 << 24)
+    assert lib.kve_workspace_bytes(ctypes.byref(big), 64) == 0
+    big32 = _shape(batch=1, n_kv_heads=1, capacity=1 << 23,
+                   kv_dtype=kve.F32)                             # 512 B rows
+    assert lib.kve_workspace_bytes(ctypes.byref(big32), 64) == 0
+    s = lib.kve_decode_attn(ctypes.byref(big), ctypes.byref(_cache()), 10,
+                            FAKE, FAKE, None, FAKE, 1 << 20, None)
+    assert s == 4
+    many = _shape(batch=65535, n_kv_heads=65535)
+    assert lib.kve_workspace_bytes(ctypes.byref(many), 64) == 0
+
+
+def test_step_checks_every_launch_before_the_first():
+    """A step whose compaction grid cannot be launched (2.2M moved rows per
+    slice need more than 65535 workgroups of 32 rows) fails with
+    KVE_ERR_UNSUPPORTED before anything is enqueued: on this machine, with
+    no GPU, an attempted launch would report KVE_ERR_LAUNCH instead. The
+    decode state is left as it was."""
+    lib = _lib()
+    B = L = 2_200_000
+    s = _shape(batch=1, n_kv_heads=1, group=1, head_dim=64,
+               capacity=B + L)
+    p = kve._Policy(B, 0, 0, L)
+    mlp = kve._Scorer(0, 0, kve.BF16, 128, 32, FAKE, None, FAKE, None)
+    state = kve._State(B + L - 1, B, 9_000_000, 7)
+    st = lib.kve_step(ctypes.byref(s), ctypes.byref(p), ctypes.byref(mlp),
+                      ctypes.byref(_cache()), ctypes.byref(state), FAKE, FAKE,
+                      None, None, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
+    assert st == 4
+    assert (state.len, state.scored_upto, state.next_position,
+            state.evicted) == (B + L - 1, B, 9_000_000, 7)
+    # a step one short of the eviction passes every check and reaches the
+    # first launch, which fails here for want of a device
+    state = kve._State(B + L - 3, B, 9_000_000, 7)
+    st = lib.kve_step(ctypes.byref(s), ctypes.byref(p), ctypes.byref(mlp),
+                      ctypes.byref(_cache()), ctypes.byref(state), FAKE, FAKE,
+                      None, None, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
+    assert st == 6
+    assert state.len == B + L - 3
+
+
 def test_policy_struct_layout_matches_header():
     """kve_policy: four int32 fields, then the log_gamma and gumbel
     pointers."""
