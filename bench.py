@@ -67,6 +67,47 @@ def achievable_copy_gbps(dev) -> float:
     return best
 
 
+def achievable_read_gbps(dev, gib: int = 4) -> float:
+    """Best of three timed reads of a `gib` GiB device buffer by the
+    read-only reference kernel (libkvebench.so: 16-byte non-temporal loads,
+    the load form of the attention's K/V stream, nothing written but one
+    word per workgroup), in GB/s: the read ceiling a streaming kernel can be
+    held against."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "learned_kv_cache_head_amd", "_lib",
+                                   "libkvebench.so"))
+    lib.kvebench_read.restype = ctypes.c_int
+    lib.kvebench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvebench_read_blocks.restype = ctypes.c_size_t
+    lib.kvebench_read_blocks.argtypes = [ctypes.c_size_t]
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    sink = torch.empty(int(lib.kvebench_read_blocks(nbytes)),
+                       dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def read():
+        rc = lib.kvebench_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"kvebench_read failed ({rc})")
+
+    read()
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = (torch.cuda.Event(enable_timing=True),
+                  torch.cuda.Event(enable_timing=True))
+        e0.record()
+        read()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
+
+
 def calib_copy(dev) -> None:
     """A plain elementwise copy of known size (1 GiB read, 1 GiB written),
     the reference that scales the HBM byte counters."""
@@ -718,7 +759,7 @@ def run_sink_gate(args, dev) -> dict:
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -810,12 +851,76 @@ def traffic_ratio(workload: str):
 
 
 # ---------------------------------------------------------------------------
+# Timing over eviction cycles
+# ---------------------------------------------------------------------------
+
+def preroll_steps(L: int, warmup: int, steps: int) -> int:
+    """Untimed decode steps that set-up runs after the prompt compression
+    (which leaves B entries; the t-th step after it evicts when t is a
+    multiple of L) so that timed step steps // 2 is an evicting step."""
+    e = steps // 2
+    return (-(warmup + 1 + e)) % L
+
+
+def attn_rows(w, n: int, evicts: bool) -> int:
+    """Rows the attention of a step reads: B after an eviction, else the
+    count after the append."""
+    return w.budget if evicts else n
+
+
+def cycle_fold(step_ms, evicts, L: int) -> float:
+    """Time of one eviction cycle (L decode steps, one of them evicting)
+    from per-step times of a window: the mean evicting step plus L - 1 mean
+    non-evicting steps. Over whole cycles this is the window's time per
+    cycle; a shorter window centred on an eviction weighs that step as one
+    step in L instead of one in the window."""
+    ev = [t for t, e in zip(step_ms, evicts) if e]
+    ne = [t for t, e in zip(step_ms, evicts) if not e]
+    if not ev:
+        raise ValueError("the timed window holds no evicting step")
+    t = sum(ev) / len(ev)
+    if L > 1:
+        if not ne:
+            raise ValueError("the timed window holds no non-evicting step")
+        t += (L - 1) * sum(ne) / len(ne)
+    return t
+
+
+def cycle_bytes(w, lens, moved, scorer: str) -> int:
+    """Algorithmic bytes of one eviction cycle over all layers: the L - 1
+    non-evicting steps at B + 1 .. B + L - 1 rows (fused append), plus the
+    evicting step (append, scorer, select, compaction of the rows the timed
+    evictions moved on average, attention over B rows)."""
+    B, L = w.budget, w.evict_len
+    per_layer = sum(attn_launch_bytes(w, n, True) for n in range(B + 1, B + L))
+    mv = list(moved.values())
+    mean_moved = sum(mv) / len(mv) if mv else 0
+    per_layer += evict_extra_bytes(w, B + L, int(round(mean_moved)), scorer)
+    per_layer += attn_launch_bytes(w, B, False)
+    return per_layer * w.layers
+
+
+def timing_note(events: bool, flushed: bool, flush_mb: int, L: int,
+                wall: float, wall_tokens_s: float) -> dict:
+    if not events:
+        return {"method": "wall clock over the timed steps"}
+    how = ("per-step HIP events on the launch stream, folded into one "
+           f"eviction cycle: mean evicting step + {L - 1} x mean "
+           "non-evicting step")
+    if flushed:
+        how += (f"; a {flush_mb} MB copy before every step, outside the "
+                "timed spans, keeps the cache out of the Infinity Cache")
+    return {"method": how, "wall_ms": round(wall * 1e3, 3),
+            "wall_tokens_per_s": round(wall_tokens_s, 1)}
+
+
+# ---------------------------------------------------------------------------
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed decode steps (default 2 eviction cycles)")
+                    help="timed decode steps (default 4 eviction cycles)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps (default 1 eviction cycle)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
@@ -887,7 +992,15 @@ def main() -> int:
     # evicts one entry every step)
     steps = args.steps if args.steps is not None else max(4 * L, 64)
     warmup = args.warmup if args.warmup is not None else max(L, 8)
-    pool = min(warmup + steps, 3 * L)
+    if steps < 1 or warmup < 0:
+        print(json.dumps({"error": "--steps must be at least 1 and --warmup "
+                          "at least 0"}))
+        return 2
+    # The cache holds B entries after set-up and evicts on every L-th step.
+    # Set-up advances it by `preroll` untimed decode steps so that an
+    # eviction falls in the middle of the timed window, whatever --steps is.
+    preroll = preroll_steps(L, warmup, steps)
+    pool = min(preroll + warmup + steps, 3 * L)
     log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")
     t0 = time.perf_counter()
@@ -899,10 +1012,14 @@ def main() -> int:
     stack = Stack(w, args.seed, pool, dev, decay=args.decay,
                   scorer=scorer, stochastic=args.stochastic,
                   start_pos=args.start_pos)
-    log(f"set-up {time.perf_counter() - t0:.1f} s")
+    for i in range(preroll):
+        stack.run_step(i)
+    torch.cuda.synchronize()
+    log(f"set-up {time.perf_counter() - t0:.1f} s (cache advanced by "
+        f"{preroll} decode steps to the phase the timed window starts at)")
 
     for i in range(warmup):
-        stack.run_step(i)
+        stack.run_step(preroll + i)
     torch.cuda.synchronize()
     log("warm-up done")
 
@@ -932,7 +1049,8 @@ def main() -> int:
     # One event after every step (plus one before the first): a step without
     # an eviction is exactly one attention launch per layer, so its duration
     # over the layer count is the mean launch duration of the kernel,
-    # measured on the stream the launches go to.
+    # measured on the stream the launches go to. The per-step times also
+    # fold the window into one eviction cycle (cycle_fold).
     use_events = not args.no_kernel_events
     events = None
     if use_events:
@@ -955,7 +1073,7 @@ def main() -> int:
         if flush is not None:
             flush[1].copy_(flush[0])
             starts[s].record()
-        stack.run_step(warmup + s, keep_for)
+        stack.run_step(preroll + warmup + s, keep_for)
         if use_events:
             events[s + 1].record()
     torch.cuda.synchronize()
@@ -995,8 +1113,24 @@ def main() -> int:
             attn_bytes += [attn_launch_bytes(w, n, True)] * n_layers
             attn_ms += [step_ms / n_layers] * n_layers
 
-    tokens_s = w.batch * steps / wall
-    step_gbps = total_bytes / wall / 1e9
+    n_evict = sum(1 for _, ev in lens if ev)
+    log(f"timed window: {n_evict} evicting step(s) of {steps}, attention "
+        f"over {sum(attn_rows(w, n, ev) for n, ev in lens) / steps:.1f} "
+        f"rows on average (cycle mean {w.budget + (L - 1) / 2:.1f})")
+    wall_tokens_s = w.batch * steps / wall
+    if use_events:
+        step_ms_all = (step_ms_list if step_ms_list is not None else
+                       [events[s].elapsed_time(events[s + 1])
+                        for s in range(steps)])
+        cyc_ms = cycle_fold(step_ms_all, [ev for _, ev in lens], L)
+        cyc_bytes = cycle_bytes(w, lens, moved, scorer)
+        tokens_s = w.batch * L / (cyc_ms * 1e-3)
+        ms_step = cyc_ms / L
+        step_gbps = cyc_bytes / (cyc_ms * 1e-3) / 1e9
+    else:
+        tokens_s = wall_tokens_s
+        ms_step = wall * 1e3 / steps
+        step_gbps = total_bytes / wall / 1e9
     roof = None
     if use_events and attn_ms:
         mean_ms = sum(attn_ms) / len(attn_ms)
@@ -1019,7 +1153,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1041,21 +1175,28 @@ def main() -> int:
                    "decay": bool(args.decay),
                    "stochastic_eviction": bool(args.stochastic),
                    "flush_mb": args.flush_mb,
-                   "parallelism": "none"},
+                   "parallelism": "none",
+                   "timed_window": {
+                       "preroll_steps": preroll,
+                       "evicting_steps": n_evict,
+                       "mean_attention_rows": round(
+                           sum(attn_rows(w, n, ev) for n, ev in lens)
+                           / steps, 2),
+                       "cycle_mean_attention_rows": w.budget + (L - 1) / 2}},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "achievable_copy_gbps": None,
+        "achievable_read_gbps": None,
         "roofline": roof,
-        "timing": ("wall clock over the timed steps" if flush is None else
-                   f"sum of per-step HIP event times; a {args.flush_mb} MB "
-                   "copy before every step, outside the timed spans, keeps "
-                   "the cache out of the Infinity Cache"),
+        "timing": timing_note(use_events, flush is not None, args.flush_mb,
+                              L, wall, wall_tokens_s),
         "prompt_compress": compress_summary(w, stack, scorer),
         "cpu_baseline": None,
     }
     del stack
     torch.cuda.empty_cache()
     result["achievable_copy_gbps"] = round(achievable_copy_gbps(dev), 1)
+    result["achievable_read_gbps"] = round(achievable_read_gbps(dev), 1)
     if not args.no_cpu_baseline:
         cs = args.cpu_steps if args.cpu_steps is not None else max(2 * L, 64)
         cbatch = args.cpu_batch

@@ -1,7 +1,8 @@
 """Build libkvevict.so in-tree with hipcc for gfx950.
 
 Each HIP source is compiled to an object in ``_build/`` (in parallel), then
-linked into ``learned_kv_cache_head_amd/_lib/libkvevict.so``.
+linked into ``learned_kv_cache_head_amd/_lib/libkvevict.so``. The benchmark's
+read-bandwidth reference kernel is linked into its own ``libkvebench.so``.
 """
 from __future__ import annotations
 
@@ -16,9 +17,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libkvevict.so")
+BENCH_LIB = os.path.join(LIBDIR, "libkvebench.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["kvevict.hip", "attention.hip", "cache_ops.hip", "score.hip",
            "mlstm.hip", "prefill.hip"]
+BENCH_SOURCES = ["bench_read.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -62,22 +65,24 @@ def build(verbose: bool = False) -> str:
         rc, out = _run(cmd)
         return src, obj, rc, out, cmd
 
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        results = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(compile_one, SOURCES + BENCH_SOURCES))
     for src, obj, rc, out, cmd in results:
         if verbose or rc != 0:
             sys.stderr.write(f"[build] {' '.join(cmd)}\n{out}\n")
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {src}")
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-           *[r[1] for r in results]]
-    rc, out = _run(cmd)
-    if verbose or rc != 0:
-        sys.stderr.write(f"[build] {' '.join(cmd)}\n{out}\n")
-    if rc != 0:
-        raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
+    objs = {r[0]: r[1] for r in results}
+    for lib, srcs in ((LIB, SOURCES), (BENCH_LIB, BENCH_SOURCES)):
+        tmp = lib + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+               *[objs[x] for x in srcs]]
+        rc, out = _run(cmd)
+        if verbose or rc != 0:
+            sys.stderr.write(f"[build] {' '.join(cmd)}\n{out}\n")
+        if rc != 0:
+            raise RuntimeError(f"link failed: {os.path.basename(lib)}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -62,3 +62,65 @@ def test_algorithmic_byte_accounting():
     select = 768 * ((1152 - 4 - 128) * 8 + 1024 * 4)
     compact = moved * 2 * (2 * 256 + 8)
     assert extra == append + score + select + compact
+
+
+def _window(L, warmup, steps):
+    """Which timed steps evict, stepping a cache from B entries through the
+    pre-roll and the warm-up the way bench.py does (the t-th step after the
+    prompt compression evicts when t is a multiple of L)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    p = bench.preroll_steps(L, warmup, steps)
+    assert 0 <= p < L
+    return [(p + warmup + 1 + s) % L == 0 for s in range(steps)]
+
+
+def test_timed_window_holds_an_eviction_at_any_step_count():
+    # the driver's short run, the default four cycles, the Qwen2.5-14B
+    # gate's L = 64, batch 8's L = 256 and the per-token eviction (L = 1)
+    for L, warmup, steps in [(128, 5, 20), (128, 128, 512), (64, 5, 20),
+                             (256, 0, 1), (256, 3, 7), (1, 5, 20),
+                             (128, 300, 2)]:
+        ev = _window(L, warmup, steps)
+        # the middle step evicts, and so does every L-th step from it
+        assert ev == [(s - steps // 2) % L == 0 for s in range(steps)], \
+            (L, warmup, steps)
+    # whole cycles: exactly one eviction per L steps
+    assert sum(_window(128, 128, 512)) == 4
+
+
+def test_cycle_fold_weighs_one_evicting_step_in_L():
+    sys.path.insert(0, ROOT)
+    import bench
+    L = 128
+    ev = _window(L, 5, 20)
+    times = [3.0 if e else 1.0 for e in ev]
+    # one evicting step of 3 ms and L - 1 steps of 1 ms per cycle
+    assert abs(bench.cycle_fold(times, ev, L) - (3.0 + 127.0)) < 1e-12
+    # over whole cycles the fold equals the window's time per cycle
+    ev = _window(L, 128, 512)
+    times = [5.0 if e else 2.0 + 0.001 * i for i, e in enumerate(ev)]
+    assert abs(bench.cycle_fold(times, ev, L) - sum(times) / 4) < 0.5
+    # L = 1: every step evicts
+    assert bench.cycle_fold([2.0, 4.0], [True, True], 1) == 3.0
+    import pytest
+    with pytest.raises(ValueError):
+        bench.cycle_fold([1.0, 1.0], [False, False], L)
+
+
+def test_cycle_bytes_sum_the_steps_of_one_cycle():
+    """One cycle of the batch-96 stack: L - 1 fused-append attentions at
+    B + 1 .. B + L - 1 rows, then the evicting step's extras and its
+    attention over B rows, in each of the 36 layers."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import synthetic as syn
+    w = syn.workload(4)
+    B, L = 1024, 128
+    moved = {(0, 0): 1000, (1, 0): 1002}
+    per_slice_rows = sum(range(B + 1, B + L)) * 2 * 256
+    per_slice_fixed = (L - 1) * (4 * 256 + 4 * 512 + 2 * 256 + 4)
+    attn = 768 * (per_slice_rows + per_slice_fixed)
+    evict = bench.evict_extra_bytes(w, B + L, 1001) + \
+        768 * (B * 2 * 256 + 4 * 256 + 4 * 512)
+    assert bench.cycle_bytes(w, [], moved, "mlp") == 36 * (attn + evict)
