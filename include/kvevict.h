@@ -307,6 +307,32 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
                     int32_t* keep_slots, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* Size of the device scratch array that kve_step_noalloc uses, bytes. */
+#define KVE_NOALLOC_SCRATCH_BYTES (2u << 20)
+
+/* kve_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument; the split-K partial results of the attention launch
+ * live in a library-owned device array of KVE_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends (its address is looked up on the first call
+ * on each device; nothing is allocated). Arguments, results, updates of
+ * *state and the failure contract are those of kve_step. A step whose
+ * attention plan needs more partial storage than the array holds returns
+ * KVE_ERR_WORKSPACE before any launch (every shape whose
+ * kve_workspace_bytes(shape, state->len + 1) is at most
+ * KVE_NOALLOC_SCRATCH_BYTES fits; use kve_step with a workspace beyond
+ * that). Every call on one GPU shares that GPU's array, and its contents
+ * are scratch: calls that overlap on one GPU (on different streams, or from
+ * host threads without ordering) race and give undefined results; order
+ * them on one stream. */
+kve_status kve_step_noalloc(const kve_shape* shape, const kve_policy* policy,
+                            const kve_scorer* scorer, kve_cache* cache,
+                            kve_decode_state* state, const void* k_new,
+                            const void* v_new, const void* hidden_new,
+                            void* hidden_buf, const void* q, float* out,
+                            float* lse, int32_t* keep_slots,
+                            hipStream_t stream);
+
 /* Prefill selection (KVpop section 3.2 "Running top-k sparse attention",
  * Appendix C.1-C.2) for a prompt of len tokens held in slots [0, len) with
  * slot s holding position s, scored in cache->score (by kve_score):

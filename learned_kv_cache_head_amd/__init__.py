@@ -100,7 +100,14 @@ _SIGS = {
                       ctypes.POINTER(_Scorer), ctypes.POINTER(_Cache),
                       ctypes.POINTER(_State), _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, ctypes.c_size_t, _P]),
+    "kve_step_noalloc": (_I, [ctypes.POINTER(_Shape), ctypes.POINTER(_Policy),
+                              ctypes.POINTER(_Scorer), ctypes.POINTER(_Cache),
+                              ctypes.POINTER(_State), _P, _P, _P, _P, _P, _P,
+                              _P, _P, _P]),
 }
+
+# Bytes of the device scratch array of kve_step_noalloc (include/kvevict.h).
+NOALLOC_SCRATCH_BYTES = 2 << 20
 
 _lib = None
 
@@ -461,7 +468,8 @@ def kve_decode_attn(shape: Shape, cache: CacheTensors, length: int, q, out,
 
 
 def _check_step_args(shape, policy, scorer, cache, k_new, v_new, q, out, lse,
-                     keep_slots, ws, hidden_new, hidden_buf) -> None:
+                     keep_slots, ws, hidden_new, hidden_buf,
+                     need_ws: bool = True) -> None:
     _check_cache(shape, cache)
     _check_policy(shape, policy)
     _check_scorer(shape, scorer)
@@ -474,7 +482,8 @@ def _check_step_args(shape, policy, scorer, cache, k_new, v_new, q, out, lse,
     _dev(v_new, row, "v_new")
     _dev(keep_slots, shape.batch * shape.n_kv_heads * policy.budget * 4,
          "keep_slots")
-    _dev(ws, 0, "ws")
+    if need_ws:
+        _dev(ws, 0, "ws")
     _dev(hidden_new, shape.batch * scorer.in_dim * 2, "hidden_new", True)
     _dev(hidden_buf, shape.batch * policy.evict_len * scorer.in_dim * 2,
          "hidden_buf", True)
@@ -495,6 +504,28 @@ def kve_step(shape: Shape, policy: Policy, scorer: Scorer,
         _ptr(hidden_new), _ptr(hidden_buf), _ptr(q), _ptr(out), _ptr(lse),
         _ptr(keep_slots), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)), "kve_step")
+    state.len, state.scored_upto = st.len, st.scored_upto
+    state.next_position, state.evicted = st.next_position, st.evicted
+    return state
+
+
+def kve_step_noalloc(shape: Shape, policy: Policy, scorer: Scorer,
+                     cache: CacheTensors, state: DecodeState, k_new, v_new, q,
+                     out, lse, keep_slots, hidden_new=None, hidden_buf=None,
+                     stream=None) -> DecodeState:
+    """``kve_step`` without a workspace: the split-K partials live in the
+    library's per-GPU scratch array, and the call allocates nothing. Calls
+    that overlap on one GPU race (order them on one stream)."""
+    _check_step_args(shape, policy, scorer, cache, k_new, v_new, q, out, lse,
+                     keep_slots, None, hidden_new, hidden_buf,
+                     need_ws=False)
+    cs, cp, csc, cc = shape.c(), policy.c(), scorer.c(), cache.c()
+    st = _State(state.len, state.scored_upto, state.next_position, 0)
+    _check(load_library().kve_step_noalloc(
+        ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(csc),
+        ctypes.byref(cc), ctypes.byref(st), _ptr(k_new), _ptr(v_new),
+        _ptr(hidden_new), _ptr(hidden_buf), _ptr(q), _ptr(out), _ptr(lse),
+        _ptr(keep_slots), _stream(stream)), "kve_step_noalloc")
     state.len, state.scored_upto = st.len, st.scored_upto
     state.next_position, state.evicted = st.next_position, st.evicted
     return state

@@ -3,6 +3,8 @@
 // library never allocates and never synchronises the device.
 #include "kvevict.h"
 
+#include <mutex>
+
 #include "kve_internal.h"
 
 namespace {
@@ -296,6 +298,47 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
   return done(kve::launch_score_gate(g, stream, check_only));
 }
 
+// Scratch of kve_step_noalloc: the split-K partial results of its
+// attention launches live in this file-scope device array (one copy per
+// GPU, held until the process ends) instead of a caller workspace.
+constexpr size_t kNoallocScratchBytes = KVE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[KVE_NOALLOC_SCRATCH_BYTES];
+
+// Device address of the current device's copy of `scratch`. The array's name
+// is a host-side stand-in in host code: the address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept. Returns null and sets *st if the lookup fails.
+void* noalloc_scratch(kve_status* st) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = KVE_ERR_LAUNCH;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *st = KVE_ERR_LAUNCH;
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+// One decode step of one layer (kve_step). With use_scratch the split-K
+// partials go to the library's scratch array and ws / ws_bytes are ignored.
+kve_status step_impl(const kve_shape* shape, const kve_policy* policy,
+                     const kve_scorer* scorer, kve_cache* cache,
+                     kve_decode_state* state, const void* k_new,
+                     const void* v_new, const void* hidden_new,
+                     void* hidden_buf, const void* q, float* out, float* lse,
+                     int32_t* keep_slots, void* ws, size_t ws_bytes,
+                     bool use_scratch, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -506,6 +549,7 @@ kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
                    nullptr, nullptr, stream);
 }
 
+
 kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
                     const kve_scorer* scorer, kve_cache* cache,
                     kve_decode_state* state, const void* k_new,
@@ -513,6 +557,34 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
                     void* hidden_buf, const void* q, float* out, float* lse,
                     int32_t* keep_slots, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
+  return step_impl(shape, policy, scorer, cache, state, k_new, v_new,
+                   hidden_new, hidden_buf, q, out, lse, keep_slots, ws,
+                   ws_bytes, false, stream);
+}
+
+kve_status kve_step_noalloc(const kve_shape* shape, const kve_policy* policy,
+                            const kve_scorer* scorer, kve_cache* cache,
+                            kve_decode_state* state, const void* k_new,
+                            const void* v_new, const void* hidden_new,
+                            void* hidden_buf, const void* q, float* out,
+                            float* lse, int32_t* keep_slots,
+                            hipStream_t stream) {
+  return step_impl(shape, policy, scorer, cache, state, k_new, v_new,
+                   hidden_new, hidden_buf, q, out, lse, keep_slots, nullptr,
+                   0, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+kve_status step_impl(const kve_shape* shape, const kve_policy* policy,
+                     const kve_scorer* scorer, kve_cache* cache,
+                     kve_decode_state* state, const void* k_new,
+                     const void* v_new, const void* hidden_new,
+                     void* hidden_buf, const void* q, float* out, float* lse,
+                     int32_t* keep_slots, void* ws, size_t ws_bytes,
+                     bool use_scratch, hipStream_t stream) {
   kve_status st = check_shape(shape);
   if (st != KVE_OK) return st;
   if ((st = check_policy(policy)) != KVE_OK) return st;
@@ -537,7 +609,8 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   if (len - scored >= L) return KVE_ERR_INVALID_ARG;  // pending buffer full
   // The attention after this step covers len + 1 rows at most, and the
   // split cap never decreases with len.
-  if (!ws || ws_bytes < ws_bytes_for(shape, split_cap(shape, len + 1)))
+  if (!use_scratch &&
+      (!ws || ws_bytes < ws_bytes_for(shape, split_cap(shape, len + 1))))
     return KVE_ERR_WORKSPACE;
 
   const int slot = len;
@@ -556,6 +629,16 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   // enqueues them.
   const int att_len = evict ? B : new_len;
   const int att_scored = score_now ? (evict ? B : new_len) : scored;
+  if (use_scratch) {
+    // The attention plan of this step must fit the scratch array; its
+    // address is looked up only then (so argument errors come first).
+    if (ws_bytes_for(shape, plan_split(shape, att_len).nsplit) >
+        kNoallocScratchBytes)
+      return KVE_ERR_WORKSPACE;
+    ws = noalloc_scratch(&st);
+    if (!ws) return st;
+    ws_bytes = kNoallocScratchBytes;
+  }
   for (int pass = 0; pass < 2; ++pass) {
     const bool chk = pass == 0;
     auto done = [chk](hipError_t e) {
@@ -598,4 +681,4 @@ kve_status kve_step(const kve_shape* shape, const kve_policy* policy,
   return KVE_OK;
 }
 
-}  // extern "C"
+}  // namespace

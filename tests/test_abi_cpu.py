@@ -235,6 +235,35 @@ def test_step_checks_every_launch_before_the_first():
     assert state.len == B + L - 3
 
 
+def test_step_noalloc_validates_before_its_scratch():
+    """kve_step_noalloc checks its arguments, then whether this step's
+    split-K plan fits the scratch array (KVE_NOALLOC_SCRATCH_BYTES), before
+    it looks up the array or launches anything. 272 slices of 8193 rows at
+    G = 8 split 16 ways on 256 CUs: 272 * 8 * 16 * 130 * 4 bytes of
+    partials, beyond 2 MiB."""
+    lib = _lib()
+    assert kve.NOALLOC_SCRATCH_BYTES == 2 << 20
+    header = open(HEADER).read()
+    assert "#define KVE_NOALLOC_SCRATCH_BYTES (2u << 20)" in header
+    mlp = kve._Scorer(0, 0, kve.BF16, 256, 64, FAKE, None, FAKE, None)
+
+    def call(shape, pol, state):
+        return lib.kve_step_noalloc(
+            ctypes.byref(shape), ctypes.byref(pol), ctypes.byref(mlp),
+            ctypes.byref(_cache()), ctypes.byref(state), FAKE, FAKE, None,
+            None, FAKE, FAKE, None, FAKE, None)
+
+    big = _shape(batch=34, group=8, capacity=8256)
+    pol = kve._Policy(8192, 4, 128, 64)
+    state = kve._State(8192, 8192, 9000, 3)
+    assert call(big, pol, state) == 5
+    assert (state.len, state.scored_upto, state.evicted) == (8192, 8192, 3)
+    # argument errors come first, as in kve_step
+    assert call(big, pol, kve._State(8192, 9000, 9000, 0)) == 1
+    assert call(_shape(capacity=1100), kve._Policy(1024, 4, 128, 128),
+                kve._State(1000, 1000, 9000, 0)) == 3
+
+
 def test_policy_struct_layout_matches_header():
     """kve_policy: four int32 fields, then the log_gamma and gumbel
     pointers."""
