@@ -13,14 +13,19 @@
 // (bitonic sort, descending); a token's rank is then the number of larger
 // pairs, summed over the chunks by binary search.
 //
-// Cutoffs: as q grows by one, one token enters E(q), and tau_q can only move
-// to a better (smaller) rank. One wave per slice keeps the inserted ranks as
-// a bitmap in LDS: when the k-th token enters, tau is the largest inserted
-// rank; afterwards a new token better than tau pushes tau to the next
-// smaller inserted rank (the predecessor in the bitmap, found 64 words at a
-// time with a ballot). Total work is O(n + n / 32) per slice. (The pages use
-// a Fenwick tree with binary lifting; the monotone cutoff makes a bitmap
-// predecessor search enough.)
+// Cutoffs: ranks are distinct, so an LDS bitmap over rank values holds the
+// eligible set E(q). One workgroup per (slice, 64-query block): it sets the
+// bits of E(q0) for the block's first query q0 in parallel and finds
+// tau_{q0}, the k-th set bit, from word popcounts and a block scan. One wave
+// then walks the block's other 63 queries in order: as q grows by one, one
+// token enters E(q) and tau_q can only move to a better (smaller) rank.
+// While |E| < k, tau = n; when the k-th token enters, tau is the largest
+// inserted rank; afterwards a new token better than tau moves tau to the
+// next smaller set rank (the predecessor in the bitmap, found 64 words at a
+// time with a ballot). (The pages use a Fenwick tree with binary lifting;
+// the monotone cutoff makes a bitmap predecessor search enough, and the
+// parallel rebuild per block replaces a chain of n sequential steps by one
+// of 64.)
 //
 // Attention: a flash-attention forward on MFMA (v_mfma_f32_16x16x32_bf16,
 // float32 accumulation) with the Eq. 26 predicate applied to each logit. A
@@ -30,7 +35,9 @@
 // them; the V^T operand comes from LDS transpose reads. The kernel
 // computes S^T = K Q^T, so a lane's accumulators hold 8 keys of one query
 // column: those are exactly the operand of P^T that O^T = V^T P^T needs,
-// and the online-softmax state is one value per lane and head.
+// and the online-softmax state is one value per lane and head. Each weight
+// enters O^T as two bf16 parts (its rounding and the remainder), two MFMAs
+// into one float32 accumulator, so P.V keeps about 17 bits of each weight.
 #include "kve_internal.h"
 
 namespace kve {
@@ -510,8 +517,10 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
         }
       }
       // Online softmax per query column, then O^T += V^T P^T, 32 keys per
-      // contraction step: half hh holds key tiles 2hh and 2hh+1.
-      uint32_t pk[GS][KT / 2][4];
+      // contraction step: half hh holds key tiles 2hh and 2hh+1. Each weight
+      // goes to the MFMA as two bf16 parts, its rounding and the remainder
+      // (pk, pl): their sum carries a relative error of at most 2^-17.
+      uint32_t pk[GS][KT / 2][4], pl[GS][KT / 2][4];
 #pragma unroll
       for (int gi = 0; gi < GS; ++gi) {
         // Raw logits (the scale is positive, so the maximum commutes with
@@ -536,14 +545,17 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
         const float mnew = move ? mx : mrun[gi];
         const float alpha = move ? __builtin_amdgcn_exp2f(mrun[gi] - mnew) : 1.f;
         const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-        // p goes to the MFMA in bf16 (relative error <= 2^-9 per weight);
-        // the normaliser, and so lse, sums the float32 values.
+        // p goes to the MFMA as hi = bf16(p) and lo = bf16(p - hi): p - hi
+        // is exact in float32 and at most 2^-9 p, so hi + lo is within
+        // 2^-17 p. The normaliser, and so lse, sums the float32 values.
         float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < KT * 4; j += 2) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(x[j], qscale, -mref));
           const float e1 = __builtin_amdgcn_exp2f(fmaf(x[j + 1], qscale, -mref));
-          pk[gi][j >> 3][(j >> 1) & 3] = pack2(e0, e1);
+          const uint32_t hi = pack2(e0, e1);
+          pk[gi][j >> 3][(j >> 1) & 3] = hi;
+          pl[gi][j >> 3][(j >> 1) & 3] = pack2(e0 - bf16lo(hi), e1 - bf16hi(hi));
           ps += e0 + e1;
         }
         lrun[gi] = lrun[gi] * alpha + ps;
@@ -575,6 +587,14 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
             const bf16x8_t B = __builtin_bit_cast(
                 bf16x8_t,
                 u32x4{pk[gi][hh][0], pk[gi][hh][1], pk[gi][hh][2], pk[gi][hh][3]});
+            o[dt][gi] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
+          }
+#pragma unroll
+          for (int gi = 0; gi < GS; ++gi) {
+            const bf16x8_t B = __builtin_bit_cast(
+                bf16x8_t,
+                u32x4{pl[gi][hh][0], pl[gi][hh][1], pl[gi][hh][2], pl[gi][hh][3]});
             o[dt][gi] =
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
           }

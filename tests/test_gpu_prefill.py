@@ -3,11 +3,12 @@
 ABI, against the float64 oracle.
 
 Ranks and cutoffs are integers decided from the same float32 keys on both
-sides: bit-exact. Attention: the GPU rounds the softmax weights to bf16 for
-the P.V contraction and normalises by the float32 sum, so each weight
-carries a relative error of at most 2^-9 and the output lies within
-2^-9 * max|V| of the exact one; the test allows 2^-8 * max|V| per tensor.
-lse is float32 math on unrounded weights: within 1e-4 absolute.
+sides: bit-exact. Attention is held to the attention contract: within
+2e-3 * max|out| of the float64 oracle per (batch, query head) output tensor.
+The GPU feeds each softmax weight to the P.V contraction as two bf16 parts
+(its rounding and the remainder, relative error at most 2^-17 together) and
+normalises by the float32 sum. lse is float32 math on unrounded weights:
+within 1e-4 absolute.
 """
 import numpy as np
 import pytest
@@ -19,6 +20,16 @@ from kvharness import kve
 pytestmark = pytest.mark.gpu
 
 LSE_TOL = 1e-4
+ATTN_RTOL = 2e-3   # |gpu - oracle| <= 2e-3 * max|out| per output tensor
+
+
+def assert_attention_close(got, ref, what=""):
+    """got, ref [H*G][n][d] of one batch row: each query head's output
+    tensor within ATTN_RTOL of its largest oracle element."""
+    for j in range(ref.shape[0]):
+        tol = ATTN_RTOL * np.abs(ref[j]).max()
+        err = np.abs(got[j] - ref[j]).max()
+        assert err <= tol, f"{what} head {j}: |err| {err:.3g} > {tol:.3g}"
 
 
 def scores_for(rng, b, H, n, kind):
@@ -147,10 +158,10 @@ def test_prefill_attention(case):
                           for h in range(H)])
         ref, ref_lse = O.prefill_attention(Q.f64[bi], K.f64[bi], V.f64[bi],
                                            masks, G)
-        tol = 2.0 ** -8 * np.abs(V.f64[bi]).max()
-        err = np.abs(out[bi] - ref).max()
-        print(f"[prefill-attn] max |err| {err:.3g} (tol {tol:.3g})", flush=True)
-        np.testing.assert_allclose(out[bi], ref, rtol=0, atol=tol)
+        rel = max(np.abs(out[bi, j] - ref[j]).max() / np.abs(ref[j]).max()
+                  for j in range(ref.shape[0]))
+        print(f"[prefill-attn] max |err| / max|out| {rel:.3g}", flush=True)
+        assert_attention_close(out[bi], ref, f"batch {bi}")
         np.testing.assert_allclose(lse[bi], ref_lse, rtol=0, atol=LSE_TOL)
 
 
@@ -163,8 +174,7 @@ def test_prefill_attention_with_decay_and_skipped_blocks():
     masks = np.stack([O.prefill_mask(rank[0, h], tau[0, h], S, W)
                       for h in range(H)])
     ref, ref_lse = O.prefill_attention(Q.f64[0], K.f64[0], V.f64[0], masks, G)
-    np.testing.assert_allclose(out[0], ref, rtol=0,
-                               atol=2.0 ** -8 * np.abs(V.f64[0]).max())
+    assert_attention_close(out[0], ref, "decay")
     np.testing.assert_allclose(lse[0], ref_lse, rtol=0, atol=LSE_TOL)
 
 
@@ -181,7 +191,11 @@ def test_prefill_full_size_sampled(case):
     """Full-size prompts in the launch shape the benchmark uses: ranks exact
     for every token, cutoffs exact at sampled positions (the definition:
     sort of the eligible ranks), attention rows at sampled (position, head)
-    pairs against decode attention over the tokens the mask keeps."""
+    pairs against decode attention over the tokens the mask keeps. The
+    sampled rows always include position 0 (its output is v_0), and each
+    (batch, query head) tensor's tolerance is 2e-3 times the largest oracle
+    element among its sampled rows: a lower bound of the tensor's maximum,
+    so the check is at least as strict as the contract."""
     import torch
     k_ = kve()
     dev = torch.device("cuda")
@@ -216,6 +230,7 @@ def test_prefill_full_size_sampled(case):
             t_gpu = tau[bi, h].cpu().numpy()
             K = c.k[bi, h].float().cpu().numpy().astype(np.float64)
             V = c.v[bi, h].float().cpu().numpy().astype(np.float64)
+            rows = {}  # query head -> [(position, gpu row, oracle row)]
             for qq in qs:
                 elig = r[S:max(qq - W + 1, S)]
                 t_ref = n if elig.shape[0] < kk else np.partition(elig, kk - 1)[kk - 1]
@@ -227,6 +242,10 @@ def test_prefill_full_size_sampled(case):
                     qv = q[bi, j, qq].float().cpu().numpy().astype(np.float64)
                     o_ref, l_ref = O.decode_attention(qv[None], K[keep], V[keep])
                     o = out[bi, j, qq].cpu().numpy()
-                    np.testing.assert_allclose(o, o_ref[0], rtol=0,
-                                               atol=2.0 ** -8 * np.abs(V).max())
+                    rows.setdefault(j, []).append((qq, o, o_ref[0]))
                     assert abs(float(lse[bi, j, qq]) - float(l_ref[0])) <= LSE_TOL
+            for j, rs in rows.items():
+                tol = ATTN_RTOL * max(np.abs(ref).max() for _, _, ref in rs)
+                for qq, o, ref in rs:
+                    err = np.abs(o - ref).max()
+                    assert err <= tol, (bi, j, qq, err, tol)
