@@ -84,6 +84,37 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), lo);
 }
 
+// One radix pass, after hist holds the pass's 256-bin histogram: the bin in
+// which the cumulative count reaches `remaining` (sh[0]), the count below
+// it (sh[1]) and its own count (sh[2]). Threads 0..255 (4 waves) scan.
+__device__ __forceinline__ void radix_find_bin(const uint32_t* hist,
+                                               uint32_t* wsum, uint32_t* sh,
+                                               uint32_t remaining) {
+  const int tid = threadIdx.x;
+  uint32_t v = 0, incl = 0;
+  if (tid < 256) {
+    v = hist[tid];
+    incl = v;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[tid >> 6] = incl;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    for (int w = 0; w < (tid >> 6); ++w) incl += wsum[w];
+    if (incl >= remaining && incl - v < remaining) {
+      sh[0] = (uint32_t)tid;
+      sh[1] = incl - v;
+      sh[2] = v;
+    }
+  }
+  __syncthreads();
+}
+
 // Radix select over 32-bit keys: the value of the `rank`-th smallest key
 // (1-based) among the entries i < len with take(i), and how many of those
 // keys equal it must still be taken (`rank` minus the number of smaller
@@ -120,29 +151,7 @@ __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
           atomicAdd(&hist[(k[v] >> shift) & 255u], 1u);
     }
     __syncthreads();
-    // Inclusive scan of the 256 bins by threads 0..255 (4 waves).
-    uint32_t v = 0, incl = 0;
-    if (tid < 256) {
-      v = hist[tid];
-      incl = v;
-      const int lane = tid & 63;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (lane == 63) wsum[tid >> 6] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < (tid >> 6); ++w) incl += wsum[w];
-      if (incl >= remaining && incl - v < remaining) {
-        sh[0] = (uint32_t)tid;
-        sh[1] = incl - v;
-        sh[2] = v;
-      }
-    }
-    __syncthreads();
+    radix_find_bin(hist, wsum, sh, remaining);
     const uint32_t digit = sh[0];
     prefix |= digit << shift;
     mask |= 255u << shift;
@@ -335,6 +344,283 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     carry = before_slab;
     __syncthreads();  // cnt_sh is rewritten by the next sweep
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Select for slices of up to kSelSmallMax entries, every entry held in
+// registers: thread tid owns slots v * kSelThreads + tid (v < kSelR). The
+// score, position (and noise) of each entry are loaded once, and the radix
+// passes and the ordered pass read registers only. Same rule, ties and
+// outputs as select_kernel.
+//
+// With FUSE the kernel also compacts the slice in place (the placement rule
+// of the compaction kernels: the j-th hole below n_keep receives the j-th
+// kept entry at or above n_keep). The ordered pass knows the rank of every
+// hole (its slot minus the kept slots before it) and of every mover (its
+// kept index), so both lists go to LDS and the rows move right after it:
+// the kept list never makes a round trip through memory. All score and
+// position reads happen before the ordered pass, and the moves read only
+// slots at or above n_keep and write only slots below it.
+// ---------------------------------------------------------------------------
+constexpr int kSelR = 8;
+constexpr int kSelSmallMax = kSelThreads * kSelR;  // 4096 entries
+constexpr int kFuseMaxMoves = kSelSmallMax / 2;    // holes <= min(n_keep, r)
+
+// radix_select over the kSelR register entries of every thread.
+__device__ void radix_select_regs(uint32_t rank, const uint32_t (&key)[kSelR],
+                                  const bool (&take)[kSelR], uint32_t* hist,
+                                  uint32_t* wsum, uint32_t* sh,
+                                  uint32_t* key_out, uint32_t* need_out,
+                                  uint32_t* count_eq_out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0, remaining = rank, count_eq = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    if (tid == 0) {
+      sh[0] = 255u;
+      sh[1] = 0u;
+      sh[2] = 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < kSelR; ++v)
+      if (take[v] && (key[v] & mask) == prefix)
+        atomicAdd(&hist[(key[v] >> shift) & 255u], 1u);
+    __syncthreads();
+    radix_find_bin(hist, wsum, sh, remaining);
+    prefix |= sh[0] << shift;
+    mask |= 255u << shift;
+    remaining -= sh[1];
+    count_eq = sh[2];
+    __syncthreads();
+  }
+  *key_out = prefix;
+  *need_out = remaining;
+  *count_eq_out = count_eq;
+}
+
+template <bool FUSE>
+__global__ __launch_bounds__(kSelThreads) void select_small_kernel(
+    float* score, int32_t* pos, const float* log_gamma, const float* gumbel,
+    int H, int cap, int len, int n_keep, int S, int W, int32_t* keep,
+    char* kc_, char* vc_, int row_bytes) {
+  const size_t slice = blockIdx.x;
+  float* sc = score + slice * (size_t)cap;
+  int32_t* ps = pos + slice * (size_t)cap;
+  const float* gs = gumbel ? gumbel + slice * (size_t)cap : nullptr;
+  int32_t* out = keep + slice * (size_t)n_keep;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  if (n_keep >= len) {  // nothing to evict: identity, nothing moves
+    for (int i = tid; i < len; i += kSelThreads) out[i] = i;
+    return;
+  }
+  const uint32_t r = (uint32_t)(len - n_keep);
+
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t sh[4];
+  __shared__ int32_t sh_max[kSelWaves];
+  __shared__ uint32_t ncand_sh;
+  __shared__ uint32_t cnt_sh[kSelR][kSelWaves];
+  __shared__ int32_t holes_sh[FUSE ? kFuseMaxMoves : 1];
+  __shared__ int32_t movers_sh[FUSE ? kFuseMaxMoves : 1];
+  __shared__ uint32_t nholes_sh;
+
+  // Every entry once: position, score (noise). Clamped indices keep all
+  // loads in bounds and in flight together; entries past len are masked.
+  int32_t p[kSelR];
+  float s[kSelR], g[kSelR];
+  bool valid[kSelR];
+#pragma unroll
+  for (int v = 0; v < kSelR; ++v) {
+    const int c = v * kSelThreads + tid;
+    const int cc = min(c, len - 1);
+    valid[v] = c < len;
+    p[v] = ps[cc];
+    s[v] = sc[cc];
+    g[v] = gs ? gs[cc] : 0.f;
+  }
+  // 1. Newest position present (clamped copies repeat a present entry).
+  int32_t mx = p[0];
+#pragma unroll
+  for (int v = 1; v < kSelR; ++v) mx = max(mx, p[v]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if (lane == 0) sh_max[wave] = mx;
+  if (tid == 0) {
+    ncand_sh = 0;
+    nholes_sh = 0;
+  }
+  __syncthreads();
+  int32_t newest = sh_max[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) newest = max(newest, sh_max[w]);
+  const long long last_eligible = (long long)newest - W;
+  const float lg = log_gamma ? log_gamma[slice % H] : 0.f;
+  const bool decay = log_gamma != nullptr;
+  bool cand[kSelR];
+  uint32_t key[kSelR], pk[kSelR];
+  float fk[kSelR];
+#pragma unroll
+  for (int v = 0; v < kSelR; ++v) {
+    cand[v] = valid[v] & (p[v] >= S) & ((long long)p[v] <= last_eligible);
+    // static priority under decay: two separately rounded operations
+    fk[v] = decay ? __fsub_rn(s[v], __fmul_rn((float)p[v], lg)) : s[v];
+    key[v] = score_key(fk[v]);
+    pk[v] = (uint32_t)p[v];
+  }
+  // The `count` first entries with take[] in (key, position) order: cut key
+  // thr and, among entries with key thr, those at positions <= pthr.
+  auto cut = [&](uint32_t count, const uint32_t (&kk)[kSelR],
+                 const bool (&take)[kSelR], uint32_t* thr_out,
+                 uint32_t* pthr_out) {
+    uint32_t thr, need, count_eq;
+    radix_select_regs(count, kk, take, hist, wsum, sh, &thr, &need,
+                      &count_eq);
+    uint32_t pthr = 0xffffffffu;
+    if (need < count_eq) {
+      bool tied[kSelR];
+#pragma unroll
+      for (int v = 0; v < kSelR; ++v) tied[v] = take[v] & (kk[v] == thr);
+      uint32_t pneed, pcount;
+      radix_select_regs(need, pk, tied, hist, wsum, sh, &pthr, &pneed,
+                        &pcount);
+    }
+    *thr_out = thr;
+    *pthr_out = pthr;
+  };
+  auto before = [&](uint32_t k, int v, uint32_t thr, uint32_t pthr) {
+    return (k < thr) | ((k == thr) & (pk[v] <= pthr));
+  };
+  bool evicted[kSelR];
+  uint32_t thr, pthr;
+  if (!gs) {
+    cut(r, key, cand, &thr, &pthr);
+#pragma unroll
+    for (int v = 0; v < kSelR; ++v)
+      evicted[v] = cand[v] & before(key[v], v, thr, pthr);
+  } else {
+    // ForesightKV: pool = the 2r lowest candidates; evict the r pool
+    // entries with the smallest descending key of -key + noise.
+    uint32_t nc = 0;
+#pragma unroll
+    for (int v = 0; v < kSelR; ++v) nc += cand[v] ? 1u : 0u;
+    atomicAdd(&ncand_sh, nc);
+    __syncthreads();
+    const uint32_t pool = min(2u * r, ncand_sh);
+    cut(pool, key, cand, &thr, &pthr);
+    bool in_pool[kSelR];
+    uint32_t dk[kSelR];
+#pragma unroll
+    for (int v = 0; v < kSelR; ++v) {
+      in_pool[v] = cand[v] & before(key[v], v, thr, pthr);
+      dk[v] = ~score_key(__fadd_rn(-fk[v], g[v]));
+    }
+    uint32_t gthr, gpthr;
+    cut(r, dk, in_pool, &gthr, &gpthr);
+#pragma unroll
+    for (int v = 0; v < kSelR; ++v)
+      evicted[v] = in_pool[v] & before(dk[v], v, gthr, gpthr);
+  }
+
+  // 4. Kept slots, ascending: slab v holds slots v * kSelThreads + tid. One
+  // ballot count per wave and slab, one barrier; a slot's kept rank is the
+  // kept count of the earlier slabs, earlier waves and lower lanes.
+  const int M = min(n_keep, (int)r);  // moves, at most
+  if (FUSE) {
+    for (int i = tid; i < M; i += kSelThreads) {
+      holes_sh[i] = -1;
+      movers_sh[i] = -1;
+    }
+  }
+  uint64_t m[kSelR];
+#pragma unroll
+  for (int v = 0; v < kSelR; ++v) {
+    const bool kept = valid[v] & !evicted[v];
+    m[v] = __builtin_amdgcn_ballot_w64(kept);
+    if (lane == 0) cnt_sh[v][wave] = (uint32_t)__builtin_popcountll(m[v]);
+  }
+  __syncthreads();
+  uint32_t before_slab = 0;
+#pragma unroll
+  for (int v = 0; v < kSelR; ++v) {
+    uint32_t in_slab = 0, slab_total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const uint32_t cw = cnt_sh[v][w];
+      in_slab += (w < wave) ? cw : 0u;
+      slab_total += cw;
+    }
+    const int c = v * kSelThreads + tid;
+    const uint32_t idx = before_slab + in_slab + lane_prefix(m[v]);
+    const bool kept = (m[v] >> lane) & 1ull;
+    if (kept && idx < (uint32_t)n_keep) out[idx] = c;
+    if (FUSE) {
+      // idx counts the kept slots before c. A hole below n_keep has hole
+      // rank c - idx; a kept slot at or above n_keep has kept rank idx,
+      // and the kept ranks of the movers are the last ones below n_keep.
+      if (!kept && valid[v] && c < n_keep) {
+        const int j = c - (int)idx;
+        if (j < M) holes_sh[j] = c;
+        atomicAdd(&nholes_sh, 1u);
+      } else if (kept && c >= n_keep && idx < (uint32_t)n_keep) {
+        const int j = (int)idx - (n_keep - M);
+        if (j >= 0) movers_sh[j] = c;
+      }
+    }
+    before_slab += slab_total;
+  }
+  if (!FUSE) return;
+  __syncthreads();
+
+  // Moves: hole j <- mover M - nh + j (the movers' kept ranks run from
+  // n_keep - nh to n_keep - 1). A slice that breaks the contract (repeated
+  // positions) can leave an entry unset: its row is skipped, never written.
+  const int nh = min((int)nholes_sh, M);
+  const int cpr = row_bytes >> 4;  // 16-byte chunks per K (or V) row
+  const int items = nh * 2 * cpr;  // K and V chunks of every moved row
+  const size_t base = slice * (size_t)cap;
+  constexpr int RB = 8;            // chunks in flight per thread
+  for (int i0 = tid; i0 < items; i0 += RB * kSelThreads) {
+    u32x4 buf[RB];
+    int dst[RB];
+    size_t doff[RB];
+    bool isv[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int it = i0 + u * kSelThreads;
+      dst[u] = -1;
+      if (it < items) {
+        const int j = it / (2 * cpr);
+        const int q = it % (2 * cpr);
+        const int d = holes_sh[j];
+        const int src = movers_sh[M - nh + j];
+        if (d >= 0 && d < n_keep && src >= n_keep && src < cap) {
+          isv[u] = q >= cpr;
+          const size_t qo = (size_t)(q % cpr) * 16;
+          const char* from = (isv[u] ? vc_ : kc_) +
+                             (base + src) * (size_t)row_bytes + qo;
+          buf[u] = *(const u32x4*)from;
+          dst[u] = d;
+          doff[u] = (base + d) * (size_t)row_bytes + qo;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      if (dst[u] >= 0) *(u32x4*)((isv[u] ? vc_ : kc_) + doff[u]) = buf[u];
+  }
+  for (int j = tid; j < nh; j += kSelThreads) {
+    const int d = holes_sh[j];
+    const int src = movers_sh[M - nh + j];
+    if (d >= 0 && d < n_keep && src >= n_keep && src < cap) {
+      sc[d] = sc[src];
+      ps[d] = ps[src];
+    }
   }
 }
 
@@ -575,6 +861,13 @@ hipError_t launch_select(const float* score, const int32_t* pos,
   const bool cache = !gumbel && len > 2048 && len <= kSelCacheMax &&
                      slices <= 256;
   if (check_only) return hipSuccess;
+  if (len <= kSelSmallMax) {
+    hipLaunchKernelGGL(select_small_kernel<false>, dim3(slices),
+                       dim3(kSelThreads), 0, s, const_cast<float*>(score),
+                       const_cast<int32_t*>(pos), log_gamma, gumbel, H, cap,
+                       len, n_keep, S, W, keep, nullptr, nullptr, 0);
+    return hipGetLastError();
+  }
   if (cache)
     hipLaunchKernelGGL(select_kernel<true>, dim3(slices), dim3(kSelThreads), 0,
                        s, score, pos, log_gamma, gumbel, H, cap, len, n_keep,
@@ -614,6 +907,30 @@ hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
   hipLaunchKernelGGL(compact_kernel, dim3(slices, groups), dim3(kCompThreads),
                      0, s, (char*)k, (char*)v, score, pos, cap, row_bytes,
                      keep, n_keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_compact(void* k, void* v, float* score, int32_t* pos,
+                                 const float* log_gamma, const float* gumbel,
+                                 int H, int slices, int cap, int row_bytes,
+                                 int len, int n_keep, int S, int W,
+                                 int32_t* keep, hipStream_t s,
+                                 bool check_only) {
+  const int moves = n_keep < len - n_keep ? n_keep : len - n_keep;
+  const bool fused = len <= kSelSmallMax && moves <= kFuseMaxMoves &&
+                     row_bytes % 16 == 0;
+  if (!fused) {
+    hipError_t e = launch_select(score, pos, log_gamma, gumbel, H, slices, cap,
+                                 len, n_keep, S, W, keep, s, check_only);
+    if (e != hipSuccess) return e;
+    return launch_compact(k, v, score, pos, slices, cap, row_bytes, len, keep,
+                          n_keep, s, check_only);
+  }
+  if (check_only) return hipSuccess;
+  hipLaunchKernelGGL(select_small_kernel<true>, dim3(slices),
+                     dim3(kSelThreads), 0, s, score, pos, log_gamma, gumbel,
+                     H, cap, len, n_keep, S, W, keep, (char*)k, (char*)v,
+                     row_bytes);
   return hipGetLastError();
 }
 

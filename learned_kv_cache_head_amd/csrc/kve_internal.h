@@ -86,6 +86,16 @@ hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
                           const int32_t* keep, int n_keep, hipStream_t s,
                           bool check_only = false);
 
+// Select followed by compaction, as one launch when the slice is short
+// enough for the register-resident select (the kept list stays on chip),
+// else launch_select then launch_compact. Same results as the two calls.
+hipError_t launch_select_compact(void* k, void* v, float* score, int32_t* pos,
+                                 const float* log_gamma, const float* gumbel,
+                                 int H, int slices, int cap, int row_bytes,
+                                 int len, int n_keep, int S, int W,
+                                 int32_t* keep, hipStream_t s,
+                                 bool check_only = false);
+
 struct MlpLaunch {
   const void* k;         // cache base
   const void* v;
@@ -96,6 +106,7 @@ struct MlpLaunch {
   const float* b2;       // [H] or null
   int batch, H, D, cap, hidden, act, is_bf16;
   int slot_begin, slot_end;
+  int cus;               // compute units of the device (workgroup sizing)
 };
 hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s,
                             bool check_only = false);

@@ -262,6 +262,7 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
     m.is_bf16 = shape->kv_dtype == KVE_BF16;
     m.slot_begin = slot_begin;
     m.slot_end = slot_end;
+    m.cus = device_cus();
     return done(kve::launch_score_mlp(m, stream, check_only));
   }
   if (sc->kind == KVE_SCORER_SINK_GATE) {
@@ -656,14 +657,11 @@ kve_status step_impl(const kve_shape* shape, const kve_policy* policy,
       if (st != KVE_OK) return st;
     }
     if (evict) {
-      st = done(kve::launch_select(
-          cache->score, cache->pos, policy->log_gamma, policy->gumbel,
-          shape->n_kv_heads, slices, shape->capacity, new_len, B,
-          policy->sinks, policy->window, keep_slots, stream, chk));
-      if (st != KVE_OK) return st;
-      st = done(kve::launch_compact(
-          cache->k, cache->v, cache->score, cache->pos, slices,
-          shape->capacity, row_bytes, new_len, keep_slots, B, stream, chk));
+      st = done(kve::launch_select_compact(
+          cache->k, cache->v, cache->score, cache->pos, policy->log_gamma,
+          policy->gumbel, shape->n_kv_heads, slices, shape->capacity,
+          row_bytes, new_len, B, policy->sinks, policy->window, keep_slots,
+          stream, chk));
       if (st != KVE_OK) return st;
     }
     st = attn_impl(shape, cache, att_len, q, out, lse, ws, ws_bytes,

@@ -34,18 +34,20 @@ __device__ __forceinline__ float activate(float a, int act) {
 }
 
 // ---------------------------------------------------------------------------
-// MLP scorer on MFMA (bf16 K/V and W1). A workgroup scores kMlpRowsPerWG
-// rows of one KV head, flattened over (batch, slot); the head's W1 is staged
-// once in LDS (rows padded by 16 bytes against bank conflicts) and every
-// wave loops over kMlpTiles tiles of 16 rows, loading the next tile's [k; v]
-// operands before the MFMAs of the current one.
+// MLP scorer on MFMA (bf16 K/V and W1). A workgroup scores kMlpWaves * TILES
+// * 16 rows of one KV head, flattened over (batch, slot); the head's W1 is
+// staged once in LDS (rows padded by 16 bytes against bank conflicts) and
+// every wave loops over TILES tiles of 16 rows, loading the next tile's
+// [k; v] operands before the MFMAs of the current one. Eight tiles per wave
+// halve the W1 staging per row for prompts; the buffered rows of a decode
+// eviction (L per slice) take fewer tiles so that every CU gets workgroups.
 // ---------------------------------------------------------------------------
 constexpr int kMlpWaves = 4;
-constexpr int kMlpTiles = 8;                       // tiles per wave
-constexpr int kMlpRowsPerWG = kMlpWaves * kMlpTiles * 16;
+constexpr int kMlpMaxTiles = 8;  // tiles per wave for long row counts
 
-template <int D, int NB>
+template <int D, int NB, int TILES>
 __global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
+  constexpr int kMlpRowsPerWG = kMlpWaves * TILES * 16;
   constexpr int HID = NB * 16;
   constexpr int IN = 2 * D;
   constexpr int KSTEPS = IN / 32;   // 32-wide contraction steps
@@ -140,12 +142,16 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
 
   bf16x8_t a0[KSTEPS], a1[KSTEPS];
   load_tile(a0, 0);
+  if constexpr (TILES == 1) {
+    compute_tile(a0, 0);
+  } else {
 #pragma unroll
-  for (int t = 0; t < kMlpTiles; t += 2) {
-    load_tile(a1, t + 1);
-    compute_tile(a0, t);
-    if (t + 2 < kMlpTiles) load_tile(a0, t + 2);
-    compute_tile(a1, t + 1);
+    for (int t = 0; t < TILES; t += 2) {
+      load_tile(a1, t + 1);
+      compute_tile(a0, t);
+      if (t + 2 < TILES) load_tile(a0, t + 2);
+      compute_tile(a1, t + 1);
+    }
   }
 }
 
@@ -594,13 +600,29 @@ hipError_t launch_score_mlp(const MlpLaunch& m, hipStream_t s,
                        (m.D == 64 || m.D == 128);
   if (mfma_ok) {
     const long long total = (long long)m.batch * rows;
-    const long long wgs = (total + kMlpRowsPerWG - 1) / kMlpRowsPerWG;
+    // Tiles per wave: the most that still give every CU two workgroups.
+    const long long want = 2LL * (m.cus > 0 ? m.cus : 256);
+    int tiles = kMlpMaxTiles;
+    while (tiles > 1 &&
+           (total + kMlpWaves * tiles * 16 - 1) / (kMlpWaves * tiles * 16) *
+                   m.H < want)
+      tiles = tiles == kMlpMaxTiles ? 2 : 1;
+    const long long rpw = kMlpWaves * tiles * 16;
+    const long long wgs = (total + rpw - 1) / rpw;
     if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 mgrid((unsigned)wgs, m.H);
 #define KVE_MLP(DD, NBB)                                                     \
   if (m.D == DD && m.hidden == NBB * 16) {                                   \
     if (check_only) return hipSuccess;                                       \
-    hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB>), mgrid, dim3(256), 0, s, m); \
+    if (tiles == kMlpMaxTiles)                                               \
+      hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB, kMlpMaxTiles>), mgrid,    \
+                         dim3(256), 0, s, m);                                \
+    else if (tiles == 2)                                                     \
+      hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB, 2>), mgrid, dim3(256), 0, \
+                         s, m);                                              \
+    else                                                                     \
+      hipLaunchKernelGGL((mlp_mfma_kernel<DD, NBB, 1>), mgrid, dim3(256), 0, \
+                         s, m);                                              \
     return hipGetLastError();                                                \
   }
     KVE_MLP(128, 1) KVE_MLP(128, 2) KVE_MLP(128, 3) KVE_MLP(128, 4)

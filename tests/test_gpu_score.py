@@ -13,6 +13,10 @@ MLP_CASES = [
     # dtype, head_dim, hidden, act, batch, H, rows (slot range), cap
     ("bf16", 128, 64, "relu", 16, 8, (1024, 1152), 1152),   # Qwen3-4B, L=128
     ("bf16", 128, 64, "relu", 1, 8, (0, 8192), 8192),       # prefill
+    # workgroup sizing by row count (256 CUs): a batch-96 decode eviction
+    # (2 tiles per wave), a prompt long enough for 8 tiles per wave
+    ("bf16", 128, 64, "relu", 96, 8, (1024, 1152), 1152),
+    ("bf16", 128, 64, "relu", 8, 8, (0, 8192), 8192),
     ("bf16", 128, 64, "silu", 2, 3, (5, 77), 100),
     ("bf16", 128, 32, "relu", 2, 2, (0, 33), 40),
     ("bf16", 64, 48, "relu", 1, 2, (3, 200), 256),

@@ -1,6 +1,8 @@
 """a3 select and a4 compact: bit-exact against the oracle when both sides
 are given the same float32 scores and positions, including every kind of
 tie and caches whose slot order is not position order."""
+import zlib
+
 import numpy as np
 import pytest
 
@@ -43,7 +45,8 @@ SELECT_CASES = [
     # keys held in LDS up to 40000 entries (few slices), global beyond
     (4, 128, 40000, 30000, 1, 2),
     (4, 128, 40001, 30000, 1, 2),
-    (4, 64, 4096, 1024, 32, 8),    # 256 slices, LDS keys
+    (4, 64, 4096, 1024, 32, 8),    # 256 slices, keys in registers (limit)
+    (4, 64, 4097, 1024, 4, 8),     # just past it: keys in LDS
 ]
 
 
@@ -233,3 +236,114 @@ def test_compact_bit_exact(case):
     # slots from n_keep on are left as they were
     assert torch.equal(K[:, :, nk:].view(iv), K0[:, :, nk:].view(iv))
     assert torch.equal(pos[:, :, nk:], p0[:, :, nk:])
+
+
+FUSED_CASES = [
+    # dtype, d, G, batch, H, B, L, S, W
+    ("bf16", 128, 4, 12, 8, 1024, 128, 4, 128),   # batch-96 decode eviction
+    ("bf16", 128, 4, 2, 8, 2048, 256, 4, 256),    # batch-8, B = 2048
+    ("f32", 64, 2, 1, 2, 192, 1, 4, 64),          # tiny workload, L = 1
+    ("bf16", 64, 2, 3, 4, 2048, 2048, 4, 2000),   # 4096 entries, 2048 moves
+    ("bf16", 64, 2, 1, 4, 2049, 2048, 4, 2000),   # 4097: two launches
+    ("bf16", 128, 1, 2, 3, 50, 20, 0, 0),         # nothing protected
+]
+
+
+@pytest.mark.parametrize("mode", ["plain", "decay", "stochastic"])
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+@pytest.mark.parametrize("pattern", ["normal", "ties3", "const", "zeros"])
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[
+    f"{c[0]}d{c[1]}b{c[3]}B{c[5]}L{c[6]}" for c in FUSED_CASES])
+def test_step_eviction_equals_separate_calls(case, pattern, order, mode):
+    """An evicting kve_step selects and compacts in one launch when the
+    slice is short (the kept list stays on chip); it must leave exactly the
+    cache and kept slots that kve_append, kve_score, kve_select_evict and
+    kve_compact leave, bitwise, whatever the ties, decay or noise."""
+    import torch
+    k = kve()
+    dev = torch.device("cuda")
+    dt, D, G, batch, H, B, L, S, W = case
+    print(f"[fused-evict] {case} {pattern} {order} {mode}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(repr((case, pattern, order, mode))
+                                           .encode()))
+    cap = B + L
+    n = cap - 1  # the next step appends at slot n and evicts
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    shape = k.Shape(batch, H, G, D, cap, k.F32 if dt == "f32" else k.BF16)
+    sc_np = np.zeros((batch, H, cap), np.float32)
+    sc_np[:, :, :n] = _scores(rng, pattern, (batch, H, n))
+    pos_np = _positions(rng, batch, H, cap, n, order)
+    kv = [torch.from_numpy(rng.standard_normal((batch, H, cap, D))
+                           .astype(np.float32)).to(tdt) for _ in range(2)]
+    lg = gum = None
+    if mode == "decay":
+        lg = torch.from_numpy(np.log(rng.uniform(0.9, 0.999999, H))
+                              .astype(np.float32)).to(dev)
+    if mode == "stochastic":
+        u = rng.uniform(1e-7, 1 - 1e-7, (batch, H, cap))
+        gum = torch.from_numpy(-np.log(-np.log(u)).astype(np.float32)).to(dev)
+    pol = k.Policy(B, S, W, L, log_gamma=lg, gumbel=gum)
+    caches = []
+    for _ in range(2):
+        c = k.CacheTensors.empty(shape, dev)
+        c.k.copy_(kv[0])
+        c.v.copy_(kv[1])
+        c.score.copy_(torch.from_numpy(sc_np))
+        c.pos.copy_(torch.from_numpy(pos_np.astype(np.int32)))
+        caches.append(c)
+    w1 = torch.from_numpy((rng.standard_normal((H, 16, 2 * D)) *
+                           (2 * D) ** -0.5).astype(np.float32)).to(tdt).to(dev)
+    w2 = torch.from_numpy(rng.standard_normal((H, 16)).astype(np.float32)
+                          ).to(dev)
+    scorer = k.Scorer.mlp(w1, w2)
+    kn, vn, q = (torch.from_numpy(rng.standard_normal(sh).astype(np.float32))
+                 .to(tdt).to(dev)
+                 for sh in ((batch, H, D), (batch, H, D), (batch, H * G, D)))
+    keeps = [torch.full((batch, H, B), -7, dtype=torch.int32, device=dev)
+             for _ in range(2)]
+    # fused: one evicting kve_step (nothing pending before it)
+    out = torch.empty((batch, H * G, D), device=dev)
+    ws = k.alloc_workspace(shape, cap, dev)
+    st = k.DecodeState(n, n, n)
+    k.kve_step(shape, pol, scorer, caches[0], st, kn, vn, q, out, None,
+               keeps[0], ws)
+    assert st.evicted == 1 and st.len == B
+    # separate calls on the other copy
+    c = caches[1]
+    k.kve_append(shape, c, n, n, kn, vn)
+    k.kve_score(shape, scorer, c, n, n + 1)
+    torch.cuda.synchronize()
+    sc_all = c.score.cpu().numpy().copy()   # the appended rows' scores too
+    k.kve_select_evict(shape, pol, c, n + 1, B, keeps[1])
+    k.kve_compact(shape, c, n + 1, keeps[1], B)
+    torch.cuda.synchronize()
+    assert torch.equal(keeps[0], keeps[1])
+    for name in ("k", "v", "score", "pos"):
+        a, b = getattr(caches[0], name), getattr(caches[1], name)
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), name
+    # the kept slots against the oracle's rule, and the compacted positions
+    # slot by slot against its placement rule
+    got_keep = keeps[0].cpu().numpy()
+    got_pos = caches[0].pos.cpu().numpy()
+    lgn = None if lg is None else lg.cpu().numpy()
+    gn = None if gum is None else gum.cpu().numpy()
+    pos_all = pos_np.copy()
+    pos_all[:, :, n] = n
+    for sl in range(min(batch * H, 16)):  # the separate calls cover all
+        bi, h = divmod(sl, H)
+        lgh = None if lgn is None else float(lgn[h])
+        if gn is None:
+            ref = O.select_keep(sc_all[bi, h, :n + 1], pos_all[bi, h, :n + 1],
+                                n + 1, B, S, W, lgh)
+        else:
+            ref = O.select_keep_stochastic(
+                sc_all[bi, h, :n + 1], pos_all[bi, h, :n + 1], n + 1, B, S,
+                W, gn[bi, h, :n + 1], lgh)
+        np.testing.assert_array_equal(got_keep[bi, h], ref,
+                                      err_msg=f"slice {bi},{h}")
+        src = O.compaction_sources(ref)
+        np.testing.assert_array_equal(got_pos[bi, h, :B],
+                                      pos_all[bi, h, src],
+                                      err_msg=f"slice {bi},{h}")

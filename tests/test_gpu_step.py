@@ -129,6 +129,18 @@ def test_qwen3_layer_structured(seed):
     assert ev == 2
 
 
+def test_qwen3_layer_full_batch():
+    """Config 2 as specified: batch 16 (128 slices, split attention), the
+    structured rows with heavy hitters, n0 = 8192 -> B = 1024, L = 128, 256
+    steps with the evictions at steps 128 and 256; every slice checked on
+    every 16th step and on each evicting step."""
+    w = syn.workload(2)
+    assert w.batch == 16
+    print(f"[step] {w.name} batch={w.batch}", flush=True)
+    ev, _ = run_e2e(w, seed=2, check_stride=16)
+    assert ev == 2
+
+
 def test_qwen3_layer_silu_and_odd_policy():
     w = syn.workload(2, batch=1, n0=700, budget=300, sinks=3, window=37,
                      evict_len=45, steps=100, act="silu", structured=False)
@@ -211,3 +223,94 @@ def test_checkpoint_resume_bitwise():
     for x, y in zip(a, b):
         assert torch.equal(x, y)
     assert first  # the first leg ran
+
+
+def _graph_case(k, dev, evicting):
+    """A batch-8 layer (64 slices, split attention) one step short of an
+    eviction, or ten steps past one."""
+    import torch
+    batch, H, G, D, B, L, S, W = 8, 8, 4, 128, 512, 64, 4, 64
+    gen = torch.Generator().manual_seed(17 + evicting)
+    cap = B + L
+    shape = k.Shape(batch, H, G, D, cap, k.BF16)
+    pol = k.Policy(B, S, W, L)
+    cache = k.CacheTensors.empty(shape, dev)
+    cache.k.copy_(torch.randn(cache.k.shape, generator=gen).to(torch.bfloat16))
+    cache.v.copy_(torch.randn(cache.v.shape, generator=gen).to(torch.bfloat16))
+    cache.score.copy_(torch.randn(cache.score.shape, generator=gen))
+    cache.pos.copy_(torch.arange(cap, dtype=torch.int32).expand(batch, H, cap))
+    w1 = (torch.randn((H, 64, 2 * D), generator=gen) * (2 * D) ** -0.5
+          ).to(torch.bfloat16).to(dev)
+    w2 = (torch.randn((H, 64), generator=gen) * 64 ** -0.5).to(dev)
+    sc = k.Scorer.mlp(w1, w2)
+    n = B + L - 1 if evicting else B + 10
+    x = [torch.randn(s_, generator=gen).to(torch.bfloat16).to(dev)
+         for s_ in ((batch, H, D), (batch, H, D), (batch, H * G, D))]
+    return shape, pol, sc, cache, n, x
+
+
+@pytest.mark.parametrize("evicting", [False, True], ids=["append", "evict"])
+def test_step_in_hip_graph(evicting):
+    """kve_step's launches replay from a captured HIP graph: the fused append
+    and split attention of a plain step, or the append, scoring, select,
+    compaction and attention of an evicting one. The library allocates
+    nothing and records no memset. Each replay runs on the cache restored
+    from its pre-step snapshot (eager copies and synchronisations between
+    replays) and must leave the cache, the kept slots and the outputs
+    bitwise equal to the eager step's."""
+    import torch
+    k = kve()
+    dev = torch.device("cuda")
+    print(f"[step-graph] evicting={evicting}", flush=True)
+    shape, pol, sc, cache, n, (kn, vn, q) = _graph_case(k, dev, evicting)
+    B = pol.budget
+    ws = k.alloc_workspace(shape, shape.capacity, dev)
+    snap = [t.clone() for t in (cache.k, cache.v, cache.score, cache.pos)]
+
+    def restore():
+        for t, s_ in zip((cache.k, cache.v, cache.score, cache.pos), snap):
+            t.copy_(s_)
+
+    out = torch.empty((shape.batch, shape.n_kv_heads * shape.group,
+                       shape.head_dim), device=dev)
+    lse = torch.empty(out.shape[:2], device=dev)
+    keep = torch.full((shape.batch, shape.n_kv_heads, B), -1,
+                      dtype=torch.int32, device=dev)
+    st = k.DecodeState(n, B, n)
+    k.kve_step(shape, pol, sc, cache, st, kn, vn, q, out, lse, keep, ws)
+    torch.cuda.synchronize()
+    assert st.evicted == int(evicting)
+    want = [t.clone() for t in (cache.k, cache.v, cache.score, cache.pos,
+                                out, lse, keep)]
+
+    restore()
+    torch.cuda.synchronize()
+    g_state = k.DecodeState(n, B, n)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            k.kve_step(shape, pol, sc, cache, g_state, kn, vn, q, out, lse,
+                       keep, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert (g_state.len, g_state.evicted) == (st.len, st.evicted)
+    other = torch.empty_like(out)
+    for rep in range(3):
+        restore()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        keep.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (cache.k, cache.v, cache.score, cache.pos, out, lse, keep)
+        for name, a, b in zip(("k", "v", "score", "pos", "out", "lse", "keep"),
+                              got, want):
+            same = torch.equal(a.view(torch.int16), b.view(torch.int16)) \
+                if a.dtype == torch.bfloat16 else torch.equal(a, b)
+            assert same, f"replay {rep}: {name} differs"
+        # eager work on the same workspace between replays
+        k.kve_decode_attn(shape, cache, B, q, other, None, ws)
+        torch.cuda.synchronize()
