@@ -10,6 +10,7 @@
 // (KVpop Appendix F) with the older entry (lower position) evicted first
 // among equal scores.
 #include "kve_internal.h"
+#include "mlp_tile.h"
 
 namespace kve {
 namespace {
@@ -349,7 +350,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 // ---------------------------------------------------------------------------
 // Select for slices of up to kSelSmallMax entries, every entry held in
-// registers: thread tid owns slots v * kSelThreads + tid (v < kSelR). The
+// registers: thread tid owns slots v * kSelThreads + tid (v < R, the fewest
+// of 3, 5 or 8 slots per thread that hold the slice). The
 // score, position (and noise) of each entry are loaded once, and the radix
 // passes and the ordered pass read registers only. Same rule, ties and
 // outputs as select_kernel.
@@ -363,44 +365,241 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // position reads happen before the ordered pass, and the moves read only
 // slots at or above n_keep and write only slots below it.
 // ---------------------------------------------------------------------------
-constexpr int kSelR = 8;
-constexpr int kSelSmallMax = kSelThreads * kSelR;  // 4096 entries
-constexpr int kFuseMaxMoves = kSelSmallMax / 2;    // holes <= min(n_keep, r)
+constexpr int kSelMaxR = 8;                          // slots per thread
+constexpr int kSelSmallMax = kSelThreads * kSelMaxR;  // 4096 entries
+constexpr int kFuseMaxMoves = kSelSmallMax / 2;       // holes <= min(n_keep, r)
 
-// radix_select over the kSelR register entries of every thread.
-__device__ void radix_select_regs(uint32_t rank, const uint32_t (&key)[kSelR],
-                                  const bool (&take)[kSelR], uint32_t* hist,
-                                  uint32_t* wsum, uint32_t* sh,
+// radix_select over the R register entries of every thread. Each pass takes
+// two barriers: the histogram is double-buffered (the next pass's buffer is
+// cleared while this one fills) and one wave scans the 256 bins.
+template <int R>
+__device__ void radix_select_regs(uint32_t rank, const uint32_t (&key)[R],
+                                  const bool (&take)[R],
+                                  uint32_t (*hist)[256], uint32_t (*sh)[4],
                                   uint32_t* key_out, uint32_t* need_out,
                                   uint32_t* count_eq_out) {
   const int tid = threadIdx.x;
+  for (int i = tid; i < 256; i += kSelThreads) hist[0][i] = 0;
+  __syncthreads();
   uint32_t prefix = 0, mask = 0, remaining = rank, count_eq = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-    if (tid == 0) {
-      sh[0] = 255u;
-      sh[1] = 0u;
-      sh[2] = 0u;
+  int cur = 0;
+  for (int shift = 24; shift >= 0; shift -= 8, cur ^= 1) {
+#pragma unroll
+    for (int v = 0; v < R; ++v)
+      if (take[v] && (key[v] & mask) == prefix)
+        atomicAdd(&hist[cur][(key[v] >> shift) & 255u], 1u);
+    // the other buffer was last read before the previous pass's second
+    // barrier
+    for (int i = tid; i < 256; i += kSelThreads) hist[cur ^ 1][i] = 0;
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 4l..4l+3; an inclusive scan over the lanes
+      const int l = tid;
+      uint32_t c[4], t = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[cur][4 * l + j];
+        t += c[j];
+      }
+      uint32_t incl = t;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (l >= off) incl += o;
+      }
+      if (l == 0) {  // default: the last bin (rank beyond the entries)
+        sh[cur][0] = 255u;
+        sh[cur][1] = 0u;
+        sh[cur][2] = 0u;
+      }
+      uint32_t run = incl - t;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t below = run;
+        run += c[j];
+        if (run >= remaining && below < remaining) {
+          sh[cur][0] = (uint32_t)(4 * l + j);
+          sh[cur][1] = below;
+          sh[cur][2] = c[j];
+        }
+      }
     }
     __syncthreads();
-#pragma unroll
-    for (int v = 0; v < kSelR; ++v)
-      if (take[v] && (key[v] & mask) == prefix)
-        atomicAdd(&hist[(key[v] >> shift) & 255u], 1u);
-    __syncthreads();
-    radix_find_bin(hist, wsum, sh, remaining);
-    prefix |= sh[0] << shift;
+    prefix |= sh[cur][0] << shift;
     mask |= 255u << shift;
-    remaining -= sh[1];
-    count_eq = sh[2];
-    __syncthreads();
+    remaining -= sh[cur][1];
+    count_eq = sh[cur][2];
   }
   *key_out = prefix;
   *need_out = remaining;
   *count_eq_out = count_eq;
 }
 
-template <bool FUSE>
+// LDS of the register-resident select.
+template <int R>
+struct SelRegsLds {
+  uint32_t hist[2][256];
+  uint32_t sh[2][4];
+  int32_t sh_max[kSelWaves];
+  uint32_t ncand;
+  uint32_t nholes;
+  uint32_t cnt[R][kSelWaves];
+};
+
+// Loads the R entries of this thread (slot v * kSelThreads + tid):
+// position, score and noise; clamped indices keep every load in bounds and
+// all of them in flight together, entries past len are masked by valid.
+template <int R>
+__device__ __forceinline__ void select_load_regs(
+    const float* sc, const int32_t* ps, const float* gs, int len,
+    int32_t (&p)[R], float (&s)[R], float (&g)[R],
+    bool (&valid)[R]) {
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    const int c = v * kSelThreads + (int)threadIdx.x;
+    const int cc = min(c, len - 1);
+    valid[v] = c < len;
+    p[v] = ps[cc];
+    s[v] = sc[cc];
+    g[v] = gs ? gs[cc] : 0.f;
+  }
+}
+
+// The select rule on the register entries (select_kernel's rule): which
+// entries are evicted when r of them must go. lg is the KV head's log decay
+// (decay: the ranking key is the static priority), g the noise (gumbel: the
+// stochastic rule). L.nholes is cleared here for the ordered pass.
+template <int R>
+__device__ void select_rule_regs(SelRegsLds<R>& L, const int32_t (&p)[R],
+                                 const float (&s)[R],
+                                 const float (&g)[R],
+                                 const bool (&valid)[R], bool decay,
+                                 float lg, bool gumbel, int S, int W,
+                                 uint32_t r, bool (&evicted)[R]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // Newest position present (clamped copies repeat a present entry).
+  int32_t mx = p[0];
+#pragma unroll
+  for (int v = 1; v < R; ++v) mx = max(mx, p[v]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if (lane == 0) L.sh_max[wave] = mx;
+  if (tid == 0) {
+    L.ncand = 0;
+    L.nholes = 0;
+  }
+  __syncthreads();
+  int32_t newest = L.sh_max[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) newest = max(newest, L.sh_max[w]);
+  const long long last_eligible = (long long)newest - W;
+  bool cand[R];
+  uint32_t key[R], pk[R];
+  float fk[R];
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    cand[v] = valid[v] & (p[v] >= S) & ((long long)p[v] <= last_eligible);
+    // static priority under decay: two separately rounded operations
+    fk[v] = decay ? __fsub_rn(s[v], __fmul_rn((float)p[v], lg)) : s[v];
+    key[v] = score_key(fk[v]);
+    pk[v] = (uint32_t)p[v];
+  }
+  // The `count` first entries with take[] in (key, position) order: cut key
+  // thr and, among entries with key thr, those at positions <= pthr.
+  auto cut = [&](uint32_t count, const uint32_t (&kk)[R],
+                 const bool (&take)[R], uint32_t* thr_out,
+                 uint32_t* pthr_out) {
+    uint32_t thr, need, count_eq;
+    radix_select_regs<R>(count, kk, take, L.hist, L.sh, &thr, &need,
+                         &count_eq);
+    uint32_t pthr = 0xffffffffu;
+    if (need < count_eq) {
+      bool tied[R];
+#pragma unroll
+      for (int v = 0; v < R; ++v) tied[v] = take[v] & (kk[v] == thr);
+      uint32_t pneed, pcount;
+      radix_select_regs<R>(need, pk, tied, L.hist, L.sh, &pthr, &pneed,
+                           &pcount);
+    }
+    *thr_out = thr;
+    *pthr_out = pthr;
+  };
+  auto before = [&](uint32_t k, int v, uint32_t thr, uint32_t pthr) {
+    return (k < thr) | ((k == thr) & (pk[v] <= pthr));
+  };
+  uint32_t thr, pthr;
+  if (!gumbel) {
+    cut(r, key, cand, &thr, &pthr);
+#pragma unroll
+    for (int v = 0; v < R; ++v)
+      evicted[v] = cand[v] & before(key[v], v, thr, pthr);
+    return;
+  }
+  // ForesightKV: pool = the 2r lowest candidates; evict the r pool entries
+  // with the smallest descending key of -key + noise.
+  uint32_t nc = 0;
+#pragma unroll
+  for (int v = 0; v < R; ++v) nc += cand[v] ? 1u : 0u;
+  atomicAdd(&L.ncand, nc);
+  __syncthreads();
+  const uint32_t pool = min(2u * r, L.ncand);
+  cut(pool, key, cand, &thr, &pthr);
+  bool in_pool[R];
+  uint32_t dk[R];
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    in_pool[v] = cand[v] & before(key[v], v, thr, pthr);
+    dk[v] = ~score_key(__fadd_rn(-fk[v], g[v]));
+  }
+  uint32_t gthr, gpthr;
+  cut(r, dk, in_pool, &gthr, &gpthr);
+#pragma unroll
+  for (int v = 0; v < R; ++v)
+    evicted[v] = in_pool[v] & before(dk[v], v, gthr, gpthr);
+}
+
+// Ordered pass: kept slots, ascending, into out[0, n_keep). Slab v holds
+// slots v * kSelThreads + tid: one ballot count per wave and slab, one
+// barrier; a slot's kept rank is the kept count of the earlier slabs,
+// earlier waves and lower lanes. on_slot(c, kept, idx) sees every valid
+// slot with idx the number of kept slots before it.
+template <int R, typename OnSlot>
+__device__ __forceinline__ void select_ordered_regs(
+    SelRegsLds<R>& L, const bool (&valid)[R], const bool (&evicted)[R],
+    int n_keep, int32_t* out, OnSlot on_slot) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint64_t m[R];
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    const bool kept = valid[v] & !evicted[v];
+    m[v] = __builtin_amdgcn_ballot_w64(kept);
+    if (lane == 0) L.cnt[v][wave] = (uint32_t)__builtin_popcountll(m[v]);
+  }
+  __syncthreads();
+  uint32_t before_slab = 0;
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    uint32_t in_slab = 0, slab_total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const uint32_t cw = L.cnt[v][w];
+      in_slab += (w < wave) ? cw : 0u;
+      slab_total += cw;
+    }
+    const int c = v * kSelThreads + tid;
+    const uint32_t idx = before_slab + in_slab + lane_prefix(m[v]);
+    const bool kept = (m[v] >> lane) & 1ull;
+    if (kept && idx < (uint32_t)n_keep) out[idx] = c;
+    if (valid[v]) on_slot(c, kept, idx);
+    before_slab += slab_total;
+  }
+}
+
+template <bool FUSE, int R>
 __global__ __launch_bounds__(kSelThreads) void select_small_kernel(
     float* score, int32_t* pos, const float* log_gamma, const float* gumbel,
     int H, int cap, int len, int n_keep, int S, int W, int32_t* keep,
@@ -411,125 +610,24 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(
   const float* gs = gumbel ? gumbel + slice * (size_t)cap : nullptr;
   int32_t* out = keep + slice * (size_t)n_keep;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
 
   if (n_keep >= len) {  // nothing to evict: identity, nothing moves
     for (int i = tid; i < len; i += kSelThreads) out[i] = i;
     return;
   }
   const uint32_t r = (uint32_t)(len - n_keep);
-
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[kSelWaves];
-  __shared__ uint32_t sh[4];
-  __shared__ int32_t sh_max[kSelWaves];
-  __shared__ uint32_t ncand_sh;
-  __shared__ uint32_t cnt_sh[kSelR][kSelWaves];
+  __shared__ SelRegsLds<R> L;
   __shared__ int32_t holes_sh[FUSE ? kFuseMaxMoves : 1];
   __shared__ int32_t movers_sh[FUSE ? kFuseMaxMoves : 1];
-  __shared__ uint32_t nholes_sh;
 
-  // Every entry once: position, score (noise). Clamped indices keep all
-  // loads in bounds and in flight together; entries past len are masked.
-  int32_t p[kSelR];
-  float s[kSelR], g[kSelR];
-  bool valid[kSelR];
-#pragma unroll
-  for (int v = 0; v < kSelR; ++v) {
-    const int c = v * kSelThreads + tid;
-    const int cc = min(c, len - 1);
-    valid[v] = c < len;
-    p[v] = ps[cc];
-    s[v] = sc[cc];
-    g[v] = gs ? gs[cc] : 0.f;
-  }
-  // 1. Newest position present (clamped copies repeat a present entry).
-  int32_t mx = p[0];
-#pragma unroll
-  for (int v = 1; v < kSelR; ++v) mx = max(mx, p[v]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
-  if (lane == 0) sh_max[wave] = mx;
-  if (tid == 0) {
-    ncand_sh = 0;
-    nholes_sh = 0;
-  }
-  __syncthreads();
-  int32_t newest = sh_max[0];
-#pragma unroll
-  for (int w = 1; w < kSelWaves; ++w) newest = max(newest, sh_max[w]);
-  const long long last_eligible = (long long)newest - W;
+  int32_t p[R];
+  float s[R], g[R];
+  bool valid[R], evicted[R];
+  select_load_regs(sc, ps, gs, len, p, s, g, valid);
   const float lg = log_gamma ? log_gamma[slice % H] : 0.f;
-  const bool decay = log_gamma != nullptr;
-  bool cand[kSelR];
-  uint32_t key[kSelR], pk[kSelR];
-  float fk[kSelR];
-#pragma unroll
-  for (int v = 0; v < kSelR; ++v) {
-    cand[v] = valid[v] & (p[v] >= S) & ((long long)p[v] <= last_eligible);
-    // static priority under decay: two separately rounded operations
-    fk[v] = decay ? __fsub_rn(s[v], __fmul_rn((float)p[v], lg)) : s[v];
-    key[v] = score_key(fk[v]);
-    pk[v] = (uint32_t)p[v];
-  }
-  // The `count` first entries with take[] in (key, position) order: cut key
-  // thr and, among entries with key thr, those at positions <= pthr.
-  auto cut = [&](uint32_t count, const uint32_t (&kk)[kSelR],
-                 const bool (&take)[kSelR], uint32_t* thr_out,
-                 uint32_t* pthr_out) {
-    uint32_t thr, need, count_eq;
-    radix_select_regs(count, kk, take, hist, wsum, sh, &thr, &need,
-                      &count_eq);
-    uint32_t pthr = 0xffffffffu;
-    if (need < count_eq) {
-      bool tied[kSelR];
-#pragma unroll
-      for (int v = 0; v < kSelR; ++v) tied[v] = take[v] & (kk[v] == thr);
-      uint32_t pneed, pcount;
-      radix_select_regs(need, pk, tied, hist, wsum, sh, &pthr, &pneed,
-                        &pcount);
-    }
-    *thr_out = thr;
-    *pthr_out = pthr;
-  };
-  auto before = [&](uint32_t k, int v, uint32_t thr, uint32_t pthr) {
-    return (k < thr) | ((k == thr) & (pk[v] <= pthr));
-  };
-  bool evicted[kSelR];
-  uint32_t thr, pthr;
-  if (!gs) {
-    cut(r, key, cand, &thr, &pthr);
-#pragma unroll
-    for (int v = 0; v < kSelR; ++v)
-      evicted[v] = cand[v] & before(key[v], v, thr, pthr);
-  } else {
-    // ForesightKV: pool = the 2r lowest candidates; evict the r pool
-    // entries with the smallest descending key of -key + noise.
-    uint32_t nc = 0;
-#pragma unroll
-    for (int v = 0; v < kSelR; ++v) nc += cand[v] ? 1u : 0u;
-    atomicAdd(&ncand_sh, nc);
-    __syncthreads();
-    const uint32_t pool = min(2u * r, ncand_sh);
-    cut(pool, key, cand, &thr, &pthr);
-    bool in_pool[kSelR];
-    uint32_t dk[kSelR];
-#pragma unroll
-    for (int v = 0; v < kSelR; ++v) {
-      in_pool[v] = cand[v] & before(key[v], v, thr, pthr);
-      dk[v] = ~score_key(__fadd_rn(-fk[v], g[v]));
-    }
-    uint32_t gthr, gpthr;
-    cut(r, dk, in_pool, &gthr, &gpthr);
-#pragma unroll
-    for (int v = 0; v < kSelR; ++v)
-      evicted[v] = in_pool[v] & before(dk[v], v, gthr, gpthr);
-  }
+  select_rule_regs(L, p, s, g, valid, log_gamma != nullptr, lg, gs != nullptr,
+                   S, W, r, evicted);
 
-  // 4. Kept slots, ascending: slab v holds slots v * kSelThreads + tid. One
-  // ballot count per wave and slab, one barrier; a slot's kept rank is the
-  // kept count of the earlier slabs, earlier waves and lower lanes.
   const int M = min(n_keep, (int)r);  // moves, at most
   if (FUSE) {
     for (int i = tid; i < M; i += kSelThreads) {
@@ -537,50 +635,28 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(
       movers_sh[i] = -1;
     }
   }
-  uint64_t m[kSelR];
-#pragma unroll
-  for (int v = 0; v < kSelR; ++v) {
-    const bool kept = valid[v] & !evicted[v];
-    m[v] = __builtin_amdgcn_ballot_w64(kept);
-    if (lane == 0) cnt_sh[v][wave] = (uint32_t)__builtin_popcountll(m[v]);
-  }
-  __syncthreads();
-  uint32_t before_slab = 0;
-#pragma unroll
-  for (int v = 0; v < kSelR; ++v) {
-    uint32_t in_slab = 0, slab_total = 0;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t cw = cnt_sh[v][w];
-      in_slab += (w < wave) ? cw : 0u;
-      slab_total += cw;
+  // idx counts the kept slots before c. A hole below n_keep has hole rank
+  // c - idx; a kept slot at or above n_keep has kept rank idx, and the kept
+  // ranks of the movers are the last ones below n_keep.
+  select_ordered_regs(L, valid, evicted, n_keep, out,
+                      [&](int c, bool kept, uint32_t idx) {
+    if (!FUSE) return;
+    if (!kept && c < n_keep) {
+      const int j = c - (int)idx;
+      if (j < M) holes_sh[j] = c;
+      atomicAdd(&L.nholes, 1u);
+    } else if (kept && c >= n_keep && idx < (uint32_t)n_keep) {
+      const int j = (int)idx - (n_keep - M);
+      if (j >= 0) movers_sh[j] = c;
     }
-    const int c = v * kSelThreads + tid;
-    const uint32_t idx = before_slab + in_slab + lane_prefix(m[v]);
-    const bool kept = (m[v] >> lane) & 1ull;
-    if (kept && idx < (uint32_t)n_keep) out[idx] = c;
-    if (FUSE) {
-      // idx counts the kept slots before c. A hole below n_keep has hole
-      // rank c - idx; a kept slot at or above n_keep has kept rank idx,
-      // and the kept ranks of the movers are the last ones below n_keep.
-      if (!kept && valid[v] && c < n_keep) {
-        const int j = c - (int)idx;
-        if (j < M) holes_sh[j] = c;
-        atomicAdd(&nholes_sh, 1u);
-      } else if (kept && c >= n_keep && idx < (uint32_t)n_keep) {
-        const int j = (int)idx - (n_keep - M);
-        if (j >= 0) movers_sh[j] = c;
-      }
-    }
-    before_slab += slab_total;
-  }
+  });
   if (!FUSE) return;
   __syncthreads();
 
   // Moves: hole j <- mover M - nh + j (the movers' kept ranks run from
   // n_keep - nh to n_keep - 1). A slice that breaks the contract (repeated
   // positions) can leave an entry unset: its row is skipped, never written.
-  const int nh = min((int)nholes_sh, M);
+  const int nh = min((int)L.nholes, M);
   const int cpr = row_bytes >> 4;  // 16-byte chunks per K (or V) row
   const int items = nh * 2 * cpr;  // K and V chunks of every moved row
   const size_t base = slice * (size_t)cap;
@@ -620,6 +696,194 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(
     if (d >= 0 && d < n_keep && src >= n_keep && src < cap) {
       sc[d] = sc[src];
       ps[d] = ps[src];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The evicting step of a bf16 MLP-scored slice in one launch: score the
+// pending rows, select, compact. The pending rows (the slots the last
+// scoring left unscored, L of them at a periodic eviction) are the newest
+// entries; when they start at or above n_keep they include every kept entry
+// at or above n_keep, i.e. every row compaction moves. Each wave loads its
+// 16-row tiles of them once, in the MFMA operand layout (a lane holds
+// 16-byte chunks of one row), scores them with the scorer's own tile
+// arithmetic (the same bits as the scorer kernel), and after the select
+// stores the same registers into the holes: the moved rows are read from
+// memory once instead of three times (scorer, compaction read) and the kept
+// list never leaves the chip. The step's new token can be appended here as
+// well (its lanes read it from k_new / v_new and store it to its slot).
+// Results equal kve_append + kve_score + kve_select_evict + kve_compact.
+// ---------------------------------------------------------------------------
+struct EvictMlpLaunch {
+  void* k;
+  void* v;
+  float* score;
+  int32_t* pos;
+  const void* w1;        // bf16 [H][hidden][2D]
+  const float* b1;       // [H][hidden] or null
+  const float* w2;       // [H][hidden]
+  const float* b2;       // [H] or null
+  int act;
+  const float* log_gamma;
+  const float* gumbel;
+  int H, cap, len, n_keep, S, W;
+  int pend0;             // pending rows: slots [pend0, len)
+  int32_t* keep;
+  // The step's new token, appended here at slot len - 1 (its K, V row and
+  // position) instead of by a launch of its own; k_new null: already there.
+  const void* k_new;     // [batch][H][D]
+  const void* v_new;
+  int new_pos;
+};
+
+// Three workgroups per CU (6 waves per SIMD, 80 VGPRs) run all 768 slices
+// of a batch-96 layer in one round; the 8-slot form cannot hold that bound.
+template <int D, int NB, int TPW, int R>
+__global__ __launch_bounds__(kSelThreads)
+__attribute__((amdgpu_waves_per_eu(R <= 3 ? 6 : 1)))
+void evict_mlp_kernel(
+    EvictMlpLaunch a) {
+  constexpr int HID = NB * 16;
+  constexpr int IN = 2 * D;
+  constexpr int KSTEPS = IN / 32;
+  constexpr int KHALF = D / 32;
+  constexpr int LSTR = IN + 8;      // bf16 per staged W1 row
+  constexpr int PMAX = kSelWaves * TPW * 16;
+  __shared__ uint16_t w1s[HID * LSTR];
+  __shared__ float nsc[PMAX];       // scores of the pending rows
+  __shared__ int32_t krank[PMAX];   // kept rank of a kept pending row >= n_keep
+  __shared__ int32_t holes_sh[PMAX];
+  __shared__ SelRegsLds<R> L;
+
+  const size_t slice = blockIdx.x;
+  const int h = (int)(slice % a.H);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t base = slice * (size_t)a.cap;
+  const int P = a.len - a.pend0;    // pending rows, 1..PMAX
+  uint16_t* kc = (uint16_t*)a.k + base * D;
+  uint16_t* vc = (uint16_t*)a.v + base * D;
+  float* sc = a.score + base;
+  int32_t* ps = a.pos + base;
+  const int kq = (lane >> 4) * 8;
+
+  // Pending rows, tile t of this wave: rows (t * kSelWaves + wave) * 16 +
+  // lane % 16 of the pending range (clamped: computed, never stored). The
+  // new token's row comes from k_new / v_new when it is appended here.
+  const int last = a.len - 1;
+  const bool app = a.k_new != nullptr;
+  const uint16_t* kn = app ? (const uint16_t*)a.k_new + slice * D : nullptr;
+  const uint16_t* vn = app ? (const uint16_t*)a.v_new + slice * D : nullptr;
+  bf16x8_t rows[TPW][KSTEPS];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    int ri = (t * kSelWaves + wave) * 16 + (lane & 15);
+    ri = ri < P ? ri : P - 1;
+    const size_t slot = (size_t)(a.pend0 + ri);
+    const bool nw = app && (int)slot == last;
+    mlp_load_row<D>(rows[t], nw ? kn : kc + slot * D, nw ? vn : vc + slot * D,
+                    kq);
+  }
+  int32_t p[R];
+  float s[R], g[R];
+  bool valid[R], evicted[R];
+  select_load_regs(sc, ps, a.gumbel ? a.gumbel + base : nullptr, a.len, p, s,
+                   g, valid);
+  if (app) {
+#pragma unroll
+    for (int v = 0; v < R; ++v)
+      if (v * kSelThreads + tid == last) p[v] = a.new_pos;
+  }
+  mlp_stage_w1<HID, IN>(w1s, LSTR, (const uint16_t*)a.w1 + (size_t)h * HID * IN,
+                        kSelThreads);
+  for (int i = tid; i < PMAX; i += kSelThreads) {
+    krank[i] = -1;
+    holes_sh[i] = -1;
+  }
+  float bias[NB], w2v[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + (lane & 15);
+    bias[nb] = a.b1 ? a.b1[(size_t)h * HID + n] : 0.f;
+    w2v[nb] = a.w2[(size_t)h * HID + n];
+  }
+  const float b2 = a.b2 ? a.b2[h] : 0.f;
+  __syncthreads();
+
+  // Scores of the pending rows, to the cache and to LDS.
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float o[4];
+    mlp_tile_scores<D, NB>(rows[t], w1s, LSTR, bias, w2v, b2, a.act, o);
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ri = (t * kSelWaves + wave) * 16 + 4 * (lane >> 4) + i;
+        if (ri < P) {
+          nsc[ri] = o[i];
+          sc[a.pend0 + ri] = o[i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < R; ++v) {
+    const int c = v * kSelThreads + tid;
+    if (valid[v] && c >= a.pend0) s[v] = nsc[c - a.pend0];
+  }
+
+  const uint32_t r = (uint32_t)(a.len - a.n_keep);
+  const float lg = a.log_gamma ? a.log_gamma[h] : 0.f;
+  select_rule_regs(L, p, s, g, valid, a.log_gamma != nullptr, lg,
+                   a.gumbel != nullptr, a.S, a.W, r, evicted);
+  int32_t* out = a.keep + slice * (size_t)a.n_keep;
+  const int n_keep = a.n_keep;
+  select_ordered_regs(L, valid, evicted, n_keep, out,
+                      [&](int c, bool kept, uint32_t idx) {
+    if (!kept && c < n_keep) {
+      const int j = c - (int)idx;  // hole rank
+      if (j < PMAX) holes_sh[j] = c;
+      atomicAdd(&L.nholes, 1u);
+    } else if (kept && c >= n_keep && idx < (uint32_t)n_keep) {
+      krank[c - a.pend0] = (int)idx;  // c >= n_keep >= pend0
+    }
+  });
+  __syncthreads();
+
+  // Moves from registers: pending row ri with kept rank idx >= n_keep - nh
+  // is mover idx - (n_keep - nh) and fills that hole (the holes and the
+  // movers each rank 0..nh-1 in slot order). The appended row is also
+  // stored to its own slot, as the append would have left it.
+  const int nh = (int)L.nholes;
+  auto store_row = [&](const bf16x8_t (&row)[KSTEPS], int d) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint16_t* to = ks < KHALF ? kc + (size_t)d * D + ks * 32 + kq
+                                : vc + (size_t)d * D + (ks - KHALF) * 32 + kq;
+      *(u32x4*)to = __builtin_bit_cast(u32x4, row[ks]);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int ri = (t * kSelWaves + wave) * 16 + (lane & 15);
+    const int kr = ri < P ? krank[ri] : -1;
+    const int j = kr - (n_keep - nh);
+    const int d = (kr >= 0 && j >= 0 && j < nh && j < PMAX) ? holes_sh[j] : -1;
+    const bool nw = app && ri < P && a.pend0 + ri == last;
+    const int32_t src_pos = nw ? a.new_pos : (ri < P ? ps[a.pend0 + ri] : 0);
+    if (d >= 0 && d < n_keep) {
+      store_row(rows[t], d);
+      if ((lane >> 4) == 0) {
+        sc[d] = nsc[ri];
+        ps[d] = src_pos;
+      }
+    }
+    if (nw) {
+      store_row(rows[t], last);
+      if ((lane >> 4) == 0) ps[last] = a.new_pos;
     }
   }
 }
@@ -862,10 +1126,16 @@ hipError_t launch_select(const float* score, const int32_t* pos,
                      slices <= 256;
   if (check_only) return hipSuccess;
   if (len <= kSelSmallMax) {
-    hipLaunchKernelGGL(select_small_kernel<false>, dim3(slices),
-                       dim3(kSelThreads), 0, s, const_cast<float*>(score),
-                       const_cast<int32_t*>(pos), log_gamma, gumbel, H, cap,
-                       len, n_keep, S, W, keep, nullptr, nullptr, 0);
+    float* sc = const_cast<float*>(score);
+    int32_t* ps = const_cast<int32_t*>(pos);
+#define KVE_SEL(RR)                                                          \
+    hipLaunchKernelGGL((select_small_kernel<false, RR>), dim3(slices),       \
+                       dim3(kSelThreads), 0, s, sc, ps, log_gamma, gumbel, H, \
+                       cap, len, n_keep, S, W, keep, nullptr, nullptr, 0)
+    if (len <= 3 * kSelThreads) KVE_SEL(3);
+    else if (len <= 5 * kSelThreads) KVE_SEL(5);
+    else KVE_SEL(kSelMaxR);
+#undef KVE_SEL
     return hipGetLastError();
   }
   if (cache)
@@ -910,6 +1180,61 @@ hipError_t launch_compact(void* k, void* v, float* score, int32_t* pos,
   return hipGetLastError();
 }
 
+bool evict_mlp_fits(int D, int hidden, int len, int n_keep, int pend0) {
+  return (D == 64 || D == 128) && hidden >= 16 && hidden <= 128 &&
+         hidden % 16 == 0 && len <= kSelSmallMax && n_keep < len &&
+         pend0 <= n_keep && len - pend0 >= 1 &&
+         len - pend0 <= kSelWaves * 16;  // one 16-row tile per wave
+}
+
+hipError_t launch_evict_mlp(const EvictMlpLaunchArgs& e, hipStream_t s,
+                            bool check_only) {
+  if (!evict_mlp_fits(e.D, e.hidden, e.len, e.n_keep, e.pend0))
+    return hipErrorInvalidValue;
+  if (check_only) return hipSuccess;
+  EvictMlpLaunch a{};
+  a.k = e.k;
+  a.v = e.v;
+  a.score = e.score;
+  a.pos = e.pos;
+  a.w1 = e.w1;
+  a.b1 = e.b1;
+  a.w2 = e.w2;
+  a.b2 = e.b2;
+  a.act = e.act;
+  a.log_gamma = e.log_gamma;
+  a.gumbel = e.gumbel;
+  a.H = e.H;
+  a.cap = e.cap;
+  a.len = e.len;
+  a.n_keep = e.n_keep;
+  a.S = e.S;
+  a.W = e.W;
+  a.pend0 = e.pend0;
+  a.keep = e.keep;
+  a.k_new = e.k_new;
+  a.v_new = e.v_new;
+  a.new_pos = e.new_pos;
+  const dim3 grid((unsigned)e.slices), block(kSelThreads);
+  const bool r3 = e.len <= 3 * kSelThreads;  // register slots per thread
+#define KVE_EVICT(DD, NBB)                                                  \
+  if (e.D == DD && e.hidden == NBB * 16) {                                  \
+    if (r3)                                                                 \
+      hipLaunchKernelGGL((evict_mlp_kernel<DD, NBB, 1, 3>), grid, block, 0, \
+                         s, a);                                             \
+    else                                                                    \
+      hipLaunchKernelGGL((evict_mlp_kernel<DD, NBB, 1, kSelMaxR>), grid,    \
+                         block, 0, s, a);                                   \
+    return hipGetLastError();                                               \
+  }
+  KVE_EVICT(128, 1) KVE_EVICT(128, 2) KVE_EVICT(128, 3) KVE_EVICT(128, 4)
+  KVE_EVICT(128, 5) KVE_EVICT(128, 6) KVE_EVICT(128, 7) KVE_EVICT(128, 8)
+  KVE_EVICT(64, 1) KVE_EVICT(64, 2) KVE_EVICT(64, 3) KVE_EVICT(64, 4)
+  KVE_EVICT(64, 5) KVE_EVICT(64, 6) KVE_EVICT(64, 7) KVE_EVICT(64, 8)
+#undef KVE_EVICT
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_select_compact(void* k, void* v, float* score, int32_t* pos,
                                  const float* log_gamma, const float* gumbel,
                                  int H, int slices, int cap, int row_bytes,
@@ -927,10 +1252,15 @@ hipError_t launch_select_compact(void* k, void* v, float* score, int32_t* pos,
                           n_keep, s, check_only);
   }
   if (check_only) return hipSuccess;
-  hipLaunchKernelGGL(select_small_kernel<true>, dim3(slices),
-                     dim3(kSelThreads), 0, s, score, pos, log_gamma, gumbel,
-                     H, cap, len, n_keep, S, W, keep, (char*)k, (char*)v,
-                     row_bytes);
+#define KVE_SEL(RR)                                                          \
+  hipLaunchKernelGGL((select_small_kernel<true, RR>), dim3(slices),          \
+                     dim3(kSelThreads), 0, s, score, pos, log_gamma, gumbel,  \
+                     H, cap, len, n_keep, S, W, keep, (char*)k, (char*)v,     \
+                     row_bytes)
+  if (len <= 3 * kSelThreads) KVE_SEL(3);
+  else if (len <= 5 * kSelThreads) KVE_SEL(5);
+  else KVE_SEL(kSelMaxR);
+#undef KVE_SEL
   return hipGetLastError();
 }
 

@@ -96,6 +96,34 @@ hipError_t launch_select_compact(void* k, void* v, float* score, int32_t* pos,
                                  int32_t* keep, hipStream_t s,
                                  bool check_only = false);
 
+// The evicting step of a bf16 MLP-scored cache in one launch (optionally
+// with the new token's append): scoring of the pending rows [pend0, len),
+// select and compaction to n_keep, the moved rows read once. Same results
+// as launch_append + launch_score_mlp + launch_select_compact. Only shapes
+// for which evict_mlp_fits holds: slices of up to 4096 entries, at most 128
+// pending rows, and pend0 <= n_keep (every row that moves is pending).
+struct EvictMlpLaunchArgs {
+  void* k;
+  void* v;
+  float* score;
+  int32_t* pos;
+  const void* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
+  int act;
+  const float* log_gamma;
+  const float* gumbel;
+  int slices, H, D, hidden, cap, len, n_keep, S, W, pend0;
+  int32_t* keep;
+  const void* k_new;     // null: the new row is already in slot len - 1
+  const void* v_new;
+  int new_pos;
+};
+bool evict_mlp_fits(int D, int hidden, int len, int n_keep, int pend0);
+hipError_t launch_evict_mlp(const EvictMlpLaunchArgs& e, hipStream_t s,
+                            bool check_only = false);
+
 struct MlpLaunch {
   const void* k;         // cache base
   const void* v;

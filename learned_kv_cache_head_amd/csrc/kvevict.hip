@@ -640,12 +640,48 @@ kve_status step_impl(const kve_shape* shape, const kve_policy* policy,
     if (!ws) return st;
     ws_bytes = kNoallocScratchBytes;
   }
+  // An evicting step of a bf16 MLP-scored cache whose pending rows cover
+  // every row compaction moves runs append, scoring, select and compaction
+  // as one launch (the same results, the moved rows read once).
+  const bool fused_mlp =
+      evict && scorer->kind == KVE_SCORER_MLP_KV &&
+      shape->kv_dtype == KVE_BF16 &&
+      kve::evict_mlp_fits(shape->head_dim, scorer->hidden, new_len, B, scored);
   for (int pass = 0; pass < 2; ++pass) {
     const bool chk = pass == 0;
     auto done = [chk](hipError_t e) {
       return chk ? from_check(e) : from_hip(e);
     };
-    if (score_now) {
+    if (fused_mlp) {
+      kve::EvictMlpLaunchArgs e{};
+      e.k = cache->k;
+      e.v = cache->v;
+      e.score = cache->score;
+      e.pos = cache->pos;
+      e.w1 = scorer->w1;
+      e.b1 = scorer->b1;
+      e.w2 = scorer->w2;
+      e.b2 = scorer->b2;
+      e.act = scorer->act;
+      e.log_gamma = policy->log_gamma;
+      e.gumbel = policy->gumbel;
+      e.slices = slices;
+      e.H = shape->n_kv_heads;
+      e.D = shape->head_dim;
+      e.hidden = scorer->hidden;
+      e.cap = shape->capacity;
+      e.len = new_len;
+      e.n_keep = B;
+      e.S = policy->sinks;
+      e.W = policy->window;
+      e.pend0 = scored;
+      e.keep = keep_slots;
+      e.k_new = k_new;
+      e.v_new = v_new;
+      e.new_pos = position;
+      st = done(kve::launch_evict_mlp(e, stream, chk));
+      if (st != KVE_OK) return st;
+    } else if (score_now) {
       st = done(kve::launch_append(
           cache->k, cache->v, cache->pos, shape->batch, shape->n_kv_heads,
           shape->head_dim, shape->capacity, elem_bytes(shape->kv_dtype), slot,
@@ -656,7 +692,7 @@ kve_status step_impl(const kve_shape* shape, const kve_policy* policy,
                       (long long)L * scorer->in_dim, stream, chk);
       if (st != KVE_OK) return st;
     }
-    if (evict) {
+    if (evict && !fused_mlp) {
       st = done(kve::launch_select_compact(
           cache->k, cache->v, cache->score, cache->pos, policy->log_gamma,
           policy->gumbel, shape->n_kv_heads, slices, shape->capacity,

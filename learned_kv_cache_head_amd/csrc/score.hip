@@ -17,20 +17,17 @@
 // C[4 * (l / 16) + i][l % 16], i = 0..3. A and B always use the same
 // contraction order, so only the row/column mapping matters.
 #include "kve_internal.h"
+#include "mlp_tile.h"
 
 namespace kve {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
+  return load_bf16x8(p);
 }
 
 __device__ __forceinline__ float activate(float a, int act) {
-  if (act == 0) return fmaxf(a, 0.f);
-  return a / (1.f + __expf(-a));  // SiLU
+  return mlp_activate(a, act);
 }
 
 // ---------------------------------------------------------------------------
@@ -51,7 +48,6 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
   constexpr int HID = NB * 16;
   constexpr int IN = 2 * D;
   constexpr int KSTEPS = IN / 32;   // 32-wide contraction steps
-  constexpr int KHALF = D / 32;     // steps taken from the key
   constexpr int LSTR = IN + 8;      // bf16 per staged W1 row
   __shared__ uint16_t w1s[HID * LSTR];
   const int h = blockIdx.y;
@@ -62,13 +58,8 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
   const long long total = (long long)p.batch * rows;
   const long long wg_row0 = (long long)blockIdx.x * kMlpRowsPerWG;
 
-  const uint16_t* w1 = (const uint16_t*)p.w1 + (size_t)h * HID * IN;
-  for (int c = tid; c < HID * IN / 8; c += 256) {
-    const int n = c / (IN / 8);
-    const int k8 = c % (IN / 8);
-    *(u32x4*)(w1s + n * LSTR + k8 * 8) =
-        *(const u32x4*)(w1 + (size_t)n * IN + k8 * 8);
-  }
+  mlp_stage_w1<HID, IN>(w1s, LSTR,
+                         (const uint16_t*)p.w1 + (size_t)h * HID * IN, 256);
   const int ncol = lane & 15;       // MFMA column = hidden unit within block
   const int kq = (lane >> 4) * 8;   // this lane's 8 contraction indices
   float bias[NB], w2v[NB];
@@ -95,38 +86,11 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
     const size_t slice = (size_t)b * p.H + h;
     const uint16_t* krow = (const uint16_t*)p.k + (slice * p.cap + slot) * D;
     const uint16_t* vrow = (const uint16_t*)p.v + (slice * p.cap + slot) * D;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      a[ks] = ks < KHALF ? load8(krow + ks * 32 + kq)
-                         : load8(vrow + (ks - KHALF) * 32 + kq);
+    mlp_load_row<D>(a, krow, vrow, kq);
   };
   auto compute_tile = [&](const bf16x8_t (&a)[KSTEPS], int t) {
-    f32x4_t acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8_t B = __builtin_bit_cast(
-            bf16x8_t, *(const u32x4*)(w1s + (nb * 16 + ncol) * LSTR +
-                                       ks * 32 + kq));
-        acc[nb] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], B, acc[nb], 0, 0, 0);
-      }
-    }
-    // Row 4 * (lane >> 4) + i of the tile: second layer over the 16 hidden
-    // units of this lane's columns, then summed over the 16 columns.
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        part[i] += activate(acc[nb][i] + bias[nb], p.act) * w2v[nb];
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], off);
+    float sc4[4];
+    mlp_tile_scores<D, NB>(a, w1s, LSTR, bias, w2v, b2, p.act, sc4);
     if (ncol == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -134,7 +98,7 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(MlpLaunch p) {
         if (rid < total) {
           const int b = (int)(rid / rows);
           const int slot = p.slot_begin + (int)(rid - (long long)b * rows);
-          p.score[((size_t)b * p.H + h) * p.cap + slot] = part[i] + b2;
+          p.score[((size_t)b * p.H + h) * p.cap + slot] = sc4[i];
         }
       }
     }

@@ -246,26 +246,33 @@ FUSED_CASES = [
     ("bf16", 64, 2, 3, 4, 2048, 2048, 4, 2000),   # 4096 entries, 2048 moves
     ("bf16", 64, 2, 1, 4, 2049, 2048, 4, 2000),   # 4097: two launches
     ("bf16", 128, 1, 2, 3, 50, 20, 0, 0),         # nothing protected
+    ("bf16", 64, 2, 4, 2, 300, 100, 4, 100),      # d = 64
 ]
 
 
+@pytest.mark.parametrize("pending", ["one", "L"])
 @pytest.mark.parametrize("mode", ["plain", "decay", "stochastic"])
 @pytest.mark.parametrize("order", ["sorted", "shuffled"])
-@pytest.mark.parametrize("pattern", ["normal", "ties3", "const", "zeros"])
+@pytest.mark.parametrize("pattern", ["normal", "ties3", "zeros"])
 @pytest.mark.parametrize("case", FUSED_CASES, ids=[
     f"{c[0]}d{c[1]}b{c[3]}B{c[5]}L{c[6]}" for c in FUSED_CASES])
-def test_step_eviction_equals_separate_calls(case, pattern, order, mode):
+def test_step_eviction_equals_separate_calls(case, pattern, order, mode,
+                                             pending):
     """An evicting kve_step selects and compacts in one launch when the
-    slice is short (the kept list stays on chip); it must leave exactly the
-    cache and kept slots that kve_append, kve_score, kve_select_evict and
-    kve_compact leave, bitwise, whatever the ties, decay or noise."""
+    slice is short (the kept list stays on chip), and with a bf16 MLP scorer
+    and up to 128 pending rows (pending "L": the L newest rows unscored, as
+    at a periodic eviction) it also appends and scores them in that launch.
+    Either way it must leave exactly the cache and kept slots that
+    kve_append, kve_score, kve_select_evict and kve_compact leave, bitwise,
+    whatever the ties, decay or noise."""
     import torch
     k = kve()
     dev = torch.device("cuda")
     dt, D, G, batch, H, B, L, S, W = case
-    print(f"[fused-evict] {case} {pattern} {order} {mode}", flush=True)
-    rng = np.random.default_rng(zlib.crc32(repr((case, pattern, order, mode))
-                                           .encode()))
+    print(f"[fused-evict] {case} {pattern} {order} {mode} {pending}",
+          flush=True)
+    rng = np.random.default_rng(zlib.crc32(repr((case, pattern, order, mode,
+                                                 pending)).encode()))
     cap = B + L
     n = cap - 1  # the next step appends at slot n and evicts
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
@@ -304,14 +311,15 @@ def test_step_eviction_equals_separate_calls(case, pattern, order, mode):
     # fused: one evicting kve_step (nothing pending before it)
     out = torch.empty((batch, H * G, D), device=dev)
     ws = k.alloc_workspace(shape, cap, dev)
-    st = k.DecodeState(n, n, n)
+    pend0 = n if pending == "one" else B  # first unscored slot
+    st = k.DecodeState(n, pend0, n)
     k.kve_step(shape, pol, scorer, caches[0], st, kn, vn, q, out, None,
                keeps[0], ws)
     assert st.evicted == 1 and st.len == B
     # separate calls on the other copy
     c = caches[1]
     k.kve_append(shape, c, n, n, kn, vn)
-    k.kve_score(shape, scorer, c, n, n + 1)
+    k.kve_score(shape, scorer, c, pend0, n + 1)
     torch.cuda.synchronize()
     sc_all = c.score.cpu().numpy().copy()   # the appended rows' scores too
     k.kve_select_evict(shape, pol, c, n + 1, B, keeps[1])
