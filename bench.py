@@ -37,7 +37,21 @@ WORKLOAD_BY_NAME = {
     "qwen3-4b-1layer-b16": 2,
     "qwen2.5-14b-48layer-131k-gate": 5,
     "tiny-1layer-fp32": 1,
+    # the batch-96 stack at the 2K budget of the batch-8 workload (S 4,
+    # W 256, L 256): the upper end of B = 1024-2048 with the chip filled
+    "qwen3-4b-36layer-b96-B2048": (4, dict(
+        name="qwen3-4b-36layer-b96-B2048", budget=2048, window=256,
+        evict_len=256)),
 }
+
+
+def workload_for(name: str):
+    """The synthetic workload a bench workload name stands for."""
+    import synthetic as syn
+    spec = WORKLOAD_BY_NAME[name]
+    if isinstance(spec, tuple):
+        return syn.workload(spec[0], **spec[1])
+    return syn.workload(spec)
 DEFAULT_WORKLOAD = "qwen3-4b-36layer-b96-B1024"
 ATTN_SOURCE = os.path.join(ROOT, "learned_kv_cache_head_amd", "csrc",
                            "attention.hip")
@@ -982,7 +996,7 @@ def main() -> int:
         log("sink gate: qwen2.5-14b layer, 131072-token prompt")
         print(json.dumps(run_sink_gate(args, dev)), flush=True)
         return 0
-    w = syn.workload(WORKLOAD_BY_NAME[args.workload])
+    w = workload_for(args.workload)
     if args.prefill:
         log(f"prefill {args.workload}: batch={w.batch} prompt={w.n0} B={w.budget}")
         print(json.dumps(run_prefill(args, w, dev)), flush=True)

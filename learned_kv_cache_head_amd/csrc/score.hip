@@ -260,16 +260,21 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(GateLaunch g) {
 constexpr int kGateSmallWaves = 16;
 constexpr int kGateSmallMaxRows = 64;  // row counts served by this kernel
 
+// With `stride` 8 only every 8th workgroup id works: workgroups are handed
+// to the 8 XCDs round-robin, so the working ones share one XCD and its L2,
+// and the weights they all read come from memory once (used when so few
+// workgroups run that one XCD's CUs hold them all).
 __global__ __launch_bounds__(64 * kGateSmallWaves) void gate_mfma_small_kernel(
-    GateLaunch g) {
+    GateLaunch g, int stride) {
   constexpr int RG = 1;  // 16-token groups per workgroup
   __shared__ f32x4_t red[kGateSmallWaves][RG][64];
+  if (blockIdx.x % stride) return;  // uniform: before any barrier
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int rows = g.slot_end - g.slot_begin;
-  const int r0 = blockIdx.x * 16 * RG;
+  const int r0 = (blockIdx.x / stride) * 16 * RG;
   const uint16_t* x[RG];
 #pragma unroll
   for (int gi = 0; gi < RG; ++gi) {
@@ -634,8 +639,11 @@ hipError_t launch_score_gate(const GateLaunch& g, hipStream_t s,
   if (rows <= 0) return hipSuccess;
   if (check_only) return hipSuccess;
   if (rows <= kGateSmallMaxRows) {
-    hipLaunchKernelGGL(gate_mfma_small_kernel, dim3((rows + 15) / 16, g.batch),
-                       dim3(64 * kGateSmallWaves), 0, s, g);
+    const int nblk = (rows + 15) / 16;
+    // One XCD (32 CUs) holds them all: group them there (see the kernel).
+    const int stride = (long long)nblk * g.batch <= 32 ? 8 : 1;
+    hipLaunchKernelGGL(gate_mfma_small_kernel, dim3(nblk * stride, g.batch),
+                       dim3(64 * kGateSmallWaves), 0, s, g, stride);
     return hipGetLastError();
   }
   const dim3 grid((rows + kGateRowsPerWG - 1) / kGateRowsPerWG, g.batch);
