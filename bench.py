@@ -972,6 +972,12 @@ def main() -> int:
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed region, run a plain 1 GiB "
                          "elementwise copy (counter calibration)")
+    ap.add_argument("--preroll", type=int, default=None,
+                    help="untimed decode steps after the prompt compression "
+                         "(default: the count that puts an eviction at timed "
+                         "step steps // 2); an explicit count lets a counter "
+                         "pass cover non-evicting steps only; needs "
+                         "--no-kernel-events")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -983,6 +989,12 @@ def main() -> int:
     if args.flush_mb > 0 and args.no_kernel_events:
         print(json.dumps({"error": "--flush-mb times every step with events; "
                           "it cannot be combined with --no-kernel-events"}))
+        return 2
+    if args.preroll is not None and (args.preroll < 0 or
+                                     not args.no_kernel_events):
+        print(json.dumps({"error": "--preroll takes a count >= 0 and needs "
+                          "--no-kernel-events (the per-step fold needs an "
+                          "evicting step in the window)"}))
         return 2
 
     import torch
@@ -1013,7 +1025,8 @@ def main() -> int:
     # The cache holds B entries after set-up and evicts on every L-th step.
     # Set-up advances it by `preroll` untimed decode steps so that an
     # eviction falls in the middle of the timed window, whatever --steps is.
-    preroll = preroll_steps(L, warmup, steps)
+    preroll = (preroll_steps(L, warmup, steps) if args.preroll is None
+               else args.preroll)
     pool = min(preroll + warmup + steps, 3 * L)
     log(f"workload {args.workload}: layers={w.layers} batch={w.batch} "
         f"B={w.budget} L={L} steps={steps} warmup={warmup}")

@@ -19,6 +19,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libkvevict.so")
 BENCH_LIB = os.path.join(LIBDIR, "libkvebench.so")
 BUILD = os.path.join(ROOT, "_build")
+RESOURCE_REPORT = os.path.join(BUILD, "kernel_resource_usage.txt")
 SOURCES = ["kvevict.hip", "attention.hip", "cache_ops.hip", "score.hip",
            "mlstm.hip", "prefill.hip"]
 BENCH_SOURCES = ["bench_read.hip"]
@@ -61,17 +62,29 @@ def build(verbose: bool = False) -> str:
     def compile_one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         cmd = [cc, *COMMON_FLAGS, *inc, "-c", os.path.join(CSRC, src),
-               "-o", obj]
+               "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
         rc, out = _run(cmd)
         return src, obj, rc, out, cmd
 
     with ThreadPoolExecutor(max_workers=4) as ex:
         results = list(ex.map(compile_one, SOURCES + BENCH_SOURCES))
+    usage = []
     for src, obj, rc, out, cmd in results:
+        remarks = [l for l in out.splitlines()
+                   if "kernel-resource-usage" in l]
+        usage += remarks
+        rest = "\n".join(l for l in out.splitlines()
+                         if "kernel-resource-usage" not in l
+                         and not l.lstrip().startswith(("|", "^"))
+                         and not l.strip().isdigit())
         if verbose or rc != 0:
-            sys.stderr.write(f"[build] {' '.join(cmd)}\n{out}\n")
+            sys.stderr.write(f"[build] {' '.join(cmd)}\n{rest}\n")
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {src}")
+    # The compiler's per-kernel resource report (registers, scratch, LDS,
+    # occupancy), kept for the check that no kernel spills to scratch.
+    with open(RESOURCE_REPORT, "w") as f:
+        f.write("\n".join(usage) + "\n")
     objs = {r[0]: r[1] for r in results}
     for lib, srcs in ((LIB, SOURCES), (BENCH_LIB, BENCH_SOURCES)):
         tmp = lib + ".tmp"

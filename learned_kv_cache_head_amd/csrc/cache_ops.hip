@@ -738,10 +738,18 @@ struct EvictMlpLaunch {
 };
 
 // Three workgroups per CU (6 waves per SIMD, 80 VGPRs) run all 768 slices
-// of a batch-96 layer in one round; the 8-slot form cannot hold that bound.
+// of a batch-96 layer in one round. That bound holds without scratch for the
+// 3-slot form up to 64 hidden units at d = 128 and 96 at d = 64; wider
+// hidden layers take 4 waves per SIMD (128 VGPRs), and 128 hidden units at
+// d = 128 and the 8-slot form no bound (the compiler's choice spills nothing).
+constexpr int evict_waves(int D, int NB, int R) {
+  if (R > 3 || (D == 128 && NB >= 8)) return 1;
+  return ((D == 128 && NB <= 4) || (D == 64 && NB <= 6)) ? 6 : 4;
+}
+
 template <int D, int NB, int TPW, int R>
 __global__ __launch_bounds__(kSelThreads)
-__attribute__((amdgpu_waves_per_eu(R <= 3 ? 6 : 1)))
+__attribute__((amdgpu_waves_per_eu(evict_waves(D, NB, R))))
 void evict_mlp_kernel(
     EvictMlpLaunch a) {
   constexpr int HID = NB * 16;
@@ -786,16 +794,6 @@ void evict_mlp_kernel(
     mlp_load_row<D>(rows[t], nw ? kn : kc + slot * D, nw ? vn : vc + slot * D,
                     kq);
   }
-  int32_t p[R];
-  float s[R], g[R];
-  bool valid[R], evicted[R];
-  select_load_regs(sc, ps, a.gumbel ? a.gumbel + base : nullptr, a.len, p, s,
-                   g, valid);
-  if (app) {
-#pragma unroll
-    for (int v = 0; v < R; ++v)
-      if (v * kSelThreads + tid == last) p[v] = a.new_pos;
-  }
   mlp_stage_w1<HID, IN>(w1s, LSTR, (const uint16_t*)a.w1 + (size_t)h * HID * IN,
                         kSelThreads);
   for (int i = tid; i < PMAX; i += kSelThreads) {
@@ -827,6 +825,20 @@ void evict_mlp_kernel(
         }
       }
     }
+  }
+  // The select's registers are loaded only now: live across the MFMA tiles
+  // they pushed the 6-waves-per-SIMD form past its 80 VGPRs into scratch.
+  // Their loads are in flight during the barrier; the pending slots' scores
+  // come from LDS below, so the stores above need not be visible to them.
+  int32_t p[R];
+  float s[R], g[R];
+  bool valid[R], evicted[R];
+  select_load_regs(sc, ps, a.gumbel ? a.gumbel + base : nullptr, a.len, p, s,
+                   g, valid);
+  if (app) {
+#pragma unroll
+    for (int v = 0; v < R; ++v)
+      if (v * kSelThreads + tid == last) p[v] = a.new_pos;
   }
   __syncthreads();
 #pragma unroll

@@ -39,6 +39,13 @@ def test_flush_needs_per_step_events():
     assert "--flush-mb" in json.loads(lines[-1])["error"]
 
 
+def test_explicit_preroll_needs_whole_region_timing():
+    for args in (["--preroll", "3"], ["--no-kernel-events", "--preroll", "-1"]):
+        rc, lines = _run(*args)
+        assert rc == 2
+        assert "--preroll" in json.loads(lines[-1])["error"]
+
+
 def test_algorithmic_byte_accounting():
     """The bytes the roofline divides by, written out by hand for the
     batch-96 Qwen3-4B layer (768 slices, d 128, bf16, G 4): per slice, n K
