@@ -876,6 +876,33 @@ def preroll_steps(L: int, warmup: int, steps: int) -> int:
     return (-(warmup + 1 + e)) % L
 
 
+def window_has_eviction(L: int, preroll: int, warmup: int, steps: int) -> bool:
+    """Whether the timed steps (the t-th decode step after the prompt
+    compression evicts when t is a multiple of L) include an evicting one."""
+    first = preroll + warmup + 1
+    last = preroll + warmup + steps
+    return last // L > (first - 1) // L
+
+
+def cycle_profile(step_ms, evicts, L: int, batch: int, pos0: int,
+                  max_points: int = 8):
+    """Throughput of whole eviction cycles inside the window (L consecutive
+    steps that end with an evicting step), at up to ``max_points`` cycles
+    spread evenly over it: the decoded position of each cycle's first token
+    and batch * L / (sum of its step times)."""
+    ends = [i for i, e in enumerate(evicts) if e and i + 1 >= L]
+    cycles = [(i + 1 - L, sum(step_ms[i + 1 - L:i + 1])) for i in ends]
+    if not cycles:
+        return []
+    if len(cycles) > max_points:
+        pick = [round(j * (len(cycles) - 1) / (max_points - 1))
+                for j in range(max_points)]
+        cycles = [cycles[j] for j in pick]
+    return [{"start_pos": pos0 + s0,
+             "tokens_per_s": round(batch * L / (ms * 1e-3), 1)}
+            for s0, ms in cycles]
+
+
 def attn_rows(w, n: int, evicts: bool) -> int:
     """Rows the attention of a step reads: B after an eviction, else the
     count after the append."""
@@ -975,9 +1002,10 @@ def main() -> int:
     ap.add_argument("--preroll", type=int, default=None,
                     help="untimed decode steps after the prompt compression "
                          "(default: the count that puts an eviction at timed "
-                         "step steps // 2); an explicit count lets a counter "
-                         "pass cover non-evicting steps only; needs "
-                         "--no-kernel-events")
+                         "step steps // 2). 0 decodes from the prompt's end "
+                         "(e.g. 8K to 32K in 24576 steps); with "
+                         "--no-kernel-events a counter pass may also stay "
+                         "clear of evictions")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -990,12 +1018,19 @@ def main() -> int:
         print(json.dumps({"error": "--flush-mb times every step with events; "
                           "it cannot be combined with --no-kernel-events"}))
         return 2
-    if args.preroll is not None and (args.preroll < 0 or
-                                     not args.no_kernel_events):
-        print(json.dumps({"error": "--preroll takes a count >= 0 and needs "
-                          "--no-kernel-events (the per-step fold needs an "
-                          "evicting step in the window)"}))
-        return 2
+    if args.preroll is not None and not (args.sink_gate or args.prefill):
+        w0 = workload_for(args.workload)
+        L0 = w0.evict_len
+        st0 = args.steps if args.steps is not None else max(4 * L0, 64)
+        wu0 = args.warmup if args.warmup is not None else max(L0, 8)
+        if args.preroll < 0 or not (args.no_kernel_events or
+                                    window_has_eviction(L0, args.preroll,
+                                                        wu0, st0)):
+            print(json.dumps({"error": "--preroll takes a count >= 0, and "
+                              "without --no-kernel-events the timed window "
+                              "must still hold an evicting step (the "
+                              "per-step fold needs one)"}))
+            return 2
 
     import torch
     import synthetic as syn
@@ -1212,6 +1247,10 @@ def main() -> int:
                        "cycle_mean_attention_rows": w.budget + (L - 1) / 2}},
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "cycles_by_position": (cycle_profile(
+            step_ms_all, [ev for _, ev in lens], L, w.batch,
+            (w.n0 if args.start_pos is None else args.start_pos)
+            + preroll + warmup) if use_events else None),
         "achievable_copy_gbps": None,
         "achievable_read_gbps": None,
         "roofline": roof,

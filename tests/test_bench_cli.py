@@ -39,11 +39,46 @@ def test_flush_needs_per_step_events():
     assert "--flush-mb" in json.loads(lines[-1])["error"]
 
 
-def test_explicit_preroll_needs_whole_region_timing():
-    for args in (["--preroll", "3"], ["--no-kernel-events", "--preroll", "-1"]):
+def test_explicit_preroll_keeps_an_eviction_in_timed_windows():
+    # 20 timed steps after 3 + 5 untimed ones end at step 28 < L = 128
+    for args in (["--preroll", "3", "--steps", "20", "--warmup", "5"],
+                 ["--no-kernel-events", "--preroll", "-1"]):
         rc, lines = _run(*args)
         assert rc == 2
         assert "--preroll" in json.loads(lines[-1])["error"]
+
+
+def test_window_has_eviction():
+    import bench
+    assert bench.window_has_eviction(128, 0, 0, 128)      # t = 1..128
+    assert not bench.window_has_eviction(128, 0, 0, 127)
+    assert not bench.window_has_eviction(128, 128, 0, 127)  # t = 129..255
+    assert bench.window_has_eviction(128, 127, 0, 1)      # t = 128
+    assert bench.window_has_eviction(1, 0, 0, 1)
+    for L, pre, wu, st in [(128, 55, 8, 128), (256, 119, 8, 256), (64, 27, 4, 64)]:
+        assert bench.window_has_eviction(L, pre, wu, st)
+    for L in (1, 64, 128, 256):
+        for wu in (0, 5, 128):
+            for st in (1, 20, 512):
+                pre = bench.preroll_steps(L, wu, st)
+                assert bench.window_has_eviction(L, pre, wu, st)
+
+
+def test_cycle_profile_sums_whole_cycles():
+    import bench
+    L = 4
+    ev = [False, True, False, False, False, True, False, False, False, True]
+    ms = [1.0] * 10
+    ms[5] = 3.0
+    prof = bench.cycle_profile(ms, ev, L, batch=8, pos0=100)
+    # cycles end at steps 5 and 9 (step 1 has no L steps before it)
+    assert [p["start_pos"] for p in prof] == [102, 106]
+    assert prof[0]["tokens_per_s"] == round(8 * 4 / 6e-3, 1)
+    assert prof[1]["tokens_per_s"] == round(8 * 4 / 4e-3, 1)
+    many = bench.cycle_profile([1.0] * 400, [(i + 1) % 4 == 0 for i in range(400)],
+                               4, 1, 0, max_points=8)
+    assert len(many) == 8 and many[0]["start_pos"] == 0
+    assert many[-1]["start_pos"] == 396
 
 
 def test_algorithmic_byte_accounting():
