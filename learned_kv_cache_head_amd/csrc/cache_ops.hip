@@ -136,6 +136,12 @@ __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
       sh[2] = 0u;
     }
     __syncthreads();
+    // Each thread counts a run of its entries that fall in one bin locally
+    // and adds the run with one atomic when the bin changes. Scores packed
+    // into a few bins (a gate's sigmoid outputs share their top key bits)
+    // would otherwise send every lane of a wave to the same LDS address for
+    // every entry; spread scores cost one compare more per entry.
+    uint32_t run_bin = 0, run_cnt = 0;
     for (int base = 0; base < len; base += kSelSweep) {
       bool t[kSelV];
       uint32_t k[kSelV];
@@ -147,10 +153,19 @@ __device__ void radix_select(int len, uint32_t rank, KeyFn key_of,
         k[v] = key_of(cc);
       }
 #pragma unroll
-      for (int v = 0; v < kSelV; ++v)
-        if (t[v] && (k[v] & mask) == prefix)
-          atomicAdd(&hist[(k[v] >> shift) & 255u], 1u);
+      for (int v = 0; v < kSelV; ++v) {
+        if (t[v] && (k[v] & mask) == prefix) {
+          const uint32_t bin = (k[v] >> shift) & 255u;
+          if (bin != run_bin) {
+            if (run_cnt) atomicAdd(&hist[run_bin], run_cnt);
+            run_bin = bin;
+            run_cnt = 0;
+          }
+          ++run_cnt;
+        }
+      }
     }
+    if (run_cnt) atomicAdd(&hist[run_bin], run_cnt);
     __syncthreads();
     radix_find_bin(hist, wsum, sh, remaining);
     const uint32_t digit = sh[0];
