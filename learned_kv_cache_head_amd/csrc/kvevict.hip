@@ -303,7 +303,7 @@ kve_status score_impl(const kve_shape* shape, const kve_scorer* sc,
 // attention launches live in this file-scope device array (one copy per
 // GPU, held until the process ends) instead of a caller workspace.
 constexpr size_t kNoallocScratchBytes = KVE_NOALLOC_SCRATCH_BYTES;
-__device__ __align__(256) unsigned char scratch[KVE_NOALLOC_SCRATCH_BYTES];
+static __device__ __align__(256) unsigned char scratch[KVE_NOALLOC_SCRATCH_BYTES];
 
 // Device address of the current device's copy of `scratch`. The array's name
 // is a host-side stand-in in host code: the address comes from
