@@ -171,8 +171,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
   }
 
   // This lane's chunk of every query head of the group (same element order
-  // as the K chunk it loads). Logits are taken in base 2.
+  // as the K chunk it loads). Logits are taken in base 2. Float32 q rows are
+  // scaled here; bf16 sums are scaled afterwards (rscale: the factor still
+  // to apply to a raw q.k sum).
   const float qscale = kLog2e * rsqrtf((float)D);
+  const float rscale = BF16 ? qscale : 1.f;
   u32x4 qv[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -283,8 +286,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
     for (int u = 0; u < U; ++u)
       ok[u] = !MASK || (row0 + s * Gm::kStageRows + u * RPL < r_end);
     if constexpr (RS) {
-      // Scores of the owned heads, raw q.k (the 1/sqrt(d) and log2(e) factor
-      // qscale > 0 is applied inside the exponentials).
+      // Scores of the owned heads, q.k as summed (the factor rscale > 0
+      // still owed to them is applied inside the exponentials).
       float sc[U][NQ];
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -304,12 +307,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][c]);
         moved |= (mx != m[c]);
-        alpha[c] = fast_exp2((m[c] - mx) * qscale);
-        const float nmx = -mx * qscale;
+        alpha[c] = fast_exp2((m[c] - mx) * rscale);
+        const float nmx = -mx * rscale;
         float lsum = l[c] * alpha[c];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          p[u][c] = fast_exp2(fmaf(sc[u][c], qscale, nmx));
+          p[u][c] = fast_exp2(fmaf(sc[u][c], rscale, nmx));
           lsum += p[u][c];
         }
         l[c] = lsum;
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float t = sum_row_lanes<LPR>(partial_dot(st, u, g));
-          if constexpr (BF16) t *= qscale;
+          t *= rscale;
           sc[u][g] = ok[u] ? t : -INFINITY;
         }
       float p[U][G], alpha[G];
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch a) {
         default: mv = quad_bcast<quad_lane_of_head(3)>(m[g >> 2]);
                  lv = quad_bcast<quad_lane_of_head(3)>(l[g >> 2]); break;
       }
-      mh[g] = mv * qscale;
+      mh[g] = mv * rscale;
       lh[g] = lv;
     } else {
       mh[g] = m[g];

@@ -35,6 +35,10 @@ CASES = [
     ("bf16", 128, 3, 4, 3, 4097, 4100, 1.0),
     ("bf16", 128, 4, 2, 2, 2000, 2048, 6.0),    # peaked softmax
     ("f32", 64, 2, 2, 1, 2303, 2304, 4.0),
+    # float32 rows of 16 lanes with whole quads of heads: the reduce-scatter
+    # path with q scaled at load (its logits were once scaled twice)
+    ("f32", 64, 4, 2, 2, 300, 320, 1.0),
+    ("f32", 64, 8, 3, 1, 8, 69, 1.0),
 ]
 
 
@@ -48,9 +52,40 @@ def _poison(t, length):
     t[:, :, length:] = float("nan")
 
 
+def _random_cases(n=24, seed=7):
+    """Seeded random shapes: group 1..8, d 64 or 128, bf16 or float32,
+    lengths from 1 to ~8000 (every split count the planner picks for them),
+    at most ~150k retained rows in all."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        length = int(np.exp(rng.uniform(0.0, np.log(8000.0))))
+        slices = int(rng.integers(1, max(2, min(96, 150000 // length))))
+        H = int(rng.integers(1, min(8, slices) + 1))
+        B = max(1, slices // H)
+        out.append(("f32" if rng.random() < 0.3 else "bf16",
+                    int(rng.choice([64, 128])), int(rng.integers(1, 9)), H, B,
+                    length, length + int(rng.integers(0, 65)),
+                    float(rng.choice([1.0, 3.0, 6.0]))))
+    return out
+
+
+RANDOM_CASES = _random_cases()
+
+
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-d{c[1]}-g{c[2]}-b{c[4]}-n{c[5]}"
                                              for c in CASES])
 def test_decode_attention_matches_oracle(case):
+    _check(case)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[
+    f"{c[0]}-d{c[1]}-g{c[2]}-h{c[3]}-b{c[4]}-n{c[5]}" for c in RANDOM_CASES])
+def test_decode_attention_random_shapes(case):
+    _check(case)
+
+
+def _check(case):
     import torch
     k = kve()
     dt, D, G, H, B, n, cap, kscale = case
