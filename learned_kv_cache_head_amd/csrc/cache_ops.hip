@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const bool decay = log_gamma != nullptr;
   auto fkey = [&](int c) {
     float r = sc[c];
-    if (decay) r = __fsub_rn(r, __fmul_rn((float)ps[c], lg));
+    if (decay) r = decayed_priority(r, ps[c], lg);
     return r;
   };
   auto skey = [&](int c) { return score_key(fkey(c)); };
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // the r pool entries with the largest float32 sum -key + noise, i.e. the
   // smallest descending key, equal sums the lower position first.
   uint32_t gthr = 0, gpthr = 0;
-  auto dkey = [&](int c) { return ~score_key(__fadd_rn(-fkey(c), gs[c])); };
+  auto dkey = [&](int c) { return ~score_key(noisy_key(fkey(c), gs[c])); };
   if (!gs) {
     if constexpr (CACHE) {
       for (int base = 0; base < len; base += kSelSweep) {
@@ -517,7 +517,7 @@ __device__ void select_rule_regs(SelRegsLds<R>& L, const int32_t (&p)[R],
   for (int v = 0; v < R; ++v) {
     cand[v] = valid[v] & (p[v] >= S) & ((long long)p[v] <= last_eligible);
     // static priority under decay: two separately rounded operations
-    fk[v] = decay ? __fsub_rn(s[v], __fmul_rn((float)p[v], lg)) : s[v];
+    fk[v] = decay ? decayed_priority(s[v], p[v], lg) : s[v];
     key[v] = score_key(fk[v]);
     pk[v] = (uint32_t)p[v];
   }
@@ -566,7 +566,7 @@ __device__ void select_rule_regs(SelRegsLds<R>& L, const int32_t (&p)[R],
 #pragma unroll
   for (int v = 0; v < R; ++v) {
     in_pool[v] = cand[v] & before(key[v], v, thr, pthr);
-    dk[v] = ~score_key(__fadd_rn(-fk[v], g[v]));
+    dk[v] = ~score_key(noisy_key(fk[v], g[v]));
   }
   uint32_t gthr, gpthr;
   cut(r, dk, in_pool, &gthr, &gpthr);

@@ -29,6 +29,23 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Static priority under temporal decay (KVpop Eq. 20), ranked in float32
+// (Appendix F): the product position * log(gamma) is rounded to float32,
+// then the difference. Contraction is off here: hipcc fuses a * b + c into
+// one multiply-add by default, which rounds once and can reorder keys that
+// the two roundings make equal or adjacent.
+__device__ __forceinline__ float decayed_priority(float s, int pos, float lg) {
+#pragma clang fp contract(off)
+  const float prod = (float)pos * lg;
+  return s - prod;
+}
+
+// The noisy key of the stochastic rule: -key + noise, one float32 add.
+__device__ __forceinline__ float noisy_key(float key, float noise) {
+#pragma clang fp contract(off)
+  return -key + noise;
+}
+
 // ---------------------------------------------------------------------------
 // Launch descriptors.
 // ---------------------------------------------------------------------------

@@ -57,7 +57,7 @@ constexpr int kSortThreads = 512;
 // rounded like the select kernel: the product, then the difference.
 __device__ __forceinline__ uint32_t priority_key(float s, int pos,
                                                  const float* lg, int h) {
-  if (lg) s = __fsub_rn(s, __fmul_rn((float)pos, lg[h]));
+  if (lg) s = decayed_priority(s, pos, lg[h]);
   return score_key(s);
 }
 
