@@ -132,6 +132,12 @@ def load_library(path: Optional[str] = None):
         raise RuntimeError(
             f"libkvevict is not built ({p} missing); run "
             "__graft_entry__.build() first")
+    # PyTorch ships its own HIP runtime (libamdhip64.so, soname
+    # libamdhip64.so.7). Loaded after torch, the library links against that
+    # copy; loaded before it, the library would bind the system's runtime and
+    # torch would then load a second one, whose device memory and streams
+    # the library's launches cannot use.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

@@ -461,3 +461,24 @@ def test_one_library_per_process(tmp_path):
     assert kve.load_library(kve.library_path()) is lib
     with pytest.raises(RuntimeError, match="already loaded"):
         kve.load_library(str(tmp_path / "libkvevict.so"))
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loaded before anything imports torch, the library still ends up with
+    the one HIP runtime torch uses: a fresh process that loads it first and
+    then uses torch maps a single libamdhip64."""
+    import subprocess
+    import sys
+    code = (
+        "import learned_kv_cache_head_amd as kve\n"
+        "kve.load_library()\n"
+        "import torch\n"
+        "torch.zeros(1)\n"
+        "maps = open('/proc/self/maps').read().split('\\n')\n"
+        "paths = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+        "print(len(paths), sorted(paths))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT,
+                         capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    n = int(out.stdout.split()[0])
+    assert n == 1, out.stdout
