@@ -359,12 +359,16 @@ kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
  * in the recent window (q - t < W) or eligible with rank(t) <= tau_q, with
  * rank and tau from kve_prefill_select. q [batch][H*G][len][d] bf16; out
  * [batch][H*G][len][d] float32; lse [batch][H*G][len] float32 natural-log
- * normaliser or NULL. bf16 caches only; MFMA (bf16 inputs, float32
- * accumulation and softmax). ws: kve_prefill_attn_workspace_bytes bytes of
- * scratch: per 64-position query block, the at most k long-range keys any
- * of its queries keeps (the attention visits only those, the sinks and the
- * block's recent windows). policy->gumbel must be NULL, as for
- * kve_prefill_select. */
+ * normaliser or NULL. bf16 caches only; MFMA with float32 accumulation and
+ * softmax: q.k in bf16; the weighted sum of V in float16 (V converted
+ * exactly, weights rounded to 11 significant bits) for a (batch, KV head)
+ * slice whose largest |v| over positions < len lies in [2^-6, 65280], else
+ * in bf16 with each weight as two parts (about 17 significant bits). ws:
+ * kve_prefill_attn_workspace_bytes bytes of scratch: per 64-position query
+ * block, the at most k long-range keys any of its queries keeps (the
+ * attention visits only those, the sinks and the block's recent windows),
+ * their count and the block's largest |v|. policy->gumbel must be NULL, as
+ * for kve_prefill_select. */
 size_t kve_prefill_attn_workspace_bytes(const kve_shape* shape,
                                         const kve_policy* policy, int32_t len);
 kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,

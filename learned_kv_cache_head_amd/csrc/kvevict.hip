@@ -406,12 +406,8 @@ kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
   if ((long long)shape->batch * shape->n_kv_heads > 65535)
     return KVE_ERR_UNSUPPORTED;  // one grid row per slice (key lists)
   const int k = policy->budget - policy->sinks - policy->window;
-  const long long nqb = (len + 63) / 64;
-  const long long slices = (long long)shape->batch * shape->n_kv_heads;
   kve::PrefillAttnLaunch a{};
   a.kmax = k > 0 ? k : 1;
-  a.list = (int32_t*)ws;
-  a.count = (int32_t*)((char*)ws + (need - (size_t)(slices * nqb) * sizeof(int32_t)));
   a.k = cache->k;
   a.v = cache->v;
   a.rank = rank;
@@ -433,7 +429,7 @@ kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
   a.nsub = (shape->group + 1) / 2;
   a.gsub = (shape->group + a.nsub - 1) / a.nsub;
   if ((long long)a.H * a.nsub > 65535) return KVE_ERR_UNSUPPORTED;
-  return from_hip(kve::launch_prefill_attn(a, stream));
+  return from_hip(kve::launch_prefill_attn(a, ws, stream));
 }
 
 const char* kve_status_str(kve_status s) {

@@ -27,17 +27,22 @@
 // parallel rebuild per block replaces a chain of n sequential steps by one
 // of 64.)
 //
-// Attention: a flash-attention forward on MFMA (v_mfma_f32_16x16x32_bf16,
-// float32 accumulation) with the Eq. 26 predicate applied to each logit. A
-// workgroup owns 64 query positions of one KV head and up to 2 of its query
-// heads (two waves per SIMD fit); the 4 waves take 16 positions each. Each
-// 64-key block of K and V is staged in LDS, row-major, and shared by all of
-// them; the V^T operand comes from LDS transpose reads. The kernel
-// computes S^T = K Q^T, so a lane's accumulators hold 8 keys of one query
-// column: those are exactly the operand of P^T that O^T = V^T P^T needs,
-// and the online-softmax state is one value per lane and head. Each weight
-// enters O^T as two bf16 parts (its rounding and the remainder), two MFMAs
-// into one float32 accumulator, so P.V keeps about 17 bits of each weight.
+// Attention: a flash-attention forward on MFMA (float32 accumulation) with
+// the Eq. 26 predicate applied to each logit. A workgroup owns 64 query
+// positions of one KV head and up to 2 of its query heads (two waves per
+// SIMD fit); the 4 waves take 16 positions each. Each 64-key block of K and
+// V is staged in LDS, row-major, and shared by all of them; the V^T operand
+// comes from LDS transpose reads. The kernel computes S^T = K Q^T
+// (v_mfma_f32_16x16x32_bf16), so a lane's accumulators hold 8 keys of one
+// query column: those are exactly the operand of P^T that O^T = V^T P^T
+// needs, and the online-softmax state is one value per lane and head.
+// O^T = V^T P^T runs in float16 (v_mfma_f32_16x16x32_f16: V converted
+// exactly when staged, each weight rounded to 11 significant bits) for
+// slices whose V fits float16, else in bf16 with each weight as two parts
+// (its rounding and the remainder, about 17 bits), two MFMAs into one
+// float32 accumulator. The key-list kernel records each query block's
+// largest |v| for that choice. Workgroups are ordered so that each XCD
+// takes whole slices, which share key rows in its L2.
 #include "kve_internal.h"
 
 namespace kve {
@@ -264,16 +269,41 @@ __global__ __launch_bounds__(kCutThreads) void cutoff_kernel(
 // cutoff only tightens as q grows, so these hold every long-range key any
 // query of the block keeps (at most k of them: the top-k of E(q0)).
 // ---------------------------------------------------------------------------
+// The same workgroup records the largest |v| of the block's V rows (the bf16
+// bit pattern without its sign), from which the attention chooses the
+// arithmetic of its P.V products for the whole slice.
 __global__ __launch_bounds__(256) void keylist_kernel(const int32_t* rank,
                                                       const int32_t* tau, int n,
                                                       int S, int W, int kmax,
                                                       int32_t* list,
-                                                      int32_t* count) {
+                                                      int32_t* count,
+                                                      const uint16_t* v, int D,
+                                                      int cap, uint32_t* vmax) {
   __shared__ int wsum[4];
+  __shared__ uint32_t wmax[4];
   const int qb = blockIdx.x;
   const int slice = blockIdx.y;
   const int nqb = gridDim.x;
   const int q0 = qb * kQBlock;
+  {
+    const int chunks = min(kQBlock, n - q0) * D / 8;  // 16-byte chunks
+    const u32x4* vr = (const u32x4*)(v + ((size_t)slice * cap + q0) * D);
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < chunks; i += 256) {
+      const u32x4 w = vr[i];
+      const uint32_t a = w.x & 0x7fff7fffu, b = w.y & 0x7fff7fffu;
+      const uint32_t c = w.z & 0x7fff7fffu, d = w.w & 0x7fff7fffu;
+      m = max(m, max(max(a >> 16, a & 0xffffu), max(b >> 16, b & 0xffffu)));
+      m = max(m, max(max(c >> 16, c & 0xffffu), max(d >> 16, d & 0xffffu)));
+    }
+    for (int off = 32; off > 0; off >>= 1)
+      m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      vmax[(size_t)slice * nqb + qb] =
+          max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  }
   const int32_t* rk = rank + (size_t)slice * n;
   const int t0 = tau[(size_t)slice * n + q0];
   int32_t* out = list + ((size_t)slice * nqb + qb) * kmax;
@@ -331,6 +361,36 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
                             __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+// Two floats to packed float16 (round to nearest even), a in the low half:
+// one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+// Two packed bf16 to packed float16 (exact for magnitudes in [2^-17, 65280]).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack2h(bf16lo(w), bf16hi(w));
+}
+// The value lane l ^ 32 (l ^ 16) of the wave holds. permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second, so lane l finds its partner in the second result below lane 32
+// and in the first from lane 32 on (rows of 16 lanes likewise for
+// permlane16_swap, which exchanges odd rows of the first operand with even
+// rows of the second).
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+template <bool B> struct Flag { static constexpr bool value = B; };
+
 constexpr int kQB = kQBlock;
 constexpr int kKB = 64;   // keys per block (measured faster than 32)
 constexpr float kLazy = 8.f;  // log2 headroom of the softmax reference
@@ -355,10 +415,20 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nqb = (p.n + kQB - 1) / kQB;
-  const int qb = nqb - 1 - blockIdx.x;  // heavy (late) query blocks first
-  const int h = blockIdx.y / p.nsub;
-  const int sub = blockIdx.y % p.nsub;
-  const int b = blockIdx.z;
+  // Workgroup L runs on XCD L % 8. Each XCD takes a contiguous range of the
+  // grid in (query block, head subset, slice) order, so the workgroups of a
+  // slice, which gather the same key rows, share one L2.
+  const uint32_t nwg = gridDim.x * gridDim.y * gridDim.z;
+  const uint32_t L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const uint32_t xq = nwg / 8, xr = nwg % 8, xcd = L % 8;
+  const uint32_t T =
+      (xcd < xr ? xcd * (xq + 1) : xr * (xq + 1) + (xcd - xr) * xq) + L / 8;
+  const int tx = T % gridDim.x;
+  const int ty = (T / gridDim.x) % gridDim.y;
+  const int qb = nqb - 1 - tx;  // heavy (late) query blocks first
+  const int h = ty / p.nsub;
+  const int sub = ty % p.nsub;
+  const int b = T / (gridDim.x * gridDim.y);
   const int q0 = qb * kQB;
   const size_t slice = (size_t)b * p.H + h;
   const uint16_t* kc = (const uint16_t*)p.k + slice * p.cap * D;
@@ -409,8 +479,8 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
     return j < nS ? j : (j < nS + nL ? lst[j - nS] : w0 + (j - nS - nL));
   };
 
-  // Staging: each of the 256 threads moves 16 B of K and 16 B of V per
-  // 32-key block (32 rows of D bf16 = D/8 chunks per row).
+  // Staging: a 64-key block is 64 rows of D bf16 (D/8 chunks of 16 B per
+  // row) of K and of V; each of the 256 threads moves D/32 chunks of each.
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   u32x4 kreg[kKB * CPR / 256], vreg[kKB * CPR / 256];
   int rreg = 0, treg = 0;
@@ -444,14 +514,20 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
       rreg = treg == 0x7fffffff ? 0x7fffffff : rk[treg];
     }
   };
-  auto stage = [&](int buf) {
+  // V is staged as float16 on the float16 path (see below).
+  auto stage = [&](int buf, auto f16) {
 #pragma unroll
     for (int c = 0; c < kKB * CPR / 256; ++c) {
       const int idx = threadIdx.x + c * 256;
       const int row = idx / CPR;
       const int ch = idx % CPR;
       *(u32x4*)(&ks[buf][row * KSTR + ch * 8]) = kreg[c];
-      *(u32x4*)(&vs[buf][row * VSTR + ch * 8]) = vreg[c];
+      if constexpr (decltype(f16)::value)
+        *(u32x4*)(&vs[buf][row * VSTR + ch * 8]) =
+            u32x4{bf16x2_to_f16x2(vreg[c].x), bf16x2_to_f16x2(vreg[c].y),
+                  bf16x2_to_f16x2(vreg[c].z), bf16x2_to_f16x2(vreg[c].w)};
+      else
+        *(u32x4*)(&vs[buf][row * VSTR + ch * 8]) = vreg[c];
     }
     if (threadIdx.x < kKB) {
       rks[buf][threadIdx.x] = rreg;
@@ -459,10 +535,27 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
     }
   };
 
+  // The P.V products of the slice. When its largest |v| lies in [2^-6,
+  // 65280], every V element converts to float16 exactly (magnitudes of at
+  // least 2^-17) or within 2^-25 absolute (below), and each weight enters
+  // one float16 MFMA, rounded to 11 significant bits (weights are at most
+  // 2^kLazy, far inside float16's range). Otherwise (larger or tiny values,
+  // NaN, inf) V stays bf16 and each weight enters as two bf16 parts. The
+  // choice is uniform per slice, from the maxima the key-list kernel
+  // recorded per query block.
+  uint32_t vm = 0;
+  for (int i = lane; i < nqb; i += 64) vm = max(vm, p.vmax[slice * nqb + i]);
+  for (int off = 32; off > 0; off >>= 1)
+    vm = max(vm, (uint32_t)__shfl_xor((int)vm, off));
+  vm = __builtin_amdgcn_readfirstlane(vm);
+  const bool fp16 = vm >= 0x3c80u && vm <= 0x477fu;  // bf16 2^-6 and 65280
+
+  auto run = [&](auto f16) {
+  constexpr bool F16 = decltype(f16)::value;
   refill(0);
   __syncthreads();
   fetch(0);
-  stage(0);
+  stage(0, f16);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
@@ -518,8 +611,9 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
       }
       // Online softmax per query column, then O^T += V^T P^T, 32 keys per
       // contraction step: half hh holds key tiles 2hh and 2hh+1. Each weight
-      // goes to the MFMA as two bf16 parts, its rounding and the remainder
-      // (pk, pl): their sum carries a relative error of at most 2^-17.
+      // goes to the MFMA as one float16 (pk), or as two bf16 parts, its
+      // rounding and the remainder (pk, pl), whose sum carries a relative
+      // error of at most 2^-17.
       uint32_t pk[GS][KT / 2][4], pl[GS][KT / 2][4];
 #pragma unroll
       for (int gi = 0; gi < GS; ++gi) {
@@ -535,8 +629,8 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
             x[kt * 4 + i] = v;
             mx = fmaxf(mx, v);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, lane_xor16(mx));
+        mx = fmaxf(mx, lane_xor32(mx));
         mx *= qscale;
         // Lazy rescaling: the reference maximum moves only when a logit
         // passes it by more than 2^kLazy (or on the first kept key), so
@@ -545,7 +639,7 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
         const float mnew = move ? mx : mrun[gi];
         const float alpha = move ? __builtin_amdgcn_exp2f(mrun[gi] - mnew) : 1.f;
         const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-        // p goes to the MFMA as hi = bf16(p) and lo = bf16(p - hi): p - hi
+        // bf16 path: p enters as hi = bf16(p) and lo = bf16(p - hi); p - hi
         // is exact in float32 and at most 2^-9 p, so hi + lo is within
         // 2^-17 p. The normaliser, and so lse, sums the float32 values.
         float ps = 0.f;
@@ -553,9 +647,13 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
         for (int j = 0; j < KT * 4; j += 2) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(x[j], qscale, -mref));
           const float e1 = __builtin_amdgcn_exp2f(fmaf(x[j + 1], qscale, -mref));
-          const uint32_t hi = pack2(e0, e1);
-          pk[gi][j >> 3][(j >> 1) & 3] = hi;
-          pl[gi][j >> 3][(j >> 1) & 3] = pack2(e0 - bf16lo(hi), e1 - bf16hi(hi));
+          if constexpr (F16) {
+            pk[gi][j >> 3][(j >> 1) & 3] = pack2h(e0, e1);
+          } else {
+            const uint32_t hi = pack2(e0, e1);
+            pk[gi][j >> 3][(j >> 1) & 3] = hi;
+            pl[gi][j >> 3][(j >> 1) & 3] = pack2(e0 - bf16lo(hi), e1 - bf16hi(hi));
+          }
           ps += e0 + e1;
         }
         lrun[gi] = lrun[gi] * alpha + ps;
@@ -579,40 +677,55 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)v0);
           const i16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 16 * VSTR));
-          const bf16x8_t A = __builtin_bit_cast(
-              bf16x8_t, u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
-                              __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y});
+          const u32x4 a = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                                __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+          if constexpr (F16) {
 #pragma unroll
-          for (int gi = 0; gi < GS; ++gi) {
-            const bf16x8_t B = __builtin_bit_cast(
-                bf16x8_t,
-                u32x4{pk[gi][hh][0], pk[gi][hh][1], pk[gi][hh][2], pk[gi][hh][3]});
-            o[dt][gi] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
-          }
+            for (int gi = 0; gi < GS; ++gi) {
+              const u32x4 bw{pk[gi][hh][0], pk[gi][hh][1], pk[gi][hh][2], pk[gi][hh][3]};
+              o[dt][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, bw),
+                  o[dt][gi], 0, 0, 0);
+            }
+          } else {
+            const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
-          for (int gi = 0; gi < GS; ++gi) {
-            const bf16x8_t B = __builtin_bit_cast(
-                bf16x8_t,
-                u32x4{pl[gi][hh][0], pl[gi][hh][1], pl[gi][hh][2], pl[gi][hh][3]});
-            o[dt][gi] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
+            for (int gi = 0; gi < GS; ++gi) {
+              const bf16x8_t B = __builtin_bit_cast(
+                  bf16x8_t,
+                  u32x4{pk[gi][hh][0], pk[gi][hh][1], pk[gi][hh][2], pk[gi][hh][3]});
+              o[dt][gi] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
+            }
+#pragma unroll
+            for (int gi = 0; gi < GS; ++gi) {
+              const bf16x8_t B = __builtin_bit_cast(
+                  bf16x8_t,
+                  u32x4{pl[gi][hh][0], pl[gi][hh][1], pl[gi][hh][2], pl[gi][hh][3]});
+              o[dt][gi] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, o[dt][gi], 0, 0, 0);
+            }
           }
         }
       }
     }
     // The other buffer was last read before the previous barrier.
-    if (kb + 1 < nkb) stage(buf ^ 1);
+    if (kb + 1 < nkb) stage(buf ^ 1, f16);
     __syncthreads();
   }
+  };
+  if (fp16)
+    run(Flag<true>{});
+  else
+    run(Flag<false>{});
 
   // Epilogue: normalise and store this lane's column (4 rows per d tile).
 #pragma unroll
   for (int gi = 0; gi < GS; ++gi) {
     const int g = sub * GS + gi;
     float l = lrun[gi];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l += lane_xor16(l);
+    l += lane_xor32(l);
     if (g >= p.G || qpos >= p.n) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     float* orow = p.out + (((size_t)b * hq + h * p.G + g) * p.n + qpos) * D;
@@ -652,17 +765,25 @@ hipError_t launch_prefill_select(const float* score, const float* lg, int H,
   return hipGetLastError();
 }
 
+// Workspace: the key lists (rounded up to 256 bytes), then one count and
+// one V maximum per (slice, query block).
 size_t prefill_attn_ws_bytes(long long slices, int n, int kmax) {
   const long long nqb = (n + kQB - 1) / kQB;
   const size_t lists = (size_t)(slices * nqb) * kmax * sizeof(int32_t);
-  const size_t counts = (size_t)(slices * nqb) * sizeof(int32_t);
-  return (lists + 255) / 256 * 256 + counts;
+  const size_t blocks = (size_t)(slices * nqb) * sizeof(int32_t);
+  return (lists + 255) / 256 * 256 + 2 * blocks;
 }
 
-hipError_t launch_prefill_attn(const PrefillAttnLaunch& a, hipStream_t s) {
+hipError_t launch_prefill_attn(PrefillAttnLaunch a, void* ws, hipStream_t s) {
   const int nqb = (a.n + kQB - 1) / kQB;
+  const size_t blocks = (size_t)a.batch * a.H * nqb;
+  const size_t lists = (blocks * a.kmax * sizeof(int32_t) + 255) / 256 * 256;
+  a.list = (int32_t*)ws;
+  a.count = (int32_t*)((char*)ws + lists);
+  a.vmax = (uint32_t*)(a.count + blocks);
   hipLaunchKernelGGL(keylist_kernel, dim3(nqb, a.batch * a.H), dim3(256), 0, s,
-                     a.rank, a.tau, a.n, a.S, a.W, a.kmax, a.list, a.count);
+                     a.rank, a.tau, a.n, a.S, a.W, a.kmax, a.list, a.count,
+                     (const uint16_t*)a.v, a.D, a.cap, a.vmax);
   const dim3 grid(nqb, a.H * a.nsub, a.batch);
 #define KVE_PA(DD, GG)                                                       \
   if (a.D == DD && a.gsub == GG) {                                           \

@@ -5,8 +5,10 @@ ABI, against the float64 oracle.
 Ranks and cutoffs are integers decided from the same float32 keys on both
 sides: bit-exact. Attention is held to the attention contract: within
 2e-3 * max|out| of the float64 oracle per (batch, query head) output tensor.
-The GPU feeds each softmax weight to the P.V contraction as two bf16 parts
-(its rounding and the remainder, relative error at most 2^-17 together) and
+The GPU feeds each softmax weight to the P.V contraction as a float16
+(relative error at most 2^-11) when every V element of the slice converts
+to float16 (largest |v| in [2^-6, 65280]), else as two bf16 parts (its
+rounding and the remainder, relative error at most 2^-17 together); it
 normalises by the float32 sum. lse is float32 math on unrounded weights:
 within 1e-4 absolute.
 """
@@ -122,7 +124,7 @@ ATTN_CASES = [
 ]
 
 
-def run_attn(b, H, G, d, n, S, W, k, seed, decay=False):
+def run_attn(b, H, G, d, n, S, W, k, seed, decay=False, vscale=None):
     import torch
     k_ = kve()
     dev = torch.device("cuda")
@@ -132,7 +134,10 @@ def run_attn(b, H, G, d, n, S, W, k, seed, decay=False):
     cache2 = k_.CacheTensors.empty(shape, dev)
     rng = np.random.default_rng(seed + 1)
     K = syn.Stored(rng.standard_normal((b, H, n, d)).astype(np.float32), "bf16")
-    V = syn.Stored(rng.standard_normal((b, H, n, d)).astype(np.float32), "bf16")
+    Vf = rng.standard_normal((b, H, n, d)).astype(np.float32)
+    if vscale is not None:
+        Vf *= np.asarray(vscale, np.float32)[None, :, None, None]
+    V = syn.Stored(Vf, "bf16")
     Q = syn.Stored((1.5 * rng.standard_normal((b, H * G, n, d))).astype(np.float32),
                    "bf16")
     cache2.k.copy_(K.torch(dev))
@@ -163,6 +168,38 @@ def test_prefill_attention(case):
         print(f"[prefill-attn] max |err| / max|out| {rel:.3g}", flush=True)
         assert_attention_close(out[bi], ref, f"batch {bi}")
         np.testing.assert_allclose(lse[bi], ref_lse, rtol=0, atol=LSE_TOL)
+
+
+VSCALE_CASES = [
+    # b, H, G, d, n, S, W, k, V scale per KV head. N(0,1) rows of V times
+    # the scale: 8e3 (largest |v| near 3e4, the float16 path near its top),
+    # 1e5 (beyond 65280: bf16 weight pairs for that slice only), 0.01 (the
+    # float16 path with values among float16's subnormals), 1e-7 (largest
+    # |v| below 2^-6: bf16 weight pairs)
+    (1, 2, 4, 128, 300, 4, 16, 60, (1.0, 8e3)),
+    (1, 2, 4, 128, 300, 4, 16, 60, (1.0, 1e5)),
+    (1, 2, 4, 128, 300, 4, 16, 60, (0.01, 1e-7)),
+    (1, 2, 2, 64, 257, 1, 8, 100, (1e5, 1.0)),
+]
+
+
+@pytest.mark.parametrize("case", VSCALE_CASES, ids=[
+    f"d{c[3]}-v{c[8][0]:g},{c[8][1]:g}" for c in VSCALE_CASES])
+def test_prefill_attention_v_range(case):
+    """Slices whose V leaves float16's range take the bf16 path, the others
+    the float16 one; both within the contract."""
+    b, H, G, d, n, S, W, k, vs = case
+    print(f"[prefill-attn-vrange] {case}", flush=True)
+    rank, tau, K, V, Q, out, lse = run_attn(b, H, G, d, n, S, W, k,
+                                            seed=n + d, vscale=vs)
+    masks = np.stack([O.prefill_mask(rank[0, h], tau[0, h], S, W)
+                      for h in range(H)])
+    ref, ref_lse = O.prefill_attention(Q.f64[0], K.f64[0], V.f64[0], masks, G)
+    rel = max(np.abs(out[0, j] - ref[j]).max() / np.abs(ref[j]).max()
+              for j in range(ref.shape[0]))
+    print(f"[prefill-attn-vrange] max |err| / max|out| {rel:.3g}", flush=True)
+    assert_attention_close(out[0], ref, f"{vs}")
+    np.testing.assert_allclose(lse[0], ref_lse, rtol=0, atol=LSE_TOL)
 
 
 def test_prefill_attention_with_decay_and_skipped_blocks():
