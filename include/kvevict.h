@@ -367,8 +367,8 @@ kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
  * kve_prefill_attn_workspace_bytes bytes of scratch: per 64-position query
  * block, the at most k long-range keys any of its queries keeps (the
  * attention visits only those, the sinks and the block's recent windows),
- * their count and the block's largest |v|. policy->gumbel must be NULL, as
- * for kve_prefill_select. */
+ * their count and the block's largest |v|, and V in float16 (len rows of d
+ * per slice). policy->gumbel must be NULL, as for kve_prefill_select. */
 size_t kve_prefill_attn_workspace_bytes(const kve_shape* shape,
                                         const kve_policy* policy, int32_t len);
 kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,

@@ -219,10 +219,11 @@ struct PrefillAttnLaunch {
   int32_t* list;         // [batch*H][query blocks][kmax] long-range keys
   int32_t* count;        // [batch*H][query blocks]
   uint32_t* vmax;        // [batch*H][query blocks] largest |v|, bf16 bits
+  uint16_t* v16;         // [batch*H][n][D] V in float16
   int kmax;              // max(k, 1)
 };
-size_t prefill_attn_ws_bytes(long long slices, int n, int kmax);
-// Carves list, count and vmax out of ws (prefill_attn_ws_bytes bytes).
+size_t prefill_attn_ws_bytes(long long slices, int n, int kmax, int D);
+// Carves list, count, vmax and v16 out of ws (prefill_attn_ws_bytes bytes).
 hipError_t launch_prefill_attn(PrefillAttnLaunch a, void* ws, hipStream_t s);
 size_t mlstm_state_floats(int D);  // 0 for an unsupported head_dim
 

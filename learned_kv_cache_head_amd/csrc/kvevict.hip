@@ -383,7 +383,7 @@ size_t kve_prefill_attn_workspace_bytes(const kve_shape* shape,
     return 0;
   const int k = policy->budget - policy->sinks - policy->window;
   return kve::prefill_attn_ws_bytes((long long)shape->batch * shape->n_kv_heads,
-                                    len, k > 0 ? k : 1);
+                                    len, k > 0 ? k : 1, shape->head_dim);
 }
 
 kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,

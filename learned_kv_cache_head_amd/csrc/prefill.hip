@@ -53,6 +53,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Two floats to packed float16 (round to nearest even), a in the low half:
+// one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+// Two packed bf16 to packed float16 (exact for magnitudes in [2^-17, 65280]).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack2h(bf16lo(w), bf16hi(w));
+}
 
 constexpr int kSortChunk = 4096;   // pairs sorted per workgroup
 constexpr int kQBlock = 64;        // query positions per attention workgroup
@@ -271,14 +285,17 @@ __global__ __launch_bounds__(kCutThreads) void cutoff_kernel(
 // ---------------------------------------------------------------------------
 // The same workgroup records the largest |v| of the block's V rows (the bf16
 // bit pattern without its sign), from which the attention chooses the
-// arithmetic of its P.V products for the whole slice.
+// arithmetic of its P.V products for the whole slice, and writes the rows in
+// float16 to v16 [slice][n][D], which the attention reads when the slice
+// fits float16 (rows of other slices are left unread).
 __global__ __launch_bounds__(256) void keylist_kernel(const int32_t* rank,
                                                       const int32_t* tau, int n,
                                                       int S, int W, int kmax,
                                                       int32_t* list,
                                                       int32_t* count,
                                                       const uint16_t* v, int D,
-                                                      int cap, uint32_t* vmax) {
+                                                      int cap, uint32_t* vmax,
+                                                      uint16_t* v16) {
   __shared__ int wsum[4];
   __shared__ uint32_t wmax[4];
   const int qb = blockIdx.x;
@@ -288,11 +305,23 @@ __global__ __launch_bounds__(256) void keylist_kernel(const int32_t* rank,
   {
     const int chunks = min(kQBlock, n - q0) * D / 8;  // 16-byte chunks
     const u32x4* vr = (const u32x4*)(v + ((size_t)slice * cap + q0) * D);
+    u32x4* vw = (u32x4*)(v16 + ((size_t)slice * n + q0) * D);
+    // At most 64 rows of 128 values: 4 chunks per thread, loaded together.
+    u32x4 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i < chunks) w[j] = vr[i];
+    }
     uint32_t m = 0;
-    for (int i = threadIdx.x; i < chunks; i += 256) {
-      const u32x4 w = vr[i];
-      const uint32_t a = w.x & 0x7fff7fffu, b = w.y & 0x7fff7fffu;
-      const uint32_t c = w.z & 0x7fff7fffu, d = w.w & 0x7fff7fffu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i >= chunks) break;
+      vw[i] = u32x4{bf16x2_to_f16x2(w[j].x), bf16x2_to_f16x2(w[j].y),
+                    bf16x2_to_f16x2(w[j].z), bf16x2_to_f16x2(w[j].w)};
+      const uint32_t a = w[j].x & 0x7fff7fffu, b = w[j].y & 0x7fff7fffu;
+      const uint32_t c = w[j].z & 0x7fff7fffu, d = w[j].w & 0x7fff7fffu;
       m = max(m, max(max(a >> 16, a & 0xffffu), max(b >> 16, b & 0xffffu)));
       m = max(m, max(max(c >> 16, c & 0xffffu), max(d >> 16, d & 0xffffu)));
     }
@@ -353,7 +382,6 @@ __device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
 }
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // Two floats to packed bf16 (round to nearest even), a in the low half:
 // one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -361,18 +389,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
                             __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-// Two floats to packed float16 (round to nearest even), a in the low half:
-// one v_cvt_pk_f16_f32.
-__device__ __forceinline__ uint32_t pack2h(float a, float b) {
-  return __builtin_bit_cast(uint32_t,
-                            __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
-}
-// Two packed bf16 to packed float16 (exact for magnitudes in [2^-17, 65280]).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  return pack2h(bf16lo(w), bf16hi(w));
-}
 // The value lane l ^ 32 (l ^ 16) of the wave holds. permlane32_swap
 // exchanges the upper half of its first operand with the lower half of its
 // second, so lane l finds its partner in the second result below lane 32
@@ -432,7 +448,7 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
   const int q0 = qb * kQB;
   const size_t slice = (size_t)b * p.H + h;
   const uint16_t* kc = (const uint16_t*)p.k + slice * p.cap * D;
-  const uint16_t* vc = (const uint16_t*)p.v + slice * p.cap * D;
+  const uint16_t* vc = (const uint16_t*)p.v + slice * p.cap * D;  // or v16
   const int32_t* rk = p.rank + slice * p.n;
   const int hq = p.H * p.G;
 
@@ -514,20 +530,14 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
       rreg = treg == 0x7fffffff ? 0x7fffffff : rk[treg];
     }
   };
-  // V is staged as float16 on the float16 path (see below).
-  auto stage = [&](int buf, auto f16) {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < kKB * CPR / 256; ++c) {
       const int idx = threadIdx.x + c * 256;
       const int row = idx / CPR;
       const int ch = idx % CPR;
       *(u32x4*)(&ks[buf][row * KSTR + ch * 8]) = kreg[c];
-      if constexpr (decltype(f16)::value)
-        *(u32x4*)(&vs[buf][row * VSTR + ch * 8]) =
-            u32x4{bf16x2_to_f16x2(vreg[c].x), bf16x2_to_f16x2(vreg[c].y),
-                  bf16x2_to_f16x2(vreg[c].z), bf16x2_to_f16x2(vreg[c].w)};
-      else
-        *(u32x4*)(&vs[buf][row * VSTR + ch * 8]) = vreg[c];
+      *(u32x4*)(&vs[buf][row * VSTR + ch * 8]) = vreg[c];
     }
     if (threadIdx.x < kKB) {
       rks[buf][threadIdx.x] = rreg;
@@ -537,10 +547,11 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
 
   // The P.V products of the slice. When its largest |v| lies in [2^-6,
   // 65280], every V element converts to float16 exactly (magnitudes of at
-  // least 2^-17) or within 2^-25 absolute (below), and each weight enters
-  // one float16 MFMA, rounded to 11 significant bits (weights are at most
-  // 2^kLazy, far inside float16's range). Otherwise (larger or tiny values,
-  // NaN, inf) V stays bf16 and each weight enters as two bf16 parts. The
+  // least 2^-17) or within 2^-25 absolute (below): the rows come from the
+  // key-list kernel's float16 copy, and each weight enters one float16 MFMA,
+  // rounded to 11 significant bits (weights are at most 2^kLazy, far inside
+  // float16's range). Otherwise (larger or tiny values, NaN, inf) V is read
+  // from the cache in bf16 and each weight enters as two bf16 parts. The
   // choice is uniform per slice, from the maxima the key-list kernel
   // recorded per query block.
   uint32_t vm = 0;
@@ -549,13 +560,14 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
     vm = max(vm, (uint32_t)__shfl_xor((int)vm, off));
   vm = __builtin_amdgcn_readfirstlane(vm);
   const bool fp16 = vm >= 0x3c80u && vm <= 0x477fu;  // bf16 2^-6 and 65280
+  if (fp16) vc = p.v16 + slice * p.n * D;
 
   auto run = [&](auto f16) {
   constexpr bool F16 = decltype(f16)::value;
   refill(0);
   __syncthreads();
   fetch(0);
-  stage(0, f16);
+  stage(0);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
@@ -710,7 +722,7 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
       }
     }
     // The other buffer was last read before the previous barrier.
-    if (kb + 1 < nkb) stage(buf ^ 1, f16);
+    if (kb + 1 < nkb) stage(buf ^ 1);
     __syncthreads();
   }
   };
@@ -765,13 +777,15 @@ hipError_t launch_prefill_select(const float* score, const float* lg, int H,
   return hipGetLastError();
 }
 
-// Workspace: the key lists (rounded up to 256 bytes), then one count and
-// one V maximum per (slice, query block).
-size_t prefill_attn_ws_bytes(long long slices, int n, int kmax) {
+// Workspace: the key lists, then one count and one V maximum per (slice,
+// query block), each part rounded up to 256 bytes, then the float16 copy of
+// V (n rows of D per slice).
+size_t prefill_attn_ws_bytes(long long slices, int n, int kmax, int D) {
   const long long nqb = (n + kQB - 1) / kQB;
   const size_t lists = (size_t)(slices * nqb) * kmax * sizeof(int32_t);
   const size_t blocks = (size_t)(slices * nqb) * sizeof(int32_t);
-  return (lists + 255) / 256 * 256 + 2 * blocks;
+  return (lists + 255) / 256 * 256 + (2 * blocks + 255) / 256 * 256 +
+         (size_t)slices * n * D * sizeof(uint16_t);
 }
 
 hipError_t launch_prefill_attn(PrefillAttnLaunch a, void* ws, hipStream_t s) {
@@ -781,9 +795,10 @@ hipError_t launch_prefill_attn(PrefillAttnLaunch a, void* ws, hipStream_t s) {
   a.list = (int32_t*)ws;
   a.count = (int32_t*)((char*)ws + lists);
   a.vmax = (uint32_t*)(a.count + blocks);
+  a.v16 = (uint16_t*)((char*)ws + lists + (2 * blocks * sizeof(int32_t) + 255) / 256 * 256);
   hipLaunchKernelGGL(keylist_kernel, dim3(nqb, a.batch * a.H), dim3(256), 0, s,
                      a.rank, a.tau, a.n, a.S, a.W, a.kmax, a.list, a.count,
-                     (const uint16_t*)a.v, a.D, a.cap, a.vmax);
+                     (const uint16_t*)a.v, a.D, a.cap, a.vmax, a.v16);
   const dim3 grid(nqb, a.H * a.nsub, a.batch);
 #define KVE_PA(DD, GG)                                                       \
   if (a.D == DD && a.gsub == GG) {                                           \

@@ -369,12 +369,14 @@ def test_prefill_workspace_and_validation():
     assert attn(100, shape=_shape(capacity=10000, kv_dtype=kve.F32)) == 4
     assert attn(9000, ws_bytes=100) == 5
     # key lists: k = 892 ints per 64-position query block and slice, then
-    # one count and one V maximum per block
+    # one count and one V maximum per block, then V in float16 (d = 128)
     wsb = lib.kve_prefill_attn_workspace_bytes(ctypes.byref(s), ctypes.byref(p),
                                                9000)
     nqb = (9000 + 63) // 64
     lists = 2 * 8 * nqb * 892 * 4
-    assert wsb == (lists + 255) // 256 * 256 + 2 * (2 * 8 * nqb * 4)
+    blocks = 2 * (2 * 8 * nqb * 4)
+    assert wsb == ((lists + 255) // 256 * 256 + (blocks + 255) // 256 * 256 +
+                   2 * 8 * 9000 * 128 * 2)
     # stochastic eviction noise: the prefill ranks are deterministic only
     p.gumbel = FAKE
     assert sel(100) == 4
