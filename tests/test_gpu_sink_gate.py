@@ -58,17 +58,13 @@ def test_sink_gate_scores(case):
     assert np.all(got[:, :, s0 + rows:] == 12345.0)
 
 
-def test_sink_gate_step_end_to_end():
-    """kve_step with the sink gate on hidden states (buffered scoring): the
-    Qwen2.5-14B layer shape cut to a 4096-token prompt, B = 1024, W = 128,
-    L = 64, 200 steps."""
+def run_e2e_sink_gate(w, seed=0, layer=0, check_stride=16):
+    """kve_step with the sink gate on hidden states (buffered scoring):
+    retained sets, scores at every eviction and attention against the
+    oracle's policy loop. Returns the number of evictions."""
     import torch
     k = kve()
     dev = torch.device("cuda")
-    w = syn.workload(5, n0=4096, budget=1024, window=128, steps=200,
-                     scorer="sink_gate")
-    print(f"[sink-gate-step] {w.name}", flush=True)
-    seed, layer = 0, 0
     ctx = syn.initial_context(w, seed, layer)
     wts = syn.draw_sink_gate_weights(w, seed, layer)
     s0 = oracle_sink_gate_scores(ctx["hidden0"].f64, wts, w.n_kv, w.group)
@@ -89,9 +85,11 @@ def test_sink_gate_step_end_to_end():
                        device=dev)
     ws = k.alloc_workspace(shape, w.capacity, dev)
     tr.prefill()
-    k.kve_select_evict(shape, pol, cache, w.n0, w.budget, keep)
-    k.kve_compact(shape, cache, w.n0, keep, w.budget)
-    n = w.budget
+    n = w.n0
+    if w.n0 > w.budget:
+        k.kve_select_evict(shape, pol, cache, w.n0, w.budget, keep)
+        k.kve_compact(shape, cache, w.n0, keep, w.budget)
+        n = w.budget
     tr.check_and_sync(cache.pos[:, :, :n].cpu().numpy().astype(np.int64))
     state = k.DecodeState(n, n, w.n0)
     hbuf = torch.zeros((w.batch, w.evict_len, w.hidden), dtype=torch.bfloat16,
@@ -108,7 +106,7 @@ def test_sink_gate_step_end_to_end():
                    ws, hidden_new=st["hidden_new"].torch(dev), hidden_buf=hbuf)
         tr.step(w.n0 + i, st["k_new"].f64, st["v_new"].f64, sn)
         evictions += state.evicted
-        if i % 16 and not state.evicted and i != w.steps - 1:
+        if i % check_stride and not state.evicted and i != w.steps - 1:
             continue
         torch.cuda.synchronize()
         gpu_pos = cache.pos[:, :, :state.len].cpu().numpy().astype(np.int64)
@@ -120,7 +118,17 @@ def test_sink_gate_step_end_to_end():
             np.testing.assert_allclose(gs, ref, rtol=0, atol=SINK_GATE_ATOL)
         ref_out, _ = tr.lay.attend(st["q"].f64)
         attn_close(out.cpu().double().numpy(), ref_out, f"step {i}")
-    assert evictions == 3
+    return evictions
+
+
+def test_sink_gate_step_end_to_end():
+    """kve_step with the sink gate on hidden states (buffered scoring): the
+    Qwen2.5-14B layer shape cut to a 4096-token prompt, B = 1024, W = 128,
+    L = 64, 200 steps."""
+    w = syn.workload(5, n0=4096, budget=1024, window=128, steps=200,
+                     scorer="sink_gate")
+    print(f"[sink-gate-step] {w.name}", flush=True)
+    assert run_e2e_sink_gate(w) == 3
 
 
 def test_sink_gate_full_prompt_sampled():
