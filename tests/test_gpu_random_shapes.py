@@ -87,3 +87,20 @@ def test_random_gate_end_to_end(case):
     w = syn.workload(5, layers=1, **case)
     evictions, _ = run_e2e(w, seed=4)
     assert evictions >= 2
+
+
+DECAY_CASES = _cases(n=8, seed=20261205)
+
+
+@pytest.mark.parametrize("case", DECAY_CASES, ids=[
+    f"b{c['batch']}h{c['n_kv']}g{c['group']}d{c['head_dim']}{c['kv_dtype']}"
+    f"-S{c['sinks']}W{c['window']}B{c['budget']}L{c['evict_len']}"
+    for c in DECAY_CASES])
+def test_random_shape_end_to_end_with_decay(case):
+    """The same loop with temporal decay in the ranking (one decay rate
+    per KV head, from 0.9 to 1 - 1e-6)."""
+    print(f"[random-decay] {case}", flush=True)
+    w = syn.workload(2, layers=1, **case)
+    gammas = np.linspace(0.9, 1 - 1e-6, w.n_kv)
+    evictions, _ = run_e2e(w, seed=7, gammas=gammas)
+    assert evictions >= 2
