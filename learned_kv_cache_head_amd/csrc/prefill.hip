@@ -36,13 +36,13 @@
 // (v_mfma_f32_16x16x32_bf16), so a lane's accumulators hold 8 keys of one
 // query column: those are exactly the operand of P^T that O^T = V^T P^T
 // needs, and the online-softmax state is one value per lane and head.
-// O^T = V^T P^T runs in float16 (v_mfma_f32_16x16x32_f16: V converted
-// exactly when staged, each weight rounded to 11 significant bits) for
-// slices whose V fits float16, else in bf16 with each weight as two parts
-// (its rounding and the remainder, about 17 bits), two MFMAs into one
-// float32 accumulator. The key-list kernel records each query block's
-// largest |v| for that choice. Workgroups are ordered so that each XCD
-// takes whole slices, which share key rows in its L2.
+// O^T = V^T P^T runs in float16 (v_mfma_f32_16x16x32_f16 on a float16 copy
+// of V, each weight rounded to 11 significant bits) for slices whose V fits
+// float16, else in bf16 with each weight as two parts (its rounding and the
+// remainder, about 17 bits), two MFMAs into one float32 accumulator. The
+// key-list kernel writes the float16 copy of its query block's V rows and
+// records their largest |v| for that choice. Workgroups are ordered so that
+// each XCD takes whole slices, which share key rows in its L2.
 #include "kve_internal.h"
 
 namespace kve {
