@@ -52,6 +52,12 @@
  * slots [0, len), with distinct positions in any slot order: new tokens are
  * appended at slot len, and compaction moves entries from the end into the
  * slots it frees.
+ * Alignment: kernels move rows with 16-byte vector accesses, so K, V, q,
+ * out, k_new, v_new, hidden states, scorer state, the scorer's w1 and
+ * workspaces must be 16-byte aligned, and float32 / int32 arrays (score,
+ * pos, lse, keep_slots, rank, tau, the scorer's other weights) 4-byte
+ * aligned (PyTorch allocations are 512-byte aligned); a
+ * misaligned pointer is KVE_ERR_INVALID_ARG.
  */
 #ifndef KVEVICT_H
 #define KVEVICT_H

@@ -48,8 +48,18 @@ kve_status check_policy(const kve_policy* p) {
   return KVE_OK;
 }
 
+// Kernels move rows with 16-byte vector accesses (some straight into LDS),
+// so buffers of K, V, q, output rows, hidden states and workspaces must be
+// 16-byte aligned, float32 and int32 arrays 4-byte aligned. Null passes
+// (nullability is checked where it matters).
+bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool a4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
 kve_status check_cache(const kve_cache* c) {
   if (!c || !c->k || !c->v || !c->score || !c->pos) return KVE_ERR_INVALID_ARG;
+  if (!a16(c->k) || !a16(c->v) || !a4(c->score) || !a4(c->pos) ||
+      !a16(c->scorer_state))
+    return KVE_ERR_INVALID_ARG;
   return KVE_OK;
 }
 
@@ -178,6 +188,8 @@ kve_status attn_impl(const kve_shape* shape, const kve_cache* cache, int len,
 
 kve_status check_scorer(const kve_shape* shape, const kve_scorer* sc) {
   if (!sc || !sc->w1) return KVE_ERR_INVALID_ARG;
+  if (!a16(sc->w1) || !a4(sc->b1) || !a4(sc->w2) || !a4(sc->b2))
+    return KVE_ERR_INVALID_ARG;
   if (sc->kind == KVE_SCORER_MLP_KV) {
     if (sc->in_dim != 2 * shape->head_dim) return KVE_ERR_UNSUPPORTED;
     if (sc->hidden < 1 || sc->hidden > 256) return KVE_ERR_UNSUPPORTED;
@@ -362,6 +374,7 @@ kve_status kve_prefill_select(const kve_shape* shape, const kve_policy* policy,
   if (policy->gumbel) return KVE_ERR_UNSUPPORTED;  // deterministic ranks only
   if ((st = check_cache(cache)) != KVE_OK) return st;
   if (!rank || !tau) return KVE_ERR_INVALID_ARG;
+  if (!a4(rank) || !a4(tau) || !a16(ws)) return KVE_ERR_INVALID_ARG;
   if (len < 1) return KVE_ERR_INVALID_ARG;
   if (len > shape->capacity) return KVE_ERR_CAPACITY;
   if (len > kve::kMaxPrefillLen) return KVE_ERR_UNSUPPORTED;
@@ -397,6 +410,8 @@ kve_status kve_prefill_attn(const kve_shape* shape, const kve_policy* policy,
   if (policy->gumbel) return KVE_ERR_UNSUPPORTED;  // deterministic ranks only
   if ((st = check_cache(cache)) != KVE_OK) return st;
   if (!rank || !tau || !q || !out) return KVE_ERR_INVALID_ARG;
+  if (!a4(rank) || !a4(tau) || !a16(q) || !a16(out) || !a4(lse) || !a16(ws))
+    return KVE_ERR_INVALID_ARG;
   if (len < 1) return KVE_ERR_INVALID_ARG;
   if (len > shape->capacity) return KVE_ERR_CAPACITY;
   if (len > kve::kMaxPrefillLen) return KVE_ERR_UNSUPPORTED;
@@ -468,6 +483,7 @@ kve_status kve_append(const kve_shape* shape, kve_cache* cache, int32_t slot,
   if (st != KVE_OK) return st;
   if ((st = check_cache(cache)) != KVE_OK) return st;
   if (!k_new || !v_new) return KVE_ERR_INVALID_ARG;
+  if (!a16(k_new) || !a16(v_new)) return KVE_ERR_INVALID_ARG;
   if (slot < 0 || slot >= shape->capacity) return KVE_ERR_CAPACITY;
   return from_hip(kve::launch_append(
       cache->k, cache->v, cache->pos, shape->batch, shape->n_kv_heads,
@@ -487,6 +503,7 @@ kve_status kve_score(const kve_shape* shape, const kve_scorer* scorer,
   const bool gate = scorer->kind == KVE_SCORER_GATE_HIDDEN ||
                     scorer->kind == KVE_SCORER_SINK_GATE;
   if (gate != (hidden != nullptr)) return KVE_ERR_INVALID_ARG;
+  if (!a16(hidden)) return KVE_ERR_INVALID_ARG;
   if (scorer->kind == KVE_SCORER_MLSTM && !cache->scorer_state)
     return KVE_ERR_INVALID_ARG;
   const long long stride = (long long)(slot_end - slot_begin) * scorer->in_dim;
@@ -502,7 +519,7 @@ kve_status kve_select_evict(const kve_shape* shape, const kve_policy* policy,
   if (st != KVE_OK) return st;
   if ((st = check_policy(policy)) != KVE_OK) return st;
   if ((st = check_cache(cache)) != KVE_OK) return st;
-  if (!keep_slots) return KVE_ERR_INVALID_ARG;
+  if (!keep_slots || !a4(keep_slots)) return KVE_ERR_INVALID_ARG;
   if (len < 0 || n_keep < 0) return KVE_ERR_INVALID_ARG;
   if (len > shape->capacity) return KVE_ERR_CAPACITY;
   if (n_keep > len) return KVE_ERR_POLICY;
@@ -522,7 +539,7 @@ kve_status kve_compact(const kve_shape* shape, kve_cache* cache, int32_t len,
   kve_status st = check_shape(shape);
   if (st != KVE_OK) return st;
   if ((st = check_cache(cache)) != KVE_OK) return st;
-  if (!keep_slots) return KVE_ERR_INVALID_ARG;
+  if (!keep_slots || !a4(keep_slots)) return KVE_ERR_INVALID_ARG;
   if (len < 0 || n_keep < 0 || n_keep > len) return KVE_ERR_INVALID_ARG;
   if (len > shape->capacity) return KVE_ERR_CAPACITY;
   if (n_keep == 0) return KVE_OK;
@@ -540,6 +557,7 @@ kve_status kve_decode_attn(const kve_shape* shape, const kve_cache* cache,
   if (st != KVE_OK) return st;
   if ((st = check_cache(cache)) != KVE_OK) return st;
   if (!q || !out) return KVE_ERR_INVALID_ARG;
+  if (!a16(q) || !a16(out) || !a4(lse) || !a16(ws)) return KVE_ERR_INVALID_ARG;
   if (len < 1) return KVE_ERR_INVALID_ARG;
   if (len > shape->capacity) return KVE_ERR_CAPACITY;
   return attn_impl(shape, cache, len, q, out, lse, ws, ws_bytes, -1, 0,
@@ -588,6 +606,9 @@ kve_status step_impl(const kve_shape* shape, const kve_policy* policy,
   if ((st = check_cache(cache)) != KVE_OK) return st;
   if ((st = check_scorer(shape, scorer)) != KVE_OK) return st;
   if (!state || !k_new || !v_new || !q || !out || !keep_slots)
+    return KVE_ERR_INVALID_ARG;
+  if (!a16(k_new) || !a16(v_new) || !a16(q) || !a16(out) || !a4(lse) ||
+      !a4(keep_slots) || !a16(hidden_new) || !a16(hidden_buf) || !a16(ws))
     return KVE_ERR_INVALID_ARG;
   const int B = policy->budget, L = policy->evict_len;
   if ((long long)B + L > shape->capacity) return KVE_ERR_CAPACITY;

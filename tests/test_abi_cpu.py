@@ -484,3 +484,38 @@ def test_library_shares_torchs_hip_runtime():
     assert out.returncode == 0, out.stderr
     n = int(out.stdout.split()[0])
     assert n == 1, out.stdout
+
+
+def test_misaligned_pointers_are_rejected():
+    """Rows move with 16-byte vector accesses: a misaligned row buffer (or a
+    float32 / int32 array off its 4-byte grid) is an argument error, reported
+    before any launch."""
+    lib, s = _lib(), _shape()
+    att = lib.kve_decode_attn
+    good = _cache()
+    assert att(ctypes.byref(s), ctypes.byref(good), 1000, FAKE + 8, FAKE,
+               None, FAKE, 1 << 20, None) == 1                 # q
+    assert att(ctypes.byref(s), ctypes.byref(good), 1000, FAKE, FAKE + 4,
+               None, FAKE, 1 << 20, None) == 1                 # out
+    assert att(ctypes.byref(s), ctypes.byref(good), 1000, FAKE, FAKE,
+               FAKE + 2, FAKE, 1 << 20, None) == 1             # lse
+    assert att(ctypes.byref(s), ctypes.byref(good), 1000, FAKE, FAKE,
+               None, FAKE + 8, 1 << 20, None) == 1             # workspace
+    for c in (kve._Cache(FAKE + 8, FAKE, FAKE, FAKE),
+              kve._Cache(FAKE, FAKE + 2, FAKE, FAKE),
+              kve._Cache(FAKE, FAKE, FAKE + 2, FAKE),
+              kve._Cache(FAKE, FAKE, FAKE, FAKE + 1)):
+        assert att(ctypes.byref(s), ctypes.byref(c), 1000, FAKE, FAKE, None,
+                   FAKE, 1 << 20, None) == 1
+    p = kve._Policy(1024, 4, 128, 128)
+    assert lib.kve_select_evict(ctypes.byref(s), ctypes.byref(p),
+                                ctypes.byref(good), 1152, 1024, FAKE + 2,
+                                None) == 1
+    assert lib.kve_compact(ctypes.byref(s), ctypes.byref(good), 1152,
+                           FAKE + 2, 1024, None) == 1
+    assert lib.kve_append(ctypes.byref(s), ctypes.byref(good), 5, 5, FAKE + 8,
+                          FAKE, None) == 1
+    sc = kve._Scorer(kve.SCORER_MLP_KV, 0, kve.BF16, 256, 64, FAKE + 8, None,
+                     FAKE, None, 0, 0)
+    assert lib.kve_score(ctypes.byref(s), ctypes.byref(sc), ctypes.byref(good),
+                         0, 10, None, None) == 1
