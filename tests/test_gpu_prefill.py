@@ -121,6 +121,8 @@ ATTN_CASES = [
     (1, 1, 8, 128, 130, 0, 1, 20),
     (1, 2, 4, 128, 100, 4, 16, 200),     # k >= n: causal attention
     (1, 1, 3, 128, 1, 4, 8, 16),         # one token
+    (1, 2, 4, 128, 150, 2, 0, 30),       # W = 0: no window, a query keeps
+    (1, 1, 2, 64, 100, 0, 0, 10),        #   itself only among its top k
 ]
 
 
