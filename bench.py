@@ -122,6 +122,101 @@ def achievable_read_gbps(dev, gib: int = 4) -> float:
     return best
 
 
+def issue_probe(dev) -> dict:
+    """How far MFMAs and vector ALU work overlap on one SIMD (libkvebench.so,
+    issue_kernel): workgroups of 8 waves, waves w and w + 4 on one SIMD.
+    Per SIMD-iteration a wave running MFMAs issues 8 independent
+    v_mfma_f32_16x16x32_bf16; a vector wave 32 float32 FMAs (or 32 v_exp_f32)
+    over 8 chains. Reports ns per SIMD-iteration; when the two overlap, the
+    combined modes take the longer of the two parts, when they serialise,
+    their sum."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "learned_kv_cache_head_amd", "_lib",
+                                   "libkvebench.so"))
+    lib.kvebench_issue.restype = ctypes.c_int
+    lib.kvebench_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, iters = 4 * cus, 4000
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    simd_iters = blocks * 4 * iters / (cus * 4)
+    modes = [("mfma", 1), ("fma", 2), ("mfma_and_fma_two_waves", 3),
+             ("mfma_and_fma_one_wave", 5), ("exp", 10),
+             ("mfma_and_exp_two_waves", 11), ("mfma_and_exp_one_wave", 13)]
+    res = {}
+    for name, mode in modes:
+        best = None
+        for _ in range(3):
+            e0, e1 = (torch.cuda.Event(enable_timing=True),
+                      torch.cuda.Event(enable_timing=True))
+            e0.record()
+            rc = lib.kvebench_issue(mode, blocks, iters, out.data_ptr(), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"kvebench_issue failed ({rc})")
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        res[name] = round(best * 1e6 / simd_iters, 1)
+    return {"ns_per_simd_iteration": res,
+            "per_iteration": {"mfma": "8 x v_mfma_f32_16x16x32_bf16",
+                              "fma": "32 x v_fma_f32", "exp": "32 x v_exp_f32"},
+            "workgroups": blocks, "iterations": iters}
+
+
+def library_reference(dev) -> dict:
+    """The vendor libraries behind torch at the shapes of two kernels here,
+    as context for their MFMA fractions: the bf16 GEMM of the sink gate's
+    projections (131072 x 5120 hidden states by 768 weight rows) and torch's
+    fused attention (scaled_dot_product_attention) over batch 8, 32 heads,
+    8192 positions, d 128, dense causal and dense non-causal, in TFLOP/s
+    (best of three)."""
+    import torch
+    import torch.nn.functional as F
+    peak = MFMA_BF16_PEAK_TFLOPS
+
+    def best_ms(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = (torch.cuda.Event(enable_timing=True),
+                      torch.cuda.Event(enable_timing=True))
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    g = torch.Generator(device=dev).manual_seed(5)
+    x = torch.randn((131072, 5120), generator=g, device=dev).to(torch.bfloat16)
+    w = torch.randn((768, 5120), generator=g, device=dev).to(torch.bfloat16)
+    ms = best_ms(lambda: x @ w.t())
+    fl = 2 * 131072 * 768 * 5120
+    out = {"gemm_131072x768x5120_bf16": {"ms": round(ms, 3),
+                                          "tflops": round(fl / ms / 1e9, 1),
+                                          "frac": round(fl / ms / 1e9 / peak, 3)}}
+    del x, w
+    b, h, n, d = 8, 32, 8192, 128
+    q, k, v = (torch.randn((b, h, n, d), generator=g, device=dev)
+               .to(torch.bfloat16) for _ in range(3))
+    for causal in (True, False):
+        ms = best_ms(lambda: F.scaled_dot_product_attention(q, k, v,
+                                                            is_causal=causal))
+        pairs = n * (n + 1) // 2 if causal else n * n
+        fl = 4 * d * pairs * b * h
+        out[f"sdpa_b8_h32_n8192_d128_{'causal' if causal else 'dense'}"] = {
+            "ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
+            "frac": round(fl / ms / 1e9 / peak, 3)}
+    del q, k, v
+    torch.cuda.empty_cache()
+    return out
+
+
 def calib_copy(dev) -> None:
     """A plain elementwise copy of known size (1 GiB read, 1 GiB written),
     the reference that scales the HBM byte counters."""
@@ -992,6 +1087,11 @@ def main() -> int:
                     help="time one layer's prompt scoring with the low-rank "
                          "sink-attention gate (Qwen2.5-14B, 131072 tokens) "
                          "instead of decode")
+    ap.add_argument("--hw-reference", action="store_true",
+                    help="print reference measurements instead of a bench "
+                         "line: the MFMA / vector-ALU issue probe and the "
+                         "vendor libraries' GEMM and fused attention at the "
+                         "sink-gate and prefill shapes")
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="copy this many MB before every timed step (not "
                          "timed) so the cache is read from HBM, not the "
@@ -1039,6 +1139,12 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.hw_reference:
+        log("hardware references: issue probe, vendor GEMM and attention")
+        print(json.dumps({"issue_probe": issue_probe(dev),
+                          "library_reference": library_reference(dev)}),
+              flush=True)
+        return 0
     if args.sink_gate:
         log("sink gate: qwen2.5-14b layer, 131072-token prompt")
         print(json.dumps(run_sink_gate(args, dev)), flush=True)
