@@ -519,3 +519,33 @@ def test_misaligned_pointers_are_rejected():
                      FAKE, None, 0, 0)
     assert lib.kve_score(ctypes.byref(s), ctypes.byref(sc), ctypes.byref(good),
                          0, 10, None, None) == 1
+
+
+def test_bench_library_exports_and_rejects_bad_arguments():
+    """libkvebench.so (the benchmark's read ceiling and issue probe) exports
+    its three calls, and each rejects bad arguments on the host, before any
+    launch."""
+    import torch  # noqa: F401  (the library binds torch's HIP runtime)
+    path = os.path.join(os.path.dirname(kve.__file__), "_lib", "libkvebench.so")
+    lib = ctypes.CDLL(path)
+    for name in ("kvebench_read", "kvebench_read_blocks", "kvebench_issue"):
+        assert hasattr(lib, name), name
+    lib.kvebench_read.restype = ctypes.c_int
+    lib.kvebench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvebench_read_blocks.restype = ctypes.c_size_t
+    lib.kvebench_read_blocks.argtypes = [ctypes.c_size_t]
+    lib.kvebench_issue.restype = ctypes.c_int
+    lib.kvebench_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    # one workgroup streams 1 MiB
+    assert lib.kvebench_read_blocks(1 << 20) == 1
+    assert lib.kvebench_read_blocks((1 << 20) + 16) == 2
+    assert lib.kvebench_read(None, 1 << 20, FAKE, None) == 1
+    assert lib.kvebench_read(FAKE, 24, FAKE, None) == 1        # not 16-byte sized
+    assert lib.kvebench_read(FAKE + 8, 64, FAKE, None) == 1    # misaligned
+    for mode in (0, 4, 6, 7, 8, 9, 12, 14, 15, 16):            # no such mode
+        assert lib.kvebench_issue(mode, 1, 1, FAKE, None) == 1
+    assert lib.kvebench_issue(1, 0, 1, FAKE, None) == 1
+    assert lib.kvebench_issue(1, 1, 0, FAKE, None) == 1
+    assert lib.kvebench_issue(1, 1, 1, None, None) == 1
