@@ -216,6 +216,7 @@ struct PrefillAttnLaunch {
   float* lse;            // [batch][H*G][n] or null
   int batch, H, G, D, cap, n, S, W;
   int gsub, nsub;        // query heads per workgroup, head subsets per KV head
+  int g0;                // first query head (of G) the launch covers
   int32_t* list;         // [batch*H][query blocks][kmax] long-range keys
   int32_t* count;        // [batch*H][query blocks]
   uint32_t* vmax;        // [batch*H][query blocks] largest |v|, bf16 bits

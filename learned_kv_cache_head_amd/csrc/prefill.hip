@@ -29,8 +29,9 @@
 //
 // Attention: a flash-attention forward on MFMA (float32 accumulation) with
 // the Eq. 26 predicate applied to each logit. A workgroup owns 64 query
-// positions of one KV head and up to 2 of its query heads (two waves per
-// SIMD fit); the 4 waves take 16 positions each. Each 64-key block of K and
+// positions of one KV head and 2 of its query heads (two waves per SIMD
+// fit; an odd last head goes to a second launch, one head per workgroup);
+// the 4 waves take 16 positions each. Each 64-key block of K and
 // V is staged in LDS, row-major, and shared by all of them; the V^T operand
 // comes from LDS transpose reads. The kernel computes S^T = K Q^T
 // (v_mfma_f32_16x16x32_bf16), so a lane's accumulators hold 8 keys of one
@@ -460,7 +461,7 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
   bf16x8_t qf[GS][KS];
 #pragma unroll
   for (int gi = 0; gi < GS; ++gi) {
-    const int g = min(sub * GS + gi, p.G - 1);
+    const int g = min(p.g0 + sub * GS + gi, p.G - 1);
     const uint16_t* qr =
         (const uint16_t*)p.q + (((size_t)b * hq + h * p.G + g) * p.n + qc) * D;
 #pragma unroll
@@ -734,7 +735,7 @@ void prefill_attn_kernel(PrefillAttnLaunch p) {
   // Epilogue: normalise and store this lane's column (4 rows per d tile).
 #pragma unroll
   for (int gi = 0; gi < GS; ++gi) {
-    const int g = sub * GS + gi;
+    const int g = p.g0 + sub * GS + gi;
     float l = lrun[gi];
     l += lane_xor16(l);
     l += lane_xor32(l);
@@ -799,15 +800,28 @@ hipError_t launch_prefill_attn(PrefillAttnLaunch a, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(keylist_kernel, dim3(nqb, a.batch * a.H), dim3(256), 0, s,
                      a.rank, a.tau, a.n, a.S, a.W, a.kmax, a.list, a.count,
                      (const uint16_t*)a.v, a.D, a.cap, a.vmax, a.v16);
-  const dim3 grid(nqb, a.H * a.nsub, a.batch);
-#define KVE_PA(DD, GG)                                                       \
-  if (a.D == DD && a.gsub == GG) {                                           \
-    hipLaunchKernelGGL((prefill_attn_kernel<DD, GG>), grid, dim3(256), 0, s, a); \
-    return hipGetLastError();                                                \
-  }
-  KVE_PA(128, 1) KVE_PA(128, 2) KVE_PA(64, 1) KVE_PA(64, 2)
-#undef KVE_PA
-  return hipErrorInvalidValue;
+  if (a.D != 128 && a.D != 64) return hipErrorInvalidValue;
+  // Query heads in pairs (two per workgroup), and an odd last head in a
+  // launch of its own with one head per workgroup, so that no workgroup
+  // computes a head twice.
+  auto launch = [&](int gs, int nsub, int g0) {
+    PrefillAttnLaunch b = a;
+    b.gsub = gs;
+    b.nsub = nsub;
+    b.g0 = g0;
+    const dim3 grid(nqb, b.H * nsub, b.batch);
+    if (b.D == 128 && gs == 2)
+      hipLaunchKernelGGL((prefill_attn_kernel<128, 2>), grid, dim3(256), 0, s, b);
+    else if (b.D == 128)
+      hipLaunchKernelGGL((prefill_attn_kernel<128, 1>), grid, dim3(256), 0, s, b);
+    else if (gs == 2)
+      hipLaunchKernelGGL((prefill_attn_kernel<64, 2>), grid, dim3(256), 0, s, b);
+    else
+      hipLaunchKernelGGL((prefill_attn_kernel<64, 1>), grid, dim3(256), 0, s, b);
+  };
+  if (a.G / 2 > 0) launch(2, a.G / 2, 0);
+  if (a.G % 2) launch(1, 1, a.G - 1);
+  return hipGetLastError();
 }
 
 }  // namespace kve
