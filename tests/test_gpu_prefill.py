@@ -116,7 +116,9 @@ ATTN_CASES = [
     # b, H, G, d, n, S, W, k
     (1, 2, 4, 128, 200, 4, 16, 40),
     (2, 1, 1, 128, 45, 2, 3, 10),
-    (1, 2, 5, 128, 333, 4, 32, 64),      # G = 5: two head subsets
+    (1, 2, 5, 128, 333, 4, 32, 64),      # G = 5: two head pairs, then the
+                                         #   fifth head in a launch of its own
+    (2, 2, 3, 64, 201, 3, 24, 50),       # G = 3, d = 64: a pair and one head
     (1, 2, 2, 64, 257, 1, 8, 100),
     (1, 1, 8, 128, 130, 0, 1, 20),
     (1, 2, 4, 128, 100, 4, 16, 200),     # k >= n: causal attention
