@@ -1,6 +1,7 @@
 """bench.py prints one JSON line with every field of its contract in each of
 its modes (decode with the per-step cycle fold and the attention roofline,
-the oracle's CPU baseline, prefill, the sink gate), run here with few steps."""
+the oracle's CPU baseline, prefill at both prefill shapes, the sink gate),
+run here with few steps; --hw-reference prints its reference measurements."""
 import json
 import os
 import subprocess
@@ -30,6 +31,9 @@ MODES = [
                  "--no-cpu-baseline"], True, False),
     ("sink-gate", ["--sink-gate", "--steps", "2", "--warmup", "1",
                    "--no-cpu-baseline"], True, False),
+    ("prefill-14b", ["--prefill", "--workload", "qwen2.5-14b-48layer-131k-gate",
+                     "--steps", "1", "--warmup", "0", "--no-cpu-baseline"],
+     True, False),
 ]
 
 
@@ -62,3 +66,26 @@ def test_bench_line_contract(mode):
         assert c["kind"] == "oracle" and c["value"] > 0
     else:
         assert d["cpu_baseline"] is None
+
+
+def test_hw_reference_line():
+    """--hw-reference prints one JSON object: the issue probe's times per
+    mode and the vendor libraries' GEMM and attention rates."""
+    print("[bench-line] hw-reference", flush=True)
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--hw-reference"],
+                       capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert p.returncode == 0, p.stderr[-2000:]
+    lines = [l for l in p.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, p.stdout
+    d = json.loads(lines[0])
+    probe = d["issue_probe"]["ns_per_simd_iteration"]
+    for mode in ("mfma", "fma", "mfma_and_fma_two_waves",
+                 "mfma_and_fma_one_wave", "exp", "mfma_and_exp_two_waves",
+                 "mfma_and_exp_one_wave"):
+        assert probe[mode] > 0, mode
+    # two kinds of work on one SIMD never take less than the longer part
+    assert probe["mfma_and_fma_two_waves"] >= 0.95 * max(probe["mfma"],
+                                                          probe["fma"])
+    for name, r in d["library_reference"].items():
+        assert r["ms"] > 0 and 0 < r["frac"] <= 1.0, name
